@@ -1,0 +1,157 @@
+"""Pins of the oracle's MXFP8 and FP8-KV quantisers: hand-worked examples,
+the scale rule's defining inequalities, half-step error bounds, power-of-two
+invariance, and the record / page layouts."""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import formats, pools, quant
+from sparse_attention_decode_topk_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf16(x):
+    return synth.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def test_mx_golden_examples():
+    g = np.ones(32, dtype=np.float32); g[5] = 3.0
+    codes, e8 = quant.mxfp8_quant(bf16(g)[None])
+    assert e8[0, 0] == 120 and codes[0, 5] == 0x7C
+    assert np.all(np.delete(codes[0], 5) == 0x70)
+    codes, e8 = quant.mxfp8_quant(bf16(np.zeros(32))[None])
+    assert e8[0, 0] == 127 and np.all(codes == 0)
+    codes, e8 = quant.mxfp8_quant(bf16(np.full(32, 448.0))[None])
+    assert e8[0, 0] == 127 and np.all(codes == 0x7E)
+    codes, e8 = quant.mxfp8_quant(bf16(np.full(32, 0.875))[None])
+    assert e8[0, 0] == 118 and np.all(codes == 0x7E)
+
+
+def test_kv_golden_examples():
+    t = np.full(576, 0.25, dtype=np.float32)
+    t[:128] = 0.5; t[9] = -7.0
+    rec = quant.kv_quant(bf16(t)[None])[0]
+    assert rec[512:516].tobytes() == bytes([0x00, 0x00, 0x80, 0x3C])
+    assert rec[9] == 0xFE and np.all(np.delete(rec[:128], 9) == 0x60)
+    z = np.zeros(576, dtype=np.float32)
+    rec = quant.kv_quant(bf16(z)[None])[0]
+    assert rec[512:516].tobytes() == np.float32(1.0).tobytes()
+    assert np.all(rec[:512] == 0)
+
+
+def _random_bf16(rng, shape, spread=True):
+    x = rng.standard_normal(shape).astype(np.float32)
+    if spread:   # per-row magnitudes spanning many binades
+        x *= np.float32(2.0) ** rng.integers(-30, 30, size=shape[:-1] + (1,)).astype(np.float32)
+    return bf16(x)
+
+
+def test_mx_scale_rule_and_error_bound():
+    rng = np.random.default_rng(1)
+    xb = _random_bf16(rng, (2000, 128))
+    codes, e8 = quant.mxfp8_quant(xb)
+    x = formats.bf16_decode(xb).reshape(2000, 4, 32)
+    amax = np.abs(x).max(axis=2)
+    e = e8.astype(np.int64) - 127
+    X = np.ldexp(1.0, e)
+    # defining inequalities of the scale: in range, and minimal
+    assert np.all(amax <= 448 * X)
+    assert np.all(amax > 448 * X / 2)
+    # no saturation, and every element within half an E4M3 step
+    y = x / X[:, :, None]
+    deq = quant.mxfp8_dequant(codes, e8).reshape(2000, 4, 32)
+    assert np.all(np.abs(deq - x) <= formats.e4m3_half_ulp(np.abs(y)) * X[:, :, None])
+
+
+def test_mx_power_of_two_invariance():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((500, 128)).astype(np.float32)
+    xb = bf16(x)
+    c0, e0 = quant.mxfp8_quant(xb)
+    for k in (-5, 2, 9):
+        ck, ek = quant.mxfp8_quant(bf16(x * np.float32(2.0 ** k)))
+        assert np.array_equal(ck, c0)
+        assert np.array_equal(ek.astype(int), e0.astype(int) + k)
+
+
+def test_mx_clamp_low():
+    # amax below 448 * 2^-127: e clamps at -127 (E8M0 0), elements still in range
+    tiny = np.full((1, 32), 2.0 ** -130, dtype=np.float32)
+    codes, e8 = quant.mxfp8_quant(bf16(tiny))
+    assert e8[0, 0] == 0
+    assert np.all(formats.e4m3_decode(codes) * 2.0 ** -127 == 2.0 ** -130)
+
+
+def test_kv_error_bound_and_saturation_free_max():
+    rng = np.random.default_rng(4)
+    kvb = _random_bf16(rng, (3000, 576))
+    rec = quant.kv_quant(kvb)
+    lat, rope = quant.kv_dequant(rec)
+    x = formats.bf16_decode(kvb[:, :512]).reshape(3000, 4, 128)
+    s = quant.kv_record_scales(rec).astype(np.float64)
+    # the scale is the IEEE float32 quotient amax / 448
+    amax = np.abs(x).max(axis=2).astype(np.float32)
+    assert np.array_equal(quant.kv_record_scales(rec), (amax / np.float32(448)).astype(np.float32))
+    # element error: half an E4M3 step at x/s (times s) plus the f32 division
+    y = np.abs(x) / s[:, :, None]
+    bound = formats.e4m3_half_ulp(np.minimum(y, 448)) * s[:, :, None] + np.abs(x) * 2.0 ** -22
+    assert np.all(np.abs(lat.reshape(3000, 4, 128) - x) <= bound)
+    # the element holding amax encodes as +-448
+    codes = rec[:, :512].reshape(3000, 4, 128)
+    am = np.abs(x).argmax(axis=2)
+    top = np.take_along_axis(codes, am[:, :, None], axis=2)[:, :, 0]
+    assert np.all((top & 0x7F) == 0x7E)
+    # rope copied bit-exactly
+    assert np.array_equal(rope, formats.bf16_decode(kvb[:, 512:]))
+
+
+def test_kv_power_of_two_invariance():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((400, 576)).astype(np.float32)
+    r0 = quant.kv_quant(bf16(x))
+    for k in (-7, 3):
+        xk = x.copy(); xk[:, :512] *= np.float32(2.0 ** k)
+        rk = quant.kv_quant(bf16(xk))
+        assert np.array_equal(rk[:, :512], r0[:, :512])
+        assert np.array_equal(quant.kv_record_scales(rk),
+                              quant.kv_record_scales(r0) * np.float32(2.0 ** k))
+
+
+def test_record_and_page_sizes():
+    assert quant.RECORD_BYTES == 656 and pools.K_PAGE_BYTES == 8448
+    assert (64 * 656) % 256 == 0 and 8448 % 256 == 0
+    # closed-form memory claims of the page-3 quantisation sections:
+    # index data 132 B/token vs 256 B bf16 (-48.4%), KV 656 vs 1152 B (-43.1%)
+    assert round(1 - 132 / 256, 3) == 0.484 and round(1 - 656 / 1152, 3) == 0.431
+
+
+def test_k_pool_roundtrip_permuted():
+    rng = np.random.default_rng(6)
+    cfg = synth.Config(99, "t", batch=3, h_index=4, h_attn=8, topk=16, ragged=(70, 200))
+    lens = np.array([70, 200, 129], dtype=np.int32)
+    bt, slots, starts, npages = synth.page_tables(cfg, lens, rng)
+    kb = _random_bf16(rng, (int(lens.sum()), 128), spread=False)
+    codes, e8 = quant.mxfp8_quant(kb)
+    pool = pools.k_pool_write(codes, e8, slots, npages)
+    for b in range(3):
+        c, e = pools.k_pool_read(pool, bt[b], int(lens[b]))
+        st = int(starts[b])
+        assert np.array_equal(c, codes[st:st + lens[b]]) and np.array_equal(e, e8[st:st + lens[b]])
+    # byte placement: token 65 of sequence 1 -> page bt[1][1], offset 1
+    p = bt[1][1]
+    st = int(starts[1])
+    assert np.array_equal(pool[p, 128:256], codes[st + 65])
+    assert np.array_equal(pool[p, 8192 + 4:8192 + 8], e8[st + 65])
+
+
+def test_kv_pool_roundtrip_and_skip():
+    rng = np.random.default_rng(8)
+    kvb = _random_bf16(rng, (130, 576), spread=False)
+    rec = quant.kv_quant(kvb)
+    slots = rng.permutation(3 * 64)[:130].astype(np.int64)
+    slots[7] = -1
+    pool = pools.kv_pool_write(rec, slots, 3)
+    assert np.array_equal(pool[slots[8]], rec[8])
+    assert not np.any(pool[np.setdiff1d(np.arange(192), slots)])
