@@ -1,0 +1,201 @@
+/*
+ * dsa.h - C ABI of the MI355X (gfx950) DSA hot path library
+ *         (libdsa_mi355x.so, built from sparse_attention_decode_topk_amd/csrc).
+ *
+ * DeepSeek-style sparse attention in two stages: a Lightning Indexer scores
+ * every causal history position of each query and keeps the Top-K; Sparse
+ * Flash Attention then attends only to those positions of an MLA latent
+ * cache ("Deep Dive into Sparse Attention and Engineering Optimizations for
+ * Efficient Inference in Kimi K3.1 Pro", section 1 "Hybrid Architecture";
+ * "Kimi K3.1 Pro Inference Acceleration: Day0 Optimization on Heterogeneous
+ * AI Hardware", sections "Lightning Indexer Three-Stream Coordination",
+ * "Full MXFP8 Quantization ...", "FP8 KVCache ..." and "Preserving a
+ * Mixed-Precision Path").
+ *
+ * Conventions shared by every entry point
+ *  - Memory: every array argument is a DEVICE pointer owned by the caller.
+ *    The library allocates nothing and keeps no pointer after returning.
+ *  - Execution: work is enqueued asynchronously on `stream` (a hipStream_t
+ *    passed as void*; NULL = the null stream).  No call synchronises.
+ *  - Return value: DSA_OK, or an error code returned BEFORE any device work
+ *    is enqueued (argument checks are pure host code), or DSA_ERR_HIP when a
+ *    launch fails.  Faults inside kernels surface at the caller's next
+ *    synchronisation, as usual for HIP.
+ *  - Inputs must be finite.  bf16/fp32 arrays are little-endian, row-major.
+ *  - Threads: entry points are re-entrant; two calls that share a workspace
+ *    must not run concurrently.
+ *
+ * Cache layouts (one block table of physical page ids serves both caches;
+ * token s of sequence b lives in page block_table[b*bt_stride + s/64] at
+ * offset s%64):
+ *  - indexer K page, DSA_K_PAGE_BYTES = 8448 bytes:
+ *      [64 tokens x 128 E4M3 codes][64 tokens x 4 E8M0 scale bytes]
+ *  - SFA KV record, DSA_KV_RECORD_BYTES = 656 bytes per token (slot p*64+o
+ *    at byte offset (p*64+o)*656 of the pool):
+ *      [512 E4M3 latent codes][4 x fp32 tile scales][64 x bf16 rope]
+ *  E4M3 is the OCP "FN" variant (max 448, no infinities); E8M0 is 2^(E-127).
+ */
+#ifndef DSA_MI355X_H
+#define DSA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_OK              0
+#define DSA_ERR_INVALID_ARG 1  /* null pointer, non-positive size, bad stride */
+#define DSA_ERR_UNSUPPORTED 2  /* a dimension the kernels are not built for   */
+#define DSA_ERR_WORKSPACE   3  /* workspace missing or smaller than required  */
+#define DSA_ERR_HIP         4  /* a HIP launch/runtime call failed            */
+
+#define DSA_PAGE_TOKENS      64
+#define DSA_INDEX_DIM        128
+#define DSA_MX_GROUP         32
+#define DSA_K_PAGE_BYTES     8448
+#define DSA_LATENT_DIM       512
+#define DSA_ROPE_DIM         64
+#define DSA_KV_TILE          128
+#define DSA_KV_RECORD_BYTES  656
+#define DSA_KV_PAGE_BYTES    41984
+#define DSA_MAX_TOPK         2048
+#define DSA_MAX_INDEX_HEADS  64
+#define DSA_MAX_ATTN_HEADS   128
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* dsa_status_str(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int dsa_version(void);
+
+/*
+ * MXFP8 quantisation of bf16 rows: every 32 consecutive elements share one
+ * E8M0 scale X = 2^e, e the smallest integer with amax <= 448*2^e (clamped
+ * to [-127,127]; e = 0 when amax is 0), and each element becomes the E4M3
+ * code of x/X rounded to nearest-even, saturating.  Defined for the indexer
+ * by "Full MXFP8 Quantization with Per-Group Dynamic Scaling for LI" (Kimi
+ * K3.1 Pro Day0 page; group size 32) and "2. Memory Optimization" of the
+ * "Deep Dive into Sparse Attention" page.
+ *
+ *   x_bf16   [rows, cols] bf16, cols % 32 == 0 (cols <= 65536)
+ *   Contiguous mode (indexer q): out_fp8 [rows, cols] E4M3 and
+ *     out_e8m0 [rows, cols/32] non-NULL; k_pool and slot_mapping NULL.
+ *   Paged mode (indexer k written into the K cache): cols == 128, k_pool and
+ *     slot_mapping [rows] (int64) non-NULL, out_* NULL; row i goes to slot
+ *     slot_mapping[i]; slots < 0 or >= pool_pages*64 are skipped.
+ */
+int mxfp8_quant(const void* x_bf16, int64_t rows, int32_t cols,
+                void* out_fp8, void* out_e8m0,
+                void* k_pool, const int64_t* slot_mapping, int64_t pool_pages,
+                void* stream);
+
+/*
+ * FP8 quantisation of KV rows into the paged SFA cache: each token's
+ * 512-wide latent is cut into four tiles of 128; a tile's scale is the IEEE
+ * float32 quotient amax/448 (1.0 when amax is 0) and each element becomes
+ * the E4M3 code of the float32 quotient x/scale, nearest-even, saturating.
+ * The 64-wide rope part is copied as bf16.  Defined by "FP8 KVCache with
+ * Per-Token-Head-Tile Quantization for SFA" (Kimi K3.1 Pro Day0 page, tile
+ * 128) and the multi-stream note that KV writes happen during decode
+ * ("System-Level Coordination", same page).
+ *
+ *   kv_bf16       [n_tokens, 576] bf16 = latent 512 | rope 64
+ *   slot_mapping  [n_tokens] int64; slots < 0 or >= pool_pages*64 skipped
+ *   kv_pool       pool of pool_pages pages of 41984 bytes
+ */
+int kv_fp8_quant_paged_write(const void* kv_bf16, int64_t n_tokens,
+                             const int64_t* slot_mapping, void* kv_pool,
+                             int64_t pool_pages, void* stream);
+
+/*
+ * Bytes of zero-initialised workspace dsa_indexer_topk needs for R query
+ * rows whose block tables have bt_stride entries.
+ */
+size_t dsa_indexer_topk_workspace_size(int32_t R, int32_t bt_stride,
+                                       int32_t H_I, int32_t topk);
+
+/*
+ * Lightning Indexer with fused head weighting and Top-K, one launch, no
+ * score matrix in HBM ("Deep Dive into Sparse Attention", section "1.
+ * Computation Optimization: ... DSA Fused Kernel"; Kimi K3.1 Pro Day0 page,
+ * "Lightning Indexer Three-Stream Coordination"):
+ *
+ *   I(t,s) = sum_h w[r,h] * max(0, q[r,h] . k[s]),  0 <= s <= t = row_pos[r]
+ *
+ * over the dequantised MXFP8 q and k; keeps the topk largest scores, ties
+ * broken by the lower position; writes the kept positions in ascending
+ * order, padded with -1 when fewer than topk positions exist.
+ *
+ *   q_fp8      [R, H_I, 128] E4M3      q_e8m0 [R, H_I, 4] E8M0
+ *   w          [R, H_I] fp32 head weights
+ *   k_pool     indexer K cache, pool_pages pages of 8448 bytes
+ *   block_table[B, bt_stride] int32 page ids; row_seq[R] int32 selects the
+ *              sequence (row of block_table); row_pos[R] int32 is t
+ *   H_I        1..64;  topk 1..2048
+ *   out_idx    [R, topk] int32 ascending positions, then -1
+ *   out_score  [R, topk] fp32 scores aligned with out_idx (-inf padding);
+ *              may be NULL
+ *   workspace  >= dsa_indexer_topk_workspace_size(...) bytes, zeroed once
+ *              by the caller before first use; every call leaves it zeroed.
+ * Results are deterministic (no floating-point atomics).  A page id outside
+ * [0, pool_pages) or a row with row_pos < 0 contributes no positions.
+ */
+int dsa_indexer_topk(const void* q_fp8, const void* q_e8m0, const float* w,
+                     const void* k_pool, int64_t pool_pages,
+                     const int32_t* block_table, int32_t bt_stride,
+                     const int32_t* row_seq, const int32_t* row_pos, int32_t R,
+                     int32_t H_I, int32_t topk,
+                     int32_t* out_idx, float* out_score,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * TEST ONLY: the full score rows of dsa_indexer_topk, computed by the same
+ * device code: out_scores[r*ld + s] = I(t,s) for s <= t, -inf for
+ * t < s < ld.  Requires ld >= max(row_pos)+1 (positions beyond ld are not
+ * written).  Arguments as for dsa_indexer_topk.
+ */
+int dsa_indexer_scores(const void* q_fp8, const void* q_e8m0, const float* w,
+                       const void* k_pool, int64_t pool_pages,
+                       const int32_t* block_table, int32_t bt_stride,
+                       const int32_t* row_seq, const int32_t* row_pos, int32_t R,
+                       int32_t H_I, float* out_scores, int64_t ld, void* stream);
+
+/* Bytes of workspace dsa_sparse_attn needs (zeroed once before first use). */
+size_t dsa_sparse_attn_workspace_size(int32_t R, int32_t H, int32_t topk);
+
+/*
+ * Sparse Flash Attention over the selected positions ("Deep Dive into
+ * Sparse Attention", section 1; "Adapting and Optimizing Kimi K3.1 Pro for
+ * Long-Sequence Inference", section 2: gather by the indices of the
+ * previous step, then attention):
+ *
+ *   z_j = scale * (q[r,h,:512] . latent_j + q[r,h,512:] . rope_j)
+ *   out[r,h,:] = sum_j softmax(z)_j * latent_j ,  lse[r,h] = ln sum_j e^{z_j}
+ *
+ * latent_j = E4M3 codes times their tile scale, rope_j bf16, for every entry
+ * j of idx[r,:] that is >= 0 (duplicates count as listed); no other mask.
+ *
+ *   q_bf16     [R, H, 576] bf16 (latent 512 | rope 64)
+ *   kv_pool    SFA cache, pool_pages pages of 41984 bytes
+ *   idx        [R, topk] int32 positions of sequence row_seq[r]; -1 = skip
+ *   H          multiple of 16, <= 128;  topk 1..2048
+ *   softmax_scale  the logit scale (1/sqrt(576) for this model)
+ *   out        [R, H, 512] fp32;  lse [R, H] fp32 (may be NULL)
+ *   A row with no valid entry gets out = 0 and lse = -inf.
+ *   workspace  >= dsa_sparse_attn_workspace_size(...) bytes, zeroed once;
+ *              every call leaves it zeroed.
+ */
+int dsa_sparse_attn(const void* q_bf16, const void* kv_pool, int64_t pool_pages,
+                    const int32_t* block_table, int32_t bt_stride,
+                    const int32_t* row_seq, const int32_t* idx, int32_t R,
+                    int32_t H, int32_t topk, float softmax_scale,
+                    float* out, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_MI355X_H */

@@ -1,0 +1,146 @@
+// MXFP8 quantisation (indexer q / paged indexer k) and FP8 per-tile KV
+// quantisation into the paged SFA cache.
+//
+// MXFP8: one E8M0 scale per 32 elements ("Full MXFP8 Quantization with
+// Per-Group Dynamic Scaling for LI", Kimi K3.1 Pro Day0 page).  KV: one fp32
+// scale amax/448 per 128-element tile of each token's latent, rope kept in
+// bf16 ("FP8 KVCache with Per-Token-Head-Tile Quantization for SFA" and
+// "Preserving a Mixed-Precision Path", same page).
+#include "common.hpp"
+
+namespace {
+
+using namespace dsa;
+
+// Four consecutive threads own one 32-element group; each thread converts 8
+// elements (one 16-byte load, one 8-byte store).
+__global__ __launch_bounds__(256) void mxfp8_quant_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int cols, uint8_t* __restrict__ out,
+    uint8_t* __restrict__ out_scale, uint8_t* __restrict__ kpool,
+    const int64_t* __restrict__ slots, int64_t pool_slots) {
+  const int64_t per_row = cols / 8;
+  const int64_t total = rows * per_row;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(x + i * 8);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    float v[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
+      v[2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+      amax = fmaxf(amax, fmaxf(fabsf(v[2 * j]), fabsf(v[2 * j + 1])));
+    }
+    // group of 4 consecutive lanes (groups never straddle the loop bound)
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    const int e = mx_exponent(amax);
+    const float inv = pow2f(-e);  // exact: -e in [-120, 127] for bf16 input
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lo |= e4m3_rne_sat(v[j] * inv) << (8 * j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hi |= e4m3_rne_sat(v[4 + j] * inv) << (8 * j);
+    const uint8_t sbyte = (uint8_t)(e + 127);
+    if (kpool == nullptr) {
+      *reinterpret_cast<uint2*>(out + i * 8) = make_uint2(lo, hi);
+      if ((i & 3) == 0) out_scale[i >> 2] = sbyte;
+    } else {
+      const int64_t row = i / per_row;
+      const int c8 = (int)(i - row * per_row);  // 0..15
+      const int64_t slot = slots[row];
+      if (slot < 0 || slot >= pool_slots) continue;
+      uint8_t* page = kpool + (slot >> 6) * (int64_t)kKPageBytes;
+      const int off = (int)(slot & 63);
+      *reinterpret_cast<uint2*>(page + off * kIdxDim + c8 * 8) = make_uint2(lo, hi);
+      if ((c8 & 3) == 0) page[kKScaleOff + off * 4 + (c8 >> 2)] = sbyte;
+    }
+  }
+}
+
+// One wave per token: lane j quantises latent elements [8j, 8j+8) (tile
+// j/16); lanes 0..7 copy the rope part.
+__global__ __launch_bounds__(256) void kv_quant_kernel(
+    const uint16_t* __restrict__ kv, int64_t n, const int64_t* __restrict__ slots,
+    uint8_t* __restrict__ pool, int64_t pool_slots) {
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  for (int64_t tok = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); tok < n;
+       tok += waves) {
+    const int64_t slot = slots[tok];
+    if (slot < 0 || slot >= pool_slots) continue;  // uniform across the wave
+    const uint16_t* src = kv + tok * kQK;
+    const uint4 raw = *reinterpret_cast<const uint4*>(src + lane * 8);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    float v[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
+      v[2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+      amax = fmaxf(amax, fmaxf(fabsf(v[2 * j]), fabsf(v[2 * j + 1])));
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+    const float scale = amax == 0.f ? 1.0f : __fdiv_rn(amax, 448.0f);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lo |= e4m3_rne_sat(__fdiv_rn(v[j], scale)) << (8 * j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hi |= e4m3_rne_sat(__fdiv_rn(v[4 + j], scale)) << (8 * j);
+    uint8_t* rec = pool + slot * (int64_t)kRec;
+    *reinterpret_cast<uint2*>(rec + lane * 8) = make_uint2(lo, hi);
+    if ((lane & 15) == 0) *reinterpret_cast<float*>(rec + kRecScaleOff + (lane >> 4) * 4) = scale;
+    if (lane < 8) {
+      const uint4 r = *reinterpret_cast<const uint4*>(src + kLatent + lane * 8);
+      *reinterpret_cast<uint4*>(rec + kRecRopeOff + lane * 16) = r;
+    }
+  }
+}
+
+int grid_for(int64_t threads, int block) {
+  int64_t g = (threads + block - 1) / block;
+  if (g < 1) g = 1;
+  if (g > 65536) g = 65536;
+  return (int)g;
+}
+
+}  // namespace
+
+extern "C" int mxfp8_quant(const void* x_bf16, int64_t rows, int32_t cols, void* out_fp8,
+                           void* out_e8m0, void* k_pool, const int64_t* slot_mapping,
+                           int64_t pool_pages, void* stream) {
+  if (x_bf16 == nullptr || rows < 0 || cols <= 0) return DSA_ERR_INVALID_ARG;
+  if (cols % 32 != 0 || cols > 65536) return DSA_ERR_UNSUPPORTED;
+  const bool paged = k_pool != nullptr || slot_mapping != nullptr;
+  if (paged) {
+    if (k_pool == nullptr || slot_mapping == nullptr || out_fp8 != nullptr || out_e8m0 != nullptr)
+      return DSA_ERR_INVALID_ARG;
+    if (cols != DSA_INDEX_DIM) return DSA_ERR_UNSUPPORTED;
+    if (pool_pages <= 0) return DSA_ERR_INVALID_ARG;
+  } else if (out_fp8 == nullptr || out_e8m0 == nullptr) {
+    return DSA_ERR_INVALID_ARG;
+  }
+  if (rows == 0) return DSA_OK;
+  const int64_t threads = rows * (cols / 8);
+  hipLaunchKernelGGL(mxfp8_quant_kernel, dim3(grid_for(threads, 256)), dim3(256), 0,
+                     dsa_host::as_stream(stream), static_cast<const uint16_t*>(x_bf16), rows,
+                     (int)cols, static_cast<uint8_t*>(out_fp8), static_cast<uint8_t*>(out_e8m0),
+                     static_cast<uint8_t*>(k_pool), slot_mapping,
+                     paged ? pool_pages * DSA_PAGE_TOKENS : (int64_t)0);
+  return dsa_host::launch_status(hipGetLastError());
+}
+
+extern "C" int kv_fp8_quant_paged_write(const void* kv_bf16, int64_t n_tokens,
+                                        const int64_t* slot_mapping, void* kv_pool,
+                                        int64_t pool_pages, void* stream) {
+  if (kv_bf16 == nullptr || slot_mapping == nullptr || kv_pool == nullptr || n_tokens < 0 ||
+      pool_pages <= 0)
+    return DSA_ERR_INVALID_ARG;
+  if (n_tokens == 0) return DSA_OK;
+  hipLaunchKernelGGL(kv_quant_kernel, dim3(grid_for(n_tokens * 64, 256)), dim3(256), 0,
+                     dsa_host::as_stream(stream), static_cast<const uint16_t*>(kv_bf16), n_tokens,
+                     slot_mapping, static_cast<uint8_t*>(kv_pool), pool_pages * DSA_PAGE_TOKENS);
+  return dsa_host::launch_status(hipGetLastError());
+}

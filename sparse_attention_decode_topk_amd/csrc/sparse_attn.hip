@@ -1,0 +1,453 @@
+// Sparse Flash Attention over the Top-K positions of an FP8 MLA latent
+// cache ("Deep Dive into Sparse Attention ...", section 1; "Adapting and
+// Optimizing Kimi K3.1 Pro for Long-Sequence Inference", section 2: gather
+// the cache entries of the selected indices, then attention; Kimi K3.1 Pro
+// Day0 page, "FP8 KVCache ..." and "Preserving a Mixed-Precision Path").
+//
+// One workgroup = (query row, group of 16 heads, split of the index list).
+// Per 64-token tile:
+//  * gather: the 64 selected 656-byte records are fetched one tile ahead
+//    into registers and staged in LDS (latent rows padded to 528 bytes);
+//  * logits: wave w owns tokens 16w..16w+15.  S^T = K Q^T on
+//    v_mfma_f32_16x16x32_bf16: E4M3 latent -> bf16 is exact, each 128-wide
+//    tile accumulates separately and is multiplied by its fp32 tile scale in
+//    fp32, the bf16 rope part adds on top; times softmax_scale*log2(e);
+//  * online softmax shared by the four waves through LDS (fp32);
+//  * P.V: wave w owns latent tile w (dims 128w..128w+127).  The tile scale
+//    of every token is folded into P (P' = p * scale * 2^(8-E), E a running
+//    power-of-two reference so P' stays well inside fp16), V is the exact
+//    E4M3 code in f16, fetched transposed by ds_read_tr8_b64;
+//    v_mfma_f32_16x16x32_f16 accumulates in fp32.
+// Splits write (O, m, l) partials; the last split of a (row, head group)
+// combines them in split order (deterministic).
+#include <algorithm>
+
+#include "common.hpp"
+
+namespace {
+
+using namespace dsa;
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kTile = 64;
+constexpr int kHG = 16;                 // heads per workgroup
+constexpr int kLatStride = 528;         // LDS bytes per staged latent row
+constexpr int kChunks = kRec / 16;      // 41 16-byte pieces per record
+constexpr int kLoads = (kTile * kChunks + kThreads - 1) / kThreads;   // 11
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kMaxSplits = 64;
+constexpr int kTargetWgs = 512;
+
+struct Params {
+  const uint16_t* q;      // [R, H, 576] bf16
+  const uint8_t* pool;
+  int64_t pool_pages;
+  const int32_t* bt;
+  int32_t bt_stride;
+  const int32_t* row_seq;
+  const int32_t* idx;     // [R, topk]
+  int32_t R, H, topk;
+  float scale_log2;       // softmax_scale * log2(e)
+  float* out;             // [R, H, 512]
+  float* lse;             // [R, H] or null
+  int32_t S, per_split;   // splits and tokens per split (multiple of 64)
+  float* part_o;          // [R*HG][S][16][512]
+  float* part_ml;         // [R*HG][S][16][2]
+  uint32_t* tick;         // [R*HG]
+  uint32_t* err;
+};
+
+struct Smem {
+  uint8_t lat[kTile * kLatStride];          // 33792
+  uint16_t rope[kTile * kRope];             // 8192
+  float scl[kTile * 4];                     // 1024
+  _Float16 pp[4][kHG][kTile];               // P' per latent tile, 8192
+  const uint8_t* rec[2][kTile];             // record pointers of the current/next tile
+  float wmax[kWaves][kHG];
+  float wsum[kWaves][kHG];
+  float alpha[kHG];
+  int32_t eref_new[4];
+  int32_t emax[4];
+};
+
+__device__ __forceinline__ void flag(uint32_t* err, uint32_t bits) {
+  if (err) __hip_atomic_fetch_or(err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// record pointer of list entry j of this row (null if j is out of range, the
+// entry is -1, or its page is not in the table/pool)
+__device__ __forceinline__ const uint8_t* record_of(const Params& P, const int32_t* idxrow,
+                                                    const int32_t* btrow, int j, int jend) {
+  if (j >= jend) return nullptr;
+  const int32_t v = idxrow[j];
+  if (v < 0) return nullptr;
+  const int pg = v >> 6;
+  if (pg >= P.bt_stride) { flag(P.err, 1u); return nullptr; }
+  const int32_t pid = btrow[pg];
+  if (pid < 0 || (int64_t)pid >= P.pool_pages) { flag(P.err, 1u); return nullptr; }
+  return P.pool + ((int64_t)pid * kPage + (v & 63)) * kRec;
+}
+
+__global__ __launch_bounds__(kThreads) void sfa_kernel(Params P) {
+  __shared__ Smem S;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int hr = lane & 15, g = lane >> 4;
+  const int HGn = (P.H + kHG - 1) / kHG;
+  const int sp = blockIdx.x % P.S;
+  const int hg = (blockIdx.x / P.S) % HGn;
+  const int row = blockIdx.x / (P.S * HGn);
+  const int seq = P.row_seq[row];
+  const int32_t* idxrow = P.idx + (int64_t)row * P.topk;
+  const int32_t* btrow = P.bt + (int64_t)seq * P.bt_stride;
+  const int j0 = sp * P.per_split;
+  const int jend = min(P.topk, j0 + P.per_split);
+  const int ntiles = jend > j0 ? (jend - j0 + kTile - 1) / kTile : 0;
+
+  // queries of this lane's head as the B operand: k-step (t, j) holds dims
+  // 128t + 32g + 8j .. +7; rope steps r hold dims 512 + 32r + 8g .. +7
+  const int head = kHG * hg + hr;
+  const bool head_ok = head < P.H;
+  v8bf qb[18];
+  {
+    const uint16_t* qrow = P.q + ((int64_t)row * P.H + (head_ok ? head : 0)) * kQK;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4 v = head_ok ? *reinterpret_cast<const uint4*>(qrow + 128 * t + 32 * g + 8 * j)
+                                : make_uint4(0, 0, 0, 0);
+        qb[4 * t + j] = __builtin_bit_cast(v8bf, v);
+      }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const uint4 v = head_ok ? *reinterpret_cast<const uint4*>(qrow + kLatent + 32 * r + 8 * g)
+                              : make_uint4(0, 0, 0, 0);
+      qb[16 + r] = __builtin_bit_cast(v8bf, v);
+    }
+  }
+
+  // running softmax state of head hr (identical in every wave) and this
+  // wave's output block: dims 128*wv + 16d + hr, heads 4g + c
+  float m_run = -__builtin_huge_valf(), l_run = 0.f;
+  int eref = -1000;                       // power-of-two reference of tile wv
+  v4f o[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) o[d] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  uint4 buf[kLoads];
+  auto issue_loads = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int c = tid + i * kThreads;
+      buf[i] = make_uint4(0, 0, 0, 0);
+      if (c < kTile * kChunks) {
+        const uint8_t* r = S.rec[slot][c / kChunks];
+        if (r) buf[i] = *reinterpret_cast<const uint4*>(r + (c % kChunks) * 16);
+      }
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int c = tid + i * kThreads;
+      if (c < kTile * kChunks) {
+        const int tok = c / kChunks, part = c % kChunks;
+        if (part < 32)
+          *reinterpret_cast<uint4*>(S.lat + tok * kLatStride + part * 16) = buf[i];
+        else if (part == 32)
+          *reinterpret_cast<uint4*>(S.scl + tok * 4) = buf[i];
+        else
+          *reinterpret_cast<uint4*>(S.rope + tok * kRope + (part - 33) * 8) = buf[i];
+      }
+    }
+  };
+
+  if (ntiles > 0) {
+    if (tid < kTile) S.rec[0][tid] = record_of(P, idxrow, btrow, j0 + tid, jend);
+    __syncthreads();
+    issue_loads(0);
+  }
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int cur = it & 1;
+    __syncthreads();                      // previous tile fully consumed
+    stage();
+    if (tid < 4) S.emax[tid] = -1000;
+    if (tid < kTile) S.rec[cur ^ 1][tid] = record_of(P, idxrow, btrow, j0 + (it + 1) * kTile + tid, jend);
+    __syncthreads();
+    if (tid < kTile && S.rec[cur][tid] != nullptr) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float s = S.scl[tid * 4 + t];
+        if (s > 0.f) atomicMax(&S.emax[t], (int)((__float_as_uint(s) >> 23) & 0xFF) - 127);
+      }
+    }
+    if (it + 1 < ntiles) issue_loads(cur ^ 1);
+
+    // ---- logits of tokens 16wv .. 16wv+15 (lane: head hr, tokens 4g+c) ----
+    const int tok_a = 16 * wv + hr;       // A-operand row of this lane
+    v4f acc[5];
+#pragma unroll
+    for (int t = 0; t < 5; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint8_t* src = S.lat + tok_a * kLatStride + 128 * t + 32 * g;
+      const uint4 a0 = *reinterpret_cast<const uint4*>(src);
+      const uint4 a1 = *reinterpret_cast<const uint4*>(src + 16);
+      const uint32_t dw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dw[2 * j], 1.0f, false);
+        const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dw[2 * j], 1.0f, true);
+        const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dw[2 * j + 1], 1.0f, false);
+        const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dw[2 * j + 1], 1.0f, true);
+        const v8bf a = v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[4 * t + j], acc[t], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const uint4 v = *reinterpret_cast<const uint4*>(S.rope + tok_a * kRope + 32 * r + 8 * g);
+      acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, v), qb[16 + r], acc[4], 0, 0, 0);
+    }
+    float z[4];
+    float zmax = -__builtin_huge_valf();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int tok = 16 * wv + 4 * g + c;
+      const float* sc = S.scl + tok * 4;
+      float v = acc[4][c];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v = __builtin_fmaf(sc[t], acc[t][c], v);
+      z[c] = S.rec[cur][tok] != nullptr ? v * P.scale_log2 : -__builtin_huge_valf();
+      zmax = fmaxf(zmax, z[c]);
+    }
+    zmax = fmaxf(zmax, __shfl_xor(zmax, 16));
+    zmax = fmaxf(zmax, __shfl_xor(zmax, 32));
+    if (lane < 16) S.wmax[wv][hr] = zmax;
+    __syncthreads();
+    float m_new = m_run;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) m_new = fmaxf(m_new, S.wmax[w][hr]);
+    const bool any = m_new != -__builtin_huge_valf();
+    const float alpha = any ? exp2f(m_run - m_new) : 1.0f;   // exp2(-inf) = 0
+    float p[4], psum = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      p[c] = any ? exp2f(z[c] - m_new) : 0.f;
+      psum += p[c];
+    }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    if (lane < 16) S.wsum[wv][hr] = psum;
+    if (wv == 0 && lane < 16) S.alpha[hr] = alpha;
+    // P' of latent tile t uses the reference wave t publishes:
+    // max(its running reference, the largest scale exponent of this tile)
+    if (lane == 0) S.eref_new[wv] = max(eref, S.emax[wv]);
+    __syncthreads();
+    // P' for every latent tile t: p * scale[t] * 2^(8 - Eref_t)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int e = S.eref_new[t];
+      const float mul = e > -1000 ? pow2f(max(-126, min(127, 8 - e))) : 0.f;
+      _Float16 h[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int tok = 16 * wv + 4 * g + c;
+        h[c] = (_Float16)(p[c] * S.scl[tok * 4 + t] * mul);
+      }
+      *reinterpret_cast<uint2*>(&S.pp[t][hr][16 * wv + 4 * g]) = __builtin_bit_cast(uint2, h);
+    }
+    __syncthreads();
+    float tile_sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) tile_sum += S.wsum[w][hr];
+    l_run = alpha * l_run + tile_sum;
+    m_run = m_new;
+
+    // ---- P'.V for latent tile wv ----
+    const int e_new = S.eref_new[wv];
+    const float resc = (eref > -1000 && e_new > eref) ? pow2f(max(-126, eref - e_new)) : 1.0f;
+    eref = e_new;
+    float al[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) al[c] = S.alpha[4 * g + c] * resc;
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[d][c] *= al[c];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint4 pa = *reinterpret_cast<const uint4*>(&S.pp[wv][hr][32 * ks + 8 * g]);
+      const v8h a = __builtin_bit_cast(v8h, pa);
+      typedef __attribute__((address_space(3))) v2i lds_v2i;
+      const int vtok = 32 * ks + 8 * g + (hr >> 1);
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const uint8_t* src = S.lat + vtok * kLatStride + 128 * wv + 16 * d + 8 * (hr & 1);
+        const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (lds_v2i*)((__attribute__((address_space(3))) uint8_t*)(src)));
+        const v2h v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[0], 1.0f, false);
+        const v2h v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[0], 1.0f, true);
+        const v2h v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[1], 1.0f, false);
+        const v2h v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[1], 1.0f, true);
+        const v8h b = v8h{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, o[d], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue ----
+  // o holds sum_j p_j * v_j / 2^(8 - eref) for heads 4g+c, dims 128wv+16d+hr
+  const float oscale = eref > -1000 ? pow2f(max(-126, min(127, eref - 8))) : 0.f;
+  const int HGs = HGn;
+  const int64_t pair = (int64_t)row * HGs + hg;
+  if (P.S == 1) {
+    // l and m of head 4g+c live in lanes whose hr == 4g+c: share via LDS
+    if (wv == 0 && lane < 16) { S.wsum[0][hr] = l_run; S.wmax[0][hr] = m_run; }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int hh = kHG * hg + 4 * g + c;
+      if (hh >= P.H) continue;
+      const float l = S.wsum[0][4 * g + c];
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      float* dst = P.out + ((int64_t)row * P.H + hh) * kLatent + 128 * wv + hr;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) dst[16 * d] = o[d][c] * oscale * inv;
+    }
+    if (P.lse && wv == 0 && lane < 16 && head_ok) {
+      P.lse[(int64_t)row * P.H + head] =
+          l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -__builtin_huge_valf();
+    }
+    return;
+  }
+  // split: write partial (O, m, l), the last split of the pair combines
+  float* po = P.part_o + (pair * P.S + sp) * (kHG * kLatent);
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int d = 0; d < 8; ++d) po[(4 * g + c) * kLatent + 128 * wv + 16 * d + hr] = o[d][c] * oscale;
+  if (wv == 0 && lane < 16) {
+    float* pm = P.part_ml + (pair * P.S + sp) * (kHG * 2);
+    pm[2 * hr] = m_run;
+    pm[2 * hr + 1] = l_run;
+  }
+  __threadfence();
+  __syncthreads();
+  __shared__ uint32_t last;
+  if (tid == 0) last = atomic_add_agent(&P.tick[pair], 1u) == (uint32_t)P.S - 1 ? 1u : 0u;
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  // combine: 16 heads x 512 dims over S splits; thread handles 32 outputs
+  for (int e = tid; e < kHG * kLatent; e += kThreads) {
+    const int h = e / kLatent, dim = e % kLatent;
+    const int hh = kHG * hg + h;
+    float M = -__builtin_huge_valf();
+    for (int s = 0; s < P.S; ++s) M = fmaxf(M, P.part_ml[((pair * P.S + s) * kHG + h) * 2]);
+    float L = 0.f, acc = 0.f;
+    if (M != -__builtin_huge_valf()) {
+      for (int s = 0; s < P.S; ++s) {
+        const float* pm = P.part_ml + ((pair * P.S + s) * kHG + h) * 2;
+        const float wgt = pm[0] == -__builtin_huge_valf() ? 0.f : exp2f(pm[0] - M);
+        L += wgt * pm[1];
+        acc += wgt * P.part_o[(pair * P.S + s) * (kHG * kLatent) + e];
+      }
+    }
+    if (hh < P.H) {
+      P.out[((int64_t)row * P.H + hh) * kLatent + dim] = L > 0.f ? acc / L : 0.f;
+      if (P.lse && dim == 0)
+        P.lse[(int64_t)row * P.H + hh] = L > 0.f ? (M + log2f(L)) * kLn2 : -__builtin_huge_valf();
+    }
+  }
+  if (tid == 0) P.tick[pair] = 0;
+}
+
+struct Plan {
+  int S, per_split, hg;
+};
+
+Plan plan_for(int R, int H, int topk) {
+  Plan p;
+  p.hg = (H + kHG - 1) / kHG;
+  const int tiles = (topk + kTile - 1) / kTile;
+  const int64_t pairs = (int64_t)R * p.hg;
+  int S = (int)std::min<int64_t>((kTargetWgs + pairs - 1) / pairs, (int64_t)tiles);
+  S = std::max(1, std::min(S, kMaxSplits));
+  const int tiles_per = (tiles + S - 1) / S;
+  p.per_split = tiles_per * kTile;
+  p.S = (topk + p.per_split - 1) / p.per_split;
+  return p;
+}
+
+struct Layout {
+  size_t err, tick, part_ml, part_o, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+Layout layout_for(int R, int H, int topk) {
+  const Plan p = plan_for(R, H, topk);
+  const int64_t pairs = (int64_t)R * p.hg;
+  Layout L;
+  size_t off = 0;
+  L.err = off; off += 256;
+  L.tick = off; off += align256((size_t)pairs * 4);
+  const bool split = p.S > 1;
+  L.part_ml = off; off += split ? align256((size_t)pairs * p.S * kHG * 2 * 4) : 0;
+  L.part_o = off; off += split ? align256((size_t)pairs * p.S * kHG * kLatent * 4) : 0;
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" size_t dsa_sparse_attn_workspace_size(int32_t R, int32_t H, int32_t topk) {
+  if (R <= 0 || H <= 0 || topk <= 0) return 256;
+  return layout_for(R, H, topk).total;
+}
+
+extern "C" int dsa_sparse_attn(const void* q_bf16, const void* kv_pool, int64_t pool_pages,
+                               const int32_t* block_table, int32_t bt_stride,
+                               const int32_t* row_seq, const int32_t* idx, int32_t R, int32_t H,
+                               int32_t topk, float softmax_scale, float* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q_bf16 || !kv_pool || !block_table || !row_seq || !idx || !out) return DSA_ERR_INVALID_ARG;
+  if (R < 0 || bt_stride <= 0 || pool_pages <= 0) return DSA_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || softmax_scale > 1e30f) return DSA_ERR_INVALID_ARG;
+  if (H < 1 || H > DSA_MAX_ATTN_HEADS) return DSA_ERR_UNSUPPORTED;
+  if (topk < 1 || topk > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
+  if (R == 0) return DSA_OK;
+  const Layout L = layout_for(R, H, topk);
+  if (workspace == nullptr || workspace_bytes < L.total) return DSA_ERR_WORKSPACE;
+  const Plan pl = plan_for(R, H, topk);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  Params P{};
+  P.q = static_cast<const uint16_t*>(q_bf16);
+  P.pool = static_cast<const uint8_t*>(kv_pool);
+  P.pool_pages = pool_pages;
+  P.bt = block_table;
+  P.bt_stride = bt_stride;
+  P.row_seq = row_seq;
+  P.idx = idx;
+  P.R = R;
+  P.H = H;
+  P.topk = topk;
+  P.scale_log2 = softmax_scale * kLog2e;
+  P.out = out;
+  P.lse = lse;
+  P.S = pl.S;
+  P.per_split = pl.per_split;
+  P.err = reinterpret_cast<uint32_t*>(ws + L.err);
+  P.tick = reinterpret_cast<uint32_t*>(ws + L.tick);
+  P.part_ml = reinterpret_cast<float*>(ws + L.part_ml);
+  P.part_o = reinterpret_cast<float*>(ws + L.part_o);
+  const int64_t grid = (int64_t)R * pl.hg * pl.S;
+  if (grid > 0x7FFFFFFF) return DSA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(sfa_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
+                     dsa_host::as_stream(stream), P);
+  return dsa_host::launch_status(hipGetLastError());
+}

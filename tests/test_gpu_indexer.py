@@ -1,0 +1,157 @@
+"""GPU parity of the fused indexer + Top-K against the oracle.
+
+Scores: within 1e-4 * max|I| of the fp64 oracle.  Selection: the pass rule
+of check_topk_row; and, bit-exactly, the kernel's selection equals the exact
+Top-K (score desc, position asc) of the kernel's own score rows."""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.pipeline import Oracle
+from sparse_attention_decode_topk_amd import ops, synth
+from tests.dsa_state import DeviceState, check_topk_row, exact_topk_of, say
+
+pytestmark = pytest.mark.gpu
+
+
+@functools.lru_cache(maxsize=2)
+def state(cfg):
+    say(f"[state] building {cfg}")
+    return DeviceState(synth.make(cfg, with_sfa=False), with_sfa=False)
+
+
+def _rows_for(cfg, R):
+    if R <= 64:
+        return list(range(R))
+    rng = np.random.default_rng(1)
+    return sorted(set([0, 1, R - 1] + rng.choice(R, 24, replace=False).tolist()))
+
+
+@pytest.mark.parametrize("cfg", ["tiny_prefill", "decode_8k_needles", "decode_ragged_b32",
+                                 "decode_128k_b8"])
+def test_indexer_parity(need_gpu, cfg):
+    st = state(cfg)
+    say(f"[indexer] {cfg} R={st.R} topk={st.topk}")
+    idx, sc = st.indexer()
+    scores = st.scores()
+    torch.cuda.synchronize()
+    idx, sc, scores = idx.cpu().numpy(), sc.cpu().numpy(), scores.cpu().numpy()
+    o = Oracle(st.inp)
+    rows = list(range(st.R)) if cfg == "tiny_prefill" else _rows_for(cfg, st.R)
+    swaps = 0
+    for r in rows:
+        t = int(st.inp["row_pos"][r])
+        ora = o.topk(r)
+        # scores of every causal position
+        gs = scores[r, :t + 1]
+        assert np.all(np.abs(gs - ora["scores"]) <= 1e-4 * ora["maxabs"]), f"row {r} scores"
+        assert np.all(np.isneginf(scores[r, t + 1:]))
+        swaps += check_topk_row(idx[r], sc[r], ora, st.topk, t)
+        # bit-exact: selection == exact Top-K of the kernel's own scores
+        assert np.array_equal(idx[r][:min(st.topk, t + 1)], exact_topk_of(scores[r], st.topk)), f"row {r}"
+    o.drop_cache()
+    say(f"[indexer] {cfg}: {len(rows)} rows ok, {swaps} tolerated swaps")
+
+
+def test_indexer_deterministic_and_workspace_reuse(need_gpu):
+    st = state("decode_8k_needles")
+    ws = ops.indexer_workspace(st.R, st.block_table.shape[1], st.H_I, st.topk)
+    a = st.indexer(workspace=ws)
+    b = st.indexer(workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    # barrier counter back at zero, no error reported
+    w = ws.view(torch.int32).cpu().numpy()
+    assert w[0] == 0 and w[2] == 0
+
+
+def test_needles_are_selected(need_gpu):
+    st = state("decode_8k_needles")
+    idx, _ = st.indexer()
+    I = st.scores()[0].cpu().numpy()
+    sel = set(idx[0].cpu().numpy().tolist())
+    nd = st.inp["needles"]
+    # every needle whose base score is positive scores x4 and is kept
+    kth = np.sort(I[np.isfinite(I)])[::-1][st.topk - 1]
+    strong = [n for n in nd if I[n] > kth]
+    assert strong and all(n in sel for n in strong)
+
+
+def test_topk_edge_cases(need_gpu):
+    """topk = 1, topk larger than the history, H_I not a multiple of 16,
+    and rows with t < 0, on a small ragged batch."""
+    say("[indexer] edge cases")
+    cfg = synth.Config(90, "edge", batch=3, h_index=20, h_attn=16, topk=1, ragged=(1, 300))
+    lens = np.array([1, 300, 129], dtype=np.int32)
+    rng = np.random.default_rng(3)
+    bt, slots, starts, npages = synth.page_tables(cfg, lens, rng)
+    R = 5
+    inp = dict(seq_lens=lens, block_table=bt, slot_mapping=slots, seq_starts=starts,
+               total_pages=np.int64(npages), topk=np.int32(1),
+               row_seq=np.array([0, 1, 1, 2, 1], dtype=np.int32),
+               row_pos=np.array([0, 299, 63, 128, 5], dtype=np.int32),
+               q_idx=synth.f32_to_bf16_bits(rng.standard_normal((R, 20, 128)).astype(np.float32)),
+               k_idx=synth.f32_to_bf16_bits(rng.standard_normal((int(lens.sum()), 128)).astype(np.float32)),
+               w=(rng.standard_normal((R, 20)) / np.sqrt(20)).astype(np.float32))
+    st = DeviceState(inp, with_sfa=False)
+    o = Oracle(inp)
+    scores = st.scores().cpu().numpy()
+    for K in (1, 7, 64, 130, 2048):
+        idx, sc = st.indexer(topk=K)
+        idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+        for r in range(R):
+            t = int(inp["row_pos"][r])
+            ora = o.topk(r, K)
+            check_topk_row(idx[r], sc[r], ora, K, t)
+            assert np.array_equal(idx[r][:min(K, t + 1)], exact_topk_of(scores[r], K))
+    # a row with no history: t = -1 -> all -1
+    inp2 = dict(inp, row_pos=np.array([-1, 299, 0, 128, 5], dtype=np.int32))
+    st2 = DeviceState(inp2, with_sfa=False)
+    idx, sc = st2.indexer(topk=16)
+    assert np.all(idx[0].cpu().numpy() == -1) and np.all(np.isneginf(sc[0].cpu().numpy()))
+    assert idx[2].cpu().numpy()[0] == 0 and np.all(idx[2].cpu().numpy()[1:] == -1)
+
+
+def test_exact_ties_lower_position_wins(need_gpu):
+    """All-zero queries give score 0 everywhere: the K lowest positions win."""
+    say("[indexer] exact ties")
+    inp = dict(synth.make("decode_8k_needles", with_sfa=False))
+    inp["q_idx"] = np.zeros_like(inp["q_idx"])
+    st = DeviceState(inp, with_sfa=False)
+    idx, sc = st.indexer()
+    assert np.array_equal(idx[0].cpu().numpy(), np.arange(st.topk))
+    assert np.all(sc[0].cpu().numpy() == 0)
+
+
+def test_page_permutation_invariance(need_gpu):
+    say("[indexer] page permutation")
+    inp = synth.make("decode_ragged_b32", with_sfa=False)
+    a = DeviceState(inp, with_sfa=False)
+    ia, sa = a.indexer()
+    ia, sa = ia.cpu().numpy(), sa.cpu().numpy()
+    del a
+    lens = inp["seq_lens"]
+    bt2 = synth.rotate_pages(inp["block_table"], lens, int(inp["total_pages"]), seed=11)
+    slots2 = np.concatenate([bt2[b, np.arange(lens[b]) // 64].astype(np.int64) * 64
+                             + np.arange(lens[b]) % 64 for b in range(len(lens))])
+    b = DeviceState(dict(inp, block_table=bt2, slot_mapping=slots2), with_sfa=False)
+    ib, sb = b.indexer()
+    assert np.array_equal(ia, ib.cpu().numpy()) and np.array_equal(sa, sb.cpu().numpy())
+
+
+def test_chunked_prefill_sampled_rows(need_gpu):
+    """8192 query rows against a 131072-token cache; sampled rows checked."""
+    say("[indexer] chunked prefill 8192 rows")
+    inp = synth.make("prefill_chunk_8k_of_128k", with_sfa=False)
+    st = DeviceState(inp, with_sfa=False)
+    idx, sc = st.indexer()
+    torch.cuda.synchronize()
+    o = Oracle(inp)
+    rng = np.random.default_rng(2)
+    rows = sorted(set([0, 8191] + rng.choice(8192, 14, replace=False).tolist()))
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    for r in rows:
+        t = int(inp["row_pos"][r])
+        check_topk_row(idx[r], sc[r], o.topk(r), st.topk, t)

@@ -1,0 +1,110 @@
+"""GPU parity of the quantisers: bitwise equal to the oracle's codes, scales,
+K pages and KV records."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import pools, quant
+from sparse_attention_decode_topk_amd import ops, synth
+from tests.dsa_state import bf16_tensor, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _spread_bf16(rng, shape):
+    x = rng.standard_normal(shape).astype(np.float32)
+    x *= np.float32(2.0) ** rng.integers(-40, 40, size=shape[:-1] + (1,)).astype(np.float32)
+    # special groups: zeros, +-448 boundaries, tiny values, exact ties
+    x[0] = 0.0
+    if shape[0] > 4:
+        x[1] = 448.0; x[2, ::2] = -448.0; x[3] = 2.0 ** -130
+        x[4] = np.float32(1.0625)
+    return synth.f32_to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (7, 128), (300, 64 * 128 // 64), (1024, 128), (33, 576)])
+def test_mxfp8_contiguous_bitwise(need_gpu, rows, cols):
+    say(f"[mxfp8 contiguous] rows={rows} cols={cols}")
+    rng = np.random.default_rng(rows * 7 + cols)
+    xb = _spread_bf16(rng, (rows, cols))
+    codes, scales = ops.mxfp8_quant(bf16_tensor(xb, "cuda"))
+    c_ref, s_ref = quant.mxfp8_quant(xb)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+
+
+@pytest.mark.parametrize("cfg", ["tiny_prefill", "decode_8k_needles"])
+def test_mxfp8_queries_of_configs(need_gpu, cfg):
+    say(f"[mxfp8 q] {cfg}")
+    inp = synth.make(cfg, with_sfa=False)
+    codes, scales = ops.mxfp8_quant(bf16_tensor(inp["q_idx"], "cuda"))
+    R, H = inp["q_idx"].shape[:2]
+    c_ref, s_ref = quant.mxfp8_quant(inp["q_idx"].reshape(R * H, 128))
+    assert np.array_equal(codes.cpu().numpy().reshape(R * H, 128), c_ref)
+    assert np.array_equal(scales.cpu().numpy().reshape(R * H, 4), s_ref)
+
+
+@pytest.mark.parametrize("cfg", ["tiny_prefill", "decode_8k_needles"])
+def test_paged_k_pool_bitwise(need_gpu, cfg):
+    say(f"[k pool] {cfg}")
+    inp = synth.make(cfg, with_sfa=False)
+    npages = int(inp["total_pages"])
+    pool = torch.zeros((npages, ops.K_PAGE_BYTES), dtype=torch.uint8, device="cuda")
+    slots = inp["slot_mapping"].copy()
+    # a few rows are skipped: negative and out-of-pool slots
+    slots[3] = -1
+    slots[5] = npages * 64 + 10
+    ops.mxfp8_quant_paged(bf16_tensor(inp["k_idx"], "cuda"), torch.from_numpy(slots).cuda(), pool)
+    codes, e8 = quant.mxfp8_quant(inp["k_idx"])
+    ref = pools.k_pool_write(codes, e8, np.where(slots >= npages * 64, -1, slots), npages)
+    assert np.array_equal(pool.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("cfg", ["tiny_prefill", "decode_8k_needles"])
+def test_kv_pool_bitwise(need_gpu, cfg):
+    say(f"[kv pool] {cfg}")
+    inp = synth.make(cfg, with_index=False)
+    npages = int(inp["total_pages"])
+    pool = torch.zeros((npages, ops.KV_PAGE_BYTES), dtype=torch.uint8, device="cuda")
+    slots = inp["slot_mapping"].copy()
+    slots[0] = -5
+    ops.kv_fp8_quant_paged_write(bf16_tensor(inp["kv"], "cuda"), torch.from_numpy(slots).cuda(), pool)
+    ref = pools.kv_pool_write(quant.kv_quant(inp["kv"]), slots, npages)
+    got = pool.cpu().numpy().reshape(npages * 64, 656)
+    assert np.array_equal(got, ref)
+
+
+def test_kv_records_wide_range(need_gpu):
+    say("[kv records] wide-range values")
+    rng = np.random.default_rng(5)
+    kvb = _spread_bf16(rng, (512, 576))
+    pool = torch.zeros((8, ops.KV_PAGE_BYTES), dtype=torch.uint8, device="cuda")
+    slots = np.arange(512, dtype=np.int64)
+    ops.kv_fp8_quant_paged_write(bf16_tensor(kvb, "cuda"), torch.from_numpy(slots).cuda(), pool)
+    got = pool.cpu().numpy().reshape(512, 656)
+    assert np.array_equal(got, quant.kv_quant(kvb))
+
+
+@pytest.mark.parametrize("cfg", ["decode_128k_b8"])
+def test_big_pools_sampled(need_gpu, cfg):
+    """Full-size cache build; sampled tokens compared bitwise."""
+    say(f"[big pools] {cfg}")
+    inp = synth.make(cfg)
+    npages = int(inp["total_pages"])
+    slots = torch.from_numpy(inp["slot_mapping"]).cuda()
+    kpool = torch.zeros((npages, ops.K_PAGE_BYTES), dtype=torch.uint8, device="cuda")
+    kvpool = torch.zeros((npages, ops.KV_PAGE_BYTES), dtype=torch.uint8, device="cuda")
+    ops.mxfp8_quant_paged(bf16_tensor(inp["k_idx"], "cuda"), slots, kpool)
+    ops.kv_fp8_quant_paged_write(bf16_tensor(inp["kv"], "cuda"), slots, kvpool)
+    rng = np.random.default_rng(0)
+    tok = np.sort(rng.choice(len(inp["slot_mapping"]), 4096, replace=False))
+    sl = inp["slot_mapping"][tok]
+    codes, e8 = quant.mxfp8_quant(inp["k_idx"][tok])
+    kp = kpool.cpu().numpy()
+    for i, s in enumerate(sl):
+        p, o = divmod(int(s), 64)
+        assert np.array_equal(kp[p, o * 128:(o + 1) * 128], codes[i])
+        assert np.array_equal(kp[p, 8192 + o * 4:8192 + o * 4 + 4], e8[i])
+    rec = quant.kv_quant(inp["kv"][tok])
+    kvp = kvpool.view(npages * 64, 656)[torch.from_numpy(sl).cuda()].cpu().numpy()
+    assert np.array_equal(kvp, rec)

@@ -1,0 +1,110 @@
+"""GPU parity of Sparse Flash Attention against the oracle.
+
+The position lists come from the oracle (its own Top-K) or are constructed
+in the test; both sides read the same quantised cache bytes, each quantising
+from the same bf16 inputs.  Bar: max abs error <= 1e-3 * max|oracle out|
+over the config's output; lse within 1e-3 absolute (it is a log)."""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.pipeline import Oracle
+from sparse_attention_decode_topk_amd import ops, synth
+from tests.dsa_state import DeviceState, check_topk_row, say
+
+pytestmark = pytest.mark.gpu
+
+
+@functools.lru_cache(maxsize=1)
+def state(cfg):
+    say(f"[state] building {cfg}")
+    return DeviceState(synth.make(cfg))
+
+
+def _compare(st, o, idx_np, rows, tag):
+    out, lse = st.sfa(torch.from_numpy(idx_np).cuda())
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    ref_o, ref_l = [], []
+    for r in rows:
+        ro, rl = o.sfa(r, idx_np[r])
+        ref_o.append(ro); ref_l.append(rl)
+    ref_o = np.stack(ref_o); ref_l = np.stack(ref_l)
+    got_o = out[rows]; got_l = lse[rows]
+    H = st.inp["q_sfa"].shape[1]
+    err = np.abs(got_o - ref_o).max()
+    bar = 1e-3 * np.abs(ref_o).max()
+    say(f"[sfa] {tag}: max err {err:.3g} vs bar {bar:.3g} (ratio {err / bar:.3f})")
+    assert err <= bar
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(np.isfinite(got_l), fin)
+    assert np.all(np.abs(got_l[fin] - ref_l[fin]) <= 1e-3)
+    return out, lse
+
+
+@pytest.mark.parametrize("cfg", ["tiny_prefill", "decode_8k_needles", "decode_128k_b8"])
+def test_sfa_on_oracle_topk(need_gpu, cfg):
+    st = state(cfg)
+    o = Oracle(st.inp)
+    R = st.R
+    rows = list(range(R)) if R <= 64 else sorted(set(range(0, R, max(1, R // 48))) | {R - 1})
+    idx = np.full((R, st.topk), -1, dtype=np.int32)
+    for r in (range(R) if R <= 64 else rows):
+        idx[r] = o.topk(r)["idx"]
+    o.drop_cache()
+    _compare(st, o, idx, rows, cfg)
+
+
+def test_sfa_all_positions_is_dense(need_gpu):
+    """When the history is no longer than K, SFA over every position equals
+    dense attention (tiny prefill rows t < 64 select everything)."""
+    st = state("tiny_prefill")
+    o = Oracle(st.inp)
+    R = st.R
+    idx = np.full((R, st.topk), -1, dtype=np.int32)
+    for r in range(64):
+        idx[r, :r + 1] = np.arange(r + 1)[::-1]   # any order
+    _compare(st, o, idx, list(range(64)), "dense prefix")
+
+
+def test_sfa_special_lists(need_gpu):
+    """-1 holes, duplicates, a single entry, and an empty row."""
+    st = state("tiny_prefill")
+    o = Oracle(st.inp)
+    R, K = st.R, st.topk
+    rng = np.random.default_rng(4)
+    idx = np.full((R, K), -1, dtype=np.int32)
+    rows = [100, 200, 300, 400, 511]
+    idx[100, ::3] = rng.integers(0, 101, size=len(idx[100, ::3]))        # holes + duplicates
+    idx[200, 5] = 17                                                       # single entry
+    idx[300] = 42                                                          # one position 64 times
+    idx[511] = rng.permutation(512)[:K]
+    # row 400 stays empty -> out 0, lse -inf
+    out, lse = _compare(st, o, idx, rows, "special lists")
+    assert np.all(out[400] == 0) and np.all(np.isneginf(lse[400]))
+
+
+def test_sfa_deterministic(need_gpu):
+    st = state("tiny_prefill")
+    o = Oracle(st.inp)
+    idx = np.stack([o.topk(r)["idx"] for r in range(st.R)])
+    t = torch.from_numpy(idx).cuda()
+    a = st.sfa(t)
+    b = st.sfa(t)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_end_to_end_decode(need_gpu):
+    """GPU indexer -> GPU SFA; rows whose selection equals the oracle's are
+    compared end to end."""
+    st = state("decode_8k_needles")
+    o = Oracle(st.inp)
+    idx, sc = st.indexer()
+    gi = idx.cpu().numpy()
+    ora = o.topk(0)
+    check_topk_row(gi[0], sc.cpu().numpy()[0], ora, st.topk, int(st.inp["row_pos"][0]))
+    if np.array_equal(gi[0], ora["idx"]):
+        _compare(st, o, gi, [0], "end to end")
