@@ -137,10 +137,15 @@ size_t dsa_indexer_topk_workspace_size(int32_t R, int32_t bt_stride,
  *   out_idx    [R, topk] int32 ascending positions, then -1
  *   out_score  [R, topk] fp32 scores aligned with out_idx (-inf padding);
  *              may be NULL
- *   workspace  >= dsa_indexer_topk_workspace_size(...) bytes, zeroed once
- *              by the caller before first use; every call leaves it zeroed.
- * Results are deterministic (no floating-point atomics).  A page id outside
- * [0, pool_pages) or a row with row_pos < 0 contributes no positions.
+ *   workspace  >= dsa_indexer_topk_workspace_size(...) bytes, zero-filled
+ *              once by the caller before first use; each call returns its
+ *              counters to zero for the next call.  Bytes [8,12) hold a
+ *              sticky status word the caller may read and clear: bit 2 = a
+ *              page id outside [0, pool_pages) was skipped, bit 3 = a row
+ *              needed the exact rescoring path (informational).
+ * Results are exact and deterministic (no floating-point atomics).  A page id
+ * outside [0, pool_pages) or a row with row_pos < 0 contributes no positions.
+ * block_table widths up to 16384 pages (1M tokens) are supported.
  */
 int dsa_indexer_topk(const void* q_fp8, const void* q_e8m0, const float* w,
                      const void* k_pool, int64_t pool_pages,

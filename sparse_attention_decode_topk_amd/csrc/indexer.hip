@@ -2,26 +2,32 @@
 // over the paged MXFP8 K cache, with no score matrix written to HBM ("Deep
 // Dive into Sparse Attention ...", section "1. Computation Optimization ...
 // DSA Fused Kernel"; Kimi K3.1 Pro Day0 page, "Lightning Indexer
-// Three-Stream Coordination").
+// Three-Stream Coordination": scoring, head weighting and Top-K selection
+// fused, with selection pipelined with the paged K-cache reads).
 //
 //   I(t,s) = sum_h w[r,h] * max(0, q[r,h] . k[s]),  s <= t = row_pos[r]
 //
-// Work decomposition (one cooperative launch of G co-resident workgroups):
-//  * every row's causal history is cut into units of `chp` pages, chp chosen
-//    on the device so that there are at most G + R units; workgroup g takes
-//    units g and g + G;
-//  * phase 1: each wave streams pages of its unit, dequantises the MXFP8 key
-//    block exactly into bf16 (E4M3 * 2^(E-127) fits bf16), runs
-//    v_mfma_f32_16x16x32_bf16 against the resident query heads, applies
-//    ReLU and the head weights in fp32 and keeps the unit's scores as
-//    order-preserving 32-bit keys in LDS; an LDS histogram of the top 12
-//    key bits is added into the row's global histogram;
-//  * one grid barrier;
-//  * phase 2: every unit finds the row's threshold bin from the histogram and
-//    appends its keys at or above it, in position order, to its slice of the
-//    candidate workspace; the last unit of a row (ticket) resolves the exact
-//    K-th key with two more LDS radix passes over the candidates, breaks ties
-//    by lower position, and writes the positions in ascending order.
+// Work decomposition (one ordinary launch; no grid barrier, no spinning):
+//  * every row's causal history is cut into units of 16 pages (1024
+//    tokens); units are numbered row by row and handed out in that order by
+//    one atomic counter, so rows complete in order and a row's selection
+//    overlaps the scan of later rows;
+//  * a unit: each wave streams pages of the unit (one page in flight ahead),
+//    dequantises the MXFP8 key block exactly into bf16 (E4M3 * 2^(E-127) is
+//    a bf16 value), runs v_mfma_f32_16x16x32_bf16 against the resident query
+//    heads, applies ReLU and the head weights in fp32, and keeps the unit's
+//    scores as order-preserving 32-bit keys in LDS;
+//  * local filter: an LDS histogram of the top 14 key bits gives the bin
+//    edge e_u below which the unit holds fewer than m of its largest keys (m
+//    is about twice the unit's expected share of the Top-K); the unit appends
+//    every key >= e_u, in position order, to its slice of the candidate
+//    workspace and records e_u;
+//  * the last unit of a row (ticket) selects the exact K-th key T among the
+//    candidates with three LDS radix passes (12+12+8 bits) and checks that
+//    no unit left out a key >= T (every e_u <= T).  A unit that fails the
+//    check is rescored in full and selection is repeated, so the result is
+//    always the exact Top-K; ties are broken by the lower position and the
+//    positions are written in ascending order.
 // No floating-point atomics are used, so results are deterministic.
 #include <algorithm>
 
@@ -33,16 +39,16 @@ using namespace dsa;
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kChpMax = 64;                       // pages per unit
-constexpr int kUnitsPerWg = 2;
-constexpr int kKeysLds = kUnitsPerWg * kChpMax * kPage;   // 8192 keys
-constexpr int kStageMax = kKeysLds / 2;           // staged candidates (uint2)
-constexpr int kBins = 4096;
-constexpr int kMaxRows = 1024;                    // rows per launch
-constexpr int kMaxGrid = 2047;
-constexpr int kMaxUnitsPerRow = kMaxGrid + 1;
+constexpr int kUnitPages = 16;
+constexpr int kUnitTok = kUnitPages * kPage;       // 1024 keys per unit
+constexpr int kLocBins = 16384;                    // 14-bit local histogram
+constexpr int kBins = 4096;                        // 12-bit finisher passes
+constexpr int kStageMax = 6656;                    // candidates staged in LDS
+constexpr int kMaxRows = 1024;                     // rows per launch
+constexpr int kMaxBtStride = 16384;                // pages per row (1M tokens)
+constexpr int kMaxUnitsPerRow = kMaxBtStride / kUnitPages;
 
-enum : uint32_t { kErrBarrierTimeout = 1u, kErrPlan = 2u, kErrBadPage = 4u };
+enum : uint32_t { kErrBadPage = 4u, kErrFallback = 8u };
 
 struct Params {
   const uint8_t* q;      // [R, H, 128] E4M3
@@ -57,33 +63,45 @@ struct Params {
   int32_t R;
   int32_t H;
   int32_t topk;
+  int32_t upr;           // units-per-row stride of ucount / uedge
   int32_t* out_idx;
   float* out_score;
   float* dump;           // score rows (test entry point only)
   int64_t ld;
-  uint32_t* ghist;       // [R][4096]
+  uint32_t* hdr;         // [0] next unit, [1] exited workgroups, [2] flags
   uint32_t* tick;        // [R]
-  uint32_t* ucount;      // [R][bt_stride]
+  uint32_t* ucount;      // [R][upr] candidates emitted per unit
+  uint32_t* uedge;       // [R][upr] smallest key a unit may have left out + 1
   uint2* cand;           // [R][bt_stride * 64] (key, position)
-  uint32_t* bar;         // count, generation, error flags
 };
 
 struct Smem {
-  uint32_t keys[kKeysLds];            // unit scores as keys; finisher staging
-  uint32_t hist[kBins];
+  union {
+    struct {
+      uint32_t keys[kUnitTok];
+      uint32_t lhist[kLocBins / 2];   // two 16-bit counters per word
+    } u;
+    struct {
+      uint2 stage[kStageMax];
+      uint32_t hist[kBins];
+    } f;
+  };
   uint32_t rowpre[kMaxRows + 1];      // exclusive prefix of units per row
   uint32_t cpre[kMaxUnitsPerRow + 1]; // finisher: candidate prefix per unit
   uint32_t red[2 * kWaves + 2];
   uint32_t misc[16];
 };
 
-__device__ __forceinline__ void flag_error(uint32_t* bar, uint32_t bits) {
-  if (bar) __hip_atomic_fetch_or(&bar[2], bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void flag_error(uint32_t* hdr, uint32_t bits) {
+  if (hdr) __hip_atomic_fetch_or(&hdr[2], bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
   return b == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(b << 23);
 }
+
+// wait until this wave's global stores have completed (vmcnt(0))
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ---- block primitives (256 threads) -------------------------------------
 
@@ -110,89 +128,99 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* red, uint32_t* total) 
   return before + x - v;
 }
 
-// Exclusive count of `flag` over the block (thread order), plus the total.
-__device__ uint32_t block_excl_count(bool flag, uint32_t* red, uint32_t* total) {
+__device__ uint32_t block_max(uint32_t v, uint32_t* red) {
   const int wv = threadIdx.x >> 6;
-  const uint64_t b = __ballot(flag);
-  if ((threadIdx.x & 63) == 0) red[wv] = (uint32_t)__popcll(b);
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    const uint32_t t = red[i];
-    before += i < wv ? t : 0;
-    tot += t;
-  }
+  for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor(v, d));
+  if ((threadIdx.x & 63) == 0) red[wv] = v;
   __syncthreads();
-  *total = tot;
-  return before + (uint32_t)__popcll(b & lanemask_lt());
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) m = max(m, red[i]);
+  __syncthreads();
+  return m;
 }
 
-// Threshold search over an LDS histogram of nbins (multiple of 256) counts:
-// the largest bin b whose suffix count sum_{b'>=b} reaches `need`.  Writes
-// out[0] = b, out[1] = suffix(b+1), out[2] = total, out[3] = found.
+// Threshold search over an LDS histogram: the largest bin b whose suffix
+// count sum_{b'>=b} reaches `need`.  PACKED: two 16-bit counters per word
+// (bin 2i in the low half).  Writes out[0] = b, out[1] = suffix(b+1),
+// out[2] = total, out[3] = found.
+template <bool PACKED>
 __device__ void find_threshold(const uint32_t* hist, int nbins, uint32_t need, uint32_t* red,
                                uint32_t* out) {
   const int per = nbins / kThreads;
   const int b0 = threadIdx.x * per;
+  auto count = [&](int b) -> uint32_t {
+    return PACKED ? ((hist[b >> 1] >> (16 * (b & 1))) & 0xFFFFu) : hist[b];
+  };
   uint32_t local = 0;
-  for (int i = 0; i < per; ++i) local += hist[b0 + i];
+  for (int i = 0; i < per; ++i) local += count(b0 + i);
   uint32_t total;
   const uint32_t incl = block_excl_scan(local, red, &total) + local;
-  uint32_t run = total - incl;  // count in bins above this thread's range
+  uint32_t run = total - incl;  // keys in bins above this thread's range
   if (threadIdx.x == 0) { out[2] = total; out[3] = 0; }
   __syncthreads();
-  for (int i = per - 1; i >= 0; --i) {
-    const uint32_t c = hist[b0 + i];
-    if (run < need && run + c >= need) {
-      out[0] = (uint32_t)(b0 + i);
-      out[1] = run;
-      out[3] = 1;
-    }
-    run += c;
-  }
-  __syncthreads();
-}
-
-// ---- grid barrier ----------------------------------------------------------
-
-__device__ void grid_barrier(uint32_t* bar, uint32_t G) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t gen = __hip_atomic_load(&bar[1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t old =
-        __hip_atomic_fetch_add(&bar[0], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == G - 1) {
-      __hip_atomic_store(&bar[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(&bar[1], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      // Co-residency is guaranteed by the cooperative launch; the time limit
-      // (about 2 s of the 100 MHz constant clock) only guards against a
-      // broken launch and reports it through the error word.
-      const uint64_t t0 = wall_clock64();
-      while (__hip_atomic_load(&bar[1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == gen) {
-        __builtin_amdgcn_s_sleep(2);
-        if (wall_clock64() - t0 > 200000000ull) {
-          flag_error(bar, kErrBarrierTimeout);
-          break;
-        }
+  if (run < need && run + local >= need) {
+    for (int i = per - 1; i >= 0; --i) {
+      const uint32_t c = count(b0 + i);
+      if (run < need && run + c >= need) {
+        out[0] = (uint32_t)(b0 + i);
+        out[1] = run;
+        out[3] = 1;
       }
+      run += c;
     }
   }
   __syncthreads();
-  __threadfence();
 }
 
-// ---- the plan ----------------------------------------------------------------
+// ---- units ------------------------------------------------------------------
 
 struct Unit {
-  int row, uir, units_r, pg0, pg1, t, slot;
+  int row, uir, units_r, pg0, pg1, t;
 };
 
 // Pages a row scans: positions 0..t, bounded by the block table width.
 __device__ __forceinline__ int row_pages(int t, int bt_stride) {
   return t < 0 ? 1 : min(t / kPage + 1, bt_stride);
+}
+__device__ __forceinline__ int row_units(int t, int bt_stride) {
+  return (row_pages(t, bt_stride) + kUnitPages - 1) / kUnitPages;
+}
+
+__device__ void plan_rows(const Params& P, Smem& S) {
+  const int per = (P.R + kThreads - 1) / kThreads;
+  const int r0 = threadIdx.x * per;
+  uint32_t lu = 0;
+  for (int i = 0; i < per; ++i)
+    if (r0 + i < P.R) lu += (uint32_t)row_units(P.row_pos[r0 + i], P.bt_stride);
+  uint32_t total;
+  uint32_t run = block_excl_scan(lu, S.red, &total);
+  for (int i = 0; i < per; ++i) {
+    if (r0 + i < P.R) {
+      S.rowpre[r0 + i] = run;
+      run += (uint32_t)row_units(P.row_pos[r0 + i], P.bt_stride);
+    }
+  }
+  if (threadIdx.x == 0) S.rowpre[P.R] = total;
+  __syncthreads();
+}
+
+__device__ Unit decode_unit(const Params& P, const Smem& S, uint32_t u) {
+  int lo = 0, hi = P.R - 1;     // row r with rowpre[r] <= u < rowpre[r+1]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (S.rowpre[mid] <= u) lo = mid; else hi = mid - 1;
+  }
+  Unit U;
+  U.row = lo;
+  U.uir = (int)(u - S.rowpre[lo]);
+  U.units_r = (int)(S.rowpre[lo + 1] - S.rowpre[lo]);
+  U.t = P.row_pos[lo];
+  const int pr = row_pages(U.t, P.bt_stride);
+  U.pg0 = U.uir * kUnitPages;
+  U.pg1 = min(pr, U.pg0 + kUnitPages);
+  return U;
 }
 
 // ---- scoring ---------------------------------------------------------------
@@ -203,6 +231,10 @@ struct QOperand {
   float w[NHT][4];  // weights of heads 16i + 4g + c
 };
 
+// Query heads as the A operand of v_mfma_f32_16x16x32_bf16: lane (head
+// 16i + lane%16, group g = lane/16) holds, for k-step s, dims 32g + 8s .. +7
+// dequantised exactly into bf16.  The key operand uses the same k order, so
+// each lane's 32 key bytes form exactly one MXFP8 group with one scale.
 template <int NHT>
 __device__ void load_q(const Params& P, int row, QOperand<NHT>& Q) {
   const int lane = threadIdx.x & 63, hr = lane & 15, g = lane >> 4;
@@ -255,7 +287,8 @@ __device__ __forceinline__ void load_page(const uint8_t* page, PageRegs& pr) {
 }
 
 // Scores of the 64 tokens of one page; lanes 0..15 end with token 16j+lane
-// of tile j in out[j].
+// of tile j in out[j].  Head sum: in-lane over the lane's heads, then across
+// the four lane groups, in a fixed order.
 template <int NHT>
 __device__ __forceinline__ void score_page(const QOperand<NHT>& Q, const PageRegs& pr,
                                            float out[4]) {
@@ -289,12 +322,12 @@ __device__ __forceinline__ void score_page(const QOperand<NHT>& Q, const PageReg
   }
 }
 
+// Score one unit: keys (or dumped scores) of its (pg1-pg0)*64 positions.
 template <int NHT, bool DUMP>
 __device__ void score_unit(const Params& P, const Unit& U, Smem& S) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int seq = P.row_seq[U.row];
   const int32_t* btrow = P.bt + (int64_t)seq * P.bt_stride;
-  uint32_t* keys = S.keys + U.slot * (kChpMax * kPage);
   QOperand<NHT> Q;
   load_q<NHT>(P, U.row, Q);
   PageRegs cur, nxt;
@@ -305,7 +338,7 @@ __device__ void score_unit(const Params& P, const Unit& U, Smem& S) {
     if (U.t < 0 || pg >= P.bt_stride) return nullptr;
     const int32_t id = btrow[pg];
     if (id < 0 || (int64_t)id >= P.pool_pages) {
-      if (lane == 0) flag_error(P.bar, kErrBadPage);
+      if (lane == 0) flag_error(P.hdr, kErrBadPage);
       return nullptr;
     }
     ok = true;
@@ -333,7 +366,7 @@ __device__ void score_unit(const Params& P, const Unit& U, Smem& S) {
         if (DUMP) {
           if (valid && pos < P.ld) P.dump[(int64_t)U.row * P.ld + pos] = sc[j] == 0.f ? 0.f : sc[j];
         } else {
-          keys[(p - U.pg0) * kPage + tok] = valid ? score_key(sc[j]) : 0u;
+          S.u.keys[(p - U.pg0) * kPage + tok] = valid ? score_key(sc[j]) : 0u;
         }
       }
     }
@@ -342,303 +375,344 @@ __device__ void score_unit(const Params& P, const Unit& U, Smem& S) {
   }
 }
 
-// ---- phase 2 helpers ---------------------------------------------------------
+// Keys a unit keeps: about twice its expected share of the Top-K plus a
+// margin (all keys when the row has no more than topk positions).
+__device__ __forceinline__ uint32_t unit_quota(int t, int topk) {
+  const int64_t n = (int64_t)t + 1;
+  if (n <= topk) return 0xFFFFFFFFu;
+  const int64_t m = (2 * (int64_t)topk * kUnitTok + n - 1) / n + 16;
+  return (uint32_t)min<int64_t>(m, kUnitTok);
+}
 
-__device__ __forceinline__ uint2 cand_at(const Params& P, const Smem& S, int row, int chp,
-                                         int n_units, uint32_t f) {
+// Append the unit's keys with 14-bit bin >= edge (all non-zero keys when
+// edge is 0), in position order, to the unit's candidate slice.
+__device__ uint32_t emit_unit_keys(const Params& P, Smem& S, const Unit& U, uint32_t edge_bin) {
+  const int ntok = (U.pg1 - U.pg0) * kPage;
+  uint2* dst = P.cand + (int64_t)U.row * P.bt_stride * kPage + (int64_t)U.pg0 * kPage;
+  constexpr int kPer = kUnitTok / kThreads;       // 4 consecutive keys per thread
+  const int i0 = threadIdx.x * kPer;
+  uint32_t k[kPer];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    k[j] = (i0 + j < ntok) ? S.u.keys[i0 + j] : 0u;
+    cnt += (k[j] != 0u && (k[j] >> 18) >= edge_bin) ? 1u : 0u;
+  }
+  uint32_t total;
+  uint32_t off = block_excl_scan(cnt, S.red, &total);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if (k[j] != 0u && (k[j] >> 18) >= edge_bin) {
+      dst[off++] = make_uint2(k[j], (uint32_t)(U.pg0 * kPage + i0 + j));
+    }
+  }
+  return total;
+}
+
+// Local filter of a scored unit: emit its candidates and record the edge.
+__device__ void filter_unit(const Params& P, Smem& S, const Unit& U) {
+  const int ntok = (U.pg1 - U.pg0) * kPage;
+  const uint32_t quota = unit_quota(U.t, P.topk);
+  uint32_t edge_bin = 0;
+  if (quota < (uint32_t)ntok) {
+    for (int i = threadIdx.x; i < kLocBins / 2; i += kThreads) S.u.lhist[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < ntok; i += kThreads) {
+      const uint32_t key = S.u.keys[i];
+      if (key) {
+        const uint32_t b = key >> 18;
+        atomicAdd(&S.u.lhist[b >> 1], (b & 1u) ? 0x10000u : 1u);
+      }
+    }
+    __syncthreads();
+    find_threshold<true>(S.u.lhist, kLocBins, quota, S.red, S.misc + 8);
+    edge_bin = S.misc[11] ? S.misc[8] : 0u;   // fewer valid keys than the quota: keep all
+  }
+  const uint32_t n = emit_unit_keys(P, S, U, edge_bin);
+  if (threadIdx.x == 0) {
+    const int64_t slot = (int64_t)U.row * P.upr + U.uir;
+    P.ucount[slot] = n;
+    P.uedge[slot] = edge_bin << 18;   // every key left out is below this
+  }
+}
+
+// ---- finisher ------------------------------------------------------------------
+
+__device__ __forceinline__ uint2 cand_at(const Params& P, const Smem& S, int row, int n_units,
+                                         uint32_t f) {
   int lo = 0, hi = n_units - 1;   // last unit u with cpre[u] <= f
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (S.cpre[mid] <= f) lo = mid; else hi = mid - 1;
   }
-  const int64_t base = (int64_t)row * P.bt_stride * kPage + (int64_t)lo * chp * kPage;
+  const int64_t base = (int64_t)row * P.bt_stride * kPage + (int64_t)lo * kUnitTok;
   return P.cand[base + (f - S.cpre[lo])];
 }
 
-__device__ void finish_row(const Params& P, Smem& S, int row, int units_r, int chp,
-                           uint32_t T1, uint32_t above1, bool take_all) {
-  const int K = P.topk;
-  // candidate counts of the row's units -> prefix
-  {
-    uint32_t local = 0;
-    const int per = (units_r + kThreads - 1) / kThreads;
-    const int u0 = threadIdx.x * per;
-    for (int i = 0; i < per; ++i)
-      if (u0 + i < units_r) local += load_agent(&P.ucount[(int64_t)row * P.bt_stride + u0 + i]);
-    uint32_t total;
-    uint32_t run = block_excl_scan(local, S.red, &total);
-    for (int i = 0; i < per; ++i) {
-      if (u0 + i < units_r) {
-        S.cpre[u0 + i] = run;
-        run += load_agent(&P.ucount[(int64_t)row * P.bt_stride + u0 + i]);
-      }
+// prefix of the units' candidate counts; returns the largest recorded edge
+__device__ uint32_t load_counts(const Params& P, Smem& S, int row, int units_r) {
+  const int per = (units_r + kThreads - 1) / kThreads;
+  const int u0 = threadIdx.x * per;
+  uint32_t local = 0, emax = 0;
+  const int64_t base = (int64_t)row * P.upr;
+  for (int i = 0; i < per; ++i) {
+    if (u0 + i < units_r) {
+      local += load_agent(&P.ucount[base + u0 + i]);
+      emax = max(emax, load_agent(&P.uedge[base + u0 + i]));
     }
-    if (threadIdx.x == 0) S.cpre[units_r] = total;
-    __syncthreads();
   }
-  const uint32_t n_c = S.cpre[units_r];
+  uint32_t total;
+  uint32_t run = block_excl_scan(local, S.red, &total);
+  for (int i = 0; i < per; ++i) {
+    if (u0 + i < units_r) {
+      S.cpre[u0 + i] = run;
+      run += load_agent(&P.ucount[base + u0 + i]);
+    }
+  }
+  if (threadIdx.x == 0) S.cpre[units_r] = total;
+  __syncthreads();
+  return block_max(emax, S.red);
+}
+
+// Exact threshold key T of rank K among candidates and the number of keys
+// equal to T to keep.  Returns false if there are fewer than K candidates.
+template <class Get>
+__device__ bool select_threshold(Smem& S, Get get, uint32_t n_c, uint32_t K, uint32_t* T_out,
+                                 uint32_t* ties_out) {
+  uint32_t* hist = S.f.hist;
+  for (int b = threadIdx.x; b < kBins; b += kThreads) hist[b] = 0;
+  __syncthreads();
+  for (uint32_t f = threadIdx.x; f < n_c; f += kThreads) atomicAdd(&hist[get(f).x >> 20], 1u);
+  __syncthreads();
+  find_threshold<false>(hist, kBins, K, S.red, S.misc + 8);
+  if (!S.misc[11]) return false;
+  const uint32_t T1 = S.misc[8], need1 = K - S.misc[9];
+  for (int b = threadIdx.x; b < kBins; b += kThreads) hist[b] = 0;
+  __syncthreads();
+  for (uint32_t f = threadIdx.x; f < n_c; f += kThreads) {
+    const uint32_t k = get(f).x;
+    if ((k >> 20) == T1) atomicAdd(&hist[(k >> 8) & 0xFFFu], 1u);
+  }
+  __syncthreads();
+  find_threshold<false>(hist, kBins, need1, S.red, S.misc + 8);
+  const uint32_t pre = (T1 << 12) | S.misc[8], need2 = need1 - S.misc[9];
+  for (int b = threadIdx.x; b < 256; b += kThreads) hist[b] = 0;
+  __syncthreads();
+  for (uint32_t f = threadIdx.x; f < n_c; f += kThreads) {
+    const uint32_t k = get(f).x;
+    if ((k >> 8) == pre) atomicAdd(&hist[k & 0xFFu], 1u);
+  }
+  __syncthreads();
+  find_threshold<false>(hist, 256, need2, S.red, S.misc + 8);
+  *T_out = (pre << 8) | S.misc[8];
+  *ties_out = need2 - S.misc[9];
+  return true;
+}
+
+// Ordered emission: keys > T, and the first `ties` keys equal to T in
+// position order.  Each thread owns a contiguous segment of candidates.
+template <class Get>
+__device__ void emit_selection(const Params& P, Smem& S, Get get, uint32_t n_c, uint32_t T,
+                               uint32_t ties, int row) {
+  const int K = P.topk;
   int32_t* oidx = P.out_idx + (int64_t)row * K;
   float* osc = P.out_score ? P.out_score + (int64_t)row * K : nullptr;
-  if (take_all) {
-    for (uint32_t f = threadIdx.x; f < n_c && f < (uint32_t)K; f += kThreads) {
-      const uint2 c = cand_at(P, S, row, chp, units_r, f);
-      oidx[f] = (int32_t)c.y;
-      if (osc) osc[f] = key_score(c.x);
-    }
-    for (uint32_t f = n_c + threadIdx.x; f < (uint32_t)K; f += kThreads) {
-      oidx[f] = -1;
-      if (osc) osc[f] = -__builtin_huge_valf();
-    }
-  } else {
-    const bool staged = n_c <= (uint32_t)kStageMax;
-    uint2* stage = reinterpret_cast<uint2*>(S.keys);
-    if (staged)
-      for (uint32_t f = threadIdx.x; f < n_c; f += kThreads) stage[f] = cand_at(P, S, row, chp, units_r, f);
-    __syncthreads();
-    auto get = [&](uint32_t f) -> uint2 { return staged ? stage[f] : cand_at(P, S, row, chp, units_r, f); };
-    // level 2: key bits 19..8 inside bin T1
-    const uint32_t need1 = (uint32_t)K - above1;
-    for (int b = threadIdx.x; b < kBins; b += kThreads) S.hist[b] = 0;
-    __syncthreads();
-    for (uint32_t f = threadIdx.x; f < n_c; f += kThreads) {
-      const uint32_t k = get(f).x;
-      if ((k >> 20) == T1) atomicAdd(&S.hist[(k >> 8) & 0xFFFu], 1u);
-    }
-    __syncthreads();
-    find_threshold(S.hist, kBins, need1, S.red, S.misc + 8);
-    const uint32_t T2 = S.misc[8], need2 = need1 - S.misc[9];
-    // level 3: key bits 7..0
-    for (int b = threadIdx.x; b < kBins; b += kThreads) S.hist[b] = 0;
-    __syncthreads();
-    const uint32_t pre = (T1 << 12) | T2;
-    for (uint32_t f = threadIdx.x; f < n_c; f += kThreads) {
-      const uint32_t k = get(f).x;
-      if ((k >> 8) == pre) atomicAdd(&S.hist[k & 0xFFu], 1u);
-    }
-    __syncthreads();
-    find_threshold(S.hist, kBins, need2, S.red, S.misc + 8);
-    const uint32_t T = (pre << 8) | S.misc[8];
-    const uint32_t need3 = need2 - S.misc[9];   // ties at exactly T to keep
-    // ordered emission: key > T, or key == T among the first need3 ties
-    uint32_t run_keep = 0, run_tie = 0;
-    for (uint32_t base = 0; base < n_c; base += kThreads) {
-      const uint32_t f = base + threadIdx.x;
-      uint2 c = make_uint2(0u, 0u);
-      if (f < n_c) c = get(f);
-      const bool eq = f < n_c && c.x == T;
-      uint32_t tie_tot;
-      const uint32_t tie_rank = run_tie + block_excl_count(eq, S.red, &tie_tot);
-      const bool keep = f < n_c && (c.x > T || (eq && tie_rank < need3));
-      uint32_t keep_tot;
-      const uint32_t opos = run_keep + block_excl_count(keep, S.red, &keep_tot);
-      if (keep && opos < (uint32_t)K) {
-        oidx[opos] = (int32_t)c.y;
-        if (osc) osc[opos] = key_score(c.x);
-      }
-      run_tie += tie_tot;
-      run_keep += keep_tot;
+  const uint32_t seg = (n_c + kThreads - 1) / kThreads;
+  const uint32_t f0 = min(n_c, threadIdx.x * seg), f1 = min(n_c, f0 + seg);
+  uint32_t eq = 0;
+  for (uint32_t f = f0; f < f1; ++f) eq += get(f).x == T ? 1u : 0u;
+  uint32_t tot;
+  const uint32_t tie_base = block_excl_scan(eq, S.red, &tot);
+  uint32_t keep = 0, tr = tie_base;
+  for (uint32_t f = f0; f < f1; ++f) {
+    const uint32_t k = get(f).x;
+    if (k > T) ++keep;
+    else if (k == T) { if (tr < ties) ++keep; ++tr; }
+  }
+  uint32_t opos = block_excl_scan(keep, S.red, &tot);
+  tr = tie_base;
+  for (uint32_t f = f0; f < f1; ++f) {
+    const uint2 c = get(f);
+    bool k = c.x > T;
+    if (c.x == T) { k = tr < ties; ++tr; }
+    if (k && opos < (uint32_t)K) {
+      oidx[opos] = (int32_t)c.y;
+      if (osc) osc[opos] = key_score(c.x);
+      ++opos;
     }
   }
-  // leave the row's workspace zeroed for the next call
-  for (int b = threadIdx.x; b < kBins; b += kThreads) P.ghist[(int64_t)row * kBins + b] = 0;
+}
+
+template <int NHT>
+__device__ void finish_row(const Params& P, Smem& S, const Unit& U0) {
+  const int row = U0.row, units_r = U0.units_r, K = P.topk;
+  const uint32_t emax = load_counts(P, S, row, units_r);
+  uint32_t n_c = S.cpre[units_r];
+  int32_t* oidx = P.out_idx + (int64_t)row * K;
+  float* osc = P.out_score ? P.out_score + (int64_t)row * K : nullptr;
+  auto from_global = [&](uint32_t f) -> uint2 { return cand_at(P, S, row, units_r, f); };
+  if (unit_quota(U0.t, K) == 0xFFFFFFFFu) {
+    // at most topk positions: every unit kept all of its keys
+    for (uint32_t f = threadIdx.x; f < (uint32_t)K; f += kThreads) {
+      if (f < n_c) {
+        const uint2 c = from_global(f);
+        oidx[f] = (int32_t)c.y;
+        if (osc) osc[f] = key_score(c.x);
+      } else {
+        oidx[f] = -1;
+        if (osc) osc[f] = -__builtin_huge_valf();
+      }
+    }
+  } else {
+    uint32_t T = 0, ties = 0;
+    bool ok;
+    const bool staged = n_c <= (uint32_t)kStageMax;
+    if (staged) {
+      for (uint32_t f = threadIdx.x; f < n_c; f += kThreads) S.f.stage[f] = from_global(f);
+      __syncthreads();
+      auto from_lds = [&](uint32_t f) -> uint2 { return S.f.stage[f]; };
+      ok = select_threshold(S, from_lds, n_c, (uint32_t)K, &T, &ties);
+      if (ok && emax <= T) {
+        emit_selection(P, S, from_lds, n_c, T, ties, row);
+        if (threadIdx.x == 0) P.tick[row] = 0;
+        return;
+      }
+    } else {
+      ok = select_threshold(S, from_global, n_c, (uint32_t)K, &T, &ties);
+    }
+    if (!ok || emax > T) {
+      // Some unit may have left out a key that belongs to the Top-K: rescore
+      // every such unit in full and select again (exact, rarely taken).
+      if (threadIdx.x == 0) flag_error(P.hdr, kErrFallback);
+      for (int u = 0; u < units_r; ++u) {
+        const uint32_t e = load_agent(&P.uedge[(int64_t)row * P.upr + u]);
+        const bool redo = ok ? (e > T) : (e > 0u);
+        if (!redo) continue;
+        __syncthreads();
+        Unit V = U0;
+        V.uir = u;
+        V.pg0 = u * kUnitPages;
+        V.pg1 = min(row_pages(V.t, P.bt_stride), V.pg0 + kUnitPages);
+        score_unit<NHT, false>(P, V, S);
+        __syncthreads();
+        const uint32_t n = emit_unit_keys(P, S, V, 0u);
+        if (threadIdx.x == 0) {
+          __hip_atomic_store(&P.ucount[(int64_t)row * P.upr + u], n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(&P.uedge[(int64_t)row * P.upr + u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      __threadfence();
+      __syncthreads();
+      load_counts(P, S, row, units_r);
+      n_c = S.cpre[units_r];
+      select_threshold(S, from_global, n_c, (uint32_t)K, &T, &ties);
+    }
+    emit_selection(P, S, from_global, n_c, T, ties, row);
+  }
   if (threadIdx.x == 0) P.tick[row] = 0;
 }
 
-// ---- the kernel -------------------------------------------------------------
+// ---- the kernels ---------------------------------------------------------------
 
-template <int NHT, bool DUMP>
-__global__ __launch_bounds__(kThreads) void indexer_kernel(Params P) {
+template <int NHT>
+__global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(Params P) {
   __shared__ Smem S;
-  const uint32_t G = gridDim.x;
-  // plan: pages per row, units of chp pages
-  {
-    uint32_t local = 0;
-    const int per = (P.R + kThreads - 1) / kThreads;
-    const int r0 = threadIdx.x * per;
-    for (int i = 0; i < per; ++i)
-      if (r0 + i < P.R) local += (uint32_t)row_pages(P.row_pos[r0 + i], P.bt_stride);
-    uint32_t total_pages;
-    block_excl_scan(local, S.red, &total_pages);
-    uint32_t chp = (total_pages + G - 1) / G;
-    if (chp < 1) chp = 1;
-    if (chp > (uint32_t)kChpMax) {
-      if (threadIdx.x == 0) flag_error(P.bar, kErrPlan);
-      chp = kChpMax;
-    }
-    uint32_t lu = 0;
-    for (int i = 0; i < per; ++i)
-      if (r0 + i < P.R) lu += ((uint32_t)row_pages(P.row_pos[r0 + i], P.bt_stride) + chp - 1) / chp;
-    uint32_t total_units;
-    uint32_t run = block_excl_scan(lu, S.red, &total_units);
-    for (int i = 0; i < per; ++i) {
-      if (r0 + i < P.R) {
-        S.rowpre[r0 + i] = run;
-        run += ((uint32_t)row_pages(P.row_pos[r0 + i], P.bt_stride) + chp - 1) / chp;
-      }
-    }
-    if (threadIdx.x == 0) {
-      S.rowpre[P.R] = total_units;
-      S.misc[0] = chp;
-      if (total_units > kUnitsPerWg * G) flag_error(P.bar, kErrPlan);
-    }
-    __syncthreads();
-  }
-  const int chp = (int)S.misc[0];
+  plan_rows(P, S);
   const uint32_t U_total = S.rowpre[P.R];
-  Unit units[kUnitsPerWg];
-  int n_my = 0;
-#pragma unroll
-  for (int k = 0; k < kUnitsPerWg; ++k) {
-    const uint32_t u = blockIdx.x + k * G;
-    Unit& U = units[k];
-    U.slot = k;
-    if (u >= U_total) { U.row = -1; continue; }
-    n_my = k + 1;
-    int lo = 0, hi = P.R - 1;     // row r with rowpre[r] <= u < rowpre[r+1]
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (S.rowpre[mid] <= u) lo = mid; else hi = mid - 1;
-    }
-    U.row = lo;
-    U.uir = (int)(u - S.rowpre[lo]);
-    U.units_r = (int)(S.rowpre[lo + 1] - S.rowpre[lo]);
-    U.t = P.row_pos[lo];
-    const int pr = row_pages(U.t, P.bt_stride);
-    U.pg0 = U.uir * chp;
-    U.pg1 = min(pr, U.pg0 + chp);
-  }
-  // phase 1: scores
-#pragma unroll
-  for (int k = 0; k < kUnitsPerWg; ++k)
-    if (k < n_my) score_unit<NHT, DUMP>(P, units[k], S);
-  if (DUMP) return;
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < kUnitsPerWg; ++k) {
-    if (k >= n_my) break;
-    const Unit& U = units[k];
-    const uint32_t* keys = S.keys + U.slot * (kChpMax * kPage);
-    const int ntok = (U.pg1 - U.pg0) * kPage;
-    for (int b = threadIdx.x; b < kBins; b += kThreads) S.hist[b] = 0;
+  for (;;) {
+    if (threadIdx.x == 0) S.misc[0] = atomic_add_agent(&P.hdr[0], 1u);
     __syncthreads();
-    for (int i = threadIdx.x; i < ntok; i += kThreads) {
-      const uint32_t key = keys[i];
-      if (key) atomicAdd(&S.hist[key >> 20], 1u);
-    }
+    const uint32_t u = S.misc[0];
     __syncthreads();
-    for (int b = threadIdx.x; b < kBins; b += kThreads) {
-      const uint32_t c = S.hist[b];
-      if (c) atomic_add_agent(&P.ghist[(int64_t)U.row * kBins + b], c);
-    }
+    if (u >= U_total) break;
+    const Unit U = decode_unit(P, S, u);
+    score_unit<NHT, false>(P, U, S);
     __syncthreads();
-  }
-  grid_barrier(P.bar, G);
-  // phase 2: per-unit threshold and ordered candidate emission
-  uint32_t T1s[kUnitsPerWg], above1s[kUnitsPerWg];
-  bool take_alls[kUnitsPerWg];
-#pragma unroll
-  for (int k = 0; k < kUnitsPerWg; ++k) {
-    if (k >= n_my) break;
-    const Unit& U = units[k];
-    for (int b = threadIdx.x; b < kBins; b += kThreads)
-      S.hist[b] = load_agent(&P.ghist[(int64_t)U.row * kBins + b]);
-    __syncthreads();
-    find_threshold(S.hist, kBins, (uint32_t)P.topk, S.red, S.misc + 8);
-    const bool take_all = S.misc[11] == 0;     // fewer valid keys than topk
-    const uint32_t T1 = take_all ? 0u : S.misc[8];
-    T1s[k] = T1;
-    above1s[k] = take_all ? 0u : S.misc[9];
-    take_alls[k] = take_all;
-    const uint32_t* keys = S.keys + U.slot * (kChpMax * kPage);
-    const int ntok = (U.pg1 - U.pg0) * kPage;
-    uint2* dst = P.cand + (int64_t)U.row * P.bt_stride * kPage + (int64_t)U.pg0 * kPage;
-    uint32_t run = 0;
-    for (int base = 0; base < ntok; base += kThreads) {
-      const int i = base + threadIdx.x;
-      const uint32_t key = i < ntok ? keys[i] : 0u;
-      const bool f = key != 0u && (key >> 20) >= T1;
-      uint32_t tot;
-      const uint32_t off = run + block_excl_count(f, S.red, &tot);
-      if (f) dst[off] = make_uint2(key, (uint32_t)(U.pg0 * kPage + i));
-      run += tot;
-    }
-    if (threadIdx.x == 0) P.ucount[(int64_t)U.row * P.bt_stride + U.uir] = run;
-    __syncthreads();
-  }
-  // tickets: the last unit of a row finishes it
-#pragma unroll
-  for (int k = 0; k < kUnitsPerWg; ++k) {
-    if (k >= n_my) break;
-    const Unit& U = units[k];
-    __threadfence();
+    filter_unit(P, S, U);
+    // publish the unit's candidates, then take the row's ticket
+    wait_vm();
     __syncthreads();
     if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       const uint32_t old = atomic_add_agent(&P.tick[U.row], 1u);
       S.misc[1] = (old == (uint32_t)U.units_r - 1) ? 1u : 0u;
+      if (S.misc[1]) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
     if (S.misc[1]) {
-      __threadfence();
-      if (U.units_r <= kMaxUnitsPerRow)
-        finish_row(P, S, U.row, U.units_r, chp, T1s[k], above1s[k], take_alls[k]);
-      else if (threadIdx.x == 0)
-        flag_error(P.bar, kErrPlan);
+      finish_row<NHT>(P, S, U);
       __syncthreads();
     }
+  }
+  // the last workgroup out re-arms the unit counter for the next call
+  if (threadIdx.x == 0) {
+    const uint32_t done = atomic_add_agent(&P.hdr[1], 1u);
+    if (done == gridDim.x - 1) {
+      __hip_atomic_store(&P.hdr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&P.hdr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Test entry: write every score of every row (units assigned statically).
+template <int NHT>
+__global__ __launch_bounds__(kThreads, 2) void indexer_dump_kernel(Params P) {
+  __shared__ Smem S;
+  plan_rows(P, S);
+  const uint32_t U_total = S.rowpre[P.R];
+  for (uint32_t u = blockIdx.x; u < U_total; u += gridDim.x) {
+    const Unit U = decode_unit(P, S, u);
+    score_unit<NHT, true>(P, U, S);
   }
 }
 
 // ---- host side ----------------------------------------------------------------
 
 struct Layout {
-  size_t bar, ghist, tick, ucount, cand, total;
+  size_t hdr, tick, ucount, uedge, cand, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+int units_stride(int64_t bt_stride) { return (int)((bt_stride + kUnitPages - 1) / kUnitPages); }
+
 Layout layout_for(int64_t rows, int64_t bt_stride) {
   Layout L;
+  const int64_t upr = units_stride(bt_stride);
   size_t off = 0;
-  L.bar = off; off += 256;
-  L.ghist = off; off += align256((size_t)rows * kBins * 4);
+  L.hdr = off; off += 256;
   L.tick = off; off += align256((size_t)rows * 4);
-  L.ucount = off; off += align256((size_t)rows * bt_stride * 4);
+  L.ucount = off; off += align256((size_t)rows * upr * 4);
+  L.uedge = off; off += align256((size_t)rows * upr * 4);
   L.cand = off; off += align256((size_t)rows * bt_stride * kPage * 8);
   L.total = off;
   return L;
 }
 
-template <int NHT, bool DUMP>
-void* kernel_ptr() { return reinterpret_cast<void*>(&indexer_kernel<NHT, DUMP>); }
-
 void* pick_kernel(int nht, bool dump) {
   switch (nht) {
-    case 1: return dump ? kernel_ptr<1, true>() : kernel_ptr<1, false>();
-    case 2: return dump ? kernel_ptr<2, true>() : kernel_ptr<2, false>();
-    case 3: return dump ? kernel_ptr<3, true>() : kernel_ptr<3, false>();
-    default: return dump ? kernel_ptr<4, true>() : kernel_ptr<4, false>();
+    case 1: return dump ? (void*)&indexer_dump_kernel<1> : (void*)&indexer_topk_kernel<1>;
+    case 2: return dump ? (void*)&indexer_dump_kernel<2> : (void*)&indexer_topk_kernel<2>;
+    case 3: return dump ? (void*)&indexer_dump_kernel<3> : (void*)&indexer_topk_kernel<3>;
+    default: return dump ? (void*)&indexer_dump_kernel<4> : (void*)&indexer_topk_kernel<4>;
   }
 }
 
-// co-resident workgroups of the fused kernel on the current device
-int coresident_capacity(void* fn) {
+// resident workgroups of a kernel on the current device (cached per device)
+int resident_capacity(void* fn, int slot) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
-  static int cached[64][4];
-  static bool have[64][4];
-  int nht_slot = 0;
-  for (int i = 1; i <= 4; ++i)
-    if (fn == pick_kernel(i, false)) nht_slot = i - 1;
-  if (dev < 64 && have[dev][nht_slot]) return cached[dev][nht_slot];
+  static int cached[64][8];
+  static bool have[64][8];
+  if (dev < 64 && have[dev][slot]) return cached[dev][slot];
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return -1;
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn),
                                                    kThreads, 0) != hipSuccess)
     return -1;
-  int cap = per_cu * prop.multiProcessorCount;
-  if (cap > kMaxGrid) cap = kMaxGrid;
-  if (dev < 64) { cached[dev][nht_slot] = cap; have[dev][nht_slot] = true; }
+  const int cap = std::max(1, per_cu) * prop.multiProcessorCount;
+  if (dev < 64) { cached[dev][slot] = cap; have[dev][slot] = true; }
   return cap;
 }
 
@@ -648,21 +722,20 @@ int validate(const void* q, const void* qs, const float* w, const void* kpool, i
   if (!q || !qs || !w || !kpool || !bt || !row_seq || !row_pos) return DSA_ERR_INVALID_ARG;
   if (R < 0 || bt_stride <= 0 || pool_pages <= 0) return DSA_ERR_INVALID_ARG;
   if (H < 1 || H > DSA_MAX_INDEX_HEADS) return DSA_ERR_UNSUPPORTED;
+  if (bt_stride > kMaxBtStride) return DSA_ERR_UNSUPPORTED;
   return DSA_OK;
 }
 
 int run(Params P, bool dump, hipStream_t stream) {
   const int nht = (P.H + 15) / 16;
   void* fn = pick_kernel(nht, dump);
-  const int cap = coresident_capacity(pick_kernel(nht, false));
+  const int cap = resident_capacity(fn, (nht - 1) + (dump ? 4 : 0));
   if (cap <= 0) return DSA_ERR_HIP;
-  const int64_t rows_by_pages = (int64_t)cap * kChpMax / P.bt_stride;
-  int64_t rpl = std::min<int64_t>({(int64_t)kMaxRows, (int64_t)cap, rows_by_pages});
-  if (rpl < 1) return DSA_ERR_UNSUPPORTED;   // one row's history exceeds one launch
   const int R = P.R;
-  for (int r0 = 0; r0 < R; r0 += (int)rpl) {
+  const int upr = units_stride(P.bt_stride);
+  for (int r0 = 0; r0 < R; r0 += kMaxRows) {
     Params Q = P;
-    const int rn = (int)std::min<int64_t>(rpl, R - r0);
+    const int rn = std::min(kMaxRows, R - r0);
     Q.R = rn;
     Q.q = P.q + (int64_t)r0 * P.H * kIdxDim;
     Q.qs = P.qs + (int64_t)r0 * P.H * 4;
@@ -675,20 +748,35 @@ int run(Params P, bool dump, hipStream_t stream) {
       Q.out_idx = P.out_idx + (int64_t)r0 * P.topk;
       Q.out_score = P.out_score ? P.out_score + (int64_t)r0 * P.topk : nullptr;
     }
-    const int64_t G = std::min<int64_t>((int64_t)cap, std::max<int64_t>((int64_t)rn, (int64_t)rn * P.bt_stride));
+    const int64_t G = std::min<int64_t>((int64_t)cap, (int64_t)rn * upr);
     void* args[] = {&Q};
-    hipError_t e;
-    if (dump)
-      e = hipLaunchKernel(fn, dim3((unsigned)G), dim3(kThreads), args, 0, stream);
-    else
-      e = hipLaunchCooperativeKernel(fn, dim3((unsigned)G), dim3(kThreads), args, 0, stream);
-    if (e != hipSuccess) return DSA_ERR_HIP;
+    if (hipLaunchKernel(fn, dim3((unsigned)G), dim3(kThreads), args, 0, stream) != hipSuccess)
+      return DSA_ERR_HIP;
   }
   return DSA_OK;
 }
 
 __global__ void fill_kernel(float* p, int64_t n, float v) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+Params base_params(const void* q_fp8, const void* q_e8m0, const float* w, const void* k_pool,
+                   int64_t pool_pages, const int32_t* block_table, int32_t bt_stride,
+                   const int32_t* row_seq, const int32_t* row_pos, int32_t R, int32_t H_I) {
+  Params P{};
+  P.q = static_cast<const uint8_t*>(q_fp8);
+  P.qs = static_cast<const uint8_t*>(q_e8m0);
+  P.w = w;
+  P.kpool = static_cast<const uint8_t*>(k_pool);
+  P.pool_pages = pool_pages;
+  P.bt = block_table;
+  P.bt_stride = bt_stride;
+  P.row_seq = row_seq;
+  P.row_pos = row_pos;
+  P.R = R;
+  P.H = H_I;
+  P.upr = units_stride(bt_stride);
+  return P;
 }
 
 }  // namespace
@@ -718,25 +806,15 @@ extern "C" int dsa_indexer_topk(const void* q_fp8, const void* q_e8m0, const flo
   const Layout L = layout_for(rows, bt_stride);
   if (workspace == nullptr || workspace_bytes < L.total) return DSA_ERR_WORKSPACE;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  Params P{};
-  P.q = static_cast<const uint8_t*>(q_fp8);
-  P.qs = static_cast<const uint8_t*>(q_e8m0);
-  P.w = w;
-  P.kpool = static_cast<const uint8_t*>(k_pool);
-  P.pool_pages = pool_pages;
-  P.bt = block_table;
-  P.bt_stride = bt_stride;
-  P.row_seq = row_seq;
-  P.row_pos = row_pos;
-  P.R = R;
-  P.H = H_I;
+  Params P = base_params(q_fp8, q_e8m0, w, k_pool, pool_pages, block_table, bt_stride, row_seq,
+                         row_pos, R, H_I);
   P.topk = topk;
   P.out_idx = out_idx;
   P.out_score = out_score;
-  P.bar = reinterpret_cast<uint32_t*>(ws + L.bar);
-  P.ghist = reinterpret_cast<uint32_t*>(ws + L.ghist);
+  P.hdr = reinterpret_cast<uint32_t*>(ws + L.hdr);
   P.tick = reinterpret_cast<uint32_t*>(ws + L.tick);
   P.ucount = reinterpret_cast<uint32_t*>(ws + L.ucount);
+  P.uedge = reinterpret_cast<uint32_t*>(ws + L.uedge);
   P.cand = reinterpret_cast<uint2*>(ws + L.cand);
   return run(P, false, dsa_host::as_stream(stream));
 }
@@ -756,21 +834,11 @@ extern "C" int dsa_indexer_scores(const void* q_fp8, const void* q_e8m0, const f
   hipLaunchKernelGGL(fill_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 65536)), dim3(256), 0, s,
                      out_scores, n, -__builtin_huge_valf());
   if (hipGetLastError() != hipSuccess) return DSA_ERR_HIP;
-  Params P{};
-  P.q = static_cast<const uint8_t*>(q_fp8);
-  P.qs = static_cast<const uint8_t*>(q_e8m0);
-  P.w = w;
-  P.kpool = static_cast<const uint8_t*>(k_pool);
-  P.pool_pages = pool_pages;
-  P.bt = block_table;
-  P.bt_stride = bt_stride;
-  P.row_seq = row_seq;
-  P.row_pos = row_pos;
-  P.R = R;
-  P.H = H_I;
+  Params P = base_params(q_fp8, q_e8m0, w, k_pool, pool_pages, block_table, bt_stride, row_seq,
+                         row_pos, R, H_I);
   P.topk = 1;
   P.dump = out_scores;
   P.ld = ld;
-  P.bar = nullptr;   // the score dump uses no workspace
+  P.hdr = nullptr;   // the score dump uses no workspace
   return run(P, true, s);
 }

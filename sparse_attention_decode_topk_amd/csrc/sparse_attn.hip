@@ -5,9 +5,11 @@
 // Day0 page, "FP8 KVCache ..." and "Preserving a Mixed-Precision Path").
 //
 // One workgroup = (query row, group of 16 heads, split of the index list).
-// Per 64-token tile:
-//  * gather: the 64 selected 656-byte records are fetched one tile ahead
-//    into registers and staged in LDS (latent rows padded to 528 bytes);
+//  * up front, every entry of the split is translated position -> page ->
+//    record slot in one parallel pass (slots kept in LDS);
+//  * per 64-token tile: the 64 selected 656-byte records are fetched one
+//    tile ahead into registers and staged in LDS (latent rows padded to 528
+//    bytes);
 //  * logits: wave w owns tokens 16w..16w+15.  S^T = K Q^T on
 //    v_mfma_f32_16x16x32_bf16: E4M3 latent -> bf16 is exact, each 128-wide
 //    tile accumulates separately and is multiplied by its fp32 tile scale in
@@ -33,8 +35,11 @@ constexpr int kWaves = 4;
 constexpr int kTile = 64;
 constexpr int kHG = 16;                 // heads per workgroup
 constexpr int kLatStride = 528;         // LDS bytes per staged latent row
+constexpr int kPPStride = 72;           // fp16 per P' row (64 + 8 pad)
 constexpr int kChunks = kRec / 16;      // 41 16-byte pieces per record
 constexpr int kLoads = (kTile * kChunks + kThreads - 1) / kThreads;   // 11
+constexpr int kMaxTiles = DSA_MAX_TOPK / kTile;                       // 32
+constexpr int kSlotsPerThread = kMaxTiles * kTile / kThreads;         // 8
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxSplits = 64;
@@ -60,37 +65,25 @@ struct Params {
 };
 
 struct Smem {
-  uint8_t lat[kTile * kLatStride];          // 33792
+  uint8_t lat[kTile * kLatStride];          // 33792 (combine: normalised split weights)
   uint16_t rope[kTile * kRope];             // 8192
   float scl[kTile * 4];                     // 1024
-  _Float16 pp[4][kHG][kTile];               // P' per latent tile, 8192
-  const uint8_t* rec[2][kTile];             // record pointers of the current/next tile
+  _Float16 pp[4][kHG][kPPStride];           // P' per latent tile, 9216
+  int32_t slot[kMaxTiles * kTile];          // record slot per entry of the split, -1 = none
   float wmax[kWaves][kHG];
   float wsum[kWaves][kHG];
   float alpha[kHG];
-  int32_t eref_new[4];
   int32_t emax[4];
+  uint32_t last;
 };
 
 __device__ __forceinline__ void flag(uint32_t* err, uint32_t bits) {
   if (err) __hip_atomic_fetch_or(err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// record pointer of list entry j of this row (null if j is out of range, the
-// entry is -1, or its page is not in the table/pool)
-__device__ __forceinline__ const uint8_t* record_of(const Params& P, const int32_t* idxrow,
-                                                    const int32_t* btrow, int j, int jend) {
-  if (j >= jend) return nullptr;
-  const int32_t v = idxrow[j];
-  if (v < 0) return nullptr;
-  const int pg = v >> 6;
-  if (pg >= P.bt_stride) { flag(P.err, 1u); return nullptr; }
-  const int32_t pid = btrow[pg];
-  if (pid < 0 || (int64_t)pid >= P.pool_pages) { flag(P.err, 1u); return nullptr; }
-  return P.pool + ((int64_t)pid * kPage + (v & 63)) * kRec;
-}
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-__global__ __launch_bounds__(kThreads) void sfa_kernel(Params P) {
+__global__ __launch_bounds__(kThreads, 2) void sfa_kernel(Params P) {
   __shared__ Smem S;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int hr = lane & 15, g = lane >> 4;
@@ -104,6 +97,34 @@ __global__ __launch_bounds__(kThreads) void sfa_kernel(Params P) {
   const int j0 = sp * P.per_split;
   const int jend = min(P.topk, j0 + P.per_split);
   const int ntiles = jend > j0 ? (jend - j0 + kTile - 1) / kTile : 0;
+
+  // ---- record slots of every entry of the split (two dependent loads, all
+  //      entries in flight together) ----
+  {
+    int32_t v[kSlotsPerThread];
+#pragma unroll
+    for (int i = 0; i < kSlotsPerThread; ++i) {
+      const int e = tid + i * kThreads;
+      v[i] = (e < ntiles * kTile && j0 + e < jend) ? idxrow[j0 + e] : -1;
+    }
+    int32_t pid[kSlotsPerThread];
+#pragma unroll
+    for (int i = 0; i < kSlotsPerThread; ++i) {
+      pid[i] = -1;
+      if (v[i] >= 0) {
+        if ((v[i] >> 6) < P.bt_stride) pid[i] = btrow[v[i] >> 6];
+        else flag(P.err, 1u);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kSlotsPerThread; ++i) {
+      const int e = tid + i * kThreads;
+      int32_t s = -1;
+      if (v[i] >= 0 && pid[i] >= 0 && (int64_t)pid[i] < P.pool_pages) s = pid[i] * kPage + (v[i] & 63);
+      else if (v[i] >= 0 && (v[i] >> 6) < P.bt_stride) flag(P.err, 1u);
+      if (e < kMaxTiles * kTile) S.slot[e] = s;
+    }
+  }
 
   // queries of this lane's head as the B operand: k-step (t, j) holds dims
   // 128t + 32g + 8j .. +7; rope steps r hold dims 512 + 32r + 8g .. +7
@@ -127,24 +148,26 @@ __global__ __launch_bounds__(kThreads) void sfa_kernel(Params P) {
       qb[16 + r] = __builtin_bit_cast(v8bf, v);
     }
   }
+  __syncthreads();
 
-  // running softmax state of head hr (identical in every wave) and this
-  // wave's output block: dims 128*wv + 16d + hr, heads 4g + c
+  // running softmax state of head hr (identical in every wave), running
+  // power-of-two references of the four latent tiles (identical in every
+  // wave), and this wave's output block: dims 128*wv + 16d + hr, heads 4g+c
   float m_run = -__builtin_huge_valf(), l_run = 0.f;
-  int eref = -1000;                       // power-of-two reference of tile wv
+  int eref[4] = {-1000, -1000, -1000, -1000};
   v4f o[8];
 #pragma unroll
   for (int d = 0; d < 8; ++d) o[d] = v4f{0.f, 0.f, 0.f, 0.f};
 
   uint4 buf[kLoads];
-  auto issue_loads = [&](int slot) {
+  auto issue_loads = [&](int it) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int c = tid + i * kThreads;
       buf[i] = make_uint4(0, 0, 0, 0);
       if (c < kTile * kChunks) {
-        const uint8_t* r = S.rec[slot][c / kChunks];
-        if (r) buf[i] = *reinterpret_cast<const uint4*>(r + (c % kChunks) * 16);
+        const int32_t s = S.slot[it * kTile + c / kChunks];
+        if (s >= 0) buf[i] = *reinterpret_cast<const uint4*>(P.pool + (int64_t)s * kRec + (c % kChunks) * 16);
       }
     }
   };
@@ -164,27 +187,21 @@ __global__ __launch_bounds__(kThreads) void sfa_kernel(Params P) {
     }
   };
 
-  if (ntiles > 0) {
-    if (tid < kTile) S.rec[0][tid] = record_of(P, idxrow, btrow, j0 + tid, jend);
-    __syncthreads();
-    issue_loads(0);
-  }
+  if (ntiles > 0) issue_loads(0);
 
   for (int it = 0; it < ntiles; ++it) {
-    const int cur = it & 1;
     __syncthreads();                      // previous tile fully consumed
     stage();
     if (tid < 4) S.emax[tid] = -1000;
-    if (tid < kTile) S.rec[cur ^ 1][tid] = record_of(P, idxrow, btrow, j0 + (it + 1) * kTile + tid, jend);
     __syncthreads();
-    if (tid < kTile && S.rec[cur][tid] != nullptr) {
+    if (it + 1 < ntiles) issue_loads(it + 1);
+    if (tid < kTile && S.slot[it * kTile + tid] >= 0) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const float s = S.scl[tid * 4 + t];
         if (s > 0.f) atomicMax(&S.emax[t], (int)((__float_as_uint(s) >> 23) & 0xFF) - 127);
       }
     }
-    if (it + 1 < ntiles) issue_loads(cur ^ 1);
 
     // ---- logits of tokens 16wv .. 16wv+15 (lane: head hr, tokens 4g+c) ----
     const int tok_a = 16 * wv + hr;       // A-operand row of this lane
@@ -221,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void sfa_kernel(Params P) {
       float v = acc[4][c];
 #pragma unroll
       for (int t = 0; t < 4; ++t) v = __builtin_fmaf(sc[t], acc[t][c], v);
-      z[c] = S.rec[cur][tok] != nullptr ? v * P.scale_log2 : -__builtin_huge_valf();
+      z[c] = S.slot[it * kTile + tok] >= 0 ? v * P.scale_log2 : -__builtin_huge_valf();
       zmax = fmaxf(zmax, z[c]);
     }
     zmax = fmaxf(zmax, __shfl_xor(zmax, 16));
@@ -243,14 +260,17 @@ __global__ __launch_bounds__(kThreads) void sfa_kernel(Params P) {
     psum += __shfl_xor(psum, 32);
     if (lane < 16) S.wsum[wv][hr] = psum;
     if (wv == 0 && lane < 16) S.alpha[hr] = alpha;
-    // P' of latent tile t uses the reference wave t publishes:
-    // max(its running reference, the largest scale exponent of this tile)
-    if (lane == 0) S.eref_new[wv] = max(eref, S.emax[wv]);
-    __syncthreads();
+    // running references: largest scale exponent seen so far per latent tile
+    int eold_w = eref[0];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t == wv) eold_w = eref[t];
+      eref[t] = max(eref[t], S.emax[t]);
+    }
     // P' for every latent tile t: p * scale[t] * 2^(8 - Eref_t)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int e = S.eref_new[t];
+      const int e = eref[t];
       const float mul = e > -1000 ? pow2f(max(-126, min(127, 8 - e))) : 0.f;
       _Float16 h[4];
 #pragma unroll
@@ -268,9 +288,11 @@ __global__ __launch_bounds__(kThreads) void sfa_kernel(Params P) {
     m_run = m_new;
 
     // ---- P'.V for latent tile wv ----
-    const int e_new = S.eref_new[wv];
-    const float resc = (eref > -1000 && e_new > eref) ? pow2f(max(-126, eref - e_new)) : 1.0f;
-    eref = e_new;
+    int enew_w = eref[0];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (t == wv) enew_w = eref[t];
+    const float resc = (eold_w > -1000 && enew_w > eold_w) ? pow2f(max(-126, eold_w - enew_w)) : 1.0f;
     float al[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) al[c] = S.alpha[4 * g + c] * resc;
@@ -300,12 +322,16 @@ __global__ __launch_bounds__(kThreads) void sfa_kernel(Params P) {
   }
 
   // ---- epilogue ----
-  // o holds sum_j p_j * v_j / 2^(8 - eref) for heads 4g+c, dims 128wv+16d+hr
-  const float oscale = eref > -1000 ? pow2f(max(-126, min(127, eref - 8))) : 0.f;
-  const int HGs = HGn;
-  const int64_t pair = (int64_t)row * HGs + hg;
+  // o holds sum_j p_j * v_j / 2^(eref_w - 8) for heads 4g+c, dims 128wv+16d+hr
+  int ew = eref[0];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    if (t == wv) ew = eref[t];
+  const float oscale = ew > -1000 ? pow2f(max(-126, min(127, ew - 8))) : 0.f;
+  const int64_t pair = (int64_t)row * HGn + hg;
   if (P.S == 1) {
     // l and m of head 4g+c live in lanes whose hr == 4g+c: share via LDS
+    __syncthreads();
     if (wv == 0 && lane < 16) { S.wsum[0][hr] = l_run; S.wmax[0][hr] = m_run; }
     __syncthreads();
 #pragma unroll
@@ -335,33 +361,68 @@ __global__ __launch_bounds__(kThreads) void sfa_kernel(Params P) {
     pm[2 * hr] = m_run;
     pm[2 * hr + 1] = l_run;
   }
-  __threadfence();
+  wait_vm();
   __syncthreads();
-  __shared__ uint32_t last;
-  if (tid == 0) last = atomic_add_agent(&P.tick[pair], 1u) == (uint32_t)P.S - 1 ? 1u : 0u;
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    S.last = atomic_add_agent(&P.tick[pair], 1u) == (uint32_t)P.S - 1 ? 1u : 0u;
+    if (S.last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
   __syncthreads();
-  if (!last) return;
-  __threadfence();
-  // combine: 16 heads x 512 dims over S splits; thread handles 32 outputs
-  for (int e = tid; e < kHG * kLatent; e += kThreads) {
-    const int h = e / kLatent, dim = e % kLatent;
-    const int hh = kHG * hg + h;
+  if (!S.last) return;
+  // normalised weights of every (split, head) in LDS; lse per head
+  float* cw = reinterpret_cast<float*>(S.lat);        // [S][16]
+  if (tid < kHG) {
+    const int h = tid;
+    const float* pm = P.part_ml + pair * P.S * (kHG * 2);
     float M = -__builtin_huge_valf();
-    for (int s = 0; s < P.S; ++s) M = fmaxf(M, P.part_ml[((pair * P.S + s) * kHG + h) * 2]);
-    float L = 0.f, acc = 0.f;
-    if (M != -__builtin_huge_valf()) {
-      for (int s = 0; s < P.S; ++s) {
-        const float* pm = P.part_ml + ((pair * P.S + s) * kHG + h) * 2;
-        const float wgt = pm[0] == -__builtin_huge_valf() ? 0.f : exp2f(pm[0] - M);
-        L += wgt * pm[1];
-        acc += wgt * P.part_o[(pair * P.S + s) * (kHG * kLatent) + e];
+    for (int s = 0; s < P.S; ++s) M = fmaxf(M, pm[(s * kHG + h) * 2]);
+    float L = 0.f;
+    for (int s = 0; s < P.S; ++s) {
+      const float m = pm[(s * kHG + h) * 2];
+      const float wgt = (M == -__builtin_huge_valf() || m == -__builtin_huge_valf()) ? 0.f : exp2f(m - M);
+      cw[s * kHG + h] = wgt;
+      L += wgt * pm[(s * kHG + h) * 2 + 1];
+    }
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    for (int s = 0; s < P.S; ++s) cw[s * kHG + h] *= inv;
+    const int hh = kHG * hg + h;
+    if (P.lse && hh < P.H)
+      P.lse[(int64_t)row * P.H + hh] = L > 0.f ? (M + log2f(L)) * kLn2 : -__builtin_huge_valf();
+  }
+  __syncthreads();
+  // 16 heads x 128 float4 per split; thread owns 8 float4 (q = tid + 256 j)
+  const float4* src4 = reinterpret_cast<const float4*>(P.part_o + pair * P.S * (kHG * kLatent));
+  float4 acc4[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc4[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < P.S; s0 += 4) {
+    float4 v[4][8];
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v[ds][j] = (s0 + ds < P.S) ? src4[(s0 + ds) * (kHG * kLatent / 4) + tid + 256 * j]
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+      if (s0 + ds >= P.S) break;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float wgt = cw[(s0 + ds) * kHG + (tid + 256 * j) / 128];
+        acc4[j].x += wgt * v[ds][j].x;
+        acc4[j].y += wgt * v[ds][j].y;
+        acc4[j].z += wgt * v[ds][j].z;
+        acc4[j].w += wgt * v[ds][j].w;
       }
     }
-    if (hh < P.H) {
-      P.out[((int64_t)row * P.H + hh) * kLatent + dim] = L > 0.f ? acc / L : 0.f;
-      if (P.lse && dim == 0)
-        P.lse[(int64_t)row * P.H + hh] = L > 0.f ? (M + log2f(L)) * kLn2 : -__builtin_huge_valf();
-    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int q = tid + 256 * j;
+    const int h = q / 128, col = q % 128;
+    const int hh = kHG * hg + h;
+    if (hh < P.H) reinterpret_cast<float4*>(P.out + ((int64_t)row * P.H + hh) * kLatent)[col] = acc4[j];
   }
   if (tid == 0) P.tick[pair] = 0;
 }
@@ -420,6 +481,7 @@ extern "C" int dsa_sparse_attn(const void* q_bf16, const void* kv_pool, int64_t 
   if (!(softmax_scale > 0.f) || softmax_scale > 1e30f) return DSA_ERR_INVALID_ARG;
   if (H < 1 || H > DSA_MAX_ATTN_HEADS) return DSA_ERR_UNSUPPORTED;
   if (topk < 1 || topk > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
+  if (pool_pages > (int64_t(1) << 25)) return DSA_ERR_UNSUPPORTED;   // slots fit int32
   if (R == 0) return DSA_OK;
   const Layout L = layout_for(R, H, topk);
   if (workspace == nullptr || workspace_bytes < L.total) return DSA_ERR_WORKSPACE;

@@ -62,9 +62,9 @@ def test_indexer_deterministic_and_workspace_reuse(need_gpu):
     b = st.indexer(workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
-    # barrier counter back at zero, no error reported
+    # work counters re-armed for the next call, no page-id error reported
     w = ws.view(torch.int32).cpu().numpy()
-    assert w[0] == 0 and w[2] == 0
+    assert w[0] == 0 and w[1] == 0 and (w[2] & 4) == 0
 
 
 def test_needles_are_selected(need_gpu):
@@ -155,3 +155,31 @@ def test_chunked_prefill_sampled_rows(need_gpu):
     for r in rows:
         t = int(inp["row_pos"][r])
         check_topk_row(idx[r], sc[r], o.topk(r), st.topk, t)
+
+
+def test_concentrated_topk_takes_exact_fallback(need_gpu):
+    """All head weights positive and the keys of positions 3000..5099 scaled
+    by 8: every Top-K position lies in that range, so the unit covering
+    3072..4095 holds far more than its quota of the Top-K.  The finisher must
+    notice and rescore it; the result still follows the pass rule, the kernel's
+    selection equals the exact Top-K of its own scores, and the workspace
+    reports that the rescore path ran."""
+    say("[indexer] concentrated Top-K (rescore path)")
+    inp = dict(synth.make("decode_8k_needles", with_sfa=False))
+    inp["w"] = np.abs(inp["w"])
+    k = inp["k_idx"].copy()
+    k[3000:5100] = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(k[3000:5100]) * np.float32(8))
+    inp["k_idx"] = k
+    st = DeviceState(inp, with_sfa=False)
+    ws = ops.indexer_workspace(st.R, st.block_table.shape[1], st.H_I, st.topk)
+    idx, sc = st.indexer(workspace=ws)
+    scores = st.scores().cpu().numpy()
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    flags = int(ws.view(torch.int32)[2].item())
+    assert flags & 8, "the rescore path was expected to run"
+    o = Oracle(inp)
+    ora = o.topk(0)
+    t = int(inp["row_pos"][0])
+    check_topk_row(idx[0], sc[0], ora, st.topk, t)
+    assert np.array_equal(idx[0], exact_topk_of(scores[0], st.topk))
+    assert np.sum((idx[0] >= 3000) & (idx[0] < 5100)) > 1900
