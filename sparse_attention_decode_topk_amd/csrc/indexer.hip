@@ -41,9 +41,9 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnitPages = 16;
 constexpr int kUnitTok = kUnitPages * kPage;       // 1024 keys per unit
-constexpr int kLocBins = 16384;                    // 14-bit local histogram
-constexpr int kBins = 4096;                        // 12-bit finisher passes
-constexpr int kStageMax = 6656;                    // candidates staged in LDS
+constexpr int kBins = 4096;                        // 12-bit histogram passes
+constexpr int kCandPer = 24;                       // finisher candidates per thread
+constexpr int kChunk = kCandPer * kThreads;        // candidates staged in LDS at once
 constexpr int kMaxRows = 1024;                     // rows per launch
 constexpr int kMaxBtStride = 16384;                // pages per row (1M tokens)
 constexpr int kMaxUnitsPerRow = kMaxBtStride / kUnitPages;
@@ -71,21 +71,14 @@ struct Params {
   uint32_t* hdr;         // [0] next unit, [1] exited workgroups, [2] flags
   uint32_t* tick;        // [R]
   uint32_t* ucount;      // [R][upr] candidates emitted per unit
-  uint32_t* uedge;       // [R][upr] smallest key a unit may have left out + 1
+  uint32_t* uedge;       // [R][upr] every key a unit left out is below this
   uint2* cand;           // [R][bt_stride * 64] (key, position)
 };
 
 struct Smem {
-  union {
-    struct {
-      uint32_t keys[kUnitTok];
-      uint32_t lhist[kLocBins / 2];   // two 16-bit counters per word
-    } u;
-    struct {
-      uint2 stage[kStageMax];
-      uint32_t hist[kBins];
-    } f;
-  };
+  uint32_t keys[kUnitTok];            // scores of the current unit as keys
+  uint2 stage[kChunk];                // finisher: a chunk of candidates
+  uint32_t hist[kBins];
   uint32_t rowpre[kMaxRows + 1];      // exclusive prefix of units per row
   uint32_t cpre[kMaxUnitsPerRow + 1]; // finisher: candidate prefix per unit
   uint32_t red[2 * kWaves + 2];
@@ -141,18 +134,14 @@ __device__ uint32_t block_max(uint32_t v, uint32_t* red) {
   return m;
 }
 
-// Threshold search over an LDS histogram: the largest bin b whose suffix
-// count sum_{b'>=b} reaches `need`.  PACKED: two 16-bit counters per word
-// (bin 2i in the low half).  Writes out[0] = b, out[1] = suffix(b+1),
-// out[2] = total, out[3] = found.
-template <bool PACKED>
+// Threshold search over an LDS histogram of nbins (a multiple of 256)
+// counts: the largest bin b whose suffix count sum_{b'>=b} reaches `need`.
+// Writes out[0] = b, out[1] = suffix(b+1), out[2] = total, out[3] = found.
 __device__ void find_threshold(const uint32_t* hist, int nbins, uint32_t need, uint32_t* red,
                                uint32_t* out) {
   const int per = nbins / kThreads;
   const int b0 = threadIdx.x * per;
-  auto count = [&](int b) -> uint32_t {
-    return PACKED ? ((hist[b >> 1] >> (16 * (b & 1))) & 0xFFFFu) : hist[b];
-  };
+  auto count = [&](int b) -> uint32_t { return hist[b]; };
   uint32_t local = 0;
   for (int i = 0; i < per; ++i) local += count(b0 + i);
   uint32_t total;
@@ -270,34 +259,38 @@ __device__ void load_q(const Params& P, int row, QOperand<NHT>& Q) {
   }
 }
 
-struct PageRegs {
-  uint4 d[8];       // token tile j: d[2j], d[2j+1] = this lane's 32 bytes
-  uint32_t s[4];    // E8M0 byte of this lane's block, per token tile
+// Half a page (two token tiles of 16) as held by one lane: for tile
+// j = 2*half + jj, d[2jj], d[2jj+1] are this lane's 32 bytes of token
+// 16j + lane%16 (dims 32g..32g+31, g = lane/16) and s[jj] its E8M0 byte.
+struct HalfRegs {
+  uint4 d[4];
+  uint32_t s[2];
 };
 
-__device__ __forceinline__ void load_page(const uint8_t* page, PageRegs& pr) {
-  const int lane = threadIdx.x & 63, hr = lane & 15, g = lane >> 4;
+__device__ __forceinline__ void load_half(const uint8_t* page, int half, HalfRegs& hr) {
+  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint8_t* src = page + (16 * j + hr) * kIdxDim + 32 * g;
-    pr.d[2 * j] = *reinterpret_cast<const uint4*>(src);
-    pr.d[2 * j + 1] = *reinterpret_cast<const uint4*>(src + 16);
-    pr.s[j] = page[kKScaleOff + (16 * j + hr) * 4 + g];
+  for (int jj = 0; jj < 2; ++jj) {
+    const int tok = 16 * (2 * half + jj) + r;
+    const uint8_t* src = page + tok * kIdxDim + 32 * g;
+    hr.d[2 * jj] = *reinterpret_cast<const uint4*>(src);
+    hr.d[2 * jj + 1] = *reinterpret_cast<const uint4*>(src + 16);
+    hr.s[jj] = page[kKScaleOff + tok * 4 + g];
   }
 }
 
-// Scores of the 64 tokens of one page; lanes 0..15 end with token 16j+lane
-// of tile j in out[j].  Head sum: in-lane over the lane's heads, then across
-// the four lane groups, in a fixed order.
+// Scores of the 32 tokens of one half page; lanes 0..15 end with token
+// 16jj + lane of the half in out[jj].  Head sum: in-lane over the lane's
+// heads, then across the four lane groups, in a fixed order.
 template <int NHT>
-__device__ __forceinline__ void score_page(const QOperand<NHT>& Q, const PageRegs& pr,
-                                           float out[4]) {
+__device__ __forceinline__ void score_half(const QOperand<NHT>& Q, const HalfRegs& hr,
+                                           float out[2]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float ks = e8m0_to_f32(pr.s[j]);
-    const uint32_t dw[8] = {pr.d[2 * j].x,     pr.d[2 * j].y,     pr.d[2 * j].z,
-                            pr.d[2 * j].w,     pr.d[2 * j + 1].x, pr.d[2 * j + 1].y,
-                            pr.d[2 * j + 1].z, pr.d[2 * j + 1].w};
+  for (int jj = 0; jj < 2; ++jj) {
+    const float ks = e8m0_to_f32(hr.s[jj]);
+    const uint32_t dw[8] = {hr.d[2 * jj].x,     hr.d[2 * jj].y,     hr.d[2 * jj].z,
+                            hr.d[2 * jj].w,     hr.d[2 * jj + 1].x, hr.d[2 * jj + 1].y,
+                            hr.d[2 * jj + 1].z, hr.d[2 * jj + 1].w};
     v8bf kb[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -318,75 +311,80 @@ __device__ __forceinline__ void score_page(const QOperand<NHT>& Q, const PageReg
     }
     part += __shfl_xor(part, 16);
     part += __shfl_xor(part, 32);
-    out[j] = part;
+    out[jj] = part;
   }
 }
 
 // Score one unit: keys (or dumped scores) of its (pg1-pg0)*64 positions.
+// Wave w takes half pages w, w+4, w+8, ... of the unit and keeps three of
+// them in flight (a ring of three register buffers, unrolled so no buffer
+// is ever copied).
 template <int NHT, bool DUMP>
 __device__ void score_unit(const Params& P, const Unit& U, Smem& S) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int seq = P.row_seq[U.row];
   const int32_t* btrow = P.bt + (int64_t)seq * P.bt_stride;
-  QOperand<NHT> Q;
-  load_q<NHT>(P, U.row, Q);
-  PageRegs cur, nxt;
-  bool cur_ok = false;
-  int p = U.pg0 + wv;
-  auto page_ptr = [&](int pg, bool& ok) -> const uint8_t* {
-    ok = false;
-    if (U.t < 0 || pg >= P.bt_stride) return nullptr;
+  const int nhalf = 2 * (U.pg1 - U.pg0);
+  auto fetch = [&](int h, HalfRegs& b) -> bool {
+    if (U.t < 0 || h >= nhalf) return false;
+    const int pg = U.pg0 + (h >> 1);
     const int32_t id = btrow[pg];
     if (id < 0 || (int64_t)id >= P.pool_pages) {
       if (lane == 0) flag_error(P.hdr, kErrBadPage);
-      return nullptr;
+      return false;
     }
-    ok = true;
-    return P.kpool + (int64_t)id * kKPageBytes;
+    load_half(P.kpool + (int64_t)id * kKPageBytes, h & 1, b);
+    return true;
   };
-  if (p < U.pg1) {
-    const uint8_t* pp = page_ptr(p, cur_ok);
-    if (cur_ok) load_page(pp, cur);
-  }
-  for (; p < U.pg1; p += kWaves) {
-    bool nxt_ok = false;
-    const int pn = p + kWaves;
-    if (pn < U.pg1) {
-      const uint8_t* pp = page_ptr(pn, nxt_ok);
-      if (nxt_ok) load_page(pp, nxt);
-    }
-    float sc[4] = {0.f, 0.f, 0.f, 0.f};
-    if (cur_ok) score_page<NHT>(Q, cur, sc);
+  auto consume = [&](int h, const HalfRegs& b, bool ok, const QOperand<NHT>& Q) {
+    float sc[2] = {0.f, 0.f};
+    if (ok) score_half<NHT>(Q, b, sc);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tok = 16 * j + lane;      // valid for lanes 0..15
-      const int pos = p * kPage + tok;
-      const bool valid = cur_ok && pos <= U.t;
+    for (int jj = 0; jj < 2; ++jj) {
+      const int tok = 32 * h + 16 * jj + lane;      // unit-local, lanes 0..15
+      const int pos = U.pg0 * kPage + tok;
+      const bool valid = ok && pos <= U.t;
       if (lane < 16) {
         if (DUMP) {
-          if (valid && pos < P.ld) P.dump[(int64_t)U.row * P.ld + pos] = sc[j] == 0.f ? 0.f : sc[j];
+          if (valid && pos < P.ld) P.dump[(int64_t)U.row * P.ld + pos] = sc[jj] == 0.f ? 0.f : sc[jj];
         } else {
-          S.u.keys[(p - U.pg0) * kPage + tok] = valid ? score_key(sc[j]) : 0u;
+          S.keys[tok] = valid ? score_key(sc[jj]) : 0u;
         }
       }
     }
-    cur = nxt;
-    cur_ok = nxt_ok;
+  };
+  HalfRegs b0, b1, b2;
+  int h = wv;
+  bool ok0 = fetch(h, b0);
+  bool ok1 = fetch(h + kWaves, b1);
+  QOperand<NHT> Q;
+  load_q<NHT>(P, U.row, Q);
+  for (; h < nhalf; h += 3 * kWaves) {
+    bool ok2 = fetch(h + 2 * kWaves, b2);
+    consume(h, b0, ok0, Q);
+    if (h + kWaves >= nhalf) break;
+    ok0 = fetch(h + 3 * kWaves, b0);
+    consume(h + kWaves, b1, ok1, Q);
+    if (h + 2 * kWaves >= nhalf) break;
+    ok1 = fetch(h + 4 * kWaves, b1);
+    consume(h + 2 * kWaves, b2, ok2, Q);
   }
 }
 
-// Keys a unit keeps: about twice its expected share of the Top-K plus a
-// margin (all keys when the row has no more than topk positions).
+// Keys a unit keeps: its expected share E of the Top-K (about
+// topk * 1024 / (t+1)) plus four standard deviations and a margin; every key
+// when the row has no more than topk positions.
 __device__ __forceinline__ uint32_t unit_quota(int t, int topk) {
   const int64_t n = (int64_t)t + 1;
   if (n <= topk) return 0xFFFFFFFFu;
-  const int64_t m = (2 * (int64_t)topk * kUnitTok + n - 1) / n + 16;
-  return (uint32_t)min<int64_t>(m, kUnitTok);
+  const float e = (float)topk * (float)kUnitTok / (float)n;
+  const float m = e + 4.0f * sqrtf(e) + 8.0f;
+  return (uint32_t)fminf(ceilf(m), (float)kUnitTok);
 }
 
-// Append the unit's keys with 14-bit bin >= edge (all non-zero keys when
-// edge is 0), in position order, to the unit's candidate slice.
-__device__ uint32_t emit_unit_keys(const Params& P, Smem& S, const Unit& U, uint32_t edge_bin) {
+// Append the unit's keys >= edge (all non-zero keys when edge is 0), in
+// position order, to the unit's candidate slice.
+__device__ uint32_t emit_unit_keys(const Params& P, Smem& S, const Unit& U, uint32_t edge) {
   const int ntok = (U.pg1 - U.pg0) * kPage;
   uint2* dst = P.cand + (int64_t)U.row * P.bt_stride * kPage + (int64_t)U.pg0 * kPage;
   constexpr int kPer = kUnitTok / kThreads;       // 4 consecutive keys per thread
@@ -395,61 +393,61 @@ __device__ uint32_t emit_unit_keys(const Params& P, Smem& S, const Unit& U, uint
   uint32_t cnt = 0;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    k[j] = (i0 + j < ntok) ? S.u.keys[i0 + j] : 0u;
-    cnt += (k[j] != 0u && (k[j] >> 18) >= edge_bin) ? 1u : 0u;
+    k[j] = (i0 + j < ntok) ? S.keys[i0 + j] : 0u;
+    cnt += (k[j] != 0u && k[j] >= edge) ? 1u : 0u;
   }
   uint32_t total;
   uint32_t off = block_excl_scan(cnt, S.red, &total);
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    if (k[j] != 0u && (k[j] >> 18) >= edge_bin) {
+    if (k[j] != 0u && k[j] >= edge) {
       dst[off++] = make_uint2(k[j], (uint32_t)(U.pg0 * kPage + i0 + j));
     }
   }
   return total;
 }
 
-// Local filter of a scored unit: emit its candidates and record the edge.
+// Local filter of a scored unit: the edge is the lower end of the 20-bit key
+// bin holding the unit's quota-th largest key (two LDS histogram passes of
+// 12 and 8 bits); keys at or above it are emitted, so every key left out is
+// below the recorded edge.
 __device__ void filter_unit(const Params& P, Smem& S, const Unit& U) {
   const int ntok = (U.pg1 - U.pg0) * kPage;
   const uint32_t quota = unit_quota(U.t, P.topk);
-  uint32_t edge_bin = 0;
+  uint32_t edge = 0;
   if (quota < (uint32_t)ntok) {
-    for (int i = threadIdx.x; i < kLocBins / 2; i += kThreads) S.u.lhist[i] = 0;
+    for (int i = threadIdx.x; i < kBins; i += kThreads) S.hist[i] = 0;
     __syncthreads();
     for (int i = threadIdx.x; i < ntok; i += kThreads) {
-      const uint32_t key = S.u.keys[i];
-      if (key) {
-        const uint32_t b = key >> 18;
-        atomicAdd(&S.u.lhist[b >> 1], (b & 1u) ? 0x10000u : 1u);
-      }
+      const uint32_t key = S.keys[i];
+      if (key) atomicAdd(&S.hist[key >> 20], 1u);
     }
     __syncthreads();
-    find_threshold<true>(S.u.lhist, kLocBins, quota, S.red, S.misc + 8);
-    edge_bin = S.misc[11] ? S.misc[8] : 0u;   // fewer valid keys than the quota: keep all
+    find_threshold(S.hist, kBins, quota, S.red, S.misc + 8);
+    if (S.misc[11]) {
+      const uint32_t T1 = S.misc[8], need = quota - S.misc[9];
+      for (int i = threadIdx.x; i < 256; i += kThreads) S.hist[i] = 0;
+      __syncthreads();
+      for (int i = threadIdx.x; i < ntok; i += kThreads) {
+        const uint32_t key = S.keys[i];
+        if (key && (key >> 20) == T1) atomicAdd(&S.hist[(key >> 12) & 0xFFu], 1u);
+      }
+      __syncthreads();
+      find_threshold(S.hist, 256, need, S.red, S.misc + 8);
+      edge = (T1 << 20) | (S.misc[8] << 12);
+    }
   }
-  const uint32_t n = emit_unit_keys(P, S, U, edge_bin);
+  const uint32_t n = emit_unit_keys(P, S, U, edge);
   if (threadIdx.x == 0) {
     const int64_t slot = (int64_t)U.row * P.upr + U.uir;
     P.ucount[slot] = n;
-    P.uedge[slot] = edge_bin << 18;   // every key left out is below this
+    P.uedge[slot] = edge;   // every key left out is below this
   }
 }
 
 // ---- finisher ------------------------------------------------------------------
 
-__device__ __forceinline__ uint2 cand_at(const Params& P, const Smem& S, int row, int n_units,
-                                         uint32_t f) {
-  int lo = 0, hi = n_units - 1;   // last unit u with cpre[u] <= f
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (S.cpre[mid] <= f) lo = mid; else hi = mid - 1;
-  }
-  const int64_t base = (int64_t)row * P.bt_stride * kPage + (int64_t)lo * kUnitTok;
-  return P.cand[base + (f - S.cpre[lo])];
-}
-
-// prefix of the units' candidate counts; returns the largest recorded edge
+// prefix of the units' candidate counts (S.cpre); returns the largest edge
 __device__ uint32_t load_counts(const Params& P, Smem& S, int row, int units_r) {
   const int per = (units_r + kThreads - 1) / kThreads;
   const int u0 = threadIdx.x * per;
@@ -474,72 +472,104 @@ __device__ uint32_t load_counts(const Params& P, Smem& S, int row, int units_r) 
   return block_max(emax, S.red);
 }
 
-// Exact threshold key T of rank K among candidates and the number of keys
-// equal to T to keep.  Returns false if there are fewer than K candidates.
-template <class Get>
-__device__ bool select_threshold(Smem& S, Get get, uint32_t n_c, uint32_t K, uint32_t* T_out,
-                                 uint32_t* ties_out) {
-  uint32_t* hist = S.f.hist;
-  for (int b = threadIdx.x; b < kBins; b += kThreads) hist[b] = 0;
-  __syncthreads();
-  for (uint32_t f = threadIdx.x; f < n_c; f += kThreads) atomicAdd(&hist[get(f).x >> 20], 1u);
-  __syncthreads();
-  find_threshold<false>(hist, kBins, K, S.red, S.misc + 8);
-  if (!S.misc[11]) return false;
-  const uint32_t T1 = S.misc[8], need1 = K - S.misc[9];
-  for (int b = threadIdx.x; b < kBins; b += kThreads) hist[b] = 0;
-  __syncthreads();
-  for (uint32_t f = threadIdx.x; f < n_c; f += kThreads) {
-    const uint32_t k = get(f).x;
-    if ((k >> 20) == T1) atomicAdd(&hist[(k >> 8) & 0xFFFu], 1u);
+// Stage candidates [ch*kChunk, ...) of the row (flat order = position
+// order) into LDS.  Element f goes to thread f % 256; every element finds its
+// unit by binary search over the count prefix, so all loads are independent
+// and in flight together.  Returns the number staged.
+__device__ uint32_t stage_chunk(const Params& P, Smem& S, int row, int units_r, uint32_t n_c,
+                                uint32_t ch) {
+  const uint32_t base = ch * kChunk;
+  const uint32_t n = base < n_c ? min((uint32_t)kChunk, n_c - base) : 0u;
+  const uint2* rowc = P.cand + (int64_t)row * P.bt_stride * kPage;
+#pragma unroll
+  for (int k = 0; k < kCandPer; ++k) {
+    const uint32_t i = threadIdx.x + k * kThreads;
+    if (i < n) {
+      const uint32_t f = base + i;
+      int u = 0, hi = units_r - 1;   // last unit with cpre[u] <= f
+      while (u < hi) {
+        const int mid = (u + hi + 1) >> 1;
+        if (S.cpre[mid] <= f) u = mid; else hi = mid - 1;
+      }
+      S.stage[i] = rowc[(int64_t)u * kUnitTok + (f - S.cpre[u])];
+    }
   }
   __syncthreads();
-  find_threshold<false>(hist, kBins, need1, S.red, S.misc + 8);
-  const uint32_t pre = (T1 << 12) | S.misc[8], need2 = need1 - S.misc[9];
-  for (int b = threadIdx.x; b < 256; b += kThreads) hist[b] = 0;
-  __syncthreads();
-  for (uint32_t f = threadIdx.x; f < n_c; f += kThreads) {
-    const uint32_t k = get(f).x;
-    if ((k >> 8) == pre) atomicAdd(&hist[k & 0xFFu], 1u);
+  return n;
+}
+
+// Exact key T of rank K among the candidates and the number of keys equal
+// to T to keep (three histogram passes of 12, 12 and 8 bits).  Returns false
+// if there are fewer than K candidates.  With more than one chunk every
+// pass restages them.
+__device__ bool select_threshold(const Params& P, Smem& S, int row, int units_r, uint32_t n_c,
+                                 uint32_t K, uint32_t* T_out, uint32_t* ties_out) {
+  const uint32_t nch = (n_c + kChunk - 1) / kChunk;
+  uint32_t prefix = 0, need = K;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int nb = pass < 2 ? kBins : 256;
+    const uint32_t shift = pass == 0 ? 20u : (pass == 1 ? 8u : 0u);
+    const uint32_t mask = pass < 2 ? 0xFFFu : 0xFFu;
+    const uint32_t pshift = pass == 1 ? 20u : 8u;
+    for (int b = threadIdx.x; b < nb; b += kThreads) S.hist[b] = 0;
+    __syncthreads();
+    for (uint32_t ch = 0; ch < nch; ++ch) {
+      const uint32_t n = nch > 1 ? stage_chunk(P, S, row, units_r, n_c, ch) : n_c;
+      for (uint32_t f = threadIdx.x; f < n; f += kThreads) {
+        const uint32_t k = S.stage[f].x;
+        if (pass == 0 || (k >> pshift) == prefix) atomicAdd(&S.hist[(k >> shift) & mask], 1u);
+      }
+      __syncthreads();
+    }
+    find_threshold(S.hist, nb, need, S.red, S.misc + 8);
+    if (!S.misc[11]) return false;
+    need -= S.misc[9];
+    prefix = (prefix << (pass < 2 ? 12 : 8)) | S.misc[8];
   }
-  __syncthreads();
-  find_threshold<false>(hist, 256, need2, S.red, S.misc + 8);
-  *T_out = (pre << 8) | S.misc[8];
-  *ties_out = need2 - S.misc[9];
+  *T_out = prefix;
+  *ties_out = need;
   return true;
 }
 
-// Ordered emission: keys > T, and the first `ties` keys equal to T in
-// position order.  Each thread owns a contiguous segment of candidates.
-template <class Get>
-__device__ void emit_selection(const Params& P, Smem& S, Get get, uint32_t n_c, uint32_t T,
-                               uint32_t ties, int row) {
+// Ordered emission of keys > T and the first `ties` keys equal to T; each
+// thread owns a contiguous segment of every staged chunk.
+__device__ void emit_selection(const Params& P, Smem& S, int row, int units_r, uint32_t n_c,
+                               uint32_t T, uint32_t ties) {
   const int K = P.topk;
   int32_t* oidx = P.out_idx + (int64_t)row * K;
   float* osc = P.out_score ? P.out_score + (int64_t)row * K : nullptr;
-  const uint32_t seg = (n_c + kThreads - 1) / kThreads;
-  const uint32_t f0 = min(n_c, threadIdx.x * seg), f1 = min(n_c, f0 + seg);
-  uint32_t eq = 0;
-  for (uint32_t f = f0; f < f1; ++f) eq += get(f).x == T ? 1u : 0u;
-  uint32_t tot;
-  const uint32_t tie_base = block_excl_scan(eq, S.red, &tot);
-  uint32_t keep = 0, tr = tie_base;
-  for (uint32_t f = f0; f < f1; ++f) {
-    const uint32_t k = get(f).x;
-    if (k > T) ++keep;
-    else if (k == T) { if (tr < ties) ++keep; ++tr; }
-  }
-  uint32_t opos = block_excl_scan(keep, S.red, &tot);
-  tr = tie_base;
-  for (uint32_t f = f0; f < f1; ++f) {
-    const uint2 c = get(f);
-    bool k = c.x > T;
-    if (c.x == T) { k = tr < ties; ++tr; }
-    if (k && opos < (uint32_t)K) {
-      oidx[opos] = (int32_t)c.y;
-      if (osc) osc[opos] = key_score(c.x);
-      ++opos;
+  const uint32_t nch = (n_c + kChunk - 1) / kChunk;
+  uint32_t run_tie = 0, run_keep = 0;
+  for (uint32_t ch = 0; ch < nch; ++ch) {
+    const uint32_t n = nch > 1 ? stage_chunk(P, S, row, units_r, n_c, ch) : n_c;
+    const uint32_t seg = (n + kThreads - 1) / kThreads;
+    const uint32_t f0 = min(n, threadIdx.x * seg), f1 = min(n, f0 + seg);
+    uint32_t eq = 0;
+    for (uint32_t f = f0; f < f1; ++f) eq += S.stage[f].x == T ? 1u : 0u;
+    uint32_t tot_eq;
+    const uint32_t tie_base = run_tie + block_excl_scan(eq, S.red, &tot_eq);
+    uint32_t keep = 0, tr = tie_base;
+    for (uint32_t f = f0; f < f1; ++f) {
+      const uint32_t k = S.stage[f].x;
+      if (k > T) ++keep;
+      else if (k == T) { if (tr < ties) ++keep; ++tr; }
     }
+    uint32_t tot_keep;
+    uint32_t opos = run_keep + block_excl_scan(keep, S.red, &tot_keep);
+    tr = tie_base;
+    for (uint32_t f = f0; f < f1; ++f) {
+      const uint2 c = S.stage[f];
+      bool kp = c.x > T;
+      if (c.x == T) { kp = tr < ties; ++tr; }
+      if (kp && opos < (uint32_t)K) {
+        oidx[opos] = (int32_t)c.y;
+        if (osc) osc[opos] = key_score(c.x);
+        ++opos;
+      }
+    }
+    run_tie += tot_eq;
+    run_keep += tot_keep;
+    __syncthreads();
   }
 }
 
@@ -550,14 +580,13 @@ __device__ void finish_row(const Params& P, Smem& S, const Unit& U0) {
   uint32_t n_c = S.cpre[units_r];
   int32_t* oidx = P.out_idx + (int64_t)row * K;
   float* osc = P.out_score ? P.out_score + (int64_t)row * K : nullptr;
-  auto from_global = [&](uint32_t f) -> uint2 { return cand_at(P, S, row, units_r, f); };
   if (unit_quota(U0.t, K) == 0xFFFFFFFFu) {
     // at most topk positions: every unit kept all of its keys
+    stage_chunk(P, S, row, units_r, n_c, 0);
     for (uint32_t f = threadIdx.x; f < (uint32_t)K; f += kThreads) {
       if (f < n_c) {
-        const uint2 c = from_global(f);
-        oidx[f] = (int32_t)c.y;
-        if (osc) osc[f] = key_score(c.x);
+        oidx[f] = (int32_t)S.stage[f].y;
+        if (osc) osc[f] = key_score(S.stage[f].x);
       } else {
         oidx[f] = -1;
         if (osc) osc[f] = -__builtin_huge_valf();
@@ -565,21 +594,8 @@ __device__ void finish_row(const Params& P, Smem& S, const Unit& U0) {
     }
   } else {
     uint32_t T = 0, ties = 0;
-    bool ok;
-    const bool staged = n_c <= (uint32_t)kStageMax;
-    if (staged) {
-      for (uint32_t f = threadIdx.x; f < n_c; f += kThreads) S.f.stage[f] = from_global(f);
-      __syncthreads();
-      auto from_lds = [&](uint32_t f) -> uint2 { return S.f.stage[f]; };
-      ok = select_threshold(S, from_lds, n_c, (uint32_t)K, &T, &ties);
-      if (ok && emax <= T) {
-        emit_selection(P, S, from_lds, n_c, T, ties, row);
-        if (threadIdx.x == 0) P.tick[row] = 0;
-        return;
-      }
-    } else {
-      ok = select_threshold(S, from_global, n_c, (uint32_t)K, &T, &ties);
-    }
+    if (n_c <= (uint32_t)kChunk) stage_chunk(P, S, row, units_r, n_c, 0);
+    bool ok = select_threshold(P, S, row, units_r, n_c, (uint32_t)K, &T, &ties);
     if (!ok || emax > T) {
       // Some unit may have left out a key that belongs to the Top-K: rescore
       // every such unit in full and select again (exact, rarely taken).
@@ -605,9 +621,10 @@ __device__ void finish_row(const Params& P, Smem& S, const Unit& U0) {
       __syncthreads();
       load_counts(P, S, row, units_r);
       n_c = S.cpre[units_r];
-      select_threshold(S, from_global, n_c, (uint32_t)K, &T, &ties);
+      if (n_c <= (uint32_t)kChunk) stage_chunk(P, S, row, units_r, n_c, 0);
+      select_threshold(P, S, row, units_r, n_c, (uint32_t)K, &T, &ties);
     }
-    emit_selection(P, S, from_global, n_c, T, ties, row);
+    emit_selection(P, S, row, units_r, n_c, T, ties);
   }
   if (threadIdx.x == 0) P.tick[row] = 0;
 }

@@ -36,6 +36,7 @@ constexpr int kTile = 64;
 constexpr int kHG = 16;                 // heads per workgroup
 constexpr int kLatStride = 528;         // LDS bytes per staged latent row
 constexpr int kPPStride = 72;           // fp16 per P' row (64 + 8 pad)
+constexpr int kQStride = 584;           // bf16 per staged query row (576 + 8 pad)
 constexpr int kChunks = kRec / 16;      // 41 16-byte pieces per record
 constexpr int kLoads = (kTile * kChunks + kThreads - 1) / kThreads;   // 11
 constexpr int kMaxTiles = DSA_MAX_TOPK / kTile;                       // 32
@@ -70,6 +71,7 @@ struct Smem {
   float scl[kTile * 4];                     // 1024
   _Float16 pp[4][kHG][kPPStride];           // P' per latent tile, 9216
   int32_t slot[kMaxTiles * kTile];          // record slot per entry of the split, -1 = none
+  uint16_t qs[kHG * kQStride];              // the workgroup's 16 query rows (bf16), 18688
   float wmax[kWaves][kHG];
   float wsum[kWaves][kHG];
   float alpha[kHG];
@@ -126,28 +128,21 @@ __global__ __launch_bounds__(kThreads, 2) void sfa_kernel(Params P) {
     }
   }
 
-  // queries of this lane's head as the B operand: k-step (t, j) holds dims
-  // 128t + 32g + 8j .. +7; rope steps r hold dims 512 + 32r + 8g .. +7
+  // the 16 query rows of this head group, staged in LDS; as the B operand,
+  // k-step (t, j) of head hr holds dims 128t + 32g + 8j .. +7 and rope step r
+  // holds dims 512 + 32r + 8g .. +7
   const int head = kHG * hg + hr;
   const bool head_ok = head < P.H;
-  v8bf qb[18];
-  {
-    const uint16_t* qrow = P.q + ((int64_t)row * P.H + (head_ok ? head : 0)) * kQK;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint4 v = head_ok ? *reinterpret_cast<const uint4*>(qrow + 128 * t + 32 * g + 8 * j)
-                                : make_uint4(0, 0, 0, 0);
-        qb[4 * t + j] = __builtin_bit_cast(v8bf, v);
-      }
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const uint4 v = head_ok ? *reinterpret_cast<const uint4*>(qrow + kLatent + 32 * r + 8 * g)
-                              : make_uint4(0, 0, 0, 0);
-      qb[16 + r] = __builtin_bit_cast(v8bf, v);
-    }
+  for (int c = tid; c < kHG * (kQK / 8); c += kThreads) {
+    const int h = c / (kQK / 8), part = c % (kQK / 8);
+    const int hh = kHG * hg + h;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (hh < P.H) v = *reinterpret_cast<const uint4*>(P.q + ((int64_t)row * P.H + hh) * kQK + 8 * part);
+    *reinterpret_cast<uint4*>(S.qs + h * kQStride + 8 * part) = v;
   }
+  auto qop = [&](int off) -> v8bf {
+    return __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(S.qs + hr * kQStride + off));
+  };
   __syncthreads();
 
   // running softmax state of head hr (identical in every wave), running
@@ -192,14 +187,22 @@ __global__ __launch_bounds__(kThreads, 2) void sfa_kernel(Params P) {
   for (int it = 0; it < ntiles; ++it) {
     __syncthreads();                      // previous tile fully consumed
     stage();
-    if (tid < 4) S.emax[tid] = -1000;
     __syncthreads();
     if (it + 1 < ntiles) issue_loads(it + 1);
-    if (tid < kTile && S.slot[it * kTile + tid] >= 0) {
+    if (wv == 0) {
+      // largest scale exponent of each latent tile over the tile's tokens:
+      // positive fp32 bit patterns order like integers, so a wave-wide
+      // integer max of the bits gives the largest scale
+      const bool ok = S.slot[it * kTile + lane] >= 0;
+      const uint4 sb = *reinterpret_cast<const uint4*>(S.scl + lane * 4);
+      uint32_t m[4] = {ok ? sb.x : 0u, ok ? sb.y : 0u, ok ? sb.z : 0u, ok ? sb.w : 0u};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float s = S.scl[tid * 4 + t];
-        if (s > 0.f) atomicMax(&S.emax[t], (int)((__float_as_uint(s) >> 23) & 0xFF) - 127);
+      for (int d = 1; d < 64; d <<= 1)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) m[t] = max(m[t], (uint32_t)__shfl_xor((int)m[t], d));
+      if (lane < 4) {
+        const uint32_t b = lane == 0 ? m[0] : lane == 1 ? m[1] : lane == 2 ? m[2] : m[3];
+        S.emax[lane] = (b & 0x7FFFFFFFu) ? (int)((b >> 23) & 0xFF) - 127 : -1000;
       }
     }
 
@@ -221,13 +224,13 @@ __global__ __launch_bounds__(kThreads, 2) void sfa_kernel(Params P) {
         const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dw[2 * j + 1], 1.0f, false);
         const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dw[2 * j + 1], 1.0f, true);
         const v8bf a = v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[4 * t + j], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop(128 * t + 32 * g + 8 * j), acc[t], 0, 0, 0);
       }
     }
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const uint4 v = *reinterpret_cast<const uint4*>(S.rope + tok_a * kRope + 32 * r + 8 * g);
-      acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, v), qb[16 + r], acc[4], 0, 0, 0);
+      acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, v), qop(kLatent + 32 * r + 8 * g), acc[4], 0, 0, 0);
     }
     float z[4];
     float zmax = -__builtin_huge_valf();
