@@ -1,33 +1,33 @@
-// Lightning Indexer: scoring, head weighting and Top-K fused in one kernel
-// over the paged MXFP8 K cache, with no score matrix written to HBM ("Deep
-// Dive into Sparse Attention ...", section "1. Computation Optimization ...
-// DSA Fused Kernel"; Kimi K3.1 Pro Day0 page, "Lightning Indexer
-// Three-Stream Coordination": scoring, head weighting and Top-K selection
-// fused, with selection pipelined with the paged K-cache reads).
+// Lightning Indexer: scoring, head weighting and Top-K over the paged MXFP8
+// K cache with no score matrix written to HBM ("Deep Dive into Sparse
+// Attention ...", section "1. Computation Optimization ... DSA Fused Kernel";
+// Kimi K3.1 Pro Day0 page, "Lightning Indexer Three-Stream Coordination":
+// scoring, head weighting and Top-K selection fused, selection pipelined with
+// the paged K-cache reads).
 //
 //   I(t,s) = sum_h w[r,h] * max(0, q[r,h] . k[s]),  s <= t = row_pos[r]
 //
-// Work decomposition (one ordinary launch; no grid barrier, no spinning):
-//  * every row's causal history is cut into units of 16 pages (1024
-//    tokens); units are numbered row by row and handed out in that order by
-//    one atomic counter, so rows complete in order and a row's selection
-//    overlaps the scan of later rows;
-//  * a unit: each wave streams pages of the unit (one page in flight ahead),
-//    dequantises the MXFP8 key block exactly into bf16 (E4M3 * 2^(E-127) is
-//    a bf16 value), runs v_mfma_f32_16x16x32_bf16 against the resident query
-//    heads, applies ReLU and the head weights in fp32, and keeps the unit's
-//    scores as order-preserving 32-bit keys in LDS;
-//  * local filter: an LDS histogram of the top 14 key bits gives the bin
-//    edge e_u below which the unit holds fewer than m of its largest keys (m
-//    is about twice the unit's expected share of the Top-K); the unit appends
-//    every key >= e_u, in position order, to its slice of the candidate
-//    workspace and records e_u;
-//  * the last unit of a row (ticket) selects the exact K-th key T among the
-//    candidates with three LDS radix passes (12+12+8 bits) and checks that
-//    no unit left out a key >= T (every e_u <= T).  A unit that fails the
-//    check is rescored in full and selection is repeated, so the result is
-//    always the exact Top-K; ties are broken by the lower position and the
-//    positions are written in ascending order.
+// Two launches on the caller's stream:
+//  1. scan: every row's causal history is cut into units of 16 pages (1024
+//     positions); workgroups take units in row-major order.  For a unit, each
+//     wave streams eight half pages through a three-deep register ring,
+//     dequantises the MXFP8 key block exactly into bf16 (E4M3 * 2^(E-127) is
+//     a bf16 value), runs v_mfma_f32_16x16x32_bf16 against the resident query
+//     heads, applies ReLU and the head weights in fp32 and keeps the unit's
+//     scores as order-preserving 32-bit keys in LDS.  A local filter (two
+//     8-bit LDS histogram passes) finds the edge e_u of the 16-bit key bin
+//     that holds the unit's quota-th largest key (quota: about the unit's
+//     expected share of the Top-K plus four standard deviations); the unit
+//     writes every key >= e_u with its position, in position order, to its
+//     slice of the candidate workspace and records e_u.
+//  2. select: one workgroup per row gathers the row's candidates into LDS,
+//     finds the exact K-th key T among those >= max_u e_u with up to three
+//     radix passes over the occupied key range, and writes the kept
+//     positions in ascending order.  Every key a unit left out is below its
+//     e_u <= T, so the result is the exact Top-K.  When fewer than K
+//     candidates reach max_u e_u, the units whose edge could hide a Top-K key
+//     are rescored in full and the selection is repeated (exact, rarely
+//     taken).  Ties are broken by the lower position.
 // No floating-point atomics are used, so results are deterministic.
 #include <algorithm>
 
@@ -40,13 +40,21 @@ using namespace dsa;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnitPages = 16;
-constexpr int kUnitTok = kUnitPages * kPage;       // 1024 keys per unit
-constexpr int kBins = 4096;                        // 12-bit histogram passes
-constexpr int kCandPer = 24;                       // finisher candidates per thread
-constexpr int kChunk = kCandPer * kThreads;        // candidates staged in LDS at once
-constexpr int kMaxRows = 1024;                     // rows per launch
-constexpr int kMaxBtStride = 16384;                // pages per row (1M tokens)
+constexpr int kUnitTok = kUnitPages * kPage;           // 1024 keys per unit
+constexpr int kHalvesPerWave = 2 * kUnitPages / kWaves;  // 8 half pages per wave
+constexpr int kRing = 3;                               // half pages in flight per wave
+constexpr int kFBins = 256;                            // filter histogram (8-bit passes)
+constexpr int kBins = 4096;                            // select histogram (12-bit passes)
+constexpr int kCandPer = 23;                           // select: candidates per thread
+constexpr int kChunk = kCandPer * kThreads;            // candidates staged in LDS at once
+constexpr int kMaxRows = 1024;                         // rows per launch
+constexpr int kMaxBtStride = 16384;                    // pages per row (1M tokens)
 constexpr int kMaxUnitsPerRow = kMaxBtStride / kUnitPages;
+static_assert(kFBins == kThreads, "one filter bin per thread");
+
+// Buffer descriptor word 3 for raw (untyped) buffer access on gfx9-class
+// GPUs: 32-bit data format, no swizzle.
+constexpr int kRawBufferWord3 = 0x00020000;
 
 enum : uint32_t { kErrBadPage = 4u, kErrFallback = 8u };
 
@@ -68,19 +76,28 @@ struct Params {
   float* out_score;
   float* dump;           // score rows (test entry point only)
   int64_t ld;
-  uint32_t* hdr;         // [0] next unit, [1] exited workgroups, [2] flags
-  uint32_t* tick;        // [R]
+  uint32_t* hdr;         // [2] sticky status bits (may be null)
   uint32_t* ucount;      // [R][upr] candidates emitted per unit
   uint32_t* uedge;       // [R][upr] every key a unit left out is below this
   uint2* cand;           // [R][bt_stride * 64] (key, position)
 };
 
-struct Smem {
+struct ScanSmem {
   uint32_t keys[kUnitTok];            // scores of the current unit as keys
-  uint2 stage[kChunk];                // finisher: a chunk of candidates
-  uint32_t hist[kBins];
+  uint32_t hist[kFBins];
   uint32_t rowpre[kMaxRows + 1];      // exclusive prefix of units per row
-  uint32_t cpre[kMaxUnitsPerRow + 1]; // finisher: candidate prefix per unit
+  uint32_t red[2 * kWaves + 2];
+  uint32_t misc[16];
+};
+
+struct SelSmem {
+  union {
+    uint2 stage[kChunk];              // a chunk of candidates (key, position)
+    uint32_t keys[kUnitTok];          // rescoring a unit
+  };
+  uint16_t owner[kChunk];             // unit of each staged candidate
+  uint32_t hist[kBins];
+  uint32_t cpre[kMaxUnitsPerRow + 1]; // candidate prefix per unit
   uint32_t red[2 * kWaves + 2];
   uint32_t misc[16];
 };
@@ -92,9 +109,6 @@ __device__ __forceinline__ void flag_error(uint32_t* hdr, uint32_t bits) {
 __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
   return b == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(b << 23);
 }
-
-// wait until this wave's global stores have completed (vmcnt(0))
-__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ---- block primitives (256 threads) -------------------------------------
 
@@ -134,33 +148,15 @@ __device__ uint32_t block_max(uint32_t v, uint32_t* red) {
   return m;
 }
 
-// Threshold search over an LDS histogram of nbins (a multiple of 256)
-// counts: the largest bin b whose suffix count sum_{b'>=b} reaches `need`.
-// Writes out[0] = b, out[1] = suffix(b+1), out[2] = total, out[3] = found.
-__device__ void find_threshold(const uint32_t* hist, int nbins, uint32_t need, uint32_t* red,
-                               uint32_t* out) {
-  const int per = nbins / kThreads;
-  const int b0 = threadIdx.x * per;
-  auto count = [&](int b) -> uint32_t { return hist[b]; };
-  uint32_t local = 0;
-  for (int i = 0; i < per; ++i) local += count(b0 + i);
-  uint32_t total;
-  const uint32_t incl = block_excl_scan(local, red, &total) + local;
-  uint32_t run = total - incl;  // keys in bins above this thread's range
-  if (threadIdx.x == 0) { out[2] = total; out[3] = 0; }
-  __syncthreads();
-  if (run < need && run + local >= need) {
-    for (int i = per - 1; i >= 0; --i) {
-      const uint32_t c = count(b0 + i);
-      if (run < need && run + c >= need) {
-        out[0] = (uint32_t)(b0 + i);
-        out[1] = run;
-        out[3] = 1;
-      }
-      run += c;
-    }
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d);
+    if (lane >= d) x += y;
   }
-  __syncthreads();
+  return x;
 }
 
 // ---- units ------------------------------------------------------------------
@@ -177,38 +173,57 @@ __device__ __forceinline__ int row_units(int t, int bt_stride) {
   return (row_pages(t, bt_stride) + kUnitPages - 1) / kUnitPages;
 }
 
-__device__ void plan_rows(const Params& P, Smem& S) {
+__device__ void plan_rows(const Params& P, uint32_t* rowpre, uint32_t* red) {
   const int per = (P.R + kThreads - 1) / kThreads;
   const int r0 = threadIdx.x * per;
   uint32_t lu = 0;
   for (int i = 0; i < per; ++i)
     if (r0 + i < P.R) lu += (uint32_t)row_units(P.row_pos[r0 + i], P.bt_stride);
   uint32_t total;
-  uint32_t run = block_excl_scan(lu, S.red, &total);
+  uint32_t run = block_excl_scan(lu, red, &total);
   for (int i = 0; i < per; ++i) {
     if (r0 + i < P.R) {
-      S.rowpre[r0 + i] = run;
+      rowpre[r0 + i] = run;
       run += (uint32_t)row_units(P.row_pos[r0 + i], P.bt_stride);
     }
   }
-  if (threadIdx.x == 0) S.rowpre[P.R] = total;
+  if (threadIdx.x == 0) rowpre[P.R] = total;
   __syncthreads();
 }
 
-__device__ Unit decode_unit(const Params& P, const Smem& S, uint32_t u) {
+__device__ Unit decode_unit(const Params& P, const uint32_t* rowpre, uint32_t u) {
   int lo = 0, hi = P.R - 1;     // row r with rowpre[r] <= u < rowpre[r+1]
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (S.rowpre[mid] <= u) lo = mid; else hi = mid - 1;
+    if (rowpre[mid] <= u) lo = mid; else hi = mid - 1;
   }
   Unit U;
   U.row = lo;
-  U.uir = (int)(u - S.rowpre[lo]);
-  U.units_r = (int)(S.rowpre[lo + 1] - S.rowpre[lo]);
+  U.uir = (int)(u - rowpre[lo]);
+  U.units_r = (int)(rowpre[lo + 1] - rowpre[lo]);
   U.t = P.row_pos[lo];
   const int pr = row_pages(U.t, P.bt_stride);
   U.pg0 = U.uir * kUnitPages;
   U.pg1 = min(pr, U.pg0 + kUnitPages);
+  // identical in every lane: keep the fields in scalar registers
+  U.row = __builtin_amdgcn_readfirstlane(U.row);
+  U.uir = __builtin_amdgcn_readfirstlane(U.uir);
+  U.units_r = __builtin_amdgcn_readfirstlane(U.units_r);
+  U.t = __builtin_amdgcn_readfirstlane(U.t);
+  U.pg0 = __builtin_amdgcn_readfirstlane(U.pg0);
+  U.pg1 = __builtin_amdgcn_readfirstlane(U.pg1);
+  return U;
+}
+
+// Unit uir of a row whose last position is t (used by the rescoring path).
+__device__ Unit row_unit(const Params& P, int row, int t, int uir) {
+  Unit U;
+  U.row = row;
+  U.uir = uir;
+  U.units_r = row_units(t, P.bt_stride);
+  U.t = t;
+  U.pg0 = uir * kUnitPages;
+  U.pg1 = min(row_pages(t, P.bt_stride), U.pg0 + kUnitPages);
   return U;
 }
 
@@ -227,22 +242,20 @@ struct QOperand {
 template <int NHT>
 __device__ void load_q(const Params& P, int row, QOperand<NHT>& Q) {
   const int lane = threadIdx.x & 63, hr = lane & 15, g = lane >> 4;
+  // every load is issued unconditionally (heads beyond H read head 0 and are
+  // zeroed afterwards) so the compiler's wait counting sees a fixed number
+  // of loads on every path
 #pragma unroll
   for (int i = 0; i < NHT; ++i) {
     const int h = 16 * i + hr;
-    uint32_t dw[8];
-    float sc = 1.0f;
-    if (h < P.H) {
-      const uint8_t* src = P.q + ((int64_t)row * P.H + h) * kIdxDim + 32 * g;
-      const uint4 a = *reinterpret_cast<const uint4*>(src);
-      const uint4 b = *reinterpret_cast<const uint4*>(src + 16);
-      dw[0] = a.x; dw[1] = a.y; dw[2] = a.z; dw[3] = a.w;
-      dw[4] = b.x; dw[5] = b.y; dw[6] = b.z; dw[7] = b.w;
-      sc = e8m0_to_f32(P.qs[((int64_t)row * P.H + h) * 4 + g]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) dw[j] = 0;
-    }
+    const bool live = h < P.H;
+    const int hs = live ? h : 0;
+    const uint8_t* src = P.q + ((int64_t)row * P.H + hs) * kIdxDim + 32 * g;
+    const uint4 a = *reinterpret_cast<const uint4*>(src);
+    const uint4 b = *reinterpret_cast<const uint4*>(src + 16);
+    const uint32_t dw[8] = {live ? a.x : 0u, live ? a.y : 0u, live ? a.z : 0u, live ? a.w : 0u,
+                            live ? b.x : 0u, live ? b.y : 0u, live ? b.z : 0u, live ? b.w : 0u};
+    const float sc = e8m0_to_f32(P.qs[((int64_t)row * P.H + hs) * 4 + g]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dw[2 * s], sc, false);
@@ -254,7 +267,8 @@ __device__ void load_q(const Params& P, int row, QOperand<NHT>& Q) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int hh = 16 * i + 4 * g + c;
-      Q.w[i][c] = hh < P.H ? P.w[(int64_t)row * P.H + hh] : 0.f;
+      const float wv = P.w[(int64_t)row * P.H + (hh < P.H ? hh : 0)];
+      Q.w[i][c] = hh < P.H ? wv : 0.f;
     }
   }
 }
@@ -267,15 +281,21 @@ struct HalfRegs {
   uint32_t s[2];
 };
 
-__device__ __forceinline__ void load_half(const uint8_t* page, int half, HalfRegs& hr) {
-  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+// Loads half `half` of the page behind `rsrc` (a raw buffer descriptor
+// covering the page, or with zero records when the half is absent: then
+// every load is out of range, reads nothing and returns 0).  off_d / off_s
+// are the lane's fixed byte offsets of its code bytes and scale byte.
+__device__ __forceinline__ void load_half(__amdgpu_buffer_rsrc_t rsrc, int half, uint32_t off_d,
+                                          uint32_t off_s, HalfRegs& hr) {
+  const uint32_t od = off_d + (uint32_t)half * 32 * kIdxDim;
+  const uint32_t os = off_s + (uint32_t)(kKScaleOff + half * 128);
 #pragma unroll
   for (int jj = 0; jj < 2; ++jj) {
-    const int tok = 16 * (2 * half + jj) + r;
-    const uint8_t* src = page + tok * kIdxDim + 32 * g;
-    hr.d[2 * jj] = *reinterpret_cast<const uint4*>(src);
-    hr.d[2 * jj + 1] = *reinterpret_cast<const uint4*>(src + 16);
-    hr.s[jj] = page[kKScaleOff + tok * 4 + g];
+    const v4u a = __builtin_amdgcn_raw_buffer_load_b128(rsrc, od + jj * 16 * kIdxDim, 0, 0);
+    const v4u b = __builtin_amdgcn_raw_buffer_load_b128(rsrc, od + jj * 16 * kIdxDim + 16, 0, 0);
+    hr.d[2 * jj] = make_uint4(a[0], a[1], a[2], a[3]);
+    hr.d[2 * jj + 1] = make_uint4(b[0], b[1], b[2], b[3]);
+    hr.s[jj] = __builtin_amdgcn_raw_buffer_load_b8(rsrc, os + jj * 64, 0, 0);
   }
 }
 
@@ -315,28 +335,42 @@ __device__ __forceinline__ void score_half(const QOperand<NHT>& Q, const HalfReg
   }
 }
 
-// Score one unit: keys (or dumped scores) of its (pg1-pg0)*64 positions.
-// Wave w takes half pages w, w+4, w+8, ... of the unit and keeps three of
-// them in flight (a ring of three register buffers, unrolled so no buffer
-// is ever copied).
+// Score one unit: all 1024 key slots of the unit (key 0 for positions past t
+// or on an absent page), or, for the dump, the scores of its positions.
+// Wave w takes half pages w, w+4, ..., w+28 of the unit, fully unrolled, with
+// kRing of them in flight.  The unit's page ids are read from the block table
+// once, one per lane, and every fetch issues the same loads (an absent half
+// gets a zero-record descriptor), so the loads retire in ring order and the
+// compiler's wait counting never has to drain the ring.
 template <int NHT, bool DUMP>
-__device__ void score_unit(const Params& P, const Unit& U, Smem& S) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int seq = P.row_seq[U.row];
-  const int32_t* btrow = P.bt + (int64_t)seq * P.bt_stride;
-  const int nhalf = 2 * (U.pg1 - U.pg0);
+__device__ void score_unit(const Params& P, const Unit& U, uint32_t* keys) {
+  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int npg = U.pg1 - U.pg0;   // <= 16
+  const int nhalf = 2 * npg;
+  int32_t pid = -1;                // -1: page absent, its positions get key 0
+  if (lane < npg && U.t >= 0) {
+    const int32_t id = P.bt[(int64_t)P.row_seq[U.row] * P.bt_stride + U.pg0 + lane];
+    const bool bad = id < 0 || (int64_t)id >= P.pool_pages;
+    if (bad) flag_error(P.hdr, kErrBadPage);
+    pid = bad ? -1 : id;
+  }
+  // the query loads go before the ring: they are then older than every
+  // ring load
+  QOperand<NHT> Q;
+  load_q<NHT>(P, U.row, Q);
+  const uint32_t off_d = (uint32_t)(r * kIdxDim + 32 * g);
+  const uint32_t off_s = (uint32_t)(r * 4 + g);
   auto fetch = [&](int h, HalfRegs& b) -> bool {
-    if (U.t < 0 || h >= nhalf) return false;
-    const int pg = U.pg0 + (h >> 1);
-    const int32_t id = btrow[pg];
-    if (id < 0 || (int64_t)id >= P.pool_pages) {
-      if (lane == 0) flag_error(P.hdr, kErrBadPage);
-      return false;
-    }
-    load_half(P.kpool + (int64_t)id * kKPageBytes, h & 1, b);
-    return true;
+    const int32_t id = h < nhalf ? __builtin_amdgcn_readlane(pid, (h >> 1) & 63) : -1;
+    const bool ok = id >= 0;
+    const uint8_t* page = P.kpool + (int64_t)(ok ? id : 0) * kKPageBytes;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(page), (short)0, ok ? kKPageBytes : 0, kRawBufferWord3);
+    load_half(rsrc, h & 1, off_d, off_s, b);
+    return ok;
   };
-  auto consume = [&](int h, const HalfRegs& b, bool ok, const QOperand<NHT>& Q) {
+  auto consume = [&](int h, const HalfRegs& b, bool ok) {
     float sc[2] = {0.f, 0.f};
     if (ok) score_half<NHT>(Q, b, sc);
 #pragma unroll
@@ -348,28 +382,23 @@ __device__ void score_unit(const Params& P, const Unit& U, Smem& S) {
         if (DUMP) {
           if (valid && pos < P.ld) P.dump[(int64_t)U.row * P.ld + pos] = sc[jj] == 0.f ? 0.f : sc[jj];
         } else {
-          S.keys[tok] = valid ? score_key(sc[jj]) : 0u;
+          keys[tok] = valid ? score_key(sc[jj]) : 0u;
         }
       }
     }
   };
-  HalfRegs b0, b1, b2;
-  int h = wv;
-  bool ok0 = fetch(h, b0);
-  bool ok1 = fetch(h + kWaves, b1);
-  QOperand<NHT> Q;
-  load_q<NHT>(P, U.row, Q);
-  for (; h < nhalf; h += 3 * kWaves) {
-    bool ok2 = fetch(h + 2 * kWaves, b2);
-    consume(h, b0, ok0, Q);
-    if (h + kWaves >= nhalf) break;
-    ok0 = fetch(h + 3 * kWaves, b0);
-    consume(h + kWaves, b1, ok1, Q);
-    if (h + 2 * kWaves >= nhalf) break;
-    ok1 = fetch(h + 4 * kWaves, b1);
-    consume(h + 2 * kWaves, b2, ok2, Q);
+  HalfRegs b[kHalvesPerWave];
+  bool ok[kHalvesPerWave];
+#pragma unroll
+  for (int k = 0; k < kRing; ++k) ok[k] = fetch(wv + kWaves * k, b[k]);
+#pragma unroll
+  for (int k = 0; k < kHalvesPerWave; ++k) {
+    if (k + kRing < kHalvesPerWave) ok[k + kRing] = fetch(wv + kWaves * (k + kRing), b[k + kRing]);
+    consume(wv + kWaves * k, b[k], ok[k]);
   }
 }
+
+// ---- scan kernel: local filter ------------------------------------------------
 
 // Keys a unit keeps: its expected share E of the Top-K (about
 // topk * 1024 / (t+1)) plus four standard deviations and a margin; every key
@@ -382,311 +411,397 @@ __device__ __forceinline__ uint32_t unit_quota(int t, int topk) {
   return (uint32_t)fminf(ceilf(m), (float)kUnitTok);
 }
 
-// Append the unit's keys >= edge (all non-zero keys when edge is 0), in
-// position order, to the unit's candidate slice.
-__device__ uint32_t emit_unit_keys(const Params& P, Smem& S, const Unit& U, uint32_t edge) {
-  const int ntok = (U.pg1 - U.pg0) * kPage;
-  uint2* dst = P.cand + (int64_t)U.row * P.bt_stride * kPage + (int64_t)U.pg0 * kPage;
-  constexpr int kPer = kUnitTok / kThreads;       // 4 consecutive keys per thread
-  const int i0 = threadIdx.x * kPer;
-  uint32_t k[kPer];
-  uint32_t cnt = 0;
+// Wave 0 walks the 256-bin histogram from the top bin down and finds the bin
+// b where the count of keys in bins >= b first reaches `need`; it clears
+// every bin it read.  misc[0] = b, misc[1] = count in bins > b, misc[2] = 1
+// if found.  Ends with a block barrier.
+__device__ void filter_threshold(uint32_t* hist, uint32_t need, uint32_t* misc) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int top = kFBins - 1 - 4 * lane;          // this lane's bins: top .. top-3
+    uint32_t c[4];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    k[j] = (i0 + j < ntok) ? S.keys[i0 + j] : 0u;
-    cnt += (k[j] != 0u && k[j] >= edge) ? 1u : 0u;
-  }
-  uint32_t total;
-  uint32_t off = block_excl_scan(cnt, S.red, &total);
+    for (int i = 0; i < 4; ++i) {
+      c[i] = hist[top - i];
+      hist[top - i] = 0;
+    }
+    const uint32_t mine = c[0] + c[1] + c[2] + c[3];
+    const uint32_t incl = wave_incl_scan(mine);
+    uint32_t run = incl - mine;                      // keys in bins above this lane's
+    if (lane == 0) misc[2] = 0;
+    if (run < need && incl >= need) {
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    if (k[j] != 0u && k[j] >= edge) {
-      dst[off++] = make_uint2(k[j], (uint32_t)(U.pg0 * kPage + i0 + j));
+      for (int i = 0; i < 4; ++i) {
+        if (run < need && run + c[i] >= need) {
+          misc[0] = (uint32_t)(top - i);
+          misc[1] = run;
+          misc[2] = 1;
+        }
+        run += c[i];
+      }
     }
   }
-  return total;
+  __syncthreads();
 }
 
-// Local filter of a scored unit: the edge is the lower end of the 20-bit key
-// bin holding the unit's quota-th largest key (two LDS histogram passes of
-// 12 and 8 bits); keys at or above it are emitted, so every key left out is
-// below the recorded edge.
-__device__ void filter_unit(const Params& P, Smem& S, const Unit& U) {
+// Local filter of a scored unit: the edge is the lower end of the 16-bit key
+// bin holding the unit's quota-th largest key (two 8-bit LDS histogram
+// passes); keys at or above it are emitted, so every key left out is below
+// the recorded edge.  The histogram is all zero on entry and on exit.
+__device__ void filter_unit(const Params& P, ScanSmem& S, const Unit& U) {
+  const int tid = threadIdx.x;
   const int ntok = (U.pg1 - U.pg0) * kPage;
   const uint32_t quota = unit_quota(U.t, P.topk);
+  const uint4 kv = *reinterpret_cast<const uint4*>(&S.keys[4 * tid]);
+  const uint32_t k[4] = {kv.x, kv.y, kv.z, kv.w};
   uint32_t edge = 0;
   if (quota < (uint32_t)ntok) {
-    for (int i = threadIdx.x; i < kBins; i += kThreads) S.hist[i] = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (k[j]) atomicAdd(&S.hist[k[j] >> 24], 1u);
     __syncthreads();
-    for (int i = threadIdx.x; i < ntok; i += kThreads) {
-      const uint32_t key = S.keys[i];
-      if (key) atomicAdd(&S.hist[key >> 20], 1u);
-    }
-    __syncthreads();
-    find_threshold(S.hist, kBins, quota, S.red, S.misc + 8);
-    if (S.misc[11]) {
-      const uint32_t T1 = S.misc[8], need = quota - S.misc[9];
-      for (int i = threadIdx.x; i < 256; i += kThreads) S.hist[i] = 0;
+    filter_threshold(S.hist, quota, S.misc);
+    if (S.misc[2]) {   // else: fewer than quota keys, keep them all
+      const uint32_t b1 = S.misc[0], need = quota - S.misc[1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (k[j] && (k[j] >> 24) == b1) atomicAdd(&S.hist[(k[j] >> 16) & 0xFFu], 1u);
       __syncthreads();
-      for (int i = threadIdx.x; i < ntok; i += kThreads) {
-        const uint32_t key = S.keys[i];
-        if (key && (key >> 20) == T1) atomicAdd(&S.hist[(key >> 12) & 0xFFu], 1u);
-      }
-      __syncthreads();
-      find_threshold(S.hist, 256, need, S.red, S.misc + 8);
-      edge = (T1 << 20) | (S.misc[8] << 12);
+      filter_threshold(S.hist, need, S.misc + 4);
+      edge = (b1 << 24) | (S.misc[4] << 16);
     }
   }
-  const uint32_t n = emit_unit_keys(P, S, U, edge);
-  if (threadIdx.x == 0) {
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cnt += (k[j] != 0u && k[j] >= edge) ? 1u : 0u;
+  uint32_t total;
+  uint32_t off = block_excl_scan(cnt, S.red, &total);
+  uint2* dst = P.cand + ((int64_t)U.row * P.bt_stride + U.pg0) * kPage;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (k[j] != 0u && k[j] >= edge) dst[off++] = make_uint2(k[j], (uint32_t)(U.pg0 * kPage + 4 * tid + j));
+  }
+  if (tid == 0) {
     const int64_t slot = (int64_t)U.row * P.upr + U.uir;
-    P.ucount[slot] = n;
-    P.uedge[slot] = edge;   // every key left out is below this
+    P.ucount[slot] = total;
+    P.uedge[slot] = edge;
   }
 }
 
-// ---- finisher ------------------------------------------------------------------
+template <int NHT>
+__global__ __launch_bounds__(kThreads, 2) void indexer_scan_kernel(Params P) {
+  __shared__ ScanSmem S;
+  S.hist[threadIdx.x] = 0;
+  plan_rows(P, S.rowpre, S.red);   // ends with a barrier
+  const uint32_t U_total = S.rowpre[P.R];
+  for (uint32_t u = blockIdx.x; u < U_total; u += gridDim.x) {
+    const Unit U = decode_unit(P, S.rowpre, u);
+    score_unit<NHT, false>(P, U, S.keys);
+    __syncthreads();
+    filter_unit(P, S, U);   // its last barrier orders the key reads before the next unit's writes
+  }
+}
 
-// prefix of the units' candidate counts (S.cpre); returns the largest edge
-__device__ uint32_t load_counts(const Params& P, Smem& S, int row, int units_r) {
-  const int per = (units_r + kThreads - 1) / kThreads;
-  const int u0 = threadIdx.x * per;
-  uint32_t local = 0, emax = 0;
+// Test entry: write every score of every row.
+template <int NHT>
+__global__ __launch_bounds__(kThreads, 2) void indexer_dump_kernel(Params P) {
+  __shared__ ScanSmem S;
+  plan_rows(P, S.rowpre, S.red);
+  const uint32_t U_total = S.rowpre[P.R];
+  for (uint32_t u = blockIdx.x; u < U_total; u += gridDim.x) {
+    const Unit U = decode_unit(P, S.rowpre, u);
+    score_unit<NHT, true>(P, U, S.keys);
+  }
+}
+
+// ---- select kernel ---------------------------------------------------------------
+
+// Candidate prefix per unit (S.cpre, S.cpre[units_r] = total); returns the
+// largest unit edge.
+__device__ uint32_t load_counts(const Params& P, SelSmem& S, int row, int units_r) {
+  constexpr int kPer = kMaxUnitsPerRow / kThreads;   // 4
+  const int u0 = threadIdx.x * kPer;
   const int64_t base = (int64_t)row * P.upr;
-  for (int i = 0; i < per; ++i) {
-    if (u0 + i < units_r) {
-      local += load_agent(&P.ucount[base + u0 + i]);
-      emax = max(emax, load_agent(&P.uedge[base + u0 + i]));
-    }
+  uint32_t c[kPer];
+  uint32_t local = 0, emax = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const bool in = u0 + i < units_r;
+    c[i] = in ? load_agent(&P.ucount[base + u0 + i]) : 0u;
+    emax = max(emax, in ? load_agent(&P.uedge[base + u0 + i]) : 0u);
+    local += c[i];
   }
   uint32_t total;
   uint32_t run = block_excl_scan(local, S.red, &total);
-  for (int i = 0; i < per; ++i) {
-    if (u0 + i < units_r) {
-      S.cpre[u0 + i] = run;
-      run += load_agent(&P.ucount[base + u0 + i]);
-    }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (u0 + i < units_r) S.cpre[u0 + i] = run;
+    run += c[i];
   }
   if (threadIdx.x == 0) S.cpre[units_r] = total;
   __syncthreads();
   return block_max(emax, S.red);
 }
 
-// Stage candidates [ch*kChunk, ...) of the row (flat order = position
-// order) into LDS.  Element f goes to thread f % 256; every element finds its
-// unit by binary search over the count prefix, so all loads are independent
-// and in flight together.  Returns the number staged.
-__device__ uint32_t stage_chunk(const Params& P, Smem& S, int row, int units_r, uint32_t n_c,
-                                uint32_t ch) {
+// Stage candidates [ch*kChunk, ...) of the row (flat order = position order)
+// into S.stage: the owner unit of every slot is filled in LDS first, then
+// every thread issues all of its loads before storing.  Returns the number
+// staged; *kmax receives the largest staged key.
+__device__ uint32_t stage_chunk(const Params& P, SelSmem& S, int row, int units_r, uint32_t n_c,
+                                uint32_t ch, uint32_t* kmax) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const uint32_t base = ch * kChunk;
   const uint32_t n = base < n_c ? min((uint32_t)kChunk, n_c - base) : 0u;
+  for (int u = wv; u < units_r; u += kWaves) {
+    const uint32_t a = max(S.cpre[u], base), b = min(S.cpre[u + 1], base + n);
+    for (uint32_t f = a + lane; f < b; f += 64) S.owner[f - base] = (uint16_t)u;
+  }
+  __syncthreads();
   const uint2* rowc = P.cand + (int64_t)row * P.bt_stride * kPage;
+  uint2 v[kCandPer];
 #pragma unroll
   for (int k = 0; k < kCandPer; ++k) {
     const uint32_t i = threadIdx.x + k * kThreads;
+    v[k] = make_uint2(0u, 0u);
     if (i < n) {
-      const uint32_t f = base + i;
-      int u = 0, hi = units_r - 1;   // last unit with cpre[u] <= f
-      while (u < hi) {
-        const int mid = (u + hi + 1) >> 1;
-        if (S.cpre[mid] <= f) u = mid; else hi = mid - 1;
-      }
-      S.stage[i] = rowc[(int64_t)u * kUnitTok + (f - S.cpre[u])];
+      const uint32_t u = S.owner[i];
+      v[k] = rowc[(int64_t)u * kUnitTok + (base + i - S.cpre[u])];
     }
   }
-  __syncthreads();
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < kCandPer; ++k) {
+    const uint32_t i = threadIdx.x + k * kThreads;
+    if (i < n) S.stage[i] = v[k];
+    m = max(m, v[k].x);
+  }
+  *kmax = block_max(m, S.red);   // its barriers also publish the stage
   return n;
 }
 
-// Exact key T of rank K among the candidates and the number of keys equal
-// to T to keep (three histogram passes of 12, 12 and 8 bits).  Returns false
-// if there are fewer than K candidates.  With more than one chunk every
-// pass restages them.
-__device__ bool select_threshold(const Params& P, Smem& S, int row, int units_r, uint32_t n_c,
-                                 uint32_t K, uint32_t* T_out, uint32_t* ties_out) {
+// One radix pass: histogram of (key - base) >> shift over the 4096 bins for
+// keys in [base, base + span) (span <= 4096 << shift), then the bin holding
+// the key of rank `need` from the top.  Returns false if fewer than `need`
+// keys fall in the range; else *bin and *above (keys in higher bins).
+__device__ bool radix_pass(const Params& P, SelSmem& S, int row, int units_r, uint32_t n_c,
+                           uint32_t base, uint32_t shift, uint64_t span, uint32_t need,
+                           uint32_t* bin, uint32_t* above) {
   const uint32_t nch = (n_c + kChunk - 1) / kChunk;
-  uint32_t prefix = 0, need = K;
-  for (int pass = 0; pass < 3; ++pass) {
-    const int nb = pass < 2 ? kBins : 256;
-    const uint32_t shift = pass == 0 ? 20u : (pass == 1 ? 8u : 0u);
-    const uint32_t mask = pass < 2 ? 0xFFFu : 0xFFu;
-    const uint32_t pshift = pass == 1 ? 20u : 8u;
-    for (int b = threadIdx.x; b < nb; b += kThreads) S.hist[b] = 0;
-    __syncthreads();
-    for (uint32_t ch = 0; ch < nch; ++ch) {
-      const uint32_t n = nch > 1 ? stage_chunk(P, S, row, units_r, n_c, ch) : n_c;
-      for (uint32_t f = threadIdx.x; f < n; f += kThreads) {
-        const uint32_t k = S.stage[f].x;
-        if (pass == 0 || (k >> pshift) == prefix) atomicAdd(&S.hist[(k >> shift) & mask], 1u);
-      }
-      __syncthreads();
-    }
-    find_threshold(S.hist, nb, need, S.red, S.misc + 8);
-    if (!S.misc[11]) return false;
-    need -= S.misc[9];
-    prefix = (prefix << (pass < 2 ? 12 : 8)) | S.misc[8];
+  {
+    uint4* h4 = reinterpret_cast<uint4*>(S.hist);
+#pragma unroll
+    for (int i = 0; i < kBins / 4 / kThreads; ++i) h4[threadIdx.x + i * kThreads] = make_uint4(0, 0, 0, 0);
   }
-  *T_out = prefix;
+  __syncthreads();
+  for (uint32_t ch = 0; ch < nch; ++ch) {
+    uint32_t dummy;
+    const uint32_t n = nch > 1 ? stage_chunk(P, S, row, units_r, n_c, ch, &dummy) : n_c;
+#pragma unroll 4
+    for (uint32_t f = threadIdx.x; f < n; f += kThreads) {
+      const uint32_t k = S.stage[f].x;
+      if (k >= base && (uint64_t)(k - base) < span) atomicAdd(&S.hist[(k - base) >> shift], 1u);
+    }
+    __syncthreads();
+  }
+  // 16 bins per thread, thread 0 holding the top bins
+  constexpr int kPer = kBins / kThreads;
+  const int top = kBins - 1 - kPer * threadIdx.x;
+  uint32_t c[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer / 4; ++i) {
+    const uint4 q = reinterpret_cast<const uint4*>(S.hist)[(top - 4 * i - 3) / 4];
+    c[4 * i] = q.w;
+    c[4 * i + 1] = q.z;
+    c[4 * i + 2] = q.y;
+    c[4 * i + 3] = q.x;
+  }
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) mine += c[i];
+  uint32_t total;
+  uint32_t run = block_excl_scan(mine, S.red, &total);
+  if (threadIdx.x == 0) S.misc[2] = 0;
+  __syncthreads();
+  if (run < need && run + mine >= need) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (run < need && run + c[i] >= need) {
+        S.misc[0] = (uint32_t)(top - i);
+        S.misc[1] = run;
+        S.misc[2] = 1;
+      }
+      run += c[i];
+    }
+  }
+  __syncthreads();
+  const bool found = S.misc[2] != 0;
+  *bin = S.misc[0];
+  *above = S.misc[1];
+  __syncthreads();
+  return found;
+}
+
+// Exact key T of rank K among the candidates with key >= lo (keys in
+// [lo, hi] are binned over the occupied range, at most three passes), and
+// the number of keys equal to T to keep.  Returns false if fewer than K
+// candidates are >= lo.
+__device__ bool select_threshold(const Params& P, SelSmem& S, int row, int units_r, uint32_t n_c,
+                                 uint32_t lo, uint32_t hi, uint32_t K, uint32_t* T_out,
+                                 uint32_t* ties_out) {
+  if (hi < lo) return false;
+  const uint32_t range = hi - lo;   // keys in [lo, lo + range]
+  int shift = range == 0 ? 0 : max(0, 32 - __builtin_clz(range) - 12);
+  uint64_t span = (uint64_t)range + 1;
+  uint32_t base = lo, need = K;
+  for (;;) {
+    uint32_t bin, above;
+    if (!radix_pass(P, S, row, units_r, n_c, base, (uint32_t)shift, span, need, &bin, &above))
+      return false;
+    base += bin << shift;
+    need -= above;
+    if (shift == 0) break;
+    span = 1ull << shift;            // the keys of the chosen bin
+    shift = max(0, shift - 12);
+  }
+  *T_out = base;
   *ties_out = need;
   return true;
 }
 
 // Ordered emission of keys > T and the first `ties` keys equal to T; each
-// thread owns a contiguous segment of every staged chunk.
-__device__ void emit_selection(const Params& P, Smem& S, int row, int units_r, uint32_t n_c,
+// thread owns a contiguous segment of every staged chunk, and one block
+// scan of the packed (equal, greater) counts places every kept key.
+__device__ void emit_selection(const Params& P, SelSmem& S, int row, int units_r, uint32_t n_c,
                                uint32_t T, uint32_t ties) {
   const int K = P.topk;
   int32_t* oidx = P.out_idx + (int64_t)row * K;
   float* osc = P.out_score ? P.out_score + (int64_t)row * K : nullptr;
   const uint32_t nch = (n_c + kChunk - 1) / kChunk;
-  uint32_t run_tie = 0, run_keep = 0;
+  uint32_t run_gt = 0, run_eq = 0;
   for (uint32_t ch = 0; ch < nch; ++ch) {
-    const uint32_t n = nch > 1 ? stage_chunk(P, S, row, units_r, n_c, ch) : n_c;
+    uint32_t dummy;
+    const uint32_t n = nch > 1 ? stage_chunk(P, S, row, units_r, n_c, ch, &dummy) : n_c;
     const uint32_t seg = (n + kThreads - 1) / kThreads;
     const uint32_t f0 = min(n, threadIdx.x * seg), f1 = min(n, f0 + seg);
-    uint32_t eq = 0;
-    for (uint32_t f = f0; f < f1; ++f) eq += S.stage[f].x == T ? 1u : 0u;
-    uint32_t tot_eq;
-    const uint32_t tie_base = run_tie + block_excl_scan(eq, S.red, &tot_eq);
-    uint32_t keep = 0, tr = tie_base;
+    uint32_t gt = 0, eq = 0;
     for (uint32_t f = f0; f < f1; ++f) {
       const uint32_t k = S.stage[f].x;
-      if (k > T) ++keep;
-      else if (k == T) { if (tr < ties) ++keep; ++tr; }
+      gt += k > T ? 1u : 0u;
+      eq += k == T ? 1u : 0u;
     }
-    uint32_t tot_keep;
-    uint32_t opos = run_keep + block_excl_scan(keep, S.red, &tot_keep);
-    tr = tie_base;
+    uint32_t tot;
+    const uint32_t pre = block_excl_scan((eq << 16) | gt, S.red, &tot);
+    uint32_t er = run_eq + (pre >> 16);                       // equal keys before mine
+    uint32_t opos = run_gt + (pre & 0xFFFFu) + min(er, ties); // kept keys before mine
     for (uint32_t f = f0; f < f1; ++f) {
       const uint2 c = S.stage[f];
       bool kp = c.x > T;
-      if (c.x == T) { kp = tr < ties; ++tr; }
+      if (c.x == T) {
+        kp = er < ties;
+        ++er;
+      }
       if (kp && opos < (uint32_t)K) {
         oidx[opos] = (int32_t)c.y;
         if (osc) osc[opos] = key_score(c.x);
         ++opos;
       }
     }
-    run_tie += tot_eq;
-    run_keep += tot_keep;
+    run_gt += tot & 0xFFFFu;
+    run_eq += tot >> 16;
     __syncthreads();
   }
 }
 
-template <int NHT>
-__device__ void finish_row(const Params& P, Smem& S, const Unit& U0) {
-  const int row = U0.row, units_r = U0.units_r, K = P.topk;
-  const uint32_t emax = load_counts(P, S, row, units_r);
-  uint32_t n_c = S.cpre[units_r];
+// All staged candidates (n_c <= K) in position order, then -1 padding.
+__device__ void emit_all(const Params& P, SelSmem& S, int row, uint32_t n_c) {
+  const int K = P.topk;
   int32_t* oidx = P.out_idx + (int64_t)row * K;
   float* osc = P.out_score ? P.out_score + (int64_t)row * K : nullptr;
-  if (unit_quota(U0.t, K) == 0xFFFFFFFFu) {
-    // at most topk positions: every unit kept all of its keys
-    stage_chunk(P, S, row, units_r, n_c, 0);
-    for (uint32_t f = threadIdx.x; f < (uint32_t)K; f += kThreads) {
-      if (f < n_c) {
-        oidx[f] = (int32_t)S.stage[f].y;
-        if (osc) osc[f] = key_score(S.stage[f].x);
-      } else {
-        oidx[f] = -1;
-        if (osc) osc[f] = -__builtin_huge_valf();
-      }
+  for (uint32_t f = threadIdx.x; f < (uint32_t)K; f += kThreads) {
+    if (f < n_c) {
+      oidx[f] = (int32_t)S.stage[f].y;
+      if (osc) osc[f] = key_score(S.stage[f].x);
+    } else {
+      oidx[f] = -1;
+      if (osc) osc[f] = -__builtin_huge_valf();
     }
-  } else {
-    uint32_t T = 0, ties = 0;
-    if (n_c <= (uint32_t)kChunk) stage_chunk(P, S, row, units_r, n_c, 0);
-    bool ok = select_threshold(P, S, row, units_r, n_c, (uint32_t)K, &T, &ties);
-    if (!ok || emax > T) {
-      // Some unit may have left out a key that belongs to the Top-K: rescore
-      // every such unit in full and select again (exact, rarely taken).
-      if (threadIdx.x == 0) flag_error(P.hdr, kErrFallback);
-      for (int u = 0; u < units_r; ++u) {
-        const uint32_t e = load_agent(&P.uedge[(int64_t)row * P.upr + u]);
-        const bool redo = ok ? (e > T) : (e > 0u);
-        if (!redo) continue;
-        __syncthreads();
-        Unit V = U0;
-        V.uir = u;
-        V.pg0 = u * kUnitPages;
-        V.pg1 = min(row_pages(V.t, P.bt_stride), V.pg0 + kUnitPages);
-        score_unit<NHT, false>(P, V, S);
-        __syncthreads();
-        const uint32_t n = emit_unit_keys(P, S, V, 0u);
-        if (threadIdx.x == 0) {
-          __hip_atomic_store(&P.ucount[(int64_t)row * P.upr + u], n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(&P.uedge[(int64_t)row * P.upr + u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-      __threadfence();
-      __syncthreads();
-      load_counts(P, S, row, units_r);
-      n_c = S.cpre[units_r];
-      if (n_c <= (uint32_t)kChunk) stage_chunk(P, S, row, units_r, n_c, 0);
-      select_threshold(P, S, row, units_r, n_c, (uint32_t)K, &T, &ties);
-    }
-    emit_selection(P, S, row, units_r, n_c, T, ties);
   }
-  if (threadIdx.x == 0) P.tick[row] = 0;
 }
 
-// ---- the kernels ---------------------------------------------------------------
-
+// Rescore unit u of the row in full and publish all of its keys.
 template <int NHT>
-__global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(Params P) {
-  __shared__ Smem S;
-  plan_rows(P, S);
-  const uint32_t U_total = S.rowpre[P.R];
-  for (;;) {
-    if (threadIdx.x == 0) S.misc[0] = atomic_add_agent(&P.hdr[0], 1u);
-    __syncthreads();
-    const uint32_t u = S.misc[0];
-    __syncthreads();
-    if (u >= U_total) break;
-    const Unit U = decode_unit(P, S, u);
-    score_unit<NHT, false>(P, U, S);
-    __syncthreads();
-    filter_unit(P, S, U);
-    // publish the unit's candidates, then take the row's ticket
-    wait_vm();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      const uint32_t old = atomic_add_agent(&P.tick[U.row], 1u);
-      S.misc[1] = (old == (uint32_t)U.units_r - 1) ? 1u : 0u;
-      if (S.misc[1]) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    }
-    __syncthreads();
-    if (S.misc[1]) {
-      finish_row<NHT>(P, S, U);
-      __syncthreads();
-    }
-  }
-  // the last workgroup out re-arms the unit counter for the next call
+__device__ void rescore_unit(const Params& P, SelSmem& S, int row, int t, int u) {
+  const Unit V = row_unit(P, row, t, u);
+  __syncthreads();
+  score_unit<NHT, false>(P, V, S.keys);
+  __syncthreads();
+  const uint4 kv = *reinterpret_cast<const uint4*>(&S.keys[4 * threadIdx.x]);
+  const uint32_t k[4] = {kv.x, kv.y, kv.z, kv.w};
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cnt += k[j] != 0u ? 1u : 0u;
+  uint32_t total;
+  uint32_t off = block_excl_scan(cnt, S.red, &total);
+  uint2* dst = P.cand + ((int64_t)row * P.bt_stride + V.pg0) * kPage;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (k[j] != 0u) dst[off++] = make_uint2(k[j], (uint32_t)(V.pg0 * kPage + 4 * threadIdx.x + j));
   if (threadIdx.x == 0) {
-    const uint32_t done = atomic_add_agent(&P.hdr[1], 1u);
-    if (done == gridDim.x - 1) {
-      __hip_atomic_store(&P.hdr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&P.hdr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    __hip_atomic_store(&P.ucount[(int64_t)row * P.upr + u], total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&P.uedge[(int64_t)row * P.upr + u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// Test entry: write every score of every row (units assigned statically).
 template <int NHT>
-__global__ __launch_bounds__(kThreads, 2) void indexer_dump_kernel(Params P) {
-  __shared__ Smem S;
-  plan_rows(P, S);
-  const uint32_t U_total = S.rowpre[P.R];
-  for (uint32_t u = blockIdx.x; u < U_total; u += gridDim.x) {
-    const Unit U = decode_unit(P, S, u);
-    score_unit<NHT, true>(P, U, S);
+__global__ __launch_bounds__(kThreads, 2) void indexer_select_kernel(Params P) {
+  __shared__ SelSmem S;
+  const int row = blockIdx.x;
+  const int K = P.topk;
+  const int t = P.row_pos[row];
+  const int units_r = row_units(t, P.bt_stride);
+  uint32_t emax = load_counts(P, S, row, units_r);
+  uint32_t n_c = S.cpre[units_r];
+  uint32_t kmax = 0xFFFFFFFFu;
+  if (n_c <= (uint32_t)kChunk) stage_chunk(P, S, row, units_r, n_c, 0, &kmax);
+  if (t < 0 || unit_quota(t, K) == 0xFFFFFFFFu) {
+    // at most K positions: every unit kept all of its keys
+    emit_all(P, S, row, n_c);
+    return;
   }
+  uint32_t T = 0, ties = 0;
+  bool ok = select_threshold(P, S, row, units_r, n_c, max(emax, 1u), kmax, (uint32_t)K, &T, &ties);
+  if (!ok) {
+    // Fewer than K candidates reach the largest unit edge: a unit may have
+    // left out a Top-K key.  Take the K-th key T0 of the current candidates
+    // (none: every unit with a non-zero edge), rescore every unit whose edge
+    // exceeds it in full, and select again.  Keys of the remaining units are
+    // below their edge <= T0 <= the new K-th key, so the result is exact.
+    if (threadIdx.x == 0) flag_error(P.hdr, kErrFallback);
+    uint32_t T0 = 0, ties0 = 0;
+    const bool ok0 = select_threshold(P, S, row, units_r, n_c, 1u, kmax, (uint32_t)K, &T0, &ties0);
+    for (int u = 0; u < units_r; ++u) {
+      const uint32_t e = load_agent(&P.uedge[(int64_t)row * P.upr + u]);
+      if (e > (ok0 ? T0 : 0u)) rescore_unit<NHT>(P, S, row, t, u);
+    }
+    __threadfence();
+    __syncthreads();
+    load_counts(P, S, row, units_r);
+    n_c = S.cpre[units_r];
+    kmax = 0xFFFFFFFFu;
+    if (n_c <= (uint32_t)kChunk) stage_chunk(P, S, row, units_r, n_c, 0, &kmax);
+    ok = select_threshold(P, S, row, units_r, n_c, 1u, kmax, (uint32_t)K, &T, &ties);
+    if (!ok) {   // fewer than K valid positions in the row
+      emit_all(P, S, row, n_c);
+      return;
+    }
+  }
+  emit_selection(P, S, row, units_r, n_c, T, ties);
 }
 
 // ---- host side ----------------------------------------------------------------
 
 struct Layout {
-  size_t hdr, tick, ucount, uedge, cand, total;
+  size_t hdr, ucount, uedge, cand, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -698,7 +813,6 @@ Layout layout_for(int64_t rows, int64_t bt_stride) {
   const int64_t upr = units_stride(bt_stride);
   size_t off = 0;
   L.hdr = off; off += 256;
-  L.tick = off; off += align256((size_t)rows * 4);
   L.ucount = off; off += align256((size_t)rows * upr * 4);
   L.uedge = off; off += align256((size_t)rows * upr * 4);
   L.cand = off; off += align256((size_t)rows * bt_stride * kPage * 8);
@@ -706,12 +820,14 @@ Layout layout_for(int64_t rows, int64_t bt_stride) {
   return L;
 }
 
-void* pick_kernel(int nht, bool dump) {
+enum KernelKind { kScan = 0, kSelect = 1, kDump = 2 };
+
+void* pick_kernel(int nht, KernelKind kind) {
   switch (nht) {
-    case 1: return dump ? (void*)&indexer_dump_kernel<1> : (void*)&indexer_topk_kernel<1>;
-    case 2: return dump ? (void*)&indexer_dump_kernel<2> : (void*)&indexer_topk_kernel<2>;
-    case 3: return dump ? (void*)&indexer_dump_kernel<3> : (void*)&indexer_topk_kernel<3>;
-    default: return dump ? (void*)&indexer_dump_kernel<4> : (void*)&indexer_topk_kernel<4>;
+    case 1: return kind == kScan ? (void*)&indexer_scan_kernel<1> : kind == kSelect ? (void*)&indexer_select_kernel<1> : (void*)&indexer_dump_kernel<1>;
+    case 2: return kind == kScan ? (void*)&indexer_scan_kernel<2> : kind == kSelect ? (void*)&indexer_select_kernel<2> : (void*)&indexer_dump_kernel<2>;
+    case 3: return kind == kScan ? (void*)&indexer_scan_kernel<3> : kind == kSelect ? (void*)&indexer_select_kernel<3> : (void*)&indexer_dump_kernel<3>;
+    default: return kind == kScan ? (void*)&indexer_scan_kernel<4> : kind == kSelect ? (void*)&indexer_select_kernel<4> : (void*)&indexer_dump_kernel<4>;
   }
 }
 
@@ -719,8 +835,8 @@ void* pick_kernel(int nht, bool dump) {
 int resident_capacity(void* fn, int slot) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
-  static int cached[64][8];
-  static bool have[64][8];
+  static int cached[64][16];
+  static bool have[64][16];
   if (dev < 64 && have[dev][slot]) return cached[dev][slot];
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return -1;
@@ -745,8 +861,10 @@ int validate(const void* q, const void* qs, const float* w, const void* kpool, i
 
 int run(Params P, bool dump, hipStream_t stream) {
   const int nht = (P.H + 15) / 16;
-  void* fn = pick_kernel(nht, dump);
-  const int cap = resident_capacity(fn, (nht - 1) + (dump ? 4 : 0));
+  const KernelKind kind = dump ? kDump : kScan;
+  void* scan = pick_kernel(nht, kind);
+  void* sel = pick_kernel(nht, kSelect);
+  const int cap = resident_capacity(scan, (nht - 1) * 3 + (int)kind);
   if (cap <= 0) return DSA_ERR_HIP;
   const int R = P.R;
   const int upr = units_stride(P.bt_stride);
@@ -767,7 +885,9 @@ int run(Params P, bool dump, hipStream_t stream) {
     }
     const int64_t G = std::min<int64_t>((int64_t)cap, (int64_t)rn * upr);
     void* args[] = {&Q};
-    if (hipLaunchKernel(fn, dim3((unsigned)G), dim3(kThreads), args, 0, stream) != hipSuccess)
+    if (hipLaunchKernel(scan, dim3((unsigned)G), dim3(kThreads), args, 0, stream) != hipSuccess)
+      return DSA_ERR_HIP;
+    if (!dump && hipLaunchKernel(sel, dim3((unsigned)rn), dim3(kThreads), args, 0, stream) != hipSuccess)
       return DSA_ERR_HIP;
   }
   return DSA_OK;
@@ -829,7 +949,6 @@ extern "C" int dsa_indexer_topk(const void* q_fp8, const void* q_e8m0, const flo
   P.out_idx = out_idx;
   P.out_score = out_score;
   P.hdr = reinterpret_cast<uint32_t*>(ws + L.hdr);
-  P.tick = reinterpret_cast<uint32_t*>(ws + L.tick);
   P.ucount = reinterpret_cast<uint32_t*>(ws + L.ucount);
   P.uedge = reinterpret_cast<uint32_t*>(ws + L.uedge);
   P.cand = reinterpret_cast<uint2*>(ws + L.cand);
