@@ -185,12 +185,17 @@ size_t dsa_sparse_attn_workspace_size(int32_t R, int32_t H, int32_t topk);
  *   q_bf16     [R, H, 576] bf16 (latent 512 | rope 64)
  *   kv_pool    SFA cache, pool_pages pages of 41984 bytes
  *   idx        [R, topk] int32 positions of sequence row_seq[r]; -1 = skip
- *   H          multiple of 16, <= 128;  topk 1..2048
+ *   H          1..128;  topk 1..2048
  *   softmax_scale  the logit scale (1/sqrt(576) for this model)
  *   out        [R, H, 512] fp32;  lse [R, H] fp32 (may be NULL)
- *   A row with no valid entry gets out = 0 and lse = -inf.
- *   workspace  >= dsa_sparse_attn_workspace_size(...) bytes, zeroed once;
- *              every call leaves it zeroed.
+ *   A row with no valid entry gets out = 0 and lse = -inf.  Entries whose
+ *   position maps to no page, or to a page id outside [0, pool_pages), are
+ *   skipped and set bit 0 of the status word at workspace bytes [0,4).
+ *   workspace  >= dsa_sparse_attn_workspace_size(...) bytes, zero-filled once
+ *              by the caller before first use: bytes [256, 1280) must stay
+ *              zero (no call writes them); the rest holds per-call partial
+ *              results.
+ * Results are deterministic (splits are combined in a fixed order).
  */
 int dsa_sparse_attn(const void* q_bf16, const void* kv_pool, int64_t pool_pages,
                     const int32_t* block_table, int32_t bt_stride,

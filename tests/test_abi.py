@@ -49,8 +49,13 @@ def test_workspace_sizes_are_host_only(lib):
     a = lib.dsa_indexer_topk_workspace_size(8, 2048, 64, 2048)
     b = lib.dsa_indexer_topk_workspace_size(16, 2048, 64, 2048)
     assert 0 < a < b
-    assert lib.dsa_sparse_attn_workspace_size(8, 128, 2048) > 0
-    assert lib.dsa_sparse_attn_workspace_size(0, 128, 2048) == 256
+    # status word + the 1 KB zero record, plus the split partials when the
+    # index list is split (8 rows of 128 heads: 8 splits of 256 entries)
+    small = lib.dsa_sparse_attn_workspace_size(0, 128, 2048)
+    assert small == 256 + 1024
+    assert lib.dsa_sparse_attn_workspace_size(8, 128, 2048) >= small + 8 * 128 * 8 * 512 * 4
+    # 512 rows of 8 heads need no split: no partials
+    assert lib.dsa_sparse_attn_workspace_size(512, 8, 64) == small
 
 
 P = ctypes.c_void_p

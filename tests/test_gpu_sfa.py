@@ -108,3 +108,19 @@ def test_end_to_end_decode(need_gpu):
     check_topk_row(gi[0], sc.cpu().numpy()[0], ora, st.topk, int(st.inp["row_pos"][0]))
     if np.array_equal(gi[0], ora["idx"]):
         _compare(st, o, gi, [0], "end to end")
+
+
+def test_sfa_split_path_with_holes(need_gpu):
+    """One row of 128 heads runs as 8 splits of 256 entries combined by the
+    second launch.  The list has -1 holes, a run of one duplicated position,
+    one split that is entirely empty, and a ragged tail."""
+    st = state("decode_8k_needles")
+    o = Oracle(st.inp)
+    K = st.topk
+    idx = o.topk(0)["idx"].copy()
+    idx[::5] = -1
+    idx[256:512] = -1               # split 1 has no entry at all
+    idx[600:650] = idx[701]         # one position listed 50 times
+    idx[K - 37:] = -1               # ragged tail of the last split
+    out, lse = _compare(st, o, idx[None, :], [0], "split path with holes")
+    assert np.all(np.isfinite(out[0]))
