@@ -21,6 +21,13 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument", f"-I{INCLUDE}"]
 
+# Per-source extras.  The attention kernel keeps its output accumulator live
+# across the whole loop and also touches it with VALU code; with the MFMA
+# results written to VGPRs (instead of the default AGPR form) the register
+# allocator keeps everything in 256 VGPRs rather than copying the
+# accumulator between register files on every iteration.
+EXTRA = {"sparse_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
 
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
@@ -34,7 +41,7 @@ def build(verbose: bool = True, jobs: int = 4) -> str:
     for src in sources():
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
         objs.append(obj)
-        cmd = [hipcc, *FLAGS, "-c", src, "-o", obj]
+        cmd = [hipcc, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
         procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
         if len(procs) >= jobs:
             _wait(procs.pop(0), verbose)

@@ -7,7 +7,7 @@
 // One workgroup = (query row, group of 32 heads, split of the index list);
 // the groups of one (row, split) are placed on one XCD so the records they
 // all read are served by that XCD's L2.  Four waves: wave w owns head tile
-// w&1 (16 heads) and the token tiles of parity w>>1.
+// w&1 (16 heads) and latent half w>>1 (256 of the 512 output dims).
 //  * up front, every entry of the split is translated position -> page ->
 //    record slot (two dependent loads, all entries in flight together);
 //  * the selected 656-byte records are copied 32 per tile straight from
@@ -18,7 +18,9 @@
 //    exact, each 128-wide latent tile accumulates separately and is scaled
 //    by its fp32 tile scale in fp32, the bf16 rope part adds on top; times
 //    softmax_scale*log2(e);
-//  * online softmax per head inside the wave (a head's 32 logits of a tile
+//  * each wave computes the logits of one of the step's two tiles and swaps
+//    them with its partner (same heads, other latent half) through LDS;
+//    online softmax per head inside the wave (a head's 64 logits of a step
 //    live in its four lanes);
 //  * O^T += V^T P'^T on v_mfma_f32_16x16x32_f16: V is the exact E4M3 code in
 //    f16 read transposed from LDS by ds_read_b64_tr_b8, and the tile scale
@@ -26,8 +28,7 @@
 //    power-of-two reference so P' stays well inside fp16).  P' never leaves
 //    the registers: the logits' output layout is the B-operand layout of
 //    the P.V product once the tile's 32 tokens are ordered to match.
-// The two token halves of a workgroup merge in LDS.  With one split the
-// workgroup writes out and lse; otherwise it writes (O, m, l) partials and a
+// With one split the workgroup writes out and lse; otherwise it writes (O, m, l) partials and a
 // second launch combines the splits of every (row, head) in split order
 // (deterministic).
 #include <algorithm>
@@ -52,10 +53,13 @@ constexpr int kMaxEntries = DSA_MAX_TOPK;     // entries of one split
 constexpr int kMaxSplits = 8;
 constexpr int kTargetWgs = 256;
 constexpr int kZeroBytes = 1024;              // zero record in the workspace
+constexpr int kMargin = 6;                    // logits may exceed the softmax reference by 2^6
+constexpr int kPBias = 8;                     // P' = p * scale * 2^(kPBias - E) < 2^(kMargin+1+kPBias)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 static_assert(kDmaPerWave * 4 >= kDmaPerTile, "DMA assignment covers a tile");
 static_assert(32 * kPieces <= kDmaPerTile * 64, "a tile fits its DMA instructions");
+static_assert(kMargin + 1 + kPBias < 16, "P' stays below the fp16 maximum");
 
 struct Params {
   const uint16_t* q;      // [R, H, 576] bf16
@@ -78,10 +82,10 @@ struct Params {
 };
 
 struct Smem {
-  uint8_t ring[kRingBytes];            // record tiles; after the loop: merge area
+  uint8_t ring[kRingBytes];            // record tiles
   uint8_t junk[1024];                  // target of padding DMA instructions
   int32_t slot[kMaxEntries];           // record slot per entry of the split, -1 = none
-  float ml[2][16][2];                  // merge: (m, l) per head tile and head
+  float zx[2][2][8 * 64];              // logits swapped between partner waves
 };
 
 __device__ __forceinline__ void flag(uint32_t* err, uint32_t bits) {
@@ -176,37 +180,58 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
 
   // ---- DMA of one step (two tiles) into ring slot k % 3: every wave issues
   //      exactly 2 * kDmaPerWave instructions per step, padding ones included,
-  //      so the waits below can count them
+  //      so the waits below can count them.  Instruction m of a wave covers
+  //      pieces 64j + lane (j = wv + 4m) of the tile: record rec_m, 16-byte
+  //      piece part_m.
   const uint32_t ring0 = lds_addr(S.ring), junk = lds_addr(S.junk);
+  int rec_m[kDmaPerWave], off_m[kDmaPerWave];
+#pragma unroll
+  for (int m = 0; m < kDmaPerWave; ++m) {
+    const int piece = 64 * (wv + 4 * m) + lane;
+    rec_m[m] = piece / kPieces;
+    off_m[m] = (piece - kPieces * rec_m[m]) * 16;
+  }
   auto issue_step = [&](int k) {
+    int32_t sl[2][kDmaPerWave];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int m = 0; m < kDmaPerWave; ++m) {
+        const bool live = wv + 4 * m < kDmaPerTile && k < nsteps && rec_m[m] < kTileTok;
+        sl[tt][m] = live ? S.slot[(2 * k + tt) * kTileTok + rec_m[m]] : -1;
+      }
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const uint32_t base = ring0 + (uint32_t)(((k % kRingSteps) * 2 + tt) * kSlotBytes);
 #pragma unroll
       for (int m = 0; m < kDmaPerWave; ++m) {
-        const int j = wv + 4 * m;
-        const uint8_t* src = P.zero;
-        uint32_t dst = junk;
-        if (j < kDmaPerTile && k < nsteps) {
-          const int piece = 64 * j + lane;
-          const int rec = piece / kPieces, part = piece - kPieces * rec;
-          const int32_t s = rec < kTileTok ? S.slot[(2 * k + tt) * kTileTok + rec] : -1;
-          src = s >= 0 ? P.pool + (int64_t)s * kRec + part * 16 : P.zero + part * 16;
-          dst = base + (uint32_t)(j * 1024);
-        }
-        dma16(src, dst);
+        const bool inst = wv + 4 * m < kDmaPerTile && k < nsteps;   // wave-uniform
+        const int32_t sv = sl[tt][m];
+        const uint8_t* src = sv >= 0 ? P.pool + (int64_t)sv * kRec + off_m[m] : P.zero + off_m[m];
+        dma16(src, inst ? base + (uint32_t)((wv + 4 * m) * 1024) : junk);
       }
     }
   };
 
-  // running softmax state of head hr (identical in the four lanes of a
-  // head), running power-of-two references of the four latent tiles
-  // (wave-uniform), and O^T: o[d][c] = dim 16d + 4g + c of head hr
-  float m_run = -__builtin_huge_valf(), l_run = 0.f;
-  int eref[4] = {-1000, -1000, -1000, -1000};
-  v4f o[32];
+  // Wave roles: head tile ht; dim half dh.  In step k the wave computes the
+  // logits of tile 2k+dh for its 16 heads and swaps them with its partner
+  // (same ht, other dh) through LDS; both then hold the step's 64 logits,
+  // run the same softmax, and the wave accumulates O^T for latent dims
+  // 256dh .. 256dh+255 (latent tiles 2dh, 2dh+1).
+  // m_ref / l_run: softmax reference and running sum of head hr (identical
+  // in the four lanes of a head and in both partners; l_run and O are
+  // relative to m_ref); eref: power-of-two references of the wave's two
+  // latent tiles (wave-uniform).  The references move only when a logit
+  // exceeds m_ref by more than kMargin or a tile scale exceeds its reference,
+  // so O is rescaled rarely.  o[d][c] = dim 256dh + 16d + 4g + c of head hr.
+  const int dh = wv >> 1;
+  float m_ref = -__builtin_huge_valf(), l_run = 0.f;
+  int eref[2] = {-1000, -1000};
+  v4f o[16];
 #pragma unroll
-  for (int d = 0; d < 32; ++d) o[d] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int d = 0; d < 16; ++d) o[d] = v4f{0.f, 0.f, 0.f, 0.f};
+  float* zx = S.zx[ht][dh];
+  const float* zpart = S.zx[ht][dh ^ 1];
 
   issue_step(0);
   issue_step(1);
@@ -215,175 +240,187 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
     // the barrier also releases the slots of step k-1
     asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
     issue_step(k + 2);
-    const uint8_t* tile = S.ring + ((k % kRingSteps) * 2 + par) * kSlotBytes;
-    const int e0 = (2 * k + par) * kTileTok;   // first entry of this tile
+    const uint8_t* tA = S.ring + ((k % kRingSteps) * 2) * kSlotBytes;
+    const uint8_t* tB = tA + kSlotBytes;
+    const uint8_t* tq = dh ? tB : tA;          // the tile whose logits this wave computes
+    const int eq0 = (2 * k + dh) * kTileTok;   // its first entry
 
-    // ---- logits of the tile's 32 tokens for the wave's 16 heads ----
+    // ---- logits of tile tq's 32 tokens for the wave's 16 heads ----
     v4f acc[2][5];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int t = 0; t < 5; ++t) acc[u][t] = v4f{0.f, 0.f, 0.f, 0.f};
+    // k-steps ordered so that consecutive MFMAs feed different accumulators
+    const uint8_t* rec0 = tq + hr * kRec;            // A-operand rows of this lane
+    const uint8_t* rec1 = tq + (16 + hr) * kRec;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint8_t* rec = tile + (16 * u + hr) * kRec;   // A-operand row of this lane
+    for (int j = 0; j < 4; ++j) {
 #pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const uint2 raw = *reinterpret_cast<const uint2*>(rec + 32 * s + 8 * g);
-        const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, false);
-        const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, true);
-        const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, 1.0f, false);
-        const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, 1.0f, true);
-        const v8bf a = v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        acc[u][s >> 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qv[s], acc[u][s >> 2], 0, 0, 0);
+      for (int t = 0; t < 4; ++t) {
+        const int s = 4 * t + j;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const uint2 raw = *reinterpret_cast<const uint2*>((u ? rec1 : rec0) + 32 * s + 8 * g);
+          const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, false);
+          const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, true);
+          const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, 1.0f, false);
+          const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, 1.0f, true);
+          const v8bf a = v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+          acc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qv[s], acc[u][t], 0, 0, 0);
+        }
       }
+    }
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const uint4 r4 = *reinterpret_cast<const uint4*>(rec + kRecRopeOff + 64 * s + 16 * g);
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint4 r4 = *reinterpret_cast<const uint4*>((u ? rec1 : rec0) + kRecRopeOff + 64 * s + 16 * g);
         acc[u][4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, r4), qv[16 + s],
                                                             acc[u][4], 0, 0, 0);
       }
-    }
-    // tile scales of the lane's 8 tokens (k order), logits z
-    float sc[8][4];
-    float z[8];
-    uint32_t smax[4] = {0u, 0u, 0u, 0u};
+    // logits of the lane's 8 tokens of tq (k order), shared with the partner
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int tok = ktok(g, i);
-      const float4 s4 = *reinterpret_cast<const float4*>(tile + tok * kRec + kRecScaleOff);
-      sc[i][0] = s4.x; sc[i][1] = s4.y; sc[i][2] = s4.z; sc[i][3] = s4.w;
+      const float4 s4 = *reinterpret_cast<const float4*>(tq + tok * kRec + kRecScaleOff);
       const int u = i >> 2, c = i & 3;
       float v = acc[u][4][c];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) v = __builtin_fmaf(sc[i][t], acc[u][t][c], v);
-      const bool valid = S.slot[e0 + tok] >= 0;
-      z[i] = valid ? v * P.scale_log2 : -__builtin_huge_valf();
-#pragma unroll
-      for (int t = 0; t < 4; ++t) smax[t] = max(smax[t], __float_as_uint(sc[i][t]));
+      v = __builtin_fmaf(s4.x, acc[u][0][c], v);
+      v = __builtin_fmaf(s4.y, acc[u][1][c], v);
+      v = __builtin_fmaf(s4.z, acc[u][2][c], v);
+      v = __builtin_fmaf(s4.w, acc[u][3][c], v);
+      zx[i * 64 + lane] = S.slot[eq0 + tok] >= 0 ? v * P.scale_log2 : -__builtin_huge_valf();
     }
-    // ---- online softmax of head hr over the tile ----
-    float zm = z[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) zm = fmaxf(zm, z[i]);
-    zm = fmaxf(zm, __shfl_xor(zm, 16));
-    zm = fmaxf(zm, __shfl_xor(zm, 32));
-    const float m_new = fmaxf(m_run, zm);
-    const bool any = m_new != -__builtin_huge_valf();
-    const float alpha = any ? exp2f(m_run - m_new) : 1.0f;   // exp2(-inf) = 0
-    float p[8], ps = 0.f;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // z[kk*8 + i]: tile kk (0 = tA, 1 = tB), k-order token i
+    float z[16];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      p[i] = any ? exp2f(z[i] - m_new) : 0.f;
+      const float own = zx[i * 64 + lane], other = zpart[i * 64 + lane];
+      z[i] = dh ? other : own;
+      z[8 + i] = dh ? own : other;
+    }
+    // scales of the wave's two latent tiles for the step's 64 tokens
+    float sc[16][2];
+    uint32_t smax[2] = {0u, 0u};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float2 s2 = *reinterpret_cast<const float2*>((kk ? tB : tA) + ktok(g, i) * kRec +
+                                                           kRecScaleOff + 8 * dh);
+        sc[8 * kk + i][0] = s2.x;
+        sc[8 * kk + i][1] = s2.y;
+        smax[0] = max(smax[0], __float_as_uint(s2.x));
+        smax[1] = max(smax[1], __float_as_uint(s2.y));
+      }
+
+    // ---- online softmax of head hr over the step (lazy references) ----
+    float zm = z[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) zm = fmaxf(zm, z[i]);
+    zm = fmaxf(zm, __shfl_xor(zm, 16));
+    zm = fmaxf(zm, __shfl_xor(zm, 32));
+    int et[2];
+    bool egrow = false;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      uint32_t b = smax[t];
+      b = max(b, (uint32_t)__shfl_xor((int)b, 16));
+      b = max(b, (uint32_t)__shfl_xor((int)b, 32));
+      et[t] = (b & 0x7FFFFFFFu) ? (int)((b >> 23) & 0xFF) - 127 : -1000;
+      egrow |= et[t] > eref[t];
+    }
+    const bool grow = zm > m_ref + (float)kMargin;   // false while zm is -inf
+    if (__builtin_amdgcn_ballot_w64(grow) || egrow) {
+      const float m_new = grow ? zm : m_ref;
+      const float fh = m_ref == -__builtin_huge_valf() ? 0.f : exp2f(m_ref - m_new);
+      float ft[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int en = max(eref[t], et[t]);
+        ft[t] = eref[t] > -1000 ? pow2f(max(-126, eref[t] - en)) : 0.f;
+        eref[t] = en;
+      }
+      if (__builtin_amdgcn_ballot_w64(l_run != 0.f)) {
+#pragma unroll
+        for (int d = 0; d < 16; ++d) {
+          const float f = fh * ft[d >> 3];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) o[d][c] *= f;
+        }
+      }
+      l_run *= fh;
+      m_ref = m_new;
+    }
+    float p[16], ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      p[i] = z[i] == -__builtin_huge_valf() ? 0.f : exp2f(z[i] - m_ref);   // <= 2^kMargin
       ps += p[i];
     }
     ps += __shfl_xor(ps, 16);
     ps += __shfl_xor(ps, 32);
-    l_run = alpha * l_run + ps;
-    m_run = m_new;
-    // ---- power-of-two references of the latent tiles (wave-uniform) ----
-    float resc[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      uint32_t b = smax[t];
-      b = max(b, (uint32_t)__shfl_xor((int)b, 16));
-      b = max(b, (uint32_t)__shfl_xor((int)b, 32));
-      const int et = (b & 0x7FFFFFFFu) ? (int)((b >> 23) & 0xFF) - 127 : -1000;
-      const int en = max(eref[t], et);
-      resc[t] = (eref[t] > -1000 && en > eref[t]) ? pow2f(max(-126, eref[t] - en)) : 1.0f;
-      eref[t] = en;
-    }
-    // rescale O^T where the running max or a reference moved
-    const bool need = alpha != 1.0f || resc[0] != 1.0f || resc[1] != 1.0f || resc[2] != 1.0f ||
-                      resc[3] != 1.0f;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-#pragma unroll
-      for (int d = 0; d < 32; ++d) {
-        const float f = alpha * resc[d >> 3];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) o[d][c] *= f;
-      }
-    }
-    // ---- O^T += V^T P'^T, latent tile t = dims 128t .. 128t+127 ----
+    l_run += ps;
+
+    // ---- O^T += V^T P'^T over the step's two tiles (k-steps) ----
     typedef __attribute__((address_space(3))) v2i lds_v2i;
-    const uint8_t* vrow = tile + ktok(g, hr >> 1) * kRec + 8 * (hr & 1);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const float mul = eref[t] > -1000 ? pow2f(max(-126, min(127, 8 - eref[t]))) : 0.f;
-      _Float16 h[8];
+    for (int t = 0; t < 2; ++t) {
+      const float mul = eref[t] > -1000 ? pow2f(max(-126, min(127, kPBias - eref[t]))) : 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) h[i] = (_Float16)(p[i] * sc[i][t] * mul);
-      const v8h b = v8h{h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7]};
+      for (int kk = 0; kk < 2; ++kk) {
+        _Float16 h[8];
 #pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const uint8_t* src = vrow + 128 * t + 16 * dd;
-        const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (lds_v2i*)((__attribute__((address_space(3))) uint8_t*)(src)));
-        const v2h v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[0], 1.0f, false);
-        const v2h v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[0], 1.0f, true);
-        const v2h v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[1], 1.0f, false);
-        const v2h v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[1], 1.0f, true);
-        const v8h a = v8h{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
-        o[8 * t + dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, o[8 * t + dd], 0, 0, 0);
+        for (int i = 0; i < 8; ++i) h[i] = (_Float16)(p[8 * kk + i] * sc[8 * kk + i][t] * mul);
+        const v8h b = v8h{h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7]};
+        const uint8_t* vrow = (kk ? tB : tA) + ktok(g, hr >> 1) * kRec + 8 * (hr & 1) +
+                              128 * (2 * dh + t);
+#pragma unroll
+        for (int dd = 0; dd < 8; ++dd) {
+          const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (lds_v2i*)((__attribute__((address_space(3))) uint8_t*)(vrow + 16 * dd)));
+          const v2h v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[0], 1.0f, false);
+          const v2h v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[0], 1.0f, true);
+          const v2h v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[1], 1.0f, false);
+          const v2h v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[1], 1.0f, true);
+          const v8h a = v8h{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+          o[8 * t + dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, o[8 * t + dd], 0, 0, 0);
+        }
       }
     }
   }
+  // no copy may still be landing in LDS when the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // ---- epilogue: true O = o * 2^(eref - 8); merge the two parities ----
+  // ---- epilogue: true O = o * 2^(eref - kPBias) ----
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const float f = eref[t] > -1000 ? pow2f(max(-126, min(127, eref[t] - 8))) : 0.f;
+  for (int t = 0; t < 2; ++t) {
+    const float f = eref[t] > -1000 ? pow2f(max(-126, min(127, eref[t] - kPBias))) : 0.f;
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd)
 #pragma unroll
       for (int c = 0; c < 4; ++c) o[8 * t + dd][c] *= f;
   }
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");   // ring free, padding copies done
-  float4* xo = reinterpret_cast<float4*>(S.ring) + ht * (32 * 64);
-  if (par == 1) {
-#pragma unroll
-    for (int d = 0; d < 32; ++d) xo[d * 64 + lane] = make_float4(o[d][0], o[d][1], o[d][2], o[d][3]);
-    if (g == 0) {
-      S.ml[ht][hr][0] = m_run;
-      S.ml[ht][hr][1] = l_run;
-    }
-  }
-  __syncthreads();
-  if (par == 1) return;
-  {
-    const float m1 = S.ml[ht][hr][0], l1 = S.ml[ht][hr][1];
-    const float M = fmaxf(m_run, m1);
-    const bool anyM = M != -__builtin_huge_valf();
-    const float a0 = anyM ? exp2f(m_run - M) : 0.f, a1 = anyM ? exp2f(m1 - M) : 0.f;
-#pragma unroll
-    for (int d = 0; d < 32; ++d) {
-      const float4 x = xo[d * 64 + lane];
-      o[d][0] = a0 * o[d][0] + a1 * x.x;
-      o[d][1] = a0 * o[d][1] + a1 * x.y;
-      o[d][2] = a0 * o[d][2] + a1 * x.z;
-      o[d][3] = a0 * o[d][3] + a1 * x.w;
-    }
-    l_run = a0 * l_run + a1 * l1;
-    m_run = M;
-  }
   if (!head_ok) return;
   if (P.S == 1) {
     const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-    float4* dst = reinterpret_cast<float4*>(P.out + ((int64_t)row * P.H + head) * kLatent);
+    float4* dst = reinterpret_cast<float4*>(P.out + ((int64_t)row * P.H + head) * kLatent) + 64 * dh;
 #pragma unroll
-    for (int d = 0; d < 32; ++d)
+    for (int d = 0; d < 16; ++d)
       dst[4 * d + g] = make_float4(o[d][0] * inv, o[d][1] * inv, o[d][2] * inv, o[d][3] * inv);
-    if (P.lse && g == 0)
+    if (P.lse && g == 0 && dh == 0)
       P.lse[(int64_t)row * P.H + head] =
-          l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -__builtin_huge_valf();
+          l_run > 0.f ? (m_ref + log2f(l_run)) * kLn2 : -__builtin_huge_valf();
     return;
   }
   const int64_t ph = ((int64_t)row * P.H + head) * P.S + sp;
-  float4* po = reinterpret_cast<float4*>(P.part_o + ph * kLatent);
+  float4* po = reinterpret_cast<float4*>(P.part_o + ph * kLatent) + 64 * dh;
 #pragma unroll
-  for (int d = 0; d < 32; ++d) po[4 * d + g] = make_float4(o[d][0], o[d][1], o[d][2], o[d][3]);
-  if (g == 0) {
-    P.part_ml[2 * ph] = m_run;
+  for (int d = 0; d < 16; ++d) po[4 * d + g] = make_float4(o[d][0], o[d][1], o[d][2], o[d][3]);
+  if (g == 0 && dh == 0) {
+    P.part_ml[2 * ph] = m_ref;
     P.part_ml[2 * ph + 1] = l_run;
   }
 }
@@ -394,18 +431,32 @@ __global__ __launch_bounds__(kThreads) void sfa_combine_kernel(Params P) {
   const int row = blockIdx.x, h = 4 * blockIdx.y + (threadIdx.x >> 6), c = threadIdx.x & 63;
   if (h >= P.H) return;
   const int64_t ph0 = ((int64_t)row * P.H + h) * P.S;
+  // every split's loads first (S <= kMaxSplits), then the fixed-order sums
+  float2 ml[kMaxSplits];
+  float4 x[kMaxSplits][2];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < P.S) {
+      ml[s] = reinterpret_cast<const float2*>(P.part_ml)[ph0 + s];
+      const float4* src = reinterpret_cast<const float4*>(P.part_o + (ph0 + s) * kLatent) + 2 * c;
+      x[s][0] = src[0];
+      x[s][1] = src[1];
+    }
+  }
   float M = -__builtin_huge_valf();
-  for (int s = 0; s < P.S; ++s) M = fmaxf(M, P.part_ml[2 * (ph0 + s)]);
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < P.S) M = fmaxf(M, ml[s].x);
   float L = 0.f;
   float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
-  for (int s = 0; s < P.S; ++s) {
-    const float m = P.part_ml[2 * (ph0 + s)], l = P.part_ml[2 * (ph0 + s) + 1];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s >= P.S) continue;
+    const float m = ml[s].x;
     const float w = (M == -__builtin_huge_valf() || m == -__builtin_huge_valf()) ? 0.f : exp2f(m - M);
-    L += w * l;
-    const float4* src = reinterpret_cast<const float4*>(P.part_o + (ph0 + s) * kLatent) + 2 * c;
-    const float4 x = src[0], y = src[1];
-    a0.x += w * x.x; a0.y += w * x.y; a0.z += w * x.z; a0.w += w * x.w;
-    a1.x += w * y.x; a1.y += w * y.y; a1.z += w * y.z; a1.w += w * y.w;
+    L += w * ml[s].y;
+    a0.x += w * x[s][0].x; a0.y += w * x[s][0].y; a0.z += w * x[s][0].z; a0.w += w * x[s][0].w;
+    a1.x += w * x[s][1].x; a1.y += w * x[s][1].y; a1.z += w * x[s][1].z; a1.w += w * x[s][1].w;
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   float4* dst = reinterpret_cast<float4*>(P.out + ((int64_t)row * P.H + h) * kLatent) + 2 * c;
