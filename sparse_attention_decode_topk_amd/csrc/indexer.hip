@@ -45,11 +45,13 @@ constexpr int kHalvesPerWave = 2 * kUnitPages / kWaves;  // 8 half pages per wav
 constexpr int kRing = 3;                               // half pages in flight per wave
 constexpr int kFBins = 256;                            // filter histogram (8-bit passes)
 constexpr int kBins = 4096;                            // select histogram (12-bit passes)
-constexpr int kCandPer = 23;                           // select: candidates per thread
-constexpr int kChunk = kCandPer * kThreads;            // candidates staged in LDS at once
+constexpr int kCandPer = 24;                           // select: candidates per thread
+constexpr int kChunk = kCandPer * kThreads;            // candidates held in registers at once
 constexpr int kMaxRows = 1024;                         // rows per launch
 constexpr int kMaxBtStride = 16384;                    // pages per row (1M tokens)
 constexpr int kMaxUnitsPerRow = kMaxBtStride / kUnitPages;
+constexpr int kFastUnits = 128;                       // select fast path: units per row
+constexpr int kFastPer = kFastUnits / kWaves;          // units per wave
 static_assert(kFBins == kThreads, "one filter bin per thread");
 
 // Buffer descriptor word 3 for raw (untyped) buffer access on gfx9-class
@@ -91,13 +93,13 @@ struct ScanSmem {
 };
 
 struct SelSmem {
-  union {
-    uint2 stage[kChunk];              // a chunk of candidates (key, position)
-    uint32_t keys[kUnitTok];          // rescoring a unit
-  };
-  uint16_t owner[kChunk];             // unit of each staged candidate
+  uint32_t keys[kUnitTok];            // rescoring a unit
   uint32_t hist[kBins];
   uint32_t cpre[kMaxUnitsPerRow + 1]; // candidate prefix per unit
+  uint32_t ucnt[kFastUnits];          // fast path: packed (equal, greater) per unit
+  uint32_t ubase[kFastUnits];         // fast path: their exclusive prefix
+  uint32_t small[64];                 // fast path: keys of the threshold bin
+  uint32_t smalln;
   uint32_t red[2 * kWaves + 2];
   uint32_t misc[16];
 };
@@ -112,16 +114,32 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
 
 // ---- block primitives (256 threads) -------------------------------------
 
+// Inclusive prefix sum / max across the 64 lanes of a wave with DPP row
+// shifts (within rows of 16 lanes) and row broadcasts (across rows).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_incl_max(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false));
+  return x;
+}
+
 // Exclusive prefix of v over the block; *total receives the block sum.
-__device__ uint32_t block_excl_scan(uint32_t v, uint32_t* red, uint32_t* total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) red[wv] = x;
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* red, uint32_t* total) {
+  const int wv = threadIdx.x >> 6;
+  const uint32_t x = wave_incl_scan(v);
+  if ((threadIdx.x & 63) == 63) red[wv] = x;
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
@@ -135,28 +153,16 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* red, uint32_t* total) 
   return before + x - v;
 }
 
-__device__ uint32_t block_max(uint32_t v, uint32_t* red) {
+__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
   const int wv = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor(v, d));
-  if ((threadIdx.x & 63) == 0) red[wv] = v;
+  const uint32_t x = wave_incl_max(v);
+  if ((threadIdx.x & 63) == 63) red[wv] = x;
   __syncthreads();
   uint32_t m = 0;
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) m = max(m, red[i]);
   __syncthreads();
   return m;
-}
-
-// Inclusive prefix sum across the 64 lanes of a wave.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  return x;
 }
 
 // ---- units ------------------------------------------------------------------
@@ -173,7 +179,7 @@ __device__ __forceinline__ int row_units(int t, int bt_stride) {
   return (row_pages(t, bt_stride) + kUnitPages - 1) / kUnitPages;
 }
 
-__device__ void plan_rows(const Params& P, uint32_t* rowpre, uint32_t* red) {
+__device__ __forceinline__ void plan_rows(const Params& P, uint32_t* rowpre, uint32_t* red) {
   const int per = (P.R + kThreads - 1) / kThreads;
   const int r0 = threadIdx.x * per;
   uint32_t lu = 0;
@@ -191,7 +197,7 @@ __device__ void plan_rows(const Params& P, uint32_t* rowpre, uint32_t* red) {
   __syncthreads();
 }
 
-__device__ Unit decode_unit(const Params& P, const uint32_t* rowpre, uint32_t u) {
+__device__ __forceinline__ Unit decode_unit(const Params& P, const uint32_t* rowpre, uint32_t u) {
   int lo = 0, hi = P.R - 1;     // row r with rowpre[r] <= u < rowpre[r+1]
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -216,7 +222,7 @@ __device__ Unit decode_unit(const Params& P, const uint32_t* rowpre, uint32_t u)
 }
 
 // Unit uir of a row whose last position is t (used by the rescoring path).
-__device__ Unit row_unit(const Params& P, int row, int t, int uir) {
+__device__ __forceinline__ Unit row_unit(const Params& P, int row, int t, int uir) {
   Unit U;
   U.row = row;
   U.uir = uir;
@@ -240,7 +246,7 @@ struct QOperand {
 // dequantised exactly into bf16.  The key operand uses the same k order, so
 // each lane's 32 key bytes form exactly one MXFP8 group with one scale.
 template <int NHT>
-__device__ void load_q(const Params& P, int row, QOperand<NHT>& Q) {
+__device__ __forceinline__ void load_q(const Params& P, int row, QOperand<NHT>& Q) {
   const int lane = threadIdx.x & 63, hr = lane & 15, g = lane >> 4;
   // every load is issued unconditionally (heads beyond H read head 0 and are
   // zeroed afterwards) so the compiler's wait counting sees a fixed number
@@ -343,7 +349,7 @@ __device__ __forceinline__ void score_half(const QOperand<NHT>& Q, const HalfReg
 // gets a zero-record descriptor), so the loads retire in ring order and the
 // compiler's wait counting never has to drain the ring.
 template <int NHT, bool DUMP>
-__device__ void score_unit(const Params& P, const Unit& U, uint32_t* keys) {
+__device__ __forceinline__ void score_unit(const Params& P, const Unit& U, uint32_t* keys) {
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int npg = U.pg1 - U.pg0;   // <= 16
@@ -415,7 +421,7 @@ __device__ __forceinline__ uint32_t unit_quota(int t, int topk) {
 // b where the count of keys in bins >= b first reaches `need`; it clears
 // every bin it read.  misc[0] = b, misc[1] = count in bins > b, misc[2] = 1
 // if found.  Ends with a block barrier.
-__device__ void filter_threshold(uint32_t* hist, uint32_t need, uint32_t* misc) {
+__device__ __forceinline__ void filter_threshold(uint32_t* hist, uint32_t need, uint32_t* misc) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const int top = kFBins - 1 - 4 * lane;          // this lane's bins: top .. top-3
@@ -448,7 +454,7 @@ __device__ void filter_threshold(uint32_t* hist, uint32_t need, uint32_t* misc) 
 // bin holding the unit's quota-th largest key (two 8-bit LDS histogram
 // passes); keys at or above it are emitted, so every key left out is below
 // the recorded edge.  The histogram is all zero on entry and on exit.
-__device__ void filter_unit(const Params& P, ScanSmem& S, const Unit& U) {
+__device__ __forceinline__ void filter_unit(const Params& P, ScanSmem& S, const Unit& U) {
   const int tid = threadIdx.x;
   const int ntok = (U.pg1 - U.pg0) * kPage;
   const uint32_t quota = unit_quota(U.t, P.topk);
@@ -515,20 +521,26 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_dump_kernel(Params P) {
 }
 
 // ---- select kernel ---------------------------------------------------------------
+//
+// Radix passes keep the histogram in LDS and the keys in registers; every
+// pass alternates between two sets of reduction slots (par = pass parity),
+// so four barriers per pass suffice.
 
-// Candidate prefix per unit (S.cpre, S.cpre[units_r] = total); returns the
-// largest unit edge.
-__device__ uint32_t load_counts(const Params& P, SelSmem& S, int row, int units_r) {
+// Candidate prefix per unit (S.cpre, S.cpre[units_r] = total); *emax
+// receives the largest unit edge and *cmax the largest unit count.
+__device__ __forceinline__ void load_counts(const Params& P, SelSmem& S, int row, int units_r,
+                                            uint32_t* emax_out, uint32_t* cmax_out) {
   constexpr int kPer = kMaxUnitsPerRow / kThreads;   // 4
   const int u0 = threadIdx.x * kPer;
   const int64_t base = (int64_t)row * P.upr;
   uint32_t c[kPer];
-  uint32_t local = 0, emax = 0;
+  uint32_t local = 0, emax = 0, cmax = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const bool in = u0 + i < units_r;
     c[i] = in ? load_agent(&P.ucount[base + u0 + i]) : 0u;
     emax = max(emax, in ? load_agent(&P.uedge[base + u0 + i]) : 0u);
+    cmax = max(cmax, c[i]);
     local += c[i];
   }
   uint32_t total;
@@ -539,73 +551,37 @@ __device__ uint32_t load_counts(const Params& P, SelSmem& S, int row, int units_
     run += c[i];
   }
   if (threadIdx.x == 0) S.cpre[units_r] = total;
-  __syncthreads();
-  return block_max(emax, S.red);
+  // (block_max's first barrier publishes cpre)
+  *emax_out = block_max(emax, S.red);
+  *cmax_out = block_max(cmax, S.red);
 }
 
-// Stage candidates [ch*kChunk, ...) of the row (flat order = position order)
-// into S.stage: the owner unit of every slot is filled in LDS first, then
-// every thread issues all of its loads before storing.  Returns the number
-// staged; *kmax receives the largest staged key.
-__device__ uint32_t stage_chunk(const Params& P, SelSmem& S, int row, int units_r, uint32_t n_c,
-                                uint32_t ch, uint32_t* kmax) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const uint32_t base = ch * kChunk;
-  const uint32_t n = base < n_c ? min((uint32_t)kChunk, n_c - base) : 0u;
-  for (int u = wv; u < units_r; u += kWaves) {
-    const uint32_t a = max(S.cpre[u], base), b = min(S.cpre[u + 1], base + n);
-    for (uint32_t f = a + lane; f < b; f += 64) S.owner[f - base] = (uint16_t)u;
-  }
-  __syncthreads();
-  const uint2* rowc = P.cand + (int64_t)row * P.bt_stride * kPage;
-  uint2 v[kCandPer];
+// Clears the histogram and the pass's result flag (no barrier).
+__device__ __forceinline__ void hist_clear(SelSmem& S, int par) {
+  uint4* h4 = reinterpret_cast<uint4*>(S.hist);
 #pragma unroll
-  for (int k = 0; k < kCandPer; ++k) {
-    const uint32_t i = threadIdx.x + k * kThreads;
-    v[k] = make_uint2(0u, 0u);
-    if (i < n) {
-      const uint32_t u = S.owner[i];
-      v[k] = rowc[(int64_t)u * kUnitTok + (base + i - S.cpre[u])];
-    }
-  }
-  uint32_t m = 0;
-#pragma unroll
-  for (int k = 0; k < kCandPer; ++k) {
-    const uint32_t i = threadIdx.x + k * kThreads;
-    if (i < n) S.stage[i] = v[k];
-    m = max(m, v[k].x);
-  }
-  *kmax = block_max(m, S.red);   // its barriers also publish the stage
-  return n;
+  for (int i = 0; i < kBins / 4 / kThreads; ++i) h4[threadIdx.x + i * kThreads] = make_uint4(0, 0, 0, 0);
+  if (threadIdx.x == 0) S.misc[4 * par + 2] = 0;
 }
 
-// One radix pass: histogram of (key - base) >> shift over the 4096 bins for
-// keys in [base, base + span) (span <= 4096 << shift), then the bin holding
-// the key of rank `need` from the top.  Returns false if fewer than `need`
-// keys fall in the range; else *bin and *above (keys in higher bins).
-__device__ bool radix_pass(const Params& P, SelSmem& S, int row, int units_r, uint32_t n_c,
-                           uint32_t base, uint32_t shift, uint64_t span, uint32_t need,
-                           uint32_t* bin, uint32_t* above) {
-  const uint32_t nch = (n_c + kChunk - 1) / kChunk;
-  {
-    uint4* h4 = reinterpret_cast<uint4*>(S.hist);
+// Adds the keys in [base, base + span) of an array held in registers.
+template <int N>
+__device__ __forceinline__ void hist_add(SelSmem& S, const uint32_t (&k)[N], uint32_t base,
+                                         uint32_t shift, uint64_t span) {
 #pragma unroll
-    for (int i = 0; i < kBins / 4 / kThreads; ++i) h4[threadIdx.x + i * kThreads] = make_uint4(0, 0, 0, 0);
-  }
-  __syncthreads();
-  for (uint32_t ch = 0; ch < nch; ++ch) {
-    uint32_t dummy;
-    const uint32_t n = nch > 1 ? stage_chunk(P, S, row, units_r, n_c, ch, &dummy) : n_c;
-#pragma unroll 4
-    for (uint32_t f = threadIdx.x; f < n; f += kThreads) {
-      const uint32_t k = S.stage[f].x;
-      if (k >= base && (uint64_t)(k - base) < span) atomicAdd(&S.hist[(k - base) >> shift], 1u);
-    }
-    __syncthreads();
-  }
-  // 16 bins per thread, thread 0 holding the top bins
-  constexpr int kPer = kBins / kThreads;
+  for (int j = 0; j < N; ++j)
+    if (k[j] >= base && (uint64_t)(k[j] - base) < span) atomicAdd(&S.hist[(k[j] - base) >> shift], 1u);
+}
+
+// With the histogram complete (a barrier after the last add): the bin b
+// holding the key of rank `need` from the top, and the count of keys in
+// bins above it.  Returns false if the histogram holds fewer than `need`
+// keys.  Two barriers; the histogram is left unchanged.
+__device__ __forceinline__ bool hist_find(SelSmem& S, uint32_t need, int par, uint32_t* bin,
+                                          uint32_t* above) {
+  constexpr int kPer = kBins / kThreads;   // 16 bins per thread, thread 0 holds the top ones
   const int top = kBins - 1 - kPer * threadIdx.x;
+  const int wv = threadIdx.x >> 6;
   uint32_t c[kPer];
 #pragma unroll
   for (int i = 0; i < kPer / 4; ++i) {
@@ -618,45 +594,105 @@ __device__ bool radix_pass(const Params& P, SelSmem& S, int row, int units_r, ui
   uint32_t mine = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) mine += c[i];
-  uint32_t total;
-  uint32_t run = block_excl_scan(mine, S.red, &total);
-  if (threadIdx.x == 0) S.misc[2] = 0;
+  const uint32_t x = wave_incl_scan(mine);
+  uint32_t* red = S.red + 4 * par;
+  if ((threadIdx.x & 63) == 63) red[wv] = x;
   __syncthreads();
+  uint32_t run = x - mine;    // keys in higher bins of this wave
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) run += i < wv ? red[i] : 0u;
+  uint32_t* misc = S.misc + 4 * par;
   if (run < need && run + mine >= need) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       if (run < need && run + c[i] >= need) {
-        S.misc[0] = (uint32_t)(top - i);
-        S.misc[1] = run;
-        S.misc[2] = 1;
+        misc[0] = (uint32_t)(top - i);
+        misc[1] = run;
+        misc[2] = 1;
       }
       run += c[i];
     }
   }
   __syncthreads();
-  const bool found = S.misc[2] != 0;
-  *bin = S.misc[0];
-  *above = S.misc[1];
-  __syncthreads();
-  return found;
+  *bin = misc[0];
+  *above = misc[1];
+  return misc[2] != 0;
+}
+
+// Number of bits to drop so that keys in [lo, lo + range] map to 4096 bins.
+__device__ __forceinline__ int range_shift(uint32_t range) {
+  return range == 0 ? 0 : max(0, 32 - __builtin_clz(range) - 12);
+}
+
+// ---- general path: contiguous segments, any number of candidates --------------
+
+// This thread's contiguous segment of chunk ch of the row's candidates
+// (flat order = position order): elements f0 .. f0 + kCandPer - 1 with
+// f0 = ch*kChunk + tid*kCandPer, key 0 past the end.  The unit of f0 comes
+// from a binary search over the count prefix, later elements walk forward;
+// every load is issued before any is used.
+struct Seg {
+  uint32_t k[kCandPer];
+  uint32_t p[kCandPer];
+};
+
+__device__ __forceinline__ void load_segment(const Params& P, const SelSmem& S, int row, int units_r,
+                                             uint32_t n_c, uint32_t ch, Seg& sg) {
+  const uint32_t f0 = ch * kChunk + threadIdx.x * kCandPer;
+  const uint2* rowc = P.cand + (int64_t)row * P.bt_stride * kPage;
+  int lo = 0, hi = units_r - 1;    // last unit with cpre[u] <= f0
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (S.cpre[mid] <= f0) lo = mid; else hi = mid - 1;
+  }
+  int u = lo;
+  uint32_t base = S.cpre[u], next = S.cpre[u + 1];
+  int32_t off[kCandPer];
+#pragma unroll
+  for (int j = 0; j < kCandPer; ++j) {
+    const uint32_t f = f0 + j;
+    off[j] = -1;
+    if (f < n_c) {
+      while (f >= next) {
+        ++u;
+        base = next;
+        next = S.cpre[u + 1];
+      }
+      off[j] = u * kUnitTok + (int32_t)(f - base);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kCandPer; ++j) {
+    const uint2 v = off[j] >= 0 ? rowc[off[j]] : make_uint2(0u, 0u);
+    sg.k[j] = v.x;
+    sg.p[j] = v.y;
+  }
 }
 
 // Exact key T of rank K among the candidates with key >= lo (keys in
 // [lo, hi] are binned over the occupied range, at most three passes), and
 // the number of keys equal to T to keep.  Returns false if fewer than K
-// candidates are >= lo.
-__device__ bool select_threshold(const Params& P, SelSmem& S, int row, int units_r, uint32_t n_c,
-                                 uint32_t lo, uint32_t hi, uint32_t K, uint32_t* T_out,
-                                 uint32_t* ties_out) {
+// candidates are >= lo.  With one chunk the segment is already in
+// registers; otherwise every pass loads every chunk again.
+__device__ __forceinline__ bool seg_threshold(const Params& P, SelSmem& S, int row, int units_r,
+                                              uint32_t n_c, Seg& sg, uint32_t lo, uint32_t hi,
+                                              uint32_t K, uint32_t* T_out, uint32_t* ties_out) {
   if (hi < lo) return false;
-  const uint32_t range = hi - lo;   // keys in [lo, lo + range]
-  int shift = range == 0 ? 0 : max(0, 32 - __builtin_clz(range) - 12);
+  const uint32_t nch = (n_c + kChunk - 1) / kChunk;
+  const uint32_t range = hi - lo;
+  int shift = range_shift(range);
   uint64_t span = (uint64_t)range + 1;
   uint32_t base = lo, need = K;
-  for (;;) {
+  for (int pass = 0;; ++pass) {
+    hist_clear(S, pass & 1);
+    __syncthreads();
+    for (uint32_t ch = 0; ch < nch; ++ch) {
+      if (nch > 1) load_segment(P, S, row, units_r, n_c, ch, sg);
+      hist_add(S, sg.k, base, (uint32_t)shift, span);
+    }
+    __syncthreads();
     uint32_t bin, above;
-    if (!radix_pass(P, S, row, units_r, n_c, base, (uint32_t)shift, span, need, &bin, &above))
-      return false;
+    if (!hist_find(S, need, pass & 1, &bin, &above)) return false;
     base += bin << shift;
     need -= above;
     if (shift == 0) break;
@@ -668,69 +704,236 @@ __device__ bool select_threshold(const Params& P, SelSmem& S, int row, int units
   return true;
 }
 
-// Ordered emission of keys > T and the first `ties` keys equal to T; each
-// thread owns a contiguous segment of every staged chunk, and one block
-// scan of the packed (equal, greater) counts places every kept key.
-__device__ void emit_selection(const Params& P, SelSmem& S, int row, int units_r, uint32_t n_c,
-                               uint32_t T, uint32_t ties) {
+// Ordered emission of keys > T and the first `ties` keys equal to T: one
+// block scan of the packed (equal, greater) counts of every segment places
+// every kept key.
+__device__ __forceinline__ void seg_emit(const Params& P, SelSmem& S, int row, int units_r,
+                                         uint32_t n_c, Seg& sg, uint32_t T, uint32_t ties) {
   const int K = P.topk;
   int32_t* oidx = P.out_idx + (int64_t)row * K;
   float* osc = P.out_score ? P.out_score + (int64_t)row * K : nullptr;
   const uint32_t nch = (n_c + kChunk - 1) / kChunk;
   uint32_t run_gt = 0, run_eq = 0;
   for (uint32_t ch = 0; ch < nch; ++ch) {
-    uint32_t dummy;
-    const uint32_t n = nch > 1 ? stage_chunk(P, S, row, units_r, n_c, ch, &dummy) : n_c;
-    const uint32_t seg = (n + kThreads - 1) / kThreads;
-    const uint32_t f0 = min(n, threadIdx.x * seg), f1 = min(n, f0 + seg);
+    if (nch > 1) load_segment(P, S, row, units_r, n_c, ch, sg);
     uint32_t gt = 0, eq = 0;
-    for (uint32_t f = f0; f < f1; ++f) {
-      const uint32_t k = S.stage[f].x;
-      gt += k > T ? 1u : 0u;
-      eq += k == T ? 1u : 0u;
+#pragma unroll
+    for (int j = 0; j < kCandPer; ++j) {
+      gt += sg.k[j] > T ? 1u : 0u;
+      eq += sg.k[j] == T ? 1u : 0u;
     }
     uint32_t tot;
     const uint32_t pre = block_excl_scan((eq << 16) | gt, S.red, &tot);
     uint32_t er = run_eq + (pre >> 16);                       // equal keys before mine
     uint32_t opos = run_gt + (pre & 0xFFFFu) + min(er, ties); // kept keys before mine
-    for (uint32_t f = f0; f < f1; ++f) {
-      const uint2 c = S.stage[f];
-      bool kp = c.x > T;
-      if (c.x == T) {
+#pragma unroll
+    for (int j = 0; j < kCandPer; ++j) {
+      const uint32_t k = sg.k[j];
+      bool kp = k > T;
+      if (k == T) {
         kp = er < ties;
         ++er;
       }
       if (kp && opos < (uint32_t)K) {
-        oidx[opos] = (int32_t)c.y;
-        if (osc) osc[opos] = key_score(c.x);
+        oidx[opos] = (int32_t)sg.p[j];
+        if (osc) osc[opos] = key_score(k);
         ++opos;
       }
     }
     run_gt += tot & 0xFFFFu;
     run_eq += tot >> 16;
-    __syncthreads();
   }
 }
 
-// All staged candidates (n_c <= K) in position order, then -1 padding.
-__device__ void emit_all(const Params& P, SelSmem& S, int row, uint32_t n_c) {
+// All candidates (n_c <= K, one chunk, already loaded) in position order,
+// then -1 padding.
+__device__ __forceinline__ void seg_emit_all(const Params& P, const Seg& sg, int row, uint32_t n_c) {
   const int K = P.topk;
   int32_t* oidx = P.out_idx + (int64_t)row * K;
   float* osc = P.out_score ? P.out_score + (int64_t)row * K : nullptr;
-  for (uint32_t f = threadIdx.x; f < (uint32_t)K; f += kThreads) {
-    if (f < n_c) {
-      oidx[f] = (int32_t)S.stage[f].y;
-      if (osc) osc[f] = key_score(S.stage[f].x);
-    } else {
-      oidx[f] = -1;
-      if (osc) osc[f] = -__builtin_huge_valf();
+  const uint32_t f0 = threadIdx.x * kCandPer;
+#pragma unroll
+  for (int j = 0; j < kCandPer; ++j) {
+    const uint32_t f = f0 + j;
+    if (f < n_c && f < (uint32_t)K) {
+      oidx[f] = (int32_t)sg.p[j];
+      if (osc) osc[f] = key_score(sg.k[j]);
     }
+  }
+  for (uint32_t f = n_c + threadIdx.x; f < (uint32_t)K; f += kThreads) {
+    oidx[f] = -1;
+    if (osc) osc[f] = -__builtin_huge_valf();
+  }
+}
+
+// ---- fast path: at most 128 units of at most 64 candidates each --------------
+//
+// Wave w holds, in registers, slot `lane` of the slices of units w, w+4, ...,
+// w+124 (unit u's candidates are slots 0 .. count-1 of its slice, in
+// position order).  These loads do not depend on the counts, so they are
+// issued first.  The threshold takes one histogram pass; the few keys of
+// the threshold bin are ranked by one wave.  Ballots give every kept key
+// its rank inside its unit, and one scan over the 128 unit totals places
+// the units.
+struct FastSet {
+  uint32_t k[kFastPer];
+  uint32_t p[kFastPer];
+};
+
+__device__ __forceinline__ void fast_issue(const Params& P, int row, int units_r, FastSet& fs) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint2* rowc = P.cand + (int64_t)row * P.bt_stride * kPage;
+#pragma unroll
+  for (int i = 0; i < kFastPer; ++i) {
+    const int u = wv + kWaves * i;
+    // every unit holds at least one page, so its slice has >= 64 slots
+    const uint2 v = u < units_r ? rowc[u * kUnitTok + lane] : make_uint2(0u, 0u);
+    fs.k[i] = v.x;
+    fs.p[i] = v.y;
+  }
+}
+
+// Masks the slots beyond each unit's count (key 0 = no candidate).
+__device__ __forceinline__ void fast_mask(const SelSmem& S, int units_r, FastSet& fs) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < kFastPer; ++i) {
+    const int u = wv + kWaves * i;
+    const uint32_t cnt = u < units_r ? S.cpre[u + 1] - S.cpre[u] : 0u;
+    if ((uint32_t)lane >= cnt) fs.k[i] = 0u;
+  }
+}
+
+// Exact T and ties for the fast set (keys >= lo).  Returns false if fewer
+// than K keys are >= lo.
+__device__ __forceinline__ bool fast_threshold(SelSmem& S, const FastSet& fs, uint32_t lo,
+                                               uint32_t hi, uint32_t K, uint32_t* T_out,
+                                               uint32_t* ties_out) {
+  if (hi < lo) return false;
+  const uint32_t range = hi - lo;
+  int shift = range_shift(range);
+  uint64_t span = (uint64_t)range + 1;
+  uint32_t base = lo, need = K;
+  for (int pass = 0;; ++pass) {
+    hist_clear(S, pass & 1);
+    if (threadIdx.x == 0) S.smalln = 0;
+    __syncthreads();
+    hist_add(S, fs.k, base, (uint32_t)shift, span);
+    __syncthreads();
+    uint32_t bin, above;
+    if (!hist_find(S, need, pass & 1, &bin, &above)) return false;
+    base += bin << shift;
+    need -= above;
+    if (shift == 0) break;
+    span = 1ull << shift;            // the keys of the chosen bin
+    shift = max(0, shift - 12);
+    const uint32_t nb = S.hist[bin];
+    if (nb <= 64) {
+      // rank the bin's keys directly: collect them, then one wave finds the
+      // key with exactly need-1 larger ones before it
+#pragma unroll
+      for (int j = 0; j < kFastPer; ++j) {
+        const uint32_t k = fs.k[j];
+        if (k >= base && (uint64_t)(k - base) < span) S.small[atomicAdd(&S.smalln, 1u)] = k;
+      }
+      __syncthreads();
+      if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const uint32_t x = lane < (int)nb ? S.small[lane] : 0u;
+        uint32_t gt = 0, ge = 0;
+        for (int j = 0; j < (int)nb; ++j) {
+          const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, j);
+          gt += y > x ? 1u : 0u;
+          ge += y >= x ? 1u : 0u;
+        }
+        if (lane < (int)nb && gt < need && need <= ge) {
+          S.misc[8] = x;
+          S.misc[9] = need - gt;
+        }
+      }
+      __syncthreads();
+      *T_out = S.misc[8];
+      *ties_out = S.misc[9];
+      return true;
+    }
+  }
+  *T_out = base;
+  *ties_out = need;
+  return true;
+}
+
+__device__ __forceinline__ void fast_emit(const Params& P, SelSmem& S, int units_r,
+                                          const FastSet& fs, int row, uint32_t T, uint32_t ties) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int K = P.topk;
+  int32_t* oidx = P.out_idx + (int64_t)row * K;
+  float* osc = P.out_score ? P.out_score + (int64_t)row * K : nullptr;
+  const uint64_t below = lanemask_lt();
+#pragma unroll
+  for (int i = 0; i < kFastPer; ++i) {
+    const int u = wv + kWaves * i;
+    const uint64_t g = __builtin_amdgcn_ballot_w64(fs.k[i] > T);
+    const uint64_t e = __builtin_amdgcn_ballot_w64(fs.k[i] == T && fs.k[i] != 0u);
+    if (lane == 0 && u < units_r)
+      S.ucnt[u] = ((uint32_t)__builtin_popcountll(e) << 16) | (uint32_t)__builtin_popcountll(g);
+  }
+  __syncthreads();
+  {
+    const int u = threadIdx.x;
+    const uint32_t v = u < units_r ? S.ucnt[u] : 0u;
+    uint32_t tot;
+    const uint32_t pre = block_excl_scan(v, S.red, &tot);
+    if (u < units_r) S.ubase[u] = pre;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kFastPer; ++i) {
+    const int u = wv + kWaves * i;
+    if (u >= units_r) continue;
+    const uint32_t pre = S.ubase[u];
+    const uint32_t gt_before = pre & 0xFFFFu, eq_before = pre >> 16;
+    const uint32_t k = fs.k[i];
+    const bool gt = k > T, eq = k == T && k != 0u;
+    const uint64_t eb = __builtin_amdgcn_ballot_w64(eq);
+    const uint32_t erank = eq_before + (uint32_t)__builtin_popcountll(eb & below);
+    const bool kept = gt || (eq && erank < ties);
+    const uint64_t kb = __builtin_amdgcn_ballot_w64(kept);
+    const uint32_t opos = gt_before + min(eq_before, ties) + (uint32_t)__builtin_popcountll(kb & below);
+    if (kept && opos < (uint32_t)K) {
+      oidx[opos] = (int32_t)fs.p[i];
+      if (osc) osc[opos] = key_score(k);
+    }
+  }
+}
+
+// All candidates (n_c <= K) in position order: unit u's slot j goes to
+// cpre[u] + j; then -1 padding.
+__device__ __forceinline__ void fast_emit_all(const Params& P, const SelSmem& S, int units_r,
+                                              const FastSet& fs, int row, uint32_t n_c) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int K = P.topk;
+  int32_t* oidx = P.out_idx + (int64_t)row * K;
+  float* osc = P.out_score ? P.out_score + (int64_t)row * K : nullptr;
+#pragma unroll
+  for (int i = 0; i < kFastPer; ++i) {
+    const int u = wv + kWaves * i;
+    if (u < units_r && fs.k[i] != 0u) {
+      const uint32_t f = S.cpre[u] + lane;
+      if (f < (uint32_t)K) {
+        oidx[f] = (int32_t)fs.p[i];
+        if (osc) osc[f] = key_score(fs.k[i]);
+      }
+    }
+  }
+  for (uint32_t f = n_c + threadIdx.x; f < (uint32_t)K; f += kThreads) {
+    oidx[f] = -1;
+    if (osc) osc[f] = -__builtin_huge_valf();
   }
 }
 
 // Rescore unit u of the row in full and publish all of its keys.
 template <int NHT>
-__device__ void rescore_unit(const Params& P, SelSmem& S, int row, int t, int u) {
+__device__ __forceinline__ void rescore_unit(const Params& P, SelSmem& S, int row, int t, int u) {
   const Unit V = row_unit(P, row, t, u);
   __syncthreads();
   score_unit<NHT, false>(P, V, S.keys);
@@ -759,17 +962,46 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_select_kernel(Params P) {
   const int K = P.topk;
   const int t = P.row_pos[row];
   const int units_r = row_units(t, P.bt_stride);
-  uint32_t emax = load_counts(P, S, row, units_r);
+  const bool take_all = t < 0 || unit_quota(t, K) == 0xFFFFFFFFu;   // at most K positions
+  FastSet fs;
+  const bool fast_shape = units_r <= kFastUnits;
+  if (fast_shape) fast_issue(P, row, units_r, fs);
+  uint32_t emax, cmax;
+  load_counts(P, S, row, units_r, &emax, &cmax);
   uint32_t n_c = S.cpre[units_r];
+  if (fast_shape && cmax <= 64u) {
+    fast_mask(S, units_r, fs);
+    if (take_all) {
+      fast_emit_all(P, S, units_r, fs, row, n_c);
+      return;
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < kFastPer; ++j) m = max(m, fs.k[j]);
+    const uint32_t kmax = block_max(m, S.red);
+    uint32_t T = 0, ties = 0;
+    if (fast_threshold(S, fs, max(emax, 1u), kmax, (uint32_t)K, &T, &ties)) {
+      fast_emit(P, S, units_r, fs, row, T, ties);
+      return;
+    }
+    // fewer than K candidates reach the largest edge: the general path below
+    // takes the rescoring route
+  }
+  Seg sg;
   uint32_t kmax = 0xFFFFFFFFu;
-  if (n_c <= (uint32_t)kChunk) stage_chunk(P, S, row, units_r, n_c, 0, &kmax);
-  if (t < 0 || unit_quota(t, K) == 0xFFFFFFFFu) {
-    // at most K positions: every unit kept all of its keys
-    emit_all(P, S, row, n_c);
+  if (n_c <= (uint32_t)kChunk) {
+    load_segment(P, S, row, units_r, n_c, 0, sg);
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < kCandPer; ++j) m = max(m, sg.k[j]);
+    kmax = block_max(m, S.red);
+  }
+  if (take_all) {
+    seg_emit_all(P, sg, row, n_c);
     return;
   }
   uint32_t T = 0, ties = 0;
-  bool ok = select_threshold(P, S, row, units_r, n_c, max(emax, 1u), kmax, (uint32_t)K, &T, &ties);
+  bool ok = seg_threshold(P, S, row, units_r, n_c, sg, max(emax, 1u), kmax, (uint32_t)K, &T, &ties);
   if (!ok) {
     // Fewer than K candidates reach the largest unit edge: a unit may have
     // left out a Top-K key.  Take the K-th key T0 of the current candidates
@@ -778,24 +1010,30 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_select_kernel(Params P) {
     // below their edge <= T0 <= the new K-th key, so the result is exact.
     if (threadIdx.x == 0) flag_error(P.hdr, kErrFallback);
     uint32_t T0 = 0, ties0 = 0;
-    const bool ok0 = select_threshold(P, S, row, units_r, n_c, 1u, kmax, (uint32_t)K, &T0, &ties0);
+    const bool ok0 = seg_threshold(P, S, row, units_r, n_c, sg, 1u, kmax, (uint32_t)K, &T0, &ties0);
     for (int u = 0; u < units_r; ++u) {
       const uint32_t e = load_agent(&P.uedge[(int64_t)row * P.upr + u]);
       if (e > (ok0 ? T0 : 0u)) rescore_unit<NHT>(P, S, row, t, u);
     }
     __threadfence();
     __syncthreads();
-    load_counts(P, S, row, units_r);
+    load_counts(P, S, row, units_r, &emax, &cmax);
     n_c = S.cpre[units_r];
     kmax = 0xFFFFFFFFu;
-    if (n_c <= (uint32_t)kChunk) stage_chunk(P, S, row, units_r, n_c, 0, &kmax);
-    ok = select_threshold(P, S, row, units_r, n_c, 1u, kmax, (uint32_t)K, &T, &ties);
-    if (!ok) {   // fewer than K valid positions in the row
-      emit_all(P, S, row, n_c);
+    if (n_c <= (uint32_t)kChunk) {
+      load_segment(P, S, row, units_r, n_c, 0, sg);
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < kCandPer; ++j) m = max(m, sg.k[j]);
+      kmax = block_max(m, S.red);
+    }
+    ok = seg_threshold(P, S, row, units_r, n_c, sg, 1u, kmax, (uint32_t)K, &T, &ties);
+    if (!ok) {   // fewer than K valid positions in the row (n_c < K <= kChunk)
+      seg_emit_all(P, sg, row, n_c);
       return;
     }
   }
-  emit_selection(P, S, row, units_r, n_c, T, ties);
+  seg_emit(P, S, row, units_r, n_c, sg, T, ties);
 }
 
 // ---- host side ----------------------------------------------------------------
