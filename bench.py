@@ -11,9 +11,16 @@ One step = the whole hot path for one decode token of each sequence:
   -> kv_fp8_quant_paged_write(new KV row) -> dsa_indexer_topk -> dsa_sparse_attn
 Caches are replicated (default 4 replicas, about 3.3 GB) and rotated per step
 so that the 256 MB Infinity Cache cannot serve one step's reads from the
-previous step.  Timing: W untimed steps, then exactly K steps between two
-device synchronisations; per-kernel durations from HIP events recorded on
-the launch stream inside the timed region.
+previous step.
+
+Timing: W untimed steps, then exactly K steps between two device
+synchronisations (no event inside the loop: an event recorded between two
+launches drains the queue and adds several microseconds).  Per-entry-point
+durations come from two further timed regions on the launch stream: K
+back-to-back dsa_indexer_topk calls, then K back-to-back dsa_sparse_attn
+calls, each bracketed by HIP events; the indexer's average is the roofline
+duration.  `traffic` is filled from the committed FETCH_SIZE/WRITE_SIZE
+summary when it was taken on the current indexer source.
 
 Prints one JSON line.  `value` is decode tokens/s (batch * steps / seconds).
 """
@@ -42,10 +49,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--config", default="decode_128k_b8")
-    ap.add_argument("--cpu-rows", type=int, default=4, help="oracle rows timed for cpu_baseline")
+    ap.add_argument("--cpu-rows", type=int, default=8, help="oracle rows timed for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", action="store_true",
                     help="only warm up and run the timed steps (for profiler runs)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only copy BYTES between two device buffers (counter calibration)")
     return ap.parse_args()
 
 
@@ -58,6 +67,9 @@ def main():
     import numpy as np
     import torch
 
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     from sparse_attention_decode_topk_amd import ops, synth
 
     torch.cuda.set_device(0)
@@ -123,17 +135,11 @@ def main():
                  ptr(row_seq), ptr(out_idx), R, H, K, ctypes.c_float(ops.DEFAULT_SCALE),
                  ptr(out), ptr(lse), ptr(ws_s), ws_s.numel(), stream)))
 
-    def step(i, ev=None):
+    def step(i):
         a = steps_args[i % args.replicas]
         st = L.mxfp8_quant(*a["qq"]) | L.mxfp8_quant(*a["kq"]) | L.kv_fp8_quant_paged_write(*a["kvq"])
-        if ev is not None:
-            ev[0].record()
         st |= L.dsa_indexer_topk(*a["idx"])
-        if ev is not None:
-            ev[1].record()
         st |= L.dsa_sparse_attn(*a["sfa"])
-        if ev is not None:
-            ev[2].record()
         if st:
             raise RuntimeError(f"library call failed (status bits {st})")
 
@@ -141,18 +147,30 @@ def main():
         step(i)
     torch.cuda.synchronize()
     K_steps = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K_steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K_steps):
-        step(i, evs[i])
+        step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     if args.profile_steps:
         print(json.dumps({"profile_steps": K_steps, "seconds": elapsed}))
         return
-    idx_ms = [evs[i][0].elapsed_time(evs[i][1]) for i in range(K_steps)]
-    sfa_ms = [evs[i][1].elapsed_time(evs[i][2]) for i in range(K_steps)]
+
+    # per-entry-point durations: K back-to-back calls between two events
+    def timed_calls(fn, key):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(K_steps):
+            if fn(*steps_args[i % args.replicas][key]):
+                raise RuntimeError(f"{key} call failed")
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / K_steps
+
+    idx_avg = timed_calls(L.dsa_indexer_topk, "idx")
+    sfa_avg = timed_calls(L.dsa_sparse_attn, "sfa")
     ms_per_step = elapsed * 1e3 / K_steps
     tokens_per_s = B * K_steps / elapsed
 
@@ -162,9 +180,9 @@ def main():
     n_sel = int((sel >= 0).sum())
     sfa_bytes = n_sel * SFA_BYTES_PER_ENTRY
     step_bytes = idx_bytes + sfa_bytes
-    idx_avg = float(np.mean(idx_ms))
     achieved = idx_bytes / (idx_avg * 1e-3) / 1e9
     err_word = int(ws_i[8:12].view(torch.int32).item())
+    traffic = measured_traffic(cfg.name)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -189,15 +207,53 @@ def main():
         "hbm_gbs_step": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "algorithmic_bytes_step": step_bytes,
         "kernel_ms": {"dsa_indexer_topk": round(idx_avg, 5),
-                      "dsa_sparse_attn": round(float(np.mean(sfa_ms)), 5)},
+                      "dsa_sparse_attn": round(sfa_avg, 5)},
         "roofline": {"bound": "hbm", "kernel": "dsa_indexer_topk", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "algorithmic_bytes": idx_bytes},
+                     "traffic": traffic, "algorithmic_bytes": idx_bytes},
         "cpu_baseline": cpu,
         "indexer_error_word": err_word,
         "input_gen_s": round(t_gen, 1),
     }
     print(json.dumps(rec))
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "dsa_indexer_topk_decode_128k_b8_traffic.txt")
+INDEXER_SOURCE = os.path.join(ROOT, "sparse_attention_decode_topk_amd", "csrc", "indexer.hip")
+
+
+def measured_traffic(workload):
+    """HBM bytes per dsa_indexer_topk call from the committed counter summary
+    (calibrated FETCH_SIZE + WRITE_SIZE), or None when the summary is missing,
+    for another workload, or was taken on a different indexer source."""
+    import hashlib
+    try:
+        fields = {}
+        with open(TRAFFIC_SUMMARY) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        with open(INDEXER_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if fields.get("indexer_source_sha256") != sha or fields.get("workload") != workload:
+            return None
+        return int(fields["traffic_bytes_per_call"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_probe(nbytes):
+    """One elementwise kernel that reads nbytes and writes nbytes (b = 2a):
+    the reference for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    torch.cuda.set_device(0)
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    torch.mul(a, 2.0, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes}))
 
 
 def cpu_baseline(inp, rows):
