@@ -50,8 +50,10 @@ constexpr int kChunk = kCandPer * kThreads;            // candidates held in reg
 constexpr int kMaxRows = 1024;                         // rows per launch
 constexpr int kMaxBtStride = 16384;                    // pages per row (1M tokens)
 constexpr int kMaxUnitsPerRow = kMaxBtStride / kUnitPages;
-constexpr int kFastUnits = 128;                       // select fast path: units per row
-constexpr int kFastPer = kFastUnits / kWaves;          // units per wave
+constexpr int kSelThreads = 1024;                      // select workgroup
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kFastUnits = 128;                        // select fast path: units per row
+constexpr int kFastPer = kFastUnits / kSelWaves;       // units per wave
 static_assert(kFBins == kThreads, "one filter bin per thread");
 
 // Buffer descriptor word 3 for raw (untyped) buffer access on gfx9-class
@@ -94,12 +96,11 @@ struct ScanSmem {
 
 struct SelSmem {
   uint32_t keys[kUnitTok];            // rescoring a unit
-  uint32_t hist[kBins];
+  uint32_t hist[2 * kBins];           // general path: the first kBins
   uint32_t cpre[kMaxUnitsPerRow + 1]; // candidate prefix per unit
-  uint32_t ucnt[kFastUnits];          // fast path: packed (equal, greater) per unit
-  uint32_t ubase[kFastUnits];         // fast path: their exclusive prefix
-  uint32_t small[64];                 // fast path: keys of the threshold bin
-  uint32_t smalln;
+  alignas(16) uint32_t wred[kSelWaves][4];  // fast path: per-wave sums and maxima
+  alignas(16) uint32_t wsum[2][kSelWaves];  // fast path: per-wave histogram sums
+  alignas(16) uint32_t wtot[kSelWaves];     // fast path: per-wave (equal, greater) counts
   uint32_t red[2 * kWaves + 2];
   uint32_t misc[16];
 };
@@ -768,167 +769,219 @@ __device__ __forceinline__ void seg_emit_all(const Params& P, const Seg& sg, int
 
 // ---- fast path: at most 128 units of at most 64 candidates each --------------
 //
-// Wave w holds, in registers, slot `lane` of the slices of units w, w+4, ...,
-// w+124 (unit u's candidates are slots 0 .. count-1 of its slice, in
-// position order).  These loads do not depend on the counts, so they are
-// issued first.  The threshold takes one histogram pass; the few keys of
-// the threshold bin are ranked by one wave.  Ballots give every kept key
-// its rank inside its unit, and one scan over the 128 unit totals places
-// the units.
-struct FastSet {
-  uint32_t k[kFastPer];
-  uint32_t p[kFastPer];
-};
+// The select workgroup has 16 waves; wave w owns units 8w .. 8w+7 of the row
+// and holds, in registers, slot `lane` of each unit's slice (a unit's
+// candidates are slots 0 .. count-1 of its slice, in position order).  Every
+// load (row position, counts, edges, candidate slots) is issued at entry,
+// before the row's length is known: loads go through buffer descriptors
+// that cover the row's part of the workspace, and units past the row's end
+// are masked afterwards.  The threshold comes from 12-bit radix passes over
+// the occupied key range with the histograms in LDS; each pass locates the
+// bin of rank `need` in two levels (per-wave bin sums, then the bins of the
+// wave that holds it, scanned again by every wave), so that every wave knows
+// the result without another barrier.  Outputs are written through
+// global-address-space pointers, which cannot alias LDS.
+typedef __attribute__((address_space(1))) int32_t gint32;
+typedef __attribute__((address_space(1))) float gfloat;
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ void fast_issue(const Params& P, int row, int units_r, FastSet& fs) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const uint2* rowc = P.cand + (int64_t)row * P.bt_stride * kPage;
-#pragma unroll
-  for (int i = 0; i < kFastPer; ++i) {
-    const int u = wv + kWaves * i;
-    // every unit holds at least one page, so its slice has >= 64 slots
-    const uint2 v = u < units_r ? rowc[u * kUnitTok + lane] : make_uint2(0u, 0u);
-    fs.k[i] = v.x;
-    fs.p[i] = v.y;
+// Bin of rank `need` from the top of histogram H (kBins bins) and the count
+// of keys in the bins above it; false when H holds fewer than `need` keys.
+// Called by every wave after the barrier that completes H; `wsum` (16 slots)
+// must not be read by any other pass in flight.
+__device__ __forceinline__ bool fast_find(SelSmem& S, const uint32_t* H, uint32_t* wsum,
+                                          uint32_t need, uint32_t* bin, uint32_t* above) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // level 1: this wave's 256 bins, the highest ones in wave 0
+  {
+    const int hb = kBins - 1 - 256 * wv - 4 * lane;
+    const uint4 q = reinterpret_cast<const uint4*>(H)[(hb - 3) / 4];
+    const uint32_t incl = wave_incl_scan(q.x + q.y + q.z + q.w);
+    if (lane == 63) wsum[wv] = incl;
   }
-}
-
-// Masks the slots beyond each unit's count (key 0 = no candidate).
-__device__ __forceinline__ void fast_mask(const SelSmem& S, int units_r, FastSet& fs) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  __syncthreads();
+  // level 2: the wave that holds rank `need`, then its bins
+  const uint32_t v = lane < kSelWaves ? wsum[lane] : 0u;
+  const uint32_t vin = wave_incl_scan(v);
+  const uint64_t wh = __builtin_amdgcn_ballot_w64(lane < kSelWaves && vin - v < need && vin >= need);
+  if (wh == 0) return false;
+  const int ws = __builtin_ctzll(wh);
+  const uint32_t wabove = (uint32_t)__builtin_amdgcn_readlane((int)(vin - v), ws);
+  const int hb = kBins - 1 - 256 * ws - 4 * lane;
+  const uint4 q = reinterpret_cast<const uint4*>(H)[(hb - 3) / 4];
+  const uint32_t c[4] = {q.w, q.z, q.y, q.x};   // bins hb, hb-1, hb-2, hb-3
+  const uint32_t mine = c[0] + c[1] + c[2] + c[3];
+  const uint32_t incl = wave_incl_scan(mine) + wabove;
+  const uint32_t excl = incl - mine;
+  const uint64_t lh = __builtin_amdgcn_ballot_w64(excl < need && incl >= need);
+  const int src = __builtin_ctzll(lh);
+  uint32_t b = (uint32_t)(hb - 3), run = excl;
+  bool done = false;
 #pragma unroll
-  for (int i = 0; i < kFastPer; ++i) {
-    const int u = wv + kWaves * i;
-    const uint32_t cnt = u < units_r ? S.cpre[u + 1] - S.cpre[u] : 0u;
-    if ((uint32_t)lane >= cnt) fs.k[i] = 0u;
-  }
-}
-
-// Exact T and ties for the fast set (keys >= lo).  Returns false if fewer
-// than K keys are >= lo.
-__device__ __forceinline__ bool fast_threshold(SelSmem& S, const FastSet& fs, uint32_t lo,
-                                               uint32_t hi, uint32_t K, uint32_t* T_out,
-                                               uint32_t* ties_out) {
-  if (hi < lo) return false;
-  const uint32_t range = hi - lo;
-  int shift = range_shift(range);
-  uint64_t span = (uint64_t)range + 1;
-  uint32_t base = lo, need = K;
-  for (int pass = 0;; ++pass) {
-    hist_clear(S, pass & 1);
-    if (threadIdx.x == 0) S.smalln = 0;
-    __syncthreads();
-    hist_add(S, fs.k, base, (uint32_t)shift, span);
-    __syncthreads();
-    uint32_t bin, above;
-    if (!hist_find(S, need, pass & 1, &bin, &above)) return false;
-    base += bin << shift;
-    need -= above;
-    if (shift == 0) break;
-    span = 1ull << shift;            // the keys of the chosen bin
-    shift = max(0, shift - 12);
-    const uint32_t nb = S.hist[bin];
-    if (nb <= 64) {
-      // rank the bin's keys directly: collect them, then one wave finds the
-      // key with exactly need-1 larger ones before it
-#pragma unroll
-      for (int j = 0; j < kFastPer; ++j) {
-        const uint32_t k = fs.k[j];
-        if (k >= base && (uint64_t)(k - base) < span) S.small[atomicAdd(&S.smalln, 1u)] = k;
-      }
-      __syncthreads();
-      if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
-        const uint32_t x = lane < (int)nb ? S.small[lane] : 0u;
-        uint32_t gt = 0, ge = 0;
-        for (int j = 0; j < (int)nb; ++j) {
-          const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, j);
-          gt += y > x ? 1u : 0u;
-          ge += y >= x ? 1u : 0u;
-        }
-        if (lane < (int)nb && gt < need && need <= ge) {
-          S.misc[8] = x;
-          S.misc[9] = need - gt;
-        }
-      }
-      __syncthreads();
-      *T_out = S.misc[8];
-      *ties_out = S.misc[9];
-      return true;
+  for (int i = 0; i < 3; ++i) {
+    if (!done && run + c[i] >= need) {
+      b = (uint32_t)(hb - i);
+      done = true;
     }
+    if (!done) run += c[i];
   }
-  *T_out = base;
-  *ties_out = need;
+  *bin = (uint32_t)__builtin_amdgcn_readlane((int)b, src);
+  *above = (uint32_t)__builtin_amdgcn_readlane((int)run, src);
   return true;
 }
 
-__device__ __forceinline__ void fast_emit(const Params& P, SelSmem& S, int units_r,
-                                          const FastSet& fs, int row, uint32_t T, uint32_t ties) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+// Returns false, having written nothing, when the row does not fit the path
+// (more than kFastUnits units, or a unit with more than 64 candidates) or
+// when fewer than K candidates reach the largest unit edge; the caller then
+// takes the general path.  Block-uniform.
+__device__ __forceinline__ bool select_fast(const Params& P, SelSmem& S, int row) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int u0 = kFastPer * wv;
   const int K = P.topk;
-  int32_t* oidx = P.out_idx + (int64_t)row * K;
-  float* osc = P.out_score ? P.out_score + (int64_t)row * K : nullptr;
+  const int nu = min(P.upr, kFastUnits);   // units whose slices exist in the workspace
+  // loads: row position; count and edge of unit u0 + lane (lanes < 8);
+  // slot `lane` of each of the wave's units
+  const int t = P.row_pos[row];
+  const int64_t ub = (int64_t)row * P.upr;
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(P.ucount + ub, (short)0, nu * 4, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(P.uedge + ub, (short)0, nu * 4, kRawBufferWord3);
+  const uint32_t uoff = lane < kFastPer ? (uint32_t)(u0 + lane) * 4u : (uint32_t)nu * 4u;
+  uint32_t cnt_l = __builtin_amdgcn_raw_buffer_load_b32(rc, uoff, 0, 0);
+  uint32_t edge_l = __builtin_amdgcn_raw_buffer_load_b32(re, uoff, 0, 0);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      P.cand + (int64_t)row * P.bt_stride * kPage, (short)0, nu * kUnitTok * 8, kRawBufferWord3);
+  uint32_t k[kFastPer], p[kFastPer];
+#pragma unroll
+  for (int i = 0; i < kFastPer; ++i) {
+    const v2u v = __builtin_amdgcn_raw_buffer_load_b64(rk, (uint32_t)(((u0 + i) * kUnitTok + lane) * 8), 0, 0);
+    k[i] = v[0];
+    p[i] = v[1];
+  }
+  // clear both radix histograms (ordered before any add by the first barrier)
+  {
+    uint4* h4 = reinterpret_cast<uint4*>(S.hist);
+#pragma unroll
+    for (int i = 0; i < 2 * kBins / 4 / kSelThreads; ++i) h4[threadIdx.x + i * kSelThreads] = make_uint4(0, 0, 0, 0);
+  }
+  const int units_r = row_units(t, P.bt_stride);
+  if (units_r > kFastUnits) return false;
+  const bool take_all = t < 0 || unit_quota(t, K) == 0xFFFFFFFFu;   // at most K positions
+  const bool uin = lane < kFastPer && u0 + lane < units_r;
+  cnt_l = uin ? cnt_l : 0u;
+  edge_l = uin ? edge_l : 0u;
+  const uint32_t csum_l = wave_incl_scan(cnt_l);   // lane i: candidates of units u0 .. u0+i
+  uint32_t km = 0;
+#pragma unroll
+  for (int i = 0; i < kFastPer; ++i) {
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)cnt_l, i);
+    if ((uint32_t)lane >= c) k[i] = 0u;
+    km = max(km, k[i]);
+  }
+  const uint32_t cmax_w = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_max(cnt_l), 63);
+  const uint32_t emax_w = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_max(edge_l), 63);
+  const uint32_t kmax_w = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_max(km), 63);
+  const uint32_t tot_w = (uint32_t)__builtin_amdgcn_readlane((int)csum_l, 63);
+  if (lane == 0) *reinterpret_cast<uint4*>(S.wred[wv]) = make_uint4(tot_w, cmax_w, emax_w, kmax_w);
+  __syncthreads();
+  uint32_t n_c = 0, cmax = 0, emax = 0, kmax = 0, wbase = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    const uint4 x = *reinterpret_cast<const uint4*>(S.wred[w]);
+    wbase += w < wv ? x.x : 0u;
+    n_c += x.x;
+    cmax = max(cmax, x.y);
+    emax = max(emax, x.z);
+    kmax = max(kmax, x.w);
+  }
+  if (cmax > 64u) return false;
+  gint32* oidx = (gint32*)(P.out_idx + (int64_t)row * K);
+  gfloat* osc = P.out_score ? (gfloat*)(P.out_score + (int64_t)row * K) : nullptr;
+  if (take_all) {
+    // every candidate is kept: unit u0+i's slot j goes to its flat index
+#pragma unroll
+    for (int i = 0; i < kFastPer; ++i) {
+      const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)cnt_l, i);
+      const uint32_t f = wbase + (uint32_t)__builtin_amdgcn_readlane((int)csum_l, i) - c + lane;
+      if ((uint32_t)lane < c && f < (uint32_t)K) {
+        oidx[f] = (int32_t)p[i];
+        if (osc) osc[f] = key_score(k[i]);
+      }
+    }
+    for (uint32_t f = n_c + threadIdx.x; f < (uint32_t)K; f += kSelThreads) {
+      oidx[f] = -1;
+      if (osc) osc[f] = -__builtin_huge_valf();
+    }
+    return true;
+  }
+  // radix passes over [lo, kmax]: pass p bins the keys of [base, base + span)
+  // by (key - base) >> shift into histogram p & 1
+  const uint32_t lo = max(emax, 1u);
+  if (kmax < lo) return false;
+  int shift = range_shift(kmax - lo);
+  uint64_t span = (uint64_t)(kmax - lo) + 1;
+  uint32_t base = lo, need = (uint32_t)K;
+  for (int pass = 0;; ++pass) {
+    uint32_t* H = S.hist + (pass & 1) * kBins;
+    if (pass >= 2) {
+      // every wave finished reading this histogram before the last barrier
+      reinterpret_cast<uint4*>(H)[threadIdx.x] = make_uint4(0, 0, 0, 0);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < kFastPer; ++i)
+      if (k[i] >= base && (uint64_t)(k[i] - base) < span) atomicAdd(&H[(k[i] - base) >> shift], 1u);
+    __syncthreads();
+    uint32_t bin, above;
+    if (!fast_find(S, H, S.wsum[pass & 1], need, &bin, &above)) return false;   // pass 0 only
+    base += bin << shift;
+    need -= above;
+    if (shift == 0) break;
+    span = 1ull << shift;   // the keys of the chosen bin
+    shift = max(0, shift - 12);
+  }
+  const uint32_t T = base, ties = need;   // T >= lo >= 1, so empty slots never equal it
+  // emission: per-wave (greater, equal) totals, then every kept key's
+  // position from the units' running sums and ballots
+  uint32_t gt_w = 0, eq_w = 0;
+#pragma unroll
+  for (int i = 0; i < kFastPer; ++i) {
+    gt_w += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(k[i] > T));
+    eq_w += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(k[i] == T));
+  }
+  if (lane == 0) S.wtot[wv] = (eq_w << 16) | gt_w;
+  __syncthreads();
+  uint32_t gt_before = 0, eq_before = 0;
+#pragma unroll
+  for (int w4 = 0; w4 < kSelWaves / 4; ++w4) {
+    const uint4 x = *reinterpret_cast<const uint4*>(&S.wtot[4 * w4]);
+    const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t v = 4 * w4 + j < wv ? xs[j] : 0u;
+      gt_before += v & 0xFFFFu;
+      eq_before += v >> 16;
+    }
+  }
   const uint64_t below = lanemask_lt();
 #pragma unroll
   for (int i = 0; i < kFastPer; ++i) {
-    const int u = wv + kWaves * i;
-    const uint64_t g = __builtin_amdgcn_ballot_w64(fs.k[i] > T);
-    const uint64_t e = __builtin_amdgcn_ballot_w64(fs.k[i] == T && fs.k[i] != 0u);
-    if (lane == 0 && u < units_r)
-      S.ucnt[u] = ((uint32_t)__builtin_popcountll(e) << 16) | (uint32_t)__builtin_popcountll(g);
-  }
-  __syncthreads();
-  {
-    const int u = threadIdx.x;
-    const uint32_t v = u < units_r ? S.ucnt[u] : 0u;
-    uint32_t tot;
-    const uint32_t pre = block_excl_scan(v, S.red, &tot);
-    if (u < units_r) S.ubase[u] = pre;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kFastPer; ++i) {
-    const int u = wv + kWaves * i;
-    if (u >= units_r) continue;
-    const uint32_t pre = S.ubase[u];
-    const uint32_t gt_before = pre & 0xFFFFu, eq_before = pre >> 16;
-    const uint32_t k = fs.k[i];
-    const bool gt = k > T, eq = k == T && k != 0u;
+    const bool gt = k[i] > T, eq = k[i] == T;
+    const uint64_t gb = __builtin_amdgcn_ballot_w64(gt);
     const uint64_t eb = __builtin_amdgcn_ballot_w64(eq);
     const uint32_t erank = eq_before + (uint32_t)__builtin_popcountll(eb & below);
     const bool kept = gt || (eq && erank < ties);
     const uint64_t kb = __builtin_amdgcn_ballot_w64(kept);
     const uint32_t opos = gt_before + min(eq_before, ties) + (uint32_t)__builtin_popcountll(kb & below);
     if (kept && opos < (uint32_t)K) {
-      oidx[opos] = (int32_t)fs.p[i];
-      if (osc) osc[opos] = key_score(k);
+      oidx[opos] = (int32_t)p[i];
+      if (osc) osc[opos] = key_score(k[i]);
     }
+    gt_before += (uint32_t)__builtin_popcountll(gb);
+    eq_before += (uint32_t)__builtin_popcountll(eb);
   }
-}
-
-// All candidates (n_c <= K) in position order: unit u's slot j goes to
-// cpre[u] + j; then -1 padding.
-__device__ __forceinline__ void fast_emit_all(const Params& P, const SelSmem& S, int units_r,
-                                              const FastSet& fs, int row, uint32_t n_c) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int K = P.topk;
-  int32_t* oidx = P.out_idx + (int64_t)row * K;
-  float* osc = P.out_score ? P.out_score + (int64_t)row * K : nullptr;
-#pragma unroll
-  for (int i = 0; i < kFastPer; ++i) {
-    const int u = wv + kWaves * i;
-    if (u < units_r && fs.k[i] != 0u) {
-      const uint32_t f = S.cpre[u] + lane;
-      if (f < (uint32_t)K) {
-        oidx[f] = (int32_t)fs.p[i];
-        if (osc) osc[f] = key_score(fs.k[i]);
-      }
-    }
-  }
-  for (uint32_t f = n_c + threadIdx.x; f < (uint32_t)K; f += kThreads) {
-    oidx[f] = -1;
-    if (osc) osc[f] = -__builtin_huge_valf();
-  }
+  return true;
 }
 
 // Rescore unit u of the row in full and publish all of its keys.
@@ -956,37 +1009,22 @@ __device__ __forceinline__ void rescore_unit(const Params& P, SelSmem& S, int ro
 }
 
 template <int NHT>
-__global__ __launch_bounds__(kThreads, 2) void indexer_select_kernel(Params P) {
+__global__ __launch_bounds__(kSelThreads, 1) void indexer_select_kernel(Params P) {
   __shared__ SelSmem S;
   const int row = blockIdx.x;
+  if (select_fast(P, S, row)) return;
+  // general path: waves 0..3 (a barrier first, so that no wave still reads
+  // what the fast path left in LDS; waves that have ended no longer count
+  // at a barrier)
+  __syncthreads();
+  if (threadIdx.x >= kThreads) return;
   const int K = P.topk;
   const int t = P.row_pos[row];
   const int units_r = row_units(t, P.bt_stride);
   const bool take_all = t < 0 || unit_quota(t, K) == 0xFFFFFFFFu;   // at most K positions
-  FastSet fs;
-  const bool fast_shape = units_r <= kFastUnits;
-  if (fast_shape) fast_issue(P, row, units_r, fs);
   uint32_t emax, cmax;
   load_counts(P, S, row, units_r, &emax, &cmax);
   uint32_t n_c = S.cpre[units_r];
-  if (fast_shape && cmax <= 64u) {
-    fast_mask(S, units_r, fs);
-    if (take_all) {
-      fast_emit_all(P, S, units_r, fs, row, n_c);
-      return;
-    }
-    uint32_t m = 0;
-#pragma unroll
-    for (int j = 0; j < kFastPer; ++j) m = max(m, fs.k[j]);
-    const uint32_t kmax = block_max(m, S.red);
-    uint32_t T = 0, ties = 0;
-    if (fast_threshold(S, fs, max(emax, 1u), kmax, (uint32_t)K, &T, &ties)) {
-      fast_emit(P, S, units_r, fs, row, T, ties);
-      return;
-    }
-    // fewer than K candidates reach the largest edge: the general path below
-    // takes the rescoring route
-  }
   Seg sg;
   uint32_t kmax = 0xFFFFFFFFu;
   if (n_c <= (uint32_t)kChunk) {
@@ -1125,7 +1163,7 @@ int run(Params P, bool dump, hipStream_t stream) {
     void* args[] = {&Q};
     if (hipLaunchKernel(scan, dim3((unsigned)G), dim3(kThreads), args, 0, stream) != hipSuccess)
       return DSA_ERR_HIP;
-    if (!dump && hipLaunchKernel(sel, dim3((unsigned)rn), dim3(kThreads), args, 0, stream) != hipSuccess)
+    if (!dump && hipLaunchKernel(sel, dim3((unsigned)rn), dim3(kSelThreads), args, 0, stream) != hipSuccess)
       return DSA_ERR_HIP;
   }
   return DSA_OK;
