@@ -6,21 +6,25 @@
 //
 // One workgroup = (query row, group of 32 heads, split of the index list);
 // the groups of one (row, split) are placed on one XCD so the records they
-// all read are served by that XCD's L2.  Four waves: wave w owns head tile
-// w&1 (16 heads) and latent half w>>1 (256 of the 512 output dims).
+// all read are served by that XCD's L2.  Eight waves in two groups of four:
+// group G takes tile G (32 tokens) of every step of 64 tokens and keeps its
+// own softmax state; the groups are merged in LDS at the end, so two waves
+// share every SIMD and each hides the other's latencies.  In a group, wave
+// (ht, dh) owns head tile ht (16 heads) and latent half dh (256 of the 512
+// dims, plus half of the rope dims).
 //  * up front, every entry of the split is translated position -> page ->
 //    record slot (two dependent loads, all entries in flight together);
 //  * the selected 656-byte records are copied 32 per tile straight from
 //    global memory into LDS (global_load_lds_dwordx4, no registers), into a
-//    ring of three steps of two tiles, two steps ahead of the compute; one
-//    barrier per step;
-//  * logits S^T = K Q^T on v_mfma_f32_16x16x32_bf16: E4M3 latent -> bf16 is
-//    exact, each 128-wide latent tile accumulates separately and is scaled
-//    by its fp32 tile scale in fp32, the bf16 rope part adds on top; times
-//    softmax_scale*log2(e);
-//  * each wave computes the logits of one of the step's two tiles and swaps
-//    them with its partner (same heads, other latent half) through LDS;
-//    online softmax per head inside the wave (a head's 64 logits of a step
+//    ring of three steps, two steps ahead of the compute; a group's four
+//    waves copy its tile;
+//  * logits S^T = K Q^T on v_mfma_f32_16x16x32_bf16, each wave over its
+//    half of the 576 dims: E4M3 latent -> bf16 is exact, each 128-wide
+//    latent tile accumulates separately and is scaled by its fp32 tile
+//    scale in fp32, the bf16 rope part adds on top; the two halves are
+//    summed through LDS in a fixed order (partner waves end with identical
+//    logits), times softmax_scale*log2(e);
+//  * online softmax per head inside the wave (a head's 32 logits of a tile
 //    live in its four lanes);
 //  * O^T += V^T P'^T on v_mfma_f32_16x16x32_f16: V is the exact E4M3 code in
 //    f16 read transposed from LDS by ds_read_b64_tr_b8, and the tile scale
@@ -39,13 +43,14 @@ namespace {
 
 using namespace dsa;
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;                 // attention workgroup: 8 waves
+constexpr int kCombineThreads = 256;
 constexpr int kHeadsWG = 32;                  // heads per workgroup (two MFMA tiles)
 constexpr int kTileTok = 32;                  // tokens per tile
-constexpr int kStepTok = 2 * kTileTok;        // tokens per step (one tile per parity)
+constexpr int kStepTok = 2 * kTileTok;        // tokens per step (one tile per wave group)
 constexpr int kPieces = kRec / 16;            // 41 16-byte pieces per record
 constexpr int kDmaPerTile = 21;               // ceil(32 * 41 / 64) DMA instructions per tile
-constexpr int kDmaPerWave = 6;                // per wave per tile (the last ones are padding)
+constexpr int kDmaPerWave = 6;                // per wave per step (the last ones are padding)
 constexpr int kSlotBytes = kDmaPerTile * 1024;  // 21504: 32 records + padding
 constexpr int kRingSteps = 3;
 constexpr int kRingBytes = kRingSteps * 2 * kSlotBytes;   // 129024
@@ -55,11 +60,13 @@ constexpr int kTargetWgs = 256;
 constexpr int kZeroBytes = 1024;              // zero record in the workspace
 constexpr int kMargin = 6;                    // logits may exceed the softmax reference by 2^6
 constexpr int kPBias = 8;                     // P' = p * scale * 2^(kPBias - E) < 2^(kMargin+1+kPBias)
+constexpr int kMergeWords = 66;               // per lane: 64 output accumulators, m, l
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-static_assert(kDmaPerWave * 4 >= kDmaPerTile, "DMA assignment covers a tile");
+static_assert(kDmaPerWave * 4 >= kDmaPerTile, "a group's DMA assignment covers its tile");
 static_assert(32 * kPieces <= kDmaPerTile * 64, "a tile fits its DMA instructions");
 static_assert(kMargin + 1 + kPBias < 16, "P' stays below the fp16 maximum");
+static_assert(4 * kMergeWords * 64 * 4 <= kRingBytes, "the merge fits the ring");
 
 struct Params {
   const uint16_t* q;      // [R, H, 576] bf16
@@ -82,10 +89,10 @@ struct Params {
 };
 
 struct Smem {
-  uint8_t ring[kRingBytes];            // record tiles
+  uint8_t ring[kRingBytes];            // record tiles; the group merge at the end
   uint8_t junk[1024];                  // target of padding DMA instructions
   int32_t slot[kMaxEntries];           // record slot per entry of the split, -1 = none
-  float zx[2][2][8 * 64];              // logits swapped between partner waves
+  float zx[2][2][2][8 * 64];           // partial logits [group][ht][dh], swapped between partners
 };
 
 __device__ __forceinline__ void flag(uint32_t* err, uint32_t bits) {
@@ -116,7 +123,7 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hr = lane & 15, g = lane >> 4;
-  const int ht = wv & 1, par = wv >> 1;
+  const int grp = wv >> 2, ht = wv & 1, dh = (wv >> 1) & 1;
   // blockIdx -> (head group, row, split): the head groups of one (row, split)
   // are R*S blocks apart, a multiple of 8 when R*S is, so they share an XCD
   const int pairs = P.R * P.S;
@@ -128,21 +135,21 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
   const int nent = max(0, jend - j0);
   const int nsteps = (nent + kStepTok - 1) / kStepTok;
 
-  // ---- query operand: B operand of S^T = K Q^T for head tile ht.  Lane
-  //      (head hr, group g) holds, for k-step s < 16, latent dims 32s+8g..+7
-  //      and for s = 16, 17 rope dims 32(s-16)+8g..+7.  Issued first so the
-  //      slot resolution's waits cover them.
+  // ---- query operand: B operand of S^T = K Q^T for head tile ht over the
+  //      wave's half of the dims.  Lane (head hr, group g) holds, for k-step
+  //      j < 8, latent dims 256dh+32j+8g..+7 and for j = 8 rope dims
+  //      32dh+8g..+7.  Issued first so the slot resolution's waits cover them.
   const int head = kHeadsWG * hg + 16 * ht + hr;
   const bool head_ok = head < P.H;
-  v8bf qv[18];
+  v8bf qv[9];
   {
     const uint16_t* qrow = P.q + ((int64_t)row * P.H + (head_ok ? head : 0)) * kQK;
 #pragma unroll
-    for (int s = 0; s < 18; ++s) {
-      const int d = s < 16 ? 32 * s + 8 * g : kLatent + 32 * (s - 16) + 8 * g;
+    for (int j = 0; j < 9; ++j) {
+      const int d = j < 8 ? 256 * dh + 32 * j + 8 * g : kLatent + 32 * dh + 8 * g;
       uint4 v = *reinterpret_cast<const uint4*>(qrow + d);
       if (!head_ok) v = make_uint4(0, 0, 0, 0);
-      qv[s] = __builtin_bit_cast(v8bf, v);
+      qv[j] = __builtin_bit_cast(v8bf, v);
     }
   }
 
@@ -150,7 +157,7 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
   {
     const int32_t* idxrow = P.idx + (int64_t)row * P.topk + j0;
     const int32_t* btrow = P.bt + (int64_t)seq * P.bt_stride;
-    constexpr int kPer = kMaxEntries / kThreads;   // 8
+    constexpr int kPer = kMaxEntries / kThreads;   // 4
     int32_t v[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -178,148 +185,133 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
   }
   __syncthreads();
 
-  // ---- DMA of one step (two tiles) into ring slot k % 3: every wave issues
-  //      exactly 2 * kDmaPerWave instructions per step, padding ones included,
-  //      so the waits below can count them.  Instruction m of a wave covers
-  //      pieces 64j + lane (j = wv + 4m) of the tile: record rec_m, 16-byte
-  //      piece part_m.
+  // ---- DMA of one step into ring slot k % 3: the four waves of group G copy
+  //      tile G, each issuing exactly kDmaPerWave instructions per step,
+  //      padding ones included, so the waits below can count them.
+  //      Instruction m of a wave covers pieces 64j + lane (j = wv%4 + 4m) of
+  //      the tile: record rec_m, 16-byte piece part_m.
   const uint32_t ring0 = lds_addr(S.ring), junk = lds_addr(S.junk);
+  const int wq = wv & 3;
   int rec_m[kDmaPerWave], off_m[kDmaPerWave];
 #pragma unroll
   for (int m = 0; m < kDmaPerWave; ++m) {
-    const int piece = 64 * (wv + 4 * m) + lane;
+    const int piece = 64 * (wq + 4 * m) + lane;
     rec_m[m] = piece / kPieces;
     off_m[m] = (piece - kPieces * rec_m[m]) * 16;
   }
   auto issue_step = [&](int k) {
-    int32_t sl[2][kDmaPerWave];
+    int32_t sl[kDmaPerWave];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int m = 0; m < kDmaPerWave; ++m) {
+      const bool live = wq + 4 * m < kDmaPerTile && k < nsteps && rec_m[m] < kTileTok;
+      sl[m] = live ? S.slot[(2 * k + grp) * kTileTok + rec_m[m]] : -1;
+    }
+    const uint32_t base = ring0 + (uint32_t)(((k % kRingSteps) * 2 + grp) * kSlotBytes);
 #pragma unroll
-      for (int m = 0; m < kDmaPerWave; ++m) {
-        const bool live = wv + 4 * m < kDmaPerTile && k < nsteps && rec_m[m] < kTileTok;
-        sl[tt][m] = live ? S.slot[(2 * k + tt) * kTileTok + rec_m[m]] : -1;
-      }
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const uint32_t base = ring0 + (uint32_t)(((k % kRingSteps) * 2 + tt) * kSlotBytes);
-#pragma unroll
-      for (int m = 0; m < kDmaPerWave; ++m) {
-        const bool inst = wv + 4 * m < kDmaPerTile && k < nsteps;   // wave-uniform
-        const int32_t sv = sl[tt][m];
-        const uint8_t* src = sv >= 0 ? P.pool + (int64_t)sv * kRec + off_m[m] : P.zero + off_m[m];
-        dma16(src, inst ? base + (uint32_t)((wv + 4 * m) * 1024) : junk);
-      }
+    for (int m = 0; m < kDmaPerWave; ++m) {
+      const bool inst = wq + 4 * m < kDmaPerTile && k < nsteps;   // wave-uniform
+      const int32_t sv = sl[m];
+      const uint8_t* src = sv >= 0 ? P.pool + (int64_t)sv * kRec + off_m[m] : P.zero + off_m[m];
+      dma16(src, inst ? base + (uint32_t)((wq + 4 * m) * 1024) : junk);
     }
   };
 
-  // Wave roles: head tile ht; dim half dh.  In step k the wave computes the
-  // logits of tile 2k+dh for its 16 heads and swaps them with its partner
-  // (same ht, other dh) through LDS; both then hold the step's 64 logits,
-  // run the same softmax, and the wave accumulates O^T for latent dims
-  // 256dh .. 256dh+255 (latent tiles 2dh, 2dh+1).
-  // m_ref / l_run: softmax reference and running sum of head hr (identical
-  // in the four lanes of a head and in both partners; l_run and O are
-  // relative to m_ref); eref: power-of-two references of the wave's two
-  // latent tiles (wave-uniform).  The references move only when a logit
-  // exceeds m_ref by more than kMargin or a tile scale exceeds its reference,
-  // so O is rescaled rarely.  o[d][c] = dim 256dh + 16d + 4g + c of head hr.
-  const int dh = wv >> 1;
+  // m_ref / l_run: softmax reference and running sum of head hr over the
+  // group's tiles (identical in the four lanes of a head and in both
+  // partners; l_run and O are relative to m_ref); eref: power-of-two
+  // references of the wave's two latent tiles (wave-uniform).  The
+  // references move only when a logit exceeds m_ref by more than kMargin or
+  // a tile scale exceeds its reference, so O is rescaled rarely.
+  // o[d][c] = dim 256dh + 16d + 4g + c of head hr.
   float m_ref = -__builtin_huge_valf(), l_run = 0.f;
   int eref[2] = {-1000, -1000};
   v4f o[16];
 #pragma unroll
   for (int d = 0; d < 16; ++d) o[d] = v4f{0.f, 0.f, 0.f, 0.f};
-  float* zx = S.zx[ht][dh];
-  const float* zpart = S.zx[ht][dh ^ 1];
+  float* zx = S.zx[grp][ht][dh];
+  const float* zpart = S.zx[grp][ht][dh ^ 1];
 
   issue_step(0);
   issue_step(1);
   for (int k = 0; k < nsteps; ++k) {
-    // this step's copies are complete once only the next step's 12 remain;
-    // the barrier also releases the slots of step k-1
-    asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+    // this step's copies are complete once only the next step's remain; the
+    // barrier also releases the slots of step k-1
+    asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
     issue_step(k + 2);
-    const uint8_t* tA = S.ring + ((k % kRingSteps) * 2) * kSlotBytes;
-    const uint8_t* tB = tA + kSlotBytes;
-    const uint8_t* tq = dh ? tB : tA;          // the tile whose logits this wave computes
-    const int eq0 = (2 * k + dh) * kTileTok;   // its first entry
+    const uint8_t* tq = S.ring + ((k % kRingSteps) * 2 + grp) * kSlotBytes;   // the group's tile
+    const int eq0 = (2 * k + grp) * kTileTok;   // its first entry
 
-    // ---- logits of tile tq's 32 tokens for the wave's 16 heads ----
-    v4f acc[2][5];
+    // ---- partial logits over the wave's half of the dims: accumulators
+    //      acc[u][t] of token rows 16u + (0..15), latent tile 2dh + t (t < 2)
+    //      or the rope half (t = 2); consecutive MFMAs feed different ones
+    v4f acc[2][3];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int t = 0; t < 5; ++t) acc[u][t] = v4f{0.f, 0.f, 0.f, 0.f};
-    // k-steps ordered so that consecutive MFMAs feed different accumulators
-    const uint8_t* rec0 = tq + hr * kRec;            // A-operand rows of this lane
-    const uint8_t* rec1 = tq + (16 + hr) * kRec;
+      for (int t = 0; t < 3; ++t) acc[u][t] = v4f{0.f, 0.f, 0.f, 0.f};
+    const uint8_t* rec0 = tq + hr * kRec + 256 * dh + 8 * g;   // A-operand rows of this lane
+    const uint8_t* rec1 = rec0 + 16 * kRec;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int jj = 0; jj < 4; ++jj) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int s = 4 * t + j;
+      for (int t = 0; t < 2; ++t) {
+        const int j = 4 * t + jj;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const uint2 raw = *reinterpret_cast<const uint2*>((u ? rec1 : rec0) + 32 * s + 8 * g);
+          const uint2 raw = *reinterpret_cast<const uint2*>((u ? rec1 : rec0) + 32 * j);
           const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, false);
           const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, true);
           const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, 1.0f, false);
           const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, 1.0f, true);
           const v8bf a = v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-          acc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qv[s], acc[u][t], 0, 0, 0);
+          acc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qv[j], acc[u][t], 0, 0, 0);
         }
       }
     }
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const uint4 r4 = *reinterpret_cast<const uint4*>((u ? rec1 : rec0) + kRecRopeOff + 64 * s + 16 * g);
-        acc[u][4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, r4), qv[16 + s],
-                                                            acc[u][4], 0, 0, 0);
-      }
-    // logits of the lane's 8 tokens of tq (k order), shared with the partner
+    for (int u = 0; u < 2; ++u) {
+      const uint4 r4 = *reinterpret_cast<const uint4*>(tq + (16 * u + hr) * kRec + kRecRopeOff +
+                                                       64 * dh + 16 * g);
+      acc[u][2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, r4), qv[8],
+                                                          acc[u][2], 0, 0, 0);
+    }
+    // scales of the wave's two latent tiles for the lane's 8 tokens (k order)
+    float sc[8][2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int tok = ktok(g, i);
-      const float4 s4 = *reinterpret_cast<const float4*>(tq + tok * kRec + kRecScaleOff);
+      const float2 s2 = *reinterpret_cast<const float2*>(tq + ktok(g, i) * kRec + kRecScaleOff + 8 * dh);
+      sc[i][0] = s2.x;
+      sc[i][1] = s2.y;
+    }
+    // this half's part of the logits of the lane's 8 tokens, shared with the
+    // partner (same heads, other half)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
       const int u = i >> 2, c = i & 3;
-      float v = acc[u][4][c];
-      v = __builtin_fmaf(s4.x, acc[u][0][c], v);
-      v = __builtin_fmaf(s4.y, acc[u][1][c], v);
-      v = __builtin_fmaf(s4.z, acc[u][2][c], v);
-      v = __builtin_fmaf(s4.w, acc[u][3][c], v);
-      zx[i * 64 + lane] = S.slot[eq0 + tok] >= 0 ? v * P.scale_log2 : -__builtin_huge_valf();
+      float v = acc[u][2][c];
+      v = __builtin_fmaf(sc[i][0], acc[u][0][c], v);
+      v = __builtin_fmaf(sc[i][1], acc[u][1][c], v);
+      zx[i * 64 + lane] = v;
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // z[kk*8 + i]: tile kk (0 = tA, 1 = tB), k-order token i
-    float z[16];
+    float z[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float own = zx[i * 64 + lane], other = zpart[i * 64 + lane];
-      z[i] = dh ? other : own;
-      z[8 + i] = dh ? own : other;
+      const float v = dh ? other + own : own + other;   // half 0 first in both partners
+      z[i] = S.slot[eq0 + ktok(g, i)] >= 0 ? v * P.scale_log2 : -__builtin_huge_valf();
     }
-    // scales of the wave's two latent tiles for the step's 64 tokens
-    float sc[16][2];
     uint32_t smax[2] = {0u, 0u};
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float2 s2 = *reinterpret_cast<const float2*>((kk ? tB : tA) + ktok(g, i) * kRec +
-                                                           kRecScaleOff + 8 * dh);
-        sc[8 * kk + i][0] = s2.x;
-        sc[8 * kk + i][1] = s2.y;
-        smax[0] = max(smax[0], __float_as_uint(s2.x));
-        smax[1] = max(smax[1], __float_as_uint(s2.y));
-      }
+    for (int i = 0; i < 8; ++i) {
+      smax[0] = max(smax[0], __float_as_uint(sc[i][0]));
+      smax[1] = max(smax[1], __float_as_uint(sc[i][1]));
+    }
 
-    // ---- online softmax of head hr over the step (lazy references) ----
+    // ---- online softmax of head hr over the tile (lazy references) ----
     float zm = z[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) zm = fmaxf(zm, z[i]);
+    for (int i = 1; i < 8; ++i) zm = fmaxf(zm, z[i]);
     zm = fmaxf(zm, __shfl_xor(zm, 16));
     zm = fmaxf(zm, __shfl_xor(zm, 32));
     int et[2];
@@ -335,7 +327,7 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
     const bool grow = zm > m_ref + (float)kMargin;   // false while zm is -inf
     if (__builtin_amdgcn_ballot_w64(grow) || egrow) {
       const float m_new = grow ? zm : m_ref;
-      const float fh = m_ref == -__builtin_huge_valf() ? 0.f : exp2f(m_ref - m_new);
+      const float fh = m_ref == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
       float ft[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -354,47 +346,44 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
       l_run *= fh;
       m_ref = m_new;
     }
-    float p[16], ps = 0.f;
+    float pr[8], ps = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      p[i] = z[i] == -__builtin_huge_valf() ? 0.f : exp2f(z[i] - m_ref);   // <= 2^kMargin
-      ps += p[i];
+    for (int i = 0; i < 8; ++i) {
+      pr[i] = z[i] == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(z[i] - m_ref);   // <= 2^kMargin
+      ps += pr[i];
     }
     ps += __shfl_xor(ps, 16);
     ps += __shfl_xor(ps, 32);
     l_run += ps;
 
-    // ---- O^T += V^T P'^T over the step's two tiles (k-steps) ----
+    // ---- O^T += V^T P'^T over the tile (one k-step of 32 tokens) ----
     typedef __attribute__((address_space(3))) v2i lds_v2i;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const float mul = eref[t] > -1000 ? pow2f(max(-126, min(127, kPBias - eref[t]))) : 0.f;
+      _Float16 h[8];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        _Float16 h[8];
+      for (int i = 0; i < 8; ++i) h[i] = (_Float16)(pr[i] * sc[i][t] * mul);
+      const v8h b = v8h{h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7]};
+      const uint8_t* vrow = tq + ktok(g, hr >> 1) * kRec + 8 * (hr & 1) + 128 * (2 * dh + t);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = (_Float16)(p[8 * kk + i] * sc[8 * kk + i][t] * mul);
-        const v8h b = v8h{h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7]};
-        const uint8_t* vrow = (kk ? tB : tA) + ktok(g, hr >> 1) * kRec + 8 * (hr & 1) +
-                              128 * (2 * dh + t);
-#pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-          const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (lds_v2i*)((__attribute__((address_space(3))) uint8_t*)(vrow + 16 * dd)));
-          const v2h v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[0], 1.0f, false);
-          const v2h v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[0], 1.0f, true);
-          const v2h v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[1], 1.0f, false);
-          const v2h v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[1], 1.0f, true);
-          const v8h a = v8h{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
-          o[8 * t + dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, o[8 * t + dd], 0, 0, 0);
-        }
+      for (int dd = 0; dd < 8; ++dd) {
+        const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (lds_v2i*)((__attribute__((address_space(3))) uint8_t*)(vrow + 16 * dd)));
+        const v2h v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[0], 1.0f, false);
+        const v2h v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[0], 1.0f, true);
+        const v2h v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[1], 1.0f, false);
+        const v2h v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[1], 1.0f, true);
+        const v8h a = v8h{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+        o[8 * t + dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, o[8 * t + dd], 0, 0, 0);
       }
     }
   }
-  // no copy may still be landing in LDS when the workgroup ends
+  // no copy may still be landing in LDS when the ring is reused or the
+  // workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // ---- epilogue: true O = o * 2^(eref - kPBias) ----
+  // ---- true O relative to m_ref: o * 2^(eref - kPBias) ----
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const float f = eref[t] > -1000 ? pow2f(max(-126, min(127, eref[t] - kPBias))) : 0.f;
@@ -402,6 +391,31 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
     for (int dd = 0; dd < 8; ++dd)
 #pragma unroll
       for (int c = 0; c < 4; ++c) o[8 * t + dd][c] *= f;
+  }
+  // ---- merge group 1 into group 0 (same lane, same wave role) ----
+  __syncthreads();
+  float* mg = reinterpret_cast<float*>(S.ring) + (wv & 3) * kMergeWords * 64 + lane;
+  if (grp == 1) {
+#pragma unroll
+    for (int d = 0; d < 16; ++d)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mg[(4 * d + c) * 64] = o[d][c];
+    mg[64 * 64] = m_ref;
+    mg[65 * 64] = l_run;
+  }
+  __syncthreads();
+  if (grp == 1) return;
+  {
+    const float m1 = mg[64 * 64], l1 = mg[65 * 64];
+    const float M = fmaxf(m_ref, m1);
+    const float f0 = m_ref == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(m_ref - M);
+    const float f1 = m1 == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+#pragma unroll
+    for (int d = 0; d < 16; ++d)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[d][c] = o[d][c] * f0 + mg[(4 * d + c) * 64] * f1;
+    l_run = l_run * f0 + l1 * f1;
+    m_ref = M;
   }
   if (!head_ok) return;
   if (P.S == 1) {
@@ -427,7 +441,7 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
 
 // Combines the S partials of every (row, head) in split order: thread t of a
 // block handles head 4*blockIdx.y + t/64, dims 8*(t%64) .. +7.
-__global__ __launch_bounds__(kThreads) void sfa_combine_kernel(Params P) {
+__global__ __launch_bounds__(kCombineThreads) void sfa_combine_kernel(Params P) {
   const int row = blockIdx.x, h = 4 * blockIdx.y + (threadIdx.x >> 6), c = threadIdx.x & 63;
   if (h >= P.H) return;
   const int64_t ph0 = ((int64_t)row * P.H + h) * P.S;
@@ -553,7 +567,7 @@ extern "C" int dsa_sparse_attn(const void* q_bf16, const void* kv_pool, int64_t 
   hipLaunchKernelGGL(sfa_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, P);
   if (hipGetLastError() != hipSuccess) return DSA_ERR_HIP;
   if (pl.S > 1) {
-    hipLaunchKernelGGL(sfa_combine_kernel, dim3((unsigned)R, (unsigned)((H + 3) / 4)), dim3(kThreads), 0, s, P);
+    hipLaunchKernelGGL(sfa_combine_kernel, dim3((unsigned)R, (unsigned)((H + 3) / 4)), dim3(kCombineThreads), 0, s, P);
     if (hipGetLastError() != hipSuccess) return DSA_ERR_HIP;
   }
   return DSA_OK;
