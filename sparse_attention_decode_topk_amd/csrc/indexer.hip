@@ -10,10 +10,11 @@
 // Two launches on the caller's stream:
 //  1. scan: every row's causal history is cut into units of 16 pages (1024
 //     positions); workgroups take units in row-major order.  For a unit, each
-//     wave streams eight half pages through a three-deep register ring,
-//     dequantises the MXFP8 key block exactly into bf16 (E4M3 * 2^(E-127) is
-//     a bf16 value), runs v_mfma_f32_16x16x32_bf16 against the resident query
-//     heads, applies ReLU and the head weights in fp32 and keeps the unit's
+//     wave streams eight half pages through a three-deep register ring and
+//     runs v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 codes of both operands,
+//     their E8M0 block scales applied by the instruction, fp32 accumulation)
+//     against the resident query heads, applies ReLU and the head weights in
+//     fp32 and keeps the unit's
 //     scores as order-preserving 32-bit keys in LDS.  A local filter (two
 //     8-bit LDS histogram passes) finds the edge e_u of the 16-bit key bin
 //     that holds the unit's quota-th largest key (quota: about the unit's
@@ -107,10 +108,6 @@ struct SelSmem {
 
 __device__ __forceinline__ void flag_error(uint32_t* hdr, uint32_t bits) {
   if (hdr) __hip_atomic_fetch_or(&hdr[2], bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
-  return b == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(b << 23);
 }
 
 // ---- block primitives (256 threads) -------------------------------------
@@ -236,16 +233,22 @@ __device__ __forceinline__ Unit row_unit(const Params& P, int row, int t, int ui
 
 // ---- scoring ---------------------------------------------------------------
 
+typedef int v8i __attribute__((ext_vector_type(8)));
+
 template <int NHT>
 struct QOperand {
-  v8bf a[NHT][4];   // A operand per head tile and k-step
+  v8i a[NHT];       // A operand per head tile: 32 E4M3 codes
+  int s[NHT];       // E8M0 scale of the lane's 32-dim block
   float w[NHT][4];  // weights of heads 16i + 4g + c
 };
 
-// Query heads as the A operand of v_mfma_f32_16x16x32_bf16: lane (head
-// 16i + lane%16, group g = lane/16) holds, for k-step s, dims 32g + 8s .. +7
-// dequantised exactly into bf16.  The key operand uses the same k order, so
-// each lane's 32 key bytes form exactly one MXFP8 group with one scale.
+// Query heads as the A operand of v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3
+// times E4M3, one E8M0 scale per operand row and 32-wide k block): lane
+// (head 16i + lane%16, group g = lane/16) holds dims 16g .. 16g+15 and
+// 64+16g .. 64+16g+15 of its head, and supplies the scale of dims
+// 32g .. 32g+31 (the instruction's k order and scale ownership; the key
+// operand uses the same ones).  No dequantisation: the instruction applies
+// both scales.
 template <int NHT>
 __device__ __forceinline__ void load_q(const Params& P, int row, QOperand<NHT>& Q) {
   const int lane = threadIdx.x & 63, hr = lane & 15, g = lane >> 4;
@@ -257,20 +260,13 @@ __device__ __forceinline__ void load_q(const Params& P, int row, QOperand<NHT>& 
     const int h = 16 * i + hr;
     const bool live = h < P.H;
     const int hs = live ? h : 0;
-    const uint8_t* src = P.q + ((int64_t)row * P.H + hs) * kIdxDim + 32 * g;
-    const uint4 a = *reinterpret_cast<const uint4*>(src);
-    const uint4 b = *reinterpret_cast<const uint4*>(src + 16);
-    const uint32_t dw[8] = {live ? a.x : 0u, live ? a.y : 0u, live ? a.z : 0u, live ? a.w : 0u,
-                            live ? b.x : 0u, live ? b.y : 0u, live ? b.z : 0u, live ? b.w : 0u};
-    const float sc = e8m0_to_f32(P.qs[((int64_t)row * P.H + hs) * 4 + g]);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dw[2 * s], sc, false);
-      const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dw[2 * s], sc, true);
-      const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dw[2 * s + 1], sc, false);
-      const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dw[2 * s + 1], sc, true);
-      Q.a[i][s] = v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-    }
+    const uint8_t* src = P.q + ((int64_t)row * P.H + hs) * kIdxDim;
+    const uint4 a = *reinterpret_cast<const uint4*>(src + 16 * g);
+    const uint4 b = *reinterpret_cast<const uint4*>(src + 64 + 16 * g);
+    Q.a[i] = v8i{(int)(live ? a.x : 0u), (int)(live ? a.y : 0u), (int)(live ? a.z : 0u),
+                 (int)(live ? a.w : 0u), (int)(live ? b.x : 0u), (int)(live ? b.y : 0u),
+                 (int)(live ? b.z : 0u), (int)(live ? b.w : 0u)};
+    Q.s[i] = (int)P.qs[((int64_t)row * P.H + hs) * 4 + g];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int hh = 16 * i + 4 * g + c;
@@ -281,8 +277,9 @@ __device__ __forceinline__ void load_q(const Params& P, int row, QOperand<NHT>& 
 }
 
 // Half a page (two token tiles of 16) as held by one lane: for tile
-// j = 2*half + jj, d[2jj], d[2jj+1] are this lane's 32 bytes of token
-// 16j + lane%16 (dims 32g..32g+31, g = lane/16) and s[jj] its E8M0 byte.
+// j = 2*half + jj, d[2jj], d[2jj+1] are this lane's 32 code bytes of token
+// 16j + lane%16 (dims 16g..16g+15 and 64+16g..64+16g+15, g = lane/16) and
+// s[jj] the E8M0 byte of its dims 32g..32g+31.
 struct HalfRegs {
   uint4 d[4];
   uint32_t s[2];
@@ -291,7 +288,7 @@ struct HalfRegs {
 // Loads half `half` of the page behind `rsrc` (a raw buffer descriptor
 // covering the page, or with zero records when the half is absent: then
 // every load is out of range, reads nothing and returns 0).  off_d / off_s
-// are the lane's fixed byte offsets of its code bytes and scale byte.
+// are the lane's fixed byte offsets of its first code bytes and scale byte.
 __device__ __forceinline__ void load_half(__amdgpu_buffer_rsrc_t rsrc, int half, uint32_t off_d,
                                           uint32_t off_s, HalfRegs& hr) {
   const uint32_t od = off_d + (uint32_t)half * 32 * kIdxDim;
@@ -299,7 +296,7 @@ __device__ __forceinline__ void load_half(__amdgpu_buffer_rsrc_t rsrc, int half,
 #pragma unroll
   for (int jj = 0; jj < 2; ++jj) {
     const v4u a = __builtin_amdgcn_raw_buffer_load_b128(rsrc, od + jj * 16 * kIdxDim, 0, 0);
-    const v4u b = __builtin_amdgcn_raw_buffer_load_b128(rsrc, od + jj * 16 * kIdxDim + 16, 0, 0);
+    const v4u b = __builtin_amdgcn_raw_buffer_load_b128(rsrc, od + jj * 16 * kIdxDim + 64, 0, 0);
     hr.d[2 * jj] = make_uint4(a[0], a[1], a[2], a[3]);
     hr.d[2 * jj + 1] = make_uint4(b[0], b[1], b[2], b[3]);
     hr.s[jj] = __builtin_amdgcn_raw_buffer_load_b8(rsrc, os + jj * 64, 0, 0);
@@ -307,32 +304,25 @@ __device__ __forceinline__ void load_half(__amdgpu_buffer_rsrc_t rsrc, int half,
 }
 
 // Scores of the 32 tokens of one half page; lanes 0..15 end with token
-// 16jj + lane of the half in out[jj].  Head sum: in-lane over the lane's
+// 16jj + lane of the half in out[jj].  One scaled FP8 MFMA per head tile
+// and token tile covers all 128 dims.  Head sum: in-lane over the lane's
 // heads, then across the four lane groups, in a fixed order.
 template <int NHT>
 __device__ __forceinline__ void score_half(const QOperand<NHT>& Q, const HalfRegs& hr,
                                            float out[2]) {
 #pragma unroll
   for (int jj = 0; jj < 2; ++jj) {
-    const float ks = e8m0_to_f32(hr.s[jj]);
-    const uint32_t dw[8] = {hr.d[2 * jj].x,     hr.d[2 * jj].y,     hr.d[2 * jj].z,
-                            hr.d[2 * jj].w,     hr.d[2 * jj + 1].x, hr.d[2 * jj + 1].y,
-                            hr.d[2 * jj + 1].z, hr.d[2 * jj + 1].w};
-    v8bf kb[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dw[2 * s], ks, false);
-      const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dw[2 * s], ks, true);
-      const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dw[2 * s + 1], ks, false);
-      const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dw[2 * s + 1], ks, true);
-      kb[s] = v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-    }
+    const uint4 lo = hr.d[2 * jj], hi = hr.d[2 * jj + 1];
+    const v8i kb = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    const int ks = (int)hr.s[jj];
     float part = 0.f;
 #pragma unroll
     for (int i = 0; i < NHT; ++i) {
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Q.a[i][s], kb[s], acc, 0, 0, 0);
+      const v4f zero = {0.f, 0.f, 0.f, 0.f};
+      // formats 0 / 0: E4M3 for both operands; scale byte 0 of each lane
+      const v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Q.a[i], kb, zero, 0, 0, 0,
+                                                                        Q.s[i], 0, ks);
 #pragma unroll
       for (int c = 0; c < 4; ++c) part = __builtin_fmaf(Q.w[i][c], fmaxf(acc[c], 0.f), part);
     }
@@ -366,7 +356,7 @@ __device__ __forceinline__ void score_unit(const Params& P, const Unit& U, uint3
   // ring load
   QOperand<NHT> Q;
   load_q<NHT>(P, U.row, Q);
-  const uint32_t off_d = (uint32_t)(r * kIdxDim + 32 * g);
+  const uint32_t off_d = (uint32_t)(r * kIdxDim + 16 * g);
   const uint32_t off_s = (uint32_t)(r * 4 + g);
   auto fetch = [&](int h, HalfRegs& b) -> bool {
     const int32_t id = h < nhalf ? __builtin_amdgcn_readlane(pid, (h >> 1) & 63) : -1;
