@@ -43,7 +43,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kUnitPages = 16;
 constexpr int kUnitTok = kUnitPages * kPage;           // 1024 keys per unit
 constexpr int kHalvesPerWave = 2 * kUnitPages / kWaves;  // 8 half pages per wave
-constexpr int kRing = 3;                               // half pages in flight per wave
+constexpr int kRing = 4;                               // half pages in flight per wave
 constexpr int kFBins = 256;                            // filter histogram (8-bit passes)
 constexpr int kBins = 4096;                            // select histogram (12-bit passes)
 constexpr int kCandPer = 24;                           // select: candidates per thread
@@ -56,6 +56,7 @@ constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kFastUnits = 128;                        // select fast path: units per row
 constexpr int kFastPer = kFastUnits / kSelWaves;       // units per wave
 static_assert(kFBins == kThreads, "one filter bin per thread");
+static_assert(kHalvesPerWave % kRing == 0, "the ring wraps at unit boundaries");
 
 // Buffer descriptor word 3 for raw (untyped) buffer access on gfx9-class
 // GPUs: 32-bit data format, no swizzle.
@@ -91,6 +92,8 @@ struct ScanSmem {
   uint32_t keys[kUnitTok];            // scores of the current unit as keys
   uint32_t hist[kFBins];
   uint32_t rowpre[kMaxRows + 1];      // exclusive prefix of units per row
+  int32_t rowt[kMaxRows];             // row_pos of every row
+  int32_t rowseq[kMaxRows];           // row_seq of every row
   uint32_t red[2 * kWaves + 2];
   uint32_t misc[16];
 };
@@ -177,25 +180,34 @@ __device__ __forceinline__ int row_units(int t, int bt_stride) {
   return (row_pages(t, bt_stride) + kUnitPages - 1) / kUnitPages;
 }
 
-__device__ __forceinline__ void plan_rows(const Params& P, uint32_t* rowpre, uint32_t* red) {
+__device__ __forceinline__ void plan_rows(const Params& P, ScanSmem& S) {
+  uint32_t* rowpre = S.rowpre;
+  uint32_t* red = S.red;
   const int per = (P.R + kThreads - 1) / kThreads;
   const int r0 = threadIdx.x * per;
   uint32_t lu = 0;
-  for (int i = 0; i < per; ++i)
-    if (r0 + i < P.R) lu += (uint32_t)row_units(P.row_pos[r0 + i], P.bt_stride);
+  for (int i = 0; i < per; ++i) {
+    if (r0 + i < P.R) {
+      const int t = P.row_pos[r0 + i];
+      S.rowt[r0 + i] = t;
+      S.rowseq[r0 + i] = P.row_seq[r0 + i];
+      lu += (uint32_t)row_units(t, P.bt_stride);
+    }
+  }
   uint32_t total;
   uint32_t run = block_excl_scan(lu, red, &total);
   for (int i = 0; i < per; ++i) {
     if (r0 + i < P.R) {
       rowpre[r0 + i] = run;
-      run += (uint32_t)row_units(P.row_pos[r0 + i], P.bt_stride);
+      run += (uint32_t)row_units(S.rowt[r0 + i], P.bt_stride);
     }
   }
   if (threadIdx.x == 0) rowpre[P.R] = total;
   __syncthreads();
 }
 
-__device__ __forceinline__ Unit decode_unit(const Params& P, const uint32_t* rowpre, uint32_t u) {
+__device__ __forceinline__ Unit decode_unit(const Params& P, const ScanSmem& S, uint32_t u) {
+  const uint32_t* rowpre = S.rowpre;
   int lo = 0, hi = P.R - 1;     // row r with rowpre[r] <= u < rowpre[r+1]
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -205,7 +217,7 @@ __device__ __forceinline__ Unit decode_unit(const Params& P, const uint32_t* row
   U.row = lo;
   U.uir = (int)(u - rowpre[lo]);
   U.units_r = (int)(rowpre[lo + 1] - rowpre[lo]);
-  U.t = P.row_pos[lo];
+  U.t = S.rowt[lo];
   const int pr = row_pages(U.t, P.bt_stride);
   U.pg0 = U.uir * kUnitPages;
   U.pg1 = min(pr, U.pg0 + kUnitPages);
@@ -332,67 +344,89 @@ __device__ __forceinline__ void score_half(const QOperand<NHT>& Q, const HalfReg
   }
 }
 
-// Score one unit: all 1024 key slots of the unit (key 0 for positions past t
-// or on an absent page), or, for the dump, the scores of its positions.
-// Wave w takes half pages w, w+4, ..., w+28 of the unit, fully unrolled, with
-// kRing of them in flight.  The unit's page ids are read from the block table
-// once, one per lane, and every fetch issues the same loads (an absent half
-// gets a zero-record descriptor), so the loads retire in ring order and the
-// compiler's wait counting never has to drain the ring.
+// Block-table entries of unit U of a row mapped to block-table row `seq`,
+// one per lane (lanes < the unit's page count; other lanes read out of range,
+// which moves nothing).  The value is not examined here: its first use is
+// when the unit's half pages are requested, so waiting for it never waits
+// for ring loads issued after it.
+__device__ __forceinline__ int32_t unit_pages(const Params& P, const Unit& U, int seq) {
+  const int lane = threadIdx.x & 63;
+  seq = __builtin_amdgcn_readfirstlane(seq);   // uniform: the descriptor lives in scalar registers
+  const bool want = lane < U.pg1 - U.pg0;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(P.bt + (int64_t)seq * P.bt_stride), (short)0, P.bt_stride * 4, kRawBufferWord3);
+  return (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+      rsrc, want ? (uint32_t)(U.pg0 + lane) * 4u : (uint32_t)P.bt_stride * 4u, 0, 0);
+}
+
+// Issues the loads of half page h of unit U (block-table entries `pid` as
+// returned by unit_pages).  Every call issues the same loads: an absent half
+// (past the unit, a row with t < 0, or a page id out of the pool, which sets
+// *bad) gets a zero-record descriptor, so the loads retire in issue order
+// and the compiler's wait counting never has to drain the ring.  Returns
+// whether the half exists.
+__device__ __forceinline__ bool fetch_half(const Params& P, const Unit& U, int32_t pid, int h,
+                                           HalfRegs& b, bool* bad) {
+  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  const bool want = h < 2 * (U.pg1 - U.pg0) && U.t >= 0;
+  const int32_t raw = __builtin_amdgcn_readlane(pid, (h >> 1) & 63);
+  const bool inpool = raw >= 0 && (int64_t)raw < P.pool_pages;
+  *bad |= want && !inpool;
+  const int32_t id = want && inpool ? raw : -1;
+  const bool ok = id >= 0;
+  const uint8_t* page = P.kpool + (int64_t)(ok ? id : 0) * kKPageBytes;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(page), (short)0, ok ? kKPageBytes : 0, kRawBufferWord3);
+  load_half(rsrc, h & 1, (uint32_t)(r * kIdxDim + 16 * g), (uint32_t)(r * 4 + g), b);
+  return ok;
+}
+
+// Scores half page h of unit U: keys of its 32 positions into keys[] (key 0
+// for positions past t or on an absent page), or, for the dump, the scores.
+template <int NHT, bool DUMP>
+__device__ __forceinline__ void consume_half(const Params& P, const Unit& U, const QOperand<NHT>& Q,
+                                             int h, const HalfRegs& b, bool ok, uint32_t* keys) {
+  const int lane = threadIdx.x & 63;
+  float sc[2] = {0.f, 0.f};
+  if (ok) score_half<NHT>(Q, b, sc);
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int tok = 32 * h + 16 * jj + lane;      // unit-local, lanes 0..15
+    const int pos = U.pg0 * kPage + tok;
+    const bool valid = ok && pos <= U.t;
+    if (lane < 16) {
+      if (DUMP) {
+        if (valid && pos < P.ld) P.dump[(int64_t)U.row * P.ld + pos] = sc[jj] == 0.f ? 0.f : sc[jj];
+      } else {
+        keys[tok] = valid ? score_key(sc[jj]) : 0u;
+      }
+    }
+  }
+}
+
+// Score one unit on its own (the dump and the rescoring of the select):
+// wave w takes half pages w, w+4, ..., w+28 of the unit, fully unrolled,
+// with kRing of them in flight.
 template <int NHT, bool DUMP>
 __device__ __forceinline__ void score_unit(const Params& P, const Unit& U, uint32_t* keys) {
-  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int npg = U.pg1 - U.pg0;   // <= 16
-  const int nhalf = 2 * npg;
-  int32_t pid = -1;                // -1: page absent, its positions get key 0
-  if (lane < npg && U.t >= 0) {
-    const int32_t id = P.bt[(int64_t)P.row_seq[U.row] * P.bt_stride + U.pg0 + lane];
-    const bool bad = id < 0 || (int64_t)id >= P.pool_pages;
-    if (bad) flag_error(P.hdr, kErrBadPage);
-    pid = bad ? -1 : id;
-  }
+  bool bad = false;
+  const int32_t pid = unit_pages(P, U, P.row_seq[U.row]);
   // the query loads go before the ring: they are then older than every
   // ring load
   QOperand<NHT> Q;
   load_q<NHT>(P, U.row, Q);
-  const uint32_t off_d = (uint32_t)(r * kIdxDim + 16 * g);
-  const uint32_t off_s = (uint32_t)(r * 4 + g);
-  auto fetch = [&](int h, HalfRegs& b) -> bool {
-    const int32_t id = h < nhalf ? __builtin_amdgcn_readlane(pid, (h >> 1) & 63) : -1;
-    const bool ok = id >= 0;
-    const uint8_t* page = P.kpool + (int64_t)(ok ? id : 0) * kKPageBytes;
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(page), (short)0, ok ? kKPageBytes : 0, kRawBufferWord3);
-    load_half(rsrc, h & 1, off_d, off_s, b);
-    return ok;
-  };
-  auto consume = [&](int h, const HalfRegs& b, bool ok) {
-    float sc[2] = {0.f, 0.f};
-    if (ok) score_half<NHT>(Q, b, sc);
+  HalfRegs b[kRing];
+  bool ok[kRing];
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int tok = 32 * h + 16 * jj + lane;      // unit-local, lanes 0..15
-      const int pos = U.pg0 * kPage + tok;
-      const bool valid = ok && pos <= U.t;
-      if (lane < 16) {
-        if (DUMP) {
-          if (valid && pos < P.ld) P.dump[(int64_t)U.row * P.ld + pos] = sc[jj] == 0.f ? 0.f : sc[jj];
-        } else {
-          keys[tok] = valid ? score_key(sc[jj]) : 0u;
-        }
-      }
-    }
-  };
-  HalfRegs b[kHalvesPerWave];
-  bool ok[kHalvesPerWave];
-#pragma unroll
-  for (int k = 0; k < kRing; ++k) ok[k] = fetch(wv + kWaves * k, b[k]);
+  for (int k = 0; k < kRing; ++k) ok[k] = fetch_half(P, U, pid, wv + kWaves * k, b[k], &bad);
 #pragma unroll
   for (int k = 0; k < kHalvesPerWave; ++k) {
-    if (k + kRing < kHalvesPerWave) ok[k + kRing] = fetch(wv + kWaves * (k + kRing), b[k + kRing]);
-    consume(wv + kWaves * k, b[k], ok[k]);
+    consume_half<NHT, DUMP>(P, U, Q, wv + kWaves * k, b[k % kRing], ok[k % kRing], keys);
+    if (k + kRing < kHalvesPerWave)
+      ok[k % kRing] = fetch_half(P, U, pid, wv + kWaves * (k + kRing), b[k % kRing], &bad);
   }
+  if (bad && (threadIdx.x & 63) == 0) flag_error(P.hdr, kErrBadPage);
 }
 
 // ---- scan kernel: local filter ------------------------------------------------
@@ -485,28 +519,71 @@ __device__ __forceinline__ void filter_unit(const Params& P, ScanSmem& S, const 
   }
 }
 
+// A workgroup takes a contiguous run of units (usually of one row, so the
+// query operand stays resident).  The half-page ring runs across the units:
+// while a unit's last half pages are scored, the first kRing half pages of
+// the next unit are already requested, so they are in flight during the
+// local filter and the memory system never idles at a unit boundary.
 template <int NHT>
 __global__ __launch_bounds__(kThreads, 2) void indexer_scan_kernel(Params P) {
   __shared__ ScanSmem S;
   S.hist[threadIdx.x] = 0;
-  plan_rows(P, S.rowpre, S.red);   // ends with a barrier
+  plan_rows(P, S);   // ends with a barrier
   const uint32_t U_total = S.rowpre[P.R];
-  for (uint32_t u = blockIdx.x; u < U_total; u += gridDim.x) {
-    const Unit U = decode_unit(P, S.rowpre, u);
-    score_unit<NHT, false>(P, U, S.keys);
+  const uint32_t per = (U_total + gridDim.x - 1) / gridDim.x;
+  uint32_t u = blockIdx.x * per;
+  const uint32_t uend = min(U_total, u + per);
+  if (u >= uend) return;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  bool bad = false;   // a page id out of the pool (flagged once at the end)
+  Unit U = decode_unit(P, S, u);
+  int32_t pid = unit_pages(P, U, S.rowseq[U.row]);
+  QOperand<NHT> Q;
+  load_q<NHT>(P, U.row, Q);
+  int qrow = U.row;
+  HalfRegs b[kRing];
+  bool ok[kRing];
+#pragma unroll
+  for (int k = 0; k < kRing; ++k) ok[k] = fetch_half(P, U, pid, wv + kWaves * k, b[k], &bad);
+  for (;;) {
+    const bool more = u + 1 < uend;
+    // the next unit (the current one again when there is none: its ring
+    // loads then get page id -1 and move nothing)
+    const Unit V = decode_unit(P, S, more ? u + 1 : u);
+    const int32_t pidn = unit_pages(P, V, S.rowseq[V.row]);
+    Unit Vf = V;          // the ring's view of the next unit: no pages when there is none
+    if (!more) Vf.t = -1;
+#pragma unroll
+    for (int k = 0; k < kHalvesPerWave; ++k) {
+      consume_half<NHT, false>(P, U, Q, wv + kWaves * k, b[k % kRing], ok[k % kRing], S.keys);
+      const int kn = k + kRing;
+      if (kn < kHalvesPerWave)
+        ok[k % kRing] = fetch_half(P, U, pid, wv + kWaves * kn, b[k % kRing], &bad);
+      else
+        ok[k % kRing] = fetch_half(P, Vf, pidn, wv + kWaves * (kn - kHalvesPerWave), b[k % kRing], &bad);
+    }
     __syncthreads();
     filter_unit(P, S, U);   // its last barrier orders the key reads before the next unit's writes
+    if (!more) break;
+    if (V.row != qrow) {
+      load_q<NHT>(P, V.row, Q);
+      qrow = V.row;
+    }
+    U = V;
+    pid = pidn;
+    ++u;
   }
+  if (bad && (threadIdx.x & 63) == 0) flag_error(P.hdr, kErrBadPage);
 }
 
 // Test entry: write every score of every row.
 template <int NHT>
 __global__ __launch_bounds__(kThreads, 2) void indexer_dump_kernel(Params P) {
   __shared__ ScanSmem S;
-  plan_rows(P, S.rowpre, S.red);
+  plan_rows(P, S);
   const uint32_t U_total = S.rowpre[P.R];
   for (uint32_t u = blockIdx.x; u < U_total; u += gridDim.x) {
-    const Unit U = decode_unit(P, S.rowpre, u);
+    const Unit U = decode_unit(P, S, u);
     score_unit<NHT, true>(P, U, S.keys);
   }
 }
