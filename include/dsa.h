@@ -110,6 +110,24 @@ int kv_fp8_quant_paged_write(const void* kv_bf16, int64_t n_tokens,
                              int64_t pool_pages, void* stream);
 
 /*
+ * The quantisations of one decode step in a single launch (the fused-prolog
+ * direction of "Lightning Indexer Three-Stream Coordination" and "System-
+ * Level Coordination", Kimi K3.1 Pro Day0 page: the quantisation prolog was
+ * a serial wait before the indexer).  Results are bit-identical to
+ *   mxfp8_quant(q_bf16, q_rows, q_cols, q_fp8, q_e8m0, NULL, NULL, 0)
+ *   mxfp8_quant(k_bf16, n_tokens, 128, NULL, NULL, k_pool, slot_mapping, pool_pages)
+ *   kv_fp8_quant_paged_write(kv_bf16, n_tokens, slot_mapping, kv_pool, pool_pages)
+ * with the same rules for skipped slots.  The K and KV caches share page ids
+ * (one slot_mapping, one pool_pages for both).  n_tokens may be 0 (then the
+ * k/kv/slot/pool arguments may be NULL).
+ */
+int dsa_decode_prolog(const void* q_bf16, int64_t q_rows, int32_t q_cols,
+                      void* q_fp8, void* q_e8m0,
+                      const void* k_bf16, const void* kv_bf16, int64_t n_tokens,
+                      const int64_t* slot_mapping, void* k_pool, void* kv_pool,
+                      int64_t pool_pages, void* stream);
+
+/*
  * Bytes of zero-initialised workspace dsa_indexer_topk needs for R query
  * rows whose block tables have bt_stride entries.
  */

@@ -40,6 +40,7 @@ SIGNATURES = {
     "dsa_version": (_c.c_int, []),
     "mxfp8_quant": (_c.c_int, [_P, _I64, _I32, _P, _P, _P, _P, _I64, _P]),
     "kv_fp8_quant_paged_write": (_c.c_int, [_P, _I64, _P, _P, _I64, _P]),
+    "dsa_decode_prolog": (_c.c_int, [_P, _I64, _I32, _P, _P, _P, _P, _I64, _P, _P, _P, _I64, _P]),
     "dsa_indexer_topk_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
     "dsa_indexer_topk": (_c.c_int, [_P, _P, _P, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _I32,
                                     _P, _P, _P, _SZ, _P]),
@@ -120,6 +121,28 @@ def kv_fp8_quant_paged_write(kv: torch.Tensor, slot_mapping: torch.Tensor, kv_po
     _need(kv_pool, torch.uint8, "kv_pool")
     _check(lib().kv_fp8_quant_paged_write(_ptr(kv), kv.shape[0], _ptr(slot_mapping), _ptr(kv_pool),
                                           kv_pool.shape[0], _stream()), "kv_fp8_quant_paged_write")
+
+
+def decode_prolog(q: torch.Tensor, k_new: torch.Tensor, kv_new: torch.Tensor,
+                  slot_mapping: torch.Tensor, k_pool: torch.Tensor, kv_pool: torch.Tensor,
+                  q_out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """One launch: mxfp8_quant(q) -> (codes, scales), the new indexer keys into
+    k_pool and the new KV rows into kv_pool (pools share page ids)."""
+    _need(q, torch.bfloat16, "q"); _need(k_new, torch.bfloat16, "k_new")
+    _need(kv_new, torch.bfloat16, "kv_new"); _need(slot_mapping, torch.int64, "slot_mapping")
+    _need(k_pool, torch.uint8, "k_pool"); _need(kv_pool, torch.uint8, "kv_pool")
+    if k_pool.shape[0] != kv_pool.shape[0]:
+        raise ValueError("k_pool and kv_pool must have the same number of pages")
+    cols = q.shape[-1]
+    rows = q.numel() // cols if cols else 0
+    if q_out is None:
+        q_out = (torch.empty(q.shape, dtype=torch.uint8, device=q.device),
+                 torch.empty(q.shape[:-1] + (cols // 32,), dtype=torch.uint8, device=q.device))
+    codes, scales = q_out
+    _check(lib().dsa_decode_prolog(_ptr(q), rows, cols, _ptr(codes), _ptr(scales), _ptr(k_new),
+                                   _ptr(kv_new), k_new.shape[0], _ptr(slot_mapping), _ptr(k_pool),
+                                   _ptr(kv_pool), k_pool.shape[0], _stream()), "dsa_decode_prolog")
+    return codes, scales
 
 
 # ------------------------------------------------------------------- indexer

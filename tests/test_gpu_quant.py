@@ -108,3 +108,45 @@ def test_big_pools_sampled(need_gpu, cfg):
     rec = quant.kv_quant(inp["kv"][tok])
     kvp = kvpool.view(npages * 64, 656)[torch.from_numpy(sl).cuda()].cpu().numpy()
     assert np.array_equal(kvp, rec)
+
+
+@pytest.mark.parametrize("cfg", ["tiny_prefill", "decode_8k_needles"])
+def test_decode_prolog_bitwise(need_gpu, cfg):
+    """The one-launch prolog: indexer q codes/scales, K pages and KV records
+    bitwise equal to the oracle's (same skipped-slot rules)."""
+    say(f"[decode prolog] {cfg}")
+    inp = synth.make(cfg)
+    npages = int(inp["total_pages"])
+    R, H = inp["q_idx"].shape[:2]
+    slots = inp["slot_mapping"].copy()
+    slots[1] = -1
+    slots[2] = npages * 64 + 3
+    kpool = torch.zeros((npages, ops.K_PAGE_BYTES), dtype=torch.uint8, device="cuda")
+    kvpool = torch.zeros((npages, ops.KV_PAGE_BYTES), dtype=torch.uint8, device="cuda")
+    codes, scales = ops.decode_prolog(bf16_tensor(inp["q_idx"], "cuda"), bf16_tensor(inp["k_idx"], "cuda"),
+                                      bf16_tensor(inp["kv"], "cuda"), torch.from_numpy(slots).cuda(),
+                                      kpool, kvpool)
+    c_ref, s_ref = quant.mxfp8_quant(inp["q_idx"].reshape(R * H, 128))
+    assert np.array_equal(codes.cpu().numpy().reshape(R * H, 128), c_ref)
+    assert np.array_equal(scales.cpu().numpy().reshape(R * H, 4), s_ref)
+    skip = np.where(slots >= npages * 64, -1, slots)
+    kc, ke = quant.mxfp8_quant(inp["k_idx"])
+    assert np.array_equal(kpool.cpu().numpy(), pools.k_pool_write(kc, ke, skip, npages))
+    kv_ref = pools.kv_pool_write(quant.kv_quant(inp["kv"]), skip, npages)
+    assert np.array_equal(kvpool.cpu().numpy().reshape(npages * 64, 656), kv_ref)
+
+
+def test_decode_prolog_no_new_tokens(need_gpu):
+    say("[decode prolog] queries only")
+    rng = np.random.default_rng(3)
+    xb = _spread_bf16(rng, (8, 64 * 128))
+    kpool = torch.zeros((1, ops.K_PAGE_BYTES), dtype=torch.uint8, device="cuda")
+    kvpool = torch.zeros((1, ops.KV_PAGE_BYTES), dtype=torch.uint8, device="cuda")
+    empty = torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda")
+    codes, scales = ops.decode_prolog(bf16_tensor(xb, "cuda"), empty,
+                                      torch.zeros((0, 576), dtype=torch.bfloat16, device="cuda"),
+                                      torch.zeros((0,), dtype=torch.int64, device="cuda"), kpool, kvpool)
+    c_ref, s_ref = quant.mxfp8_quant(xb)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert int(kpool.sum()) == 0 and int(kvpool.sum()) == 0
