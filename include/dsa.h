@@ -174,6 +174,39 @@ int dsa_indexer_topk(const void* q_fp8, const void* q_e8m0, const float* w,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of zero-initialised workspace dsa_indexer_topk_seq needs for R query
+ * rows of a sequence of n_pages pages.
+ */
+size_t dsa_indexer_topk_seq_workspace_size(int32_t R, int32_t n_pages,
+                                           int32_t H_I, int32_t topk);
+
+/*
+ * dsa_indexer_topk for R query rows that all belong to ONE sequence: a chunk
+ * of a causal prefill (each query scores its own history, "Lightning Indexer
+ * ... scores every causal history position" with the triangular workload of
+ * the chunked-prefill case) or the several query tokens of one sequence.  The
+ * rows are taken in tiles of 8 consecutive rows whose K pages are read once
+ * per tile; tiles are dealt to work-groups longest first in alternating
+ * order, which balances the triangle (the load-balancing concern of the
+ * pages' context-parallel zigzag split, "Adapting and Optimizing Kimi K3.1
+ * Pro for Long-Sequence Inference", applied to work-groups on one GPU).
+ *
+ *   block_table_row [n_pages] int32 page ids of the sequence (n_pages <= 4096)
+ *   row_pos         [R] int32, t of each row (any order; < 0 = no positions)
+ *   other arguments, outputs, status bits and workspace rules as for
+ *   dsa_indexer_topk, with the workspace from
+ *   dsa_indexer_topk_seq_workspace_size.
+ * Scores are computed with the same operations in the same order as
+ * dsa_indexer_topk, so both entry points return identical bits.
+ */
+int dsa_indexer_topk_seq(const void* q_fp8, const void* q_e8m0, const float* w,
+                         const void* k_pool, int64_t pool_pages,
+                         const int32_t* block_table_row, int32_t n_pages,
+                         const int32_t* row_pos, int32_t R, int32_t H_I,
+                         int32_t topk, int32_t* out_idx, float* out_score,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * TEST ONLY: the full score rows of dsa_indexer_topk, computed by the same
  * device code: out_scores[r*ld + s] = I(t,s) for s <= t, -inf for
  * t < s < ld.  Requires ld >= max(row_pos)+1 (positions beyond ld are not

@@ -72,7 +72,7 @@ struct Params {
   int64_t pool_pages;
   const int32_t* bt;
   int32_t bt_stride;
-  const int32_t* row_seq;
+  const int32_t* row_seq;  // null: every row reads block-table row 0
   const int32_t* row_pos;
   int32_t R;
   int32_t H;
@@ -110,7 +110,10 @@ struct SelSmem {
 };
 
 __device__ __forceinline__ void flag_error(uint32_t* hdr, uint32_t bits) {
-  if (hdr) __hip_atomic_fetch_or(&hdr[2], bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // through a global-address-space pointer: a flat atomic here would need an
+  // aperture check
+  typedef __attribute__((address_space(1))) uint32_t guint32;
+  if (hdr) __hip_atomic_fetch_or((guint32*)hdr + 2, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---- block primitives (256 threads) -------------------------------------
@@ -190,7 +193,7 @@ __device__ __forceinline__ void plan_rows(const Params& P, ScanSmem& S) {
     if (r0 + i < P.R) {
       const int t = P.row_pos[r0 + i];
       S.rowt[r0 + i] = t;
-      S.rowseq[r0 + i] = P.row_seq[r0 + i];
+      S.rowseq[r0 + i] = P.row_seq ? P.row_seq[r0 + i] : 0;
       lu += (uint32_t)row_units(t, P.bt_stride);
     }
   }
@@ -315,6 +318,37 @@ __device__ __forceinline__ void load_half(__amdgpu_buffer_rsrc_t rsrc, int half,
   }
 }
 
+// ReLU in one instruction (v_maximum3_f32, the NaN-propagating maximum;
+// fmaxf would add a canonicalising max per element for signalling NaNs).
+// maximum(-0, +0) is +0.
+__device__ __forceinline__ float relu(float x) {
+  return __builtin_elementwise_maximum(x, 0.f);
+}
+
+// Sum over the four 16-lane rows of a wave, every lane receiving the total,
+// associated as (row0 + row1) + (row2 + row3); cross-row moves with
+// v_permlane16_swap / v_permlane32_swap.
+__device__ __forceinline__ float rows_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);   // rows 0,0,2,2 | 1,1,3,3
+  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const unsigned v = __float_as_uint(s);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);   // pairs 01 | 23
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Four per-lane partial sums p[j] (row g holds its share of item j): row g
+// returns item g's total over the four rows, associated exactly as rows_sum.
+__device__ __forceinline__ float rows_sum_scatter(const float (&p)[4]) {
+  const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(p[0]), __float_as_uint(p[1]), false, false);
+  const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(p[2]), __float_as_uint(p[3]), false, false);
+  // rows 0..3: items 0,1,0,1 (x) and 2,3,2,3 (y), each summed over its row pair
+  const float sa = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  const float sb = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+  const auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(sa), __float_as_uint(sb), false, false);
+  return __uint_as_float(z[0]) + __uint_as_float(z[1]);
+}
+
 // Scores of the 32 tokens of one half page; lanes 0..15 end with token
 // 16jj + lane of the half in out[jj].  One scaled FP8 MFMA per head tile
 // and token tile covers all 128 dims.  Head sum: in-lane over the lane's
@@ -336,11 +370,9 @@ __device__ __forceinline__ void score_half(const QOperand<NHT>& Q, const HalfReg
       const v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Q.a[i], kb, zero, 0, 0, 0,
                                                                         Q.s[i], 0, ks);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) part = __builtin_fmaf(Q.w[i][c], fmaxf(acc[c], 0.f), part);
+      for (int c = 0; c < 4; ++c) part = __builtin_fmaf(Q.w[i][c], relu(acc[c]), part);
     }
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
-    out[jj] = part;
+    out[jj] = rows_sum(part);
   }
 }
 
@@ -411,7 +443,7 @@ template <int NHT, bool DUMP>
 __device__ __forceinline__ void score_unit(const Params& P, const Unit& U, uint32_t* keys) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   bool bad = false;
-  const int32_t pid = unit_pages(P, U, P.row_seq[U.row]);
+  const int32_t pid = unit_pages(P, U, P.row_seq ? P.row_seq[U.row] : 0);
   // the query loads go before the ring: they are then older than every
   // ring load
   QOperand<NHT> Q;
@@ -1141,6 +1173,287 @@ __global__ __launch_bounds__(kSelThreads, 1) void indexer_select_kernel(Params P
   seg_emit(P, S, row, units_r, n_c, sg, T, ties);
 }
 
+// ---- row-tiled scan: query rows of one sequence share the K stream -------------
+//
+// The rows of a chunked prefill (or the several query tokens of one sequence)
+// read the same K pages.  A work-group takes a tile of kTileRows consecutive
+// rows; each page is copied once into an LDS ring (global_load_lds, kPgRing
+// pages, kPgAhead ahead; each lane's 16-byte source is chosen so that token
+// rows land 144 bytes apart) and every wave scores it for its two rows, whose
+// query operands stay in registers.  Lane l ends a page with the key of
+// position 64p + l of each of its rows, so after the 16 pages of a unit a
+// row's 1024 keys sit 16 per lane in position order: the wave runs the
+// unit's local filter itself (a wave-private LDS histogram, no work-group
+// barrier) and writes the candidates, count and edge exactly as the per-row
+// scan does.  A score takes the per-row scan's operations in the same order,
+// so both paths produce the same bits and the same selection.
+//
+// Tiles are dealt to work-groups in rounds, longest first, alternating the
+// direction every round, so a work-group's tiles pair long with short rows of
+// a triangular (causal) chunk.
+
+constexpr int kTileRows = 8;
+constexpr int kTileRowsPerWave = kTileRows / kWaves;   // 2
+constexpr int kPgRing = 4;                             // page buffers
+constexpr int kPgAhead = kPgRing - 1;                  // pages copied ahead
+// A page in LDS: token rows of 144 bytes (128 code bytes + 16 bytes of
+// padding, so that the 16 token rows one MFMA operand reads fall on distinct
+// banks), then the 256 scale bytes.  Counted in 16-byte granules:
+constexpr int kTokGran = kIdxDim / 16 + 1;             // 9 per token row
+constexpr int kScaleGran0 = kPage * kTokGran;          // 576: first scale granule
+constexpr int kPgGran = kScaleGran0 + kPage * 4 / 16;  // 592
+constexpr int kPgBlocks = (kPgGran + 63) / 64;         // 10 one-KB copy blocks per page
+constexpr int kPgDmaPerWave = (kPgBlocks + kWaves - 1) / kWaves;   // 3
+constexpr int kPgBytes = kPgBlocks * 1024;
+constexpr int kTileMaxPages = 4096;                    // page ids of a tile held in LDS
+constexpr int kSeqChunkRows = 4096;                    // rows per launch of the tiled path
+static_assert(kTileRowsPerWave == 2, "two rows per wave");
+static_assert(kPgDmaPerWave * kWaves >= kPgBlocks, "the copy blocks cover a page");
+static_assert(kUnitPages == 16, "16 pages per unit: one key per lane and page");
+
+struct TileSmem {
+  uint8_t ring[kPgRing][kPgBytes];
+  uint8_t junk[1024];                 // target of padding copies
+  int32_t pt[kTileMaxPages];          // page id per page of the tile, -1 = absent
+  uint32_t hist[kWaves][kFBins];      // wave-private filter histograms, zero between uses
+};
+
+// LDS byte address of a shared object: the low half of its flat address in
+// the shared aperture (no address-space cast, hence no null check).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// 16 bytes per lane from global memory into LDS at lds_base + 16*lane.
+// Inline assembly so that the compiler pairs it with no automatic wait;
+// completion is tracked by the explicit vmcnt waits of the page loop.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// filter_threshold for one wave and its private histogram: the bin b where
+// the count of keys in bins >= b first reaches `need` (from the top) and the
+// count in bins above it; every bin is cleared.  False if the histogram holds
+// fewer than `need` keys.
+__device__ __forceinline__ bool wave_hist_find(TileSmem& S, int wv, uint32_t need, uint32_t* bin,
+                                               uint32_t* above) {
+  uint32_t* hist = S.hist[wv];
+  const int lane = threadIdx.x & 63;
+  const int top = kFBins - 1 - 4 * lane;            // this lane's bins: top .. top-3
+  uint32_t c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[i] = hist[top - i];
+    hist[top - i] = 0;
+  }
+  const uint32_t mine = c[0] + c[1] + c[2] + c[3];
+  const uint32_t incl = wave_incl_scan(mine);
+  uint32_t run = incl - mine;
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(run < need && incl >= need);
+  if (hit == 0) return false;
+  const int src = __builtin_ctzll(hit);
+  uint32_t b = (uint32_t)(top - 3);
+  bool done = false;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    if (!done && run + c[i] >= need) {
+      b = (uint32_t)(top - i);
+      done = true;
+    }
+    if (!done) run += c[i];
+  }
+  *bin = (uint32_t)__builtin_amdgcn_readlane((int)b, src);
+  *above = (uint32_t)__builtin_amdgcn_readlane((int)run, src);
+  return true;
+}
+
+// Local filter of unit u of one row (keys k[i] = position 64(16u+i) + lane),
+// the per-row scan's filter_unit done by one wave: same quota, same edge,
+// same candidates in position order.  Every call issues exactly
+// kTileStores buffer stores (lanes with nothing to write address out of
+// range), so the page loop can count them in its waits.
+constexpr int kTileStores = kUnitPages + 2;
+__device__ __forceinline__ void filter_wave(const Params& P, TileSmem& S, int wv, int row, bool live_row,
+                                            int t, int np_row, int u, const uint32_t (&k)[kUnitPages]) {
+  const int lane = threadIdx.x & 63;
+  const int pg0 = kUnitPages * u;
+  const int npg = min(np_row, pg0 + kUnitPages) - pg0;
+  const bool live = live_row && npg > 0;
+  uint32_t edge = 0;
+  const uint32_t quota = unit_quota(t, P.topk);
+  if (live && quota < (uint32_t)(npg * kPage)) {
+#pragma unroll
+    for (int i = 0; i < kUnitPages; ++i)
+      if (k[i]) atomicAdd(&S.hist[wv][k[i] >> 24], 1u);
+    uint32_t b1, above;
+    if (wave_hist_find(S, wv, quota, &b1, &above)) {   // else: fewer than quota keys, keep all
+#pragma unroll
+      for (int i = 0; i < kUnitPages; ++i)
+        if (k[i] && (k[i] >> 24) == b1) atomicAdd(&S.hist[wv][(k[i] >> 16) & 0xFFu], 1u);
+      uint32_t b2, above2;
+      wave_hist_find(S, wv, quota - above, &b2, &above2);
+      edge = (b1 << 24) | (b2 << 16);
+    }
+  }
+  const int64_t slice = ((int64_t)(live ? row : 0) * P.bt_stride + pg0) * kPage;
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      P.cand + slice, (short)0, live ? kUnitTok * 8 : 0, kRawBufferWord3);
+  const uint64_t below = lanemask_lt();
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int i = 0; i < kUnitPages; ++i) {
+    const bool kept = live && k[i] != 0u && k[i] >= edge;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(kept);
+    const uint32_t off = cnt + (uint32_t)__builtin_popcountll(m & below);
+    const v2u v = {k[i], (uint32_t)((pg0 + i) * kPage + lane)};
+    __builtin_amdgcn_raw_buffer_store_b64(v, rc, kept ? off * 8u : 0x7FFFFFF0u, 0, 0);
+    cnt += (uint32_t)__builtin_popcountll(m);
+  }
+  const int64_t us = (int64_t)(live ? row : 0) * P.upr;
+  // descriptors stay wave-uniform (a per-lane one would be split into a loop)
+  const __amdgpu_buffer_rsrc_t rn = __builtin_amdgcn_make_buffer_rsrc(P.ucount + us, (short)0, live ? P.upr * 4 : 0, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(P.uedge + us, (short)0, live ? P.upr * 4 : 0, kRawBufferWord3);
+  const uint32_t uoff = lane == 0 ? (uint32_t)u * 4u : 0x7FFFFFF0u;
+  __builtin_amdgcn_raw_buffer_store_b32(cnt, rn, uoff, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(edge, re, uoff, 0, 0);
+}
+
+// One row's per-lane share of the score of a token tile, before the sum over
+// the four rows (the per-row scan's score_half for one jj).
+template <int NHT>
+__device__ __forceinline__ float tile_part(const QOperand<NHT>& Q, const v8i& kb, int ks) {
+  float part = 0.f;
+#pragma unroll
+  for (int i = 0; i < NHT; ++i) {
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    const v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Q.a[i], kb, zero, 0, 0, 0,
+                                                                      Q.s[i], 0, ks);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) part = __builtin_fmaf(Q.w[i][c], relu(acc[c]), part);
+  }
+  return part;
+}
+
+template <int NHT>
+__global__ __launch_bounds__(kThreads, 2) void indexer_tile_kernel(Params P) {
+  __shared__ __attribute__((aligned(16))) TileSmem S;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hr = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) S.hist[wv][lane + 64 * i] = 0;
+  const uint32_t ring0 = lds_addr(S.ring), junk = lds_addr(S.junk);
+  const int ntiles = (P.R + kTileRows - 1) / kTileRows;
+  bool bad = false;
+  for (int round = 0;; ++round) {
+    const int slot = round * (int)gridDim.x +
+                     ((round & 1) ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    if (slot >= ntiles) break;
+    const int r0 = (ntiles - 1 - slot) * kTileRows;   // longest (last) tiles first
+    // rows of the tile: lane i < 8 holds row r0+i's position and page count
+    const bool rin = lane < kTileRows && r0 + lane < P.R;
+    const int t_l = rin ? P.row_pos[r0 + lane] : -1;
+    const int np_l = rin ? row_pages(t_l, P.bt_stride) : 0;
+    const int npt = __builtin_amdgcn_readlane((int)wave_incl_max((uint32_t)np_l), 63);
+    const int ra = r0 + kTileRowsPerWave * wv, rb = ra + 1;
+    const bool la = ra < P.R, lb = rb < P.R;
+    const int ta = __builtin_amdgcn_readlane(t_l, kTileRowsPerWave * wv);
+    const int tb = __builtin_amdgcn_readlane(t_l, kTileRowsPerWave * wv + 1);
+    const int npa = __builtin_amdgcn_readlane(np_l, kTileRowsPerWave * wv);
+    const int npb = __builtin_amdgcn_readlane(np_l, kTileRowsPerWave * wv + 1);
+    // every wave is done with the previous tile's ring and page ids
+    __syncthreads();
+    for (int p = tid; p < npt; p += kThreads) {
+      const int32_t id = P.bt[p];
+      const bool ok = id >= 0 && (int64_t)id < P.pool_pages;
+      bad |= !ok;
+      S.pt[p] = ok ? id : -1;
+    }
+    QOperand<NHT> Qa, Qb;
+    load_q<NHT>(P, la ? ra : r0, Qa);
+    load_q<NHT>(P, lb ? rb : r0, Qb);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): nothing but page copies outstanding below
+    __syncthreads();
+    // Units are visited in rotated order, starting at a phase that depends on
+    // the work-group's index within its XCD: the 64 work-groups of an XCD then
+    // stream 8 different pages at any time instead of all hammering the same
+    // L2 lines.  Logical page q is page 16*((q/16 + u0) % nun) + q%16.
+    const int nun = (npt + kUnitPages - 1) / kUnitPages;
+    const int u0 = (int)(((blockIdx.x >> 3) & 7) * (uint32_t)nun / 8u);
+    auto phys = [&](int q) {
+      const int uq = q / kUnitPages + u0;
+      return kUnitPages * (uq >= nun ? uq - nun : uq) + q % kUnitPages;
+    };
+    auto issue_page = [&](int q) {
+      const int pq = phys(q);
+      const bool live = q < kUnitPages * nun && pq < npt;          // uniform
+      const int32_t id = __builtin_amdgcn_readfirstlane(live ? S.pt[pq] : -1);
+      const uint8_t* page = P.kpool + (int64_t)(id >= 0 ? id : 0) * kKPageBytes;
+      const uint32_t base = ring0 + (uint32_t)((q % kPgRing) * kPgBytes);
+#pragma unroll
+      for (int m = 0; m < kPgDmaPerWave; ++m) {
+        const int j = wv + kWaves * m;                             // copy block
+        const int gs = 64 * j + lane;                              // LDS granule of this lane
+        const int tok = gs / kTokGran, c = gs - tok * kTokGran;
+        // source granule: a code granule, a scale granule, or (padding) any
+        const int src_g = gs < kScaleGran0 ? (c < kIdxDim / 16 ? tok * (kIdxDim / 16) + c : 0)
+                                           : (gs < kPgGran ? kKScaleOff / 16 + (gs - kScaleGran0) : 0);
+        dma16(page + 16 * src_g, live && j < kPgBlocks ? base + (uint32_t)(j * 1024) : junk);
+      }
+    };
+#pragma unroll
+    for (int q = 0; q < kPgAhead; ++q) issue_page(q);
+    for (int uu = 0; uu < nun; ++uu) {
+      const int u = uu + u0 >= nun ? uu + u0 - nun : uu + u0;   // physical unit
+      uint32_t ka[kUnitPages], kb[kUnitPages];
+#pragma unroll
+      for (int pi = 0; pi < kUnitPages; ++pi) {
+        ka[pi] = 0u;
+        kb[pi] = 0u;
+        const int L = kUnitPages * uu + pi;                        // logical page
+        const int p = kUnitPages * u + pi;                         // physical page
+        // page L has landed once only the kPgAhead-1 younger pages (and, just
+        // after a unit's filter, its kTileStores stores per row) remain.
+        // Every logical page takes this step, present or not, so that each
+        // step consumes exactly one page's copies.
+        if (uu > 0 && pi < kPgAhead)
+          asm volatile("s_waitcnt vmcnt(42)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(6)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        issue_page(L + kPgAhead);
+        if (p >= npt) continue;                                    // uniform: past the tile
+        const uint8_t* pg = S.ring[L % kPgRing];
+        const bool pok = S.pt[p] >= 0;
+        float pa[4], pb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint8_t* tok = pg + (16 * j + hr) * (16 * kTokGran) + 16 * g;
+          const uint4 lo = *reinterpret_cast<const uint4*>(tok);
+          const uint4 hi = *reinterpret_cast<const uint4*>(tok + 64);
+          const int ks = (int)pg[16 * kScaleGran0 + (16 * j + hr) * 4 + g];
+          const v8i kv = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          pa[j] = tile_part<NHT>(Qa, kv, ks);
+          pb[j] = tile_part<NHT>(Qb, kv, ks);
+        }
+        // lane group g receives token tile g: lane l holds position 64p + l
+        const float sa = rows_sum_scatter(pa), sb = rows_sum_scatter(pb);
+        const int pos = p * kPage + lane;
+        ka[pi] = pok && pos <= ta ? score_key(sa) : 0u;
+        kb[pi] = pok && pos <= tb ? score_key(sb) : 0u;
+      }
+      filter_wave(P, S, wv, ra, la, ta, npa, u, ka);
+      filter_wave(P, S, wv, rb, lb, tb, npb, u, kb);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // the padding copies past the tile have landed
+  }
+  if (bad && tid == 0) flag_error(P.hdr, kErrBadPage);
+}
+static_assert(kTileRowsPerWave * kTileStores + kPgDmaPerWave * (kPgAhead - 1) == 42,
+              "the page loop's wait after a filter");
+static_assert(kPgDmaPerWave * (kPgAhead - 1) == 6, "the page loop's wait");
+
 // ---- host side ----------------------------------------------------------------
 
 struct Layout {
@@ -1171,6 +1484,15 @@ void* pick_kernel(int nht, KernelKind kind) {
     case 2: return kind == kScan ? (void*)&indexer_scan_kernel<2> : kind == kSelect ? (void*)&indexer_select_kernel<2> : (void*)&indexer_dump_kernel<2>;
     case 3: return kind == kScan ? (void*)&indexer_scan_kernel<3> : kind == kSelect ? (void*)&indexer_select_kernel<3> : (void*)&indexer_dump_kernel<3>;
     default: return kind == kScan ? (void*)&indexer_scan_kernel<4> : kind == kSelect ? (void*)&indexer_select_kernel<4> : (void*)&indexer_dump_kernel<4>;
+  }
+}
+
+void* pick_tile_kernel(int nht) {
+  switch (nht) {
+    case 1: return (void*)&indexer_tile_kernel<1>;
+    case 2: return (void*)&indexer_tile_kernel<2>;
+    case 3: return (void*)&indexer_tile_kernel<3>;
+    default: return (void*)&indexer_tile_kernel<4>;
   }
 }
 
@@ -1320,4 +1642,61 @@ extern "C" int dsa_indexer_scores(const void* q_fp8, const void* q_e8m0, const f
   P.ld = ld;
   P.hdr = nullptr;   // the score dump uses no workspace
   return run(P, true, s);
+}
+
+extern "C" size_t dsa_indexer_topk_seq_workspace_size(int32_t R, int32_t n_pages, int32_t H_I,
+                                                      int32_t topk) {
+  (void)H_I;
+  (void)topk;
+  if (R <= 0 || n_pages <= 0) return 256;
+  const int64_t rows = std::min<int64_t>(R, kSeqChunkRows);
+  return layout_for(rows, n_pages).total;
+}
+
+extern "C" int dsa_indexer_topk_seq(const void* q_fp8, const void* q_e8m0, const float* w,
+                                    const void* k_pool, int64_t pool_pages,
+                                    const int32_t* block_table_row, int32_t n_pages,
+                                    const int32_t* row_pos, int32_t R, int32_t H_I, int32_t topk,
+                                    int32_t* out_idx, float* out_score, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (!q_fp8 || !q_e8m0 || !w || !k_pool || !block_table_row || !row_pos || !out_idx)
+    return DSA_ERR_INVALID_ARG;
+  if (R < 0 || n_pages <= 0 || pool_pages <= 0) return DSA_ERR_INVALID_ARG;
+  if (H_I < 1 || H_I > DSA_MAX_INDEX_HEADS) return DSA_ERR_UNSUPPORTED;
+  if (n_pages > kTileMaxPages) return DSA_ERR_UNSUPPORTED;
+  if (topk < 1 || topk > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
+  if (R == 0) return DSA_OK;
+  const int64_t rows = std::min<int64_t>(R, kSeqChunkRows);
+  const Layout L = layout_for(rows, n_pages);
+  if (workspace == nullptr || workspace_bytes < L.total) return DSA_ERR_WORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipStream_t s = dsa_host::as_stream(stream);
+  const int nht = (H_I + 15) / 16;
+  void* tk = pick_tile_kernel(nht);
+  void* sel = pick_kernel(nht, kSelect);
+  const int cap = resident_capacity(tk, 12 + nht - 1);
+  if (cap <= 0) return DSA_ERR_HIP;
+  for (int r0 = 0; r0 < R; r0 += kSeqChunkRows) {
+    const int rn = std::min(kSeqChunkRows, R - r0);
+    Params P = base_params(q_fp8, q_e8m0, w, k_pool, pool_pages, block_table_row, n_pages, nullptr,
+                           row_pos + r0, rn, H_I);
+    P.q += (int64_t)r0 * H_I * kIdxDim;
+    P.qs += (int64_t)r0 * H_I * 4;
+    P.w += (int64_t)r0 * H_I;
+    P.topk = topk;
+    P.out_idx = out_idx + (int64_t)r0 * topk;
+    P.out_score = out_score ? out_score + (int64_t)r0 * topk : nullptr;
+    P.hdr = reinterpret_cast<uint32_t*>(ws + L.hdr);
+    P.ucount = reinterpret_cast<uint32_t*>(ws + L.ucount);
+    P.uedge = reinterpret_cast<uint32_t*>(ws + L.uedge);
+    P.cand = reinterpret_cast<uint2*>(ws + L.cand);
+    const int ntiles = (rn + kTileRows - 1) / kTileRows;
+    const int G = std::min(cap, ntiles);
+    void* args[] = {&P};
+    if (hipLaunchKernel(tk, dim3((unsigned)G), dim3(kThreads), args, 0, s) != hipSuccess)
+      return DSA_ERR_HIP;
+    if (hipLaunchKernel(sel, dim3((unsigned)rn), dim3(kSelThreads), args, 0, s) != hipSuccess)
+      return DSA_ERR_HIP;
+  }
+  return DSA_OK;
 }

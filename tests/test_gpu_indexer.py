@@ -187,3 +187,72 @@ def test_concentrated_topk_takes_exact_fallback(need_gpu):
     check_topk_row(idx[0], sc[0], ora, st.topk, t)
     assert np.array_equal(idx[0], exact_topk_of(scores[0], st.topk))
     assert np.sum((idx[0] >= 3000) & (idx[0] < 5100)) > 1900
+
+
+def _seq_topk(st, q_fp8=None, q_e8m0=None, w=None, row_pos=None, topk=None, workspace=None):
+    seqs = np.unique(st.inp["row_seq"])
+    assert len(seqs) == 1, "one sequence"
+    bt_row = st.block_table[int(seqs[0])].contiguous()
+    return ops.dsa_indexer_topk_seq(st.q_fp8 if q_fp8 is None else q_fp8,
+                                    st.q_e8m0 if q_e8m0 is None else q_e8m0,
+                                    st.w if w is None else w, st.k_pool, bt_row,
+                                    st.row_pos if row_pos is None else row_pos,
+                                    st.topk if topk is None else topk, workspace=workspace)
+
+
+@pytest.mark.parametrize("cfg", ["tiny_prefill", "decode_8k_needles", "prefill_chunk_8k_of_128k"])
+def test_seq_path_matches_per_row(need_gpu, cfg):
+    """The row-tiled entry point returns the per-row entry point's bits
+    (indices and scores) on every row, and passes the oracle rule."""
+    st = state(cfg)
+    say(f"[indexer seq] {cfg} R={st.R}")
+    a_idx, a_sc = st.indexer()
+    b_idx, b_sc = _seq_topk(st)
+    torch.cuda.synchronize()
+    assert torch.equal(a_idx, b_idx)
+    assert torch.equal(a_sc, b_sc)
+    o = Oracle(st.inp)
+    rows = list(range(st.R)) if st.R <= 64 else _rows_for(cfg, st.R)
+    b_idx, b_sc = b_idx.cpu().numpy(), b_sc.cpu().numpy()
+    for r in (rows if st.R <= 64 else rows[:4]):   # bit-equality above covers every row
+        check_topk_row(b_idx[r], b_sc[r], o.topk(r), st.topk, int(st.inp["row_pos"][r]))
+    o.drop_cache()
+
+
+def test_seq_path_ragged_rows(need_gpu):
+    """Partial last tile, rows with t < 0, rows out of order, short rows and a
+    row past the cache: bit-equal to the per-row path."""
+    st = state("tiny_prefill")
+    say("[indexer seq] ragged rows")
+    rng = np.random.default_rng(11)
+    R = 37
+    pos = rng.integers(-1, 512, size=R).astype(np.int32)
+    pos[0], pos[1], pos[2], pos[5] = -1, 511, 0, 2000
+    rp = torch.from_numpy(pos).cuda()
+    q, qs, w = st.q_fp8[:R].contiguous(), st.q_e8m0[:R].contiguous(), st.w[:R].contiguous()
+    rs = torch.zeros(R, dtype=torch.int32, device="cuda")
+    for K in (st.topk, 1, 700):
+        a_idx, a_sc = ops.dsa_indexer_topk(q, qs, w, st.k_pool, st.block_table, rs, rp, K)
+        b_idx, b_sc = _seq_topk(st, q, qs, w, rp, K)
+        torch.cuda.synchronize()
+        assert torch.equal(a_idx, b_idx), f"K={K}"
+        assert torch.equal(a_sc, b_sc), f"K={K}"
+
+
+def test_seq_path_exact_fallback(need_gpu):
+    """The rescoring path of the selection (a unit holding far more than its
+    quota) through the row-tiled entry point: same bits as the per-row path,
+    status bit 3 set."""
+    say("[indexer seq] concentrated Top-K (rescore path)")
+    inp = dict(synth.make("decode_8k_needles", with_sfa=False))
+    inp["w"] = np.abs(inp["w"])
+    k = inp["k_idx"].copy()
+    k[3000:5100] = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(k[3000:5100]) * np.float32(8))
+    inp["k_idx"] = k
+    st = DeviceState(inp, with_sfa=False)
+    a_idx, a_sc = st.indexer()
+    ws = ops.indexer_seq_workspace(st.R, st.block_table.shape[1], st.H_I, st.topk)
+    b_idx, b_sc = _seq_topk(st, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a_idx, b_idx) and torch.equal(a_sc, b_sc)
+    assert (int(ws.view(torch.int32)[2].item()) & 8) != 0
