@@ -349,6 +349,36 @@ __device__ __forceinline__ float rows_sum_scatter(const float (&p)[4]) {
   return __uint_as_float(z[0]) + __uint_as_float(z[1]);
 }
 
+// One head tile's terms of a lane's weighted ReLU sum: for the lane's four
+// heads c of head tile i, p += w * ReLU(S), a chain of FMAs (head tile 0
+// starts the chain with a product).
+template <int NHT>
+__device__ __forceinline__ float head_acc(const QOperand<NHT>& Q, int i, const v4f& acc, float p) {
+  p = i == 0 ? Q.w[0][0] * relu(acc[0]) : __builtin_fmaf(Q.w[i][0], relu(acc[0]), p);
+#pragma unroll
+  for (int c = 1; c < 4; ++c) p = __builtin_fmaf(Q.w[i][c], relu(acc[c]), p);
+  return p;
+}
+
+// One scaled FP8 MFMA: head tile i of Q against a token tile (formats 0 / 0:
+// E4M3 for both operands; scale byte 0 of each lane).
+template <int NHT>
+__device__ __forceinline__ v4f head_mfma(const QOperand<NHT>& Q, int i, const v8i& kb, int ks) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Q.a[i], kb, zero, 0, 0, 0, Q.s[i], 0, ks);
+}
+
+// A lane's share of the weighted ReLU sum over the heads of one token tile:
+// one chain over head tiles i = 0..NHT-1 and heads c = 0..3.  Every scoring
+// path takes these operations in this order, so all produce the same bits.
+template <int NHT>
+__device__ __forceinline__ float head_part(const QOperand<NHT>& Q, const v8i& kb, int ks) {
+  float p = 0.f;
+#pragma unroll
+  for (int i = 0; i < NHT; ++i) p = head_acc(Q, i, head_mfma(Q, i, kb, ks), p);
+  return p;
+}
+
 // Scores of the 32 tokens of one half page; lanes 0..15 end with token
 // 16jj + lane of the half in out[jj].  One scaled FP8 MFMA per head tile
 // and token tile covers all 128 dims.  Head sum: in-lane over the lane's
@@ -362,17 +392,7 @@ __device__ __forceinline__ void score_half(const QOperand<NHT>& Q, const HalfReg
     const v8i kb = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     const int ks = (int)hr.s[jj];
-    float part = 0.f;
-#pragma unroll
-    for (int i = 0; i < NHT; ++i) {
-      const v4f zero = {0.f, 0.f, 0.f, 0.f};
-      // formats 0 / 0: E4M3 for both operands; scale byte 0 of each lane
-      const v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Q.a[i], kb, zero, 0, 0, 0,
-                                                                        Q.s[i], 0, ks);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) part = __builtin_fmaf(Q.w[i][c], relu(acc[c]), part);
-    }
-    out[jj] = rows_sum(part);
+    out[jj] = rows_sum(head_part<NHT>(Q, kb, ks));
   }
 }
 
@@ -1183,10 +1203,17 @@ __global__ __launch_bounds__(kSelThreads, 1) void indexer_select_kernel(Params P
 // query operands stay in registers.  Lane l ends a page with the key of
 // position 64p + l of each of its rows, so after the 16 pages of a unit a
 // row's 1024 keys sit 16 per lane in position order: the wave runs the
-// unit's local filter itself (a wave-private LDS histogram, no work-group
-// barrier) and writes the candidates, count and edge exactly as the per-row
-// scan does.  A score takes the per-row scan's operations in the same order,
-// so both paths produce the same bits and the same selection.
+// unit's local filter itself (a bitwise search for the edge with ballot
+// counts, no LDS, no work-group barrier) and writes the candidates, count
+// and edge in the per-row scan's layout.  Its edge never exceeds the unit's
+// quota-th largest key, as the per-row filter's does not, though the two
+// edges may differ.  A score takes the per-row scan's operations in the
+// same order, so both paths produce the same bits, and the exact selection
+// the same Top-K.
+//
+// The scoring of a page is software-pipelined: the next scaled MFMA is
+// issued before the ReLU/FMA chain reads the previous one, so the matrix
+// and vector units overlap.
 //
 // Tiles are dealt to work-groups in rounds, longest first, alternating the
 // direction every round, so a work-group's tiles pair long with short rows of
@@ -1215,7 +1242,6 @@ struct TileSmem {
   uint8_t ring[kPgRing][kPgBytes];
   uint8_t junk[1024];                 // target of padding copies
   int32_t pt[kTileMaxPages];          // page id per page of the tile, -1 = absent
-  uint32_t hist[kWaves][kFBins];      // wave-private filter histograms, zero between uses
 };
 
 // LDS byte address of a shared object: the low half of its flat address in
@@ -1232,81 +1258,102 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
                : "memory", "m0");
 }
 
-// filter_threshold for one wave and its private histogram: the bin b where
-// the count of keys in bins >= b first reaches `need` (from the top) and the
-// count in bins above it; every bin is cleared.  False if the histogram holds
-// fewer than `need` keys.
-__device__ __forceinline__ bool wave_hist_find(TileSmem& S, int wv, uint32_t need, uint32_t* bin,
-                                               uint32_t* above) {
-  uint32_t* hist = S.hist[wv];
-  const int lane = threadIdx.x & 63;
-  const int top = kFBins - 1 - 4 * lane;            // this lane's bins: top .. top-3
-  uint32_t c[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    c[i] = hist[top - i];
-    hist[top - i] = 0;
-  }
-  const uint32_t mine = c[0] + c[1] + c[2] + c[3];
-  const uint32_t incl = wave_incl_scan(mine);
-  uint32_t run = incl - mine;
-  const uint64_t hit = __builtin_amdgcn_ballot_w64(run < need && incl >= need);
-  if (hit == 0) return false;
-  const int src = __builtin_ctzll(hit);
-  uint32_t b = (uint32_t)(top - 3);
-  bool done = false;
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    if (!done && run + c[i] >= need) {
-      b = (uint32_t)(top - i);
-      done = true;
-    }
-    if (!done) run += c[i];
-  }
-  *bin = (uint32_t)__builtin_amdgcn_readlane((int)b, src);
-  *above = (uint32_t)__builtin_amdgcn_readlane((int)run, src);
-  return true;
+__device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
+  return max(min(a, b), min(max(a, b), c));   // one v_med3_u32
 }
 
-// Local filter of unit u of one row (keys k[i] = position 64(16u+i) + lane),
-// the per-row scan's filter_unit done by one wave: same quota, same edge,
-// same candidates in position order.  Every call issues exactly
-// kTileStores buffer stores (lanes with nothing to write address out of
-// range), so the page loop can count them in its waits.
+// The three largest of a lane's keys, m[0] >= m[1] >= m[2] (0 = none).
+__device__ __forceinline__ void lane_top3(const uint32_t (&k)[kUnitPages], uint32_t (&m)[3]) {
+  m[0] = m[1] = m[2] = 0u;
+#pragma unroll
+  for (int i = 0; i < kUnitPages; ++i) {
+    m[2] = umed3(m[1], m[2], k[i]);
+    m[1] = umed3(m[0], m[1], k[i]);
+    m[0] = max(m[0], k[i]);
+  }
+}
+
+// Edges of two rows' units (values va, vb: D per lane over the wave): the
+// largest key T with zero low 16 bits such that at least `need` of the
+// values are >= T, found bit by bit from the top with ballot counts (no
+// memory traffic, no atomics); 0 when fewer than `need` values reach
+// 2^16.  The values are the unit's keys or a subset of them, so at least
+// `need` of the unit's keys are >= T: T never exceeds the unit's need-th
+// largest key.
+template <int D>
+__device__ __forceinline__ void key_floor2(const uint32_t (&va)[D], const uint32_t (&vb)[D],
+                                           uint32_t na, uint32_t nb, uint32_t* ta, uint32_t* tb) {
+  uint32_t a = 0u, b = 0u;
+#pragma unroll
+  for (int bit = 31; bit >= 16; --bit) {
+    const uint32_t ca = a | (1u << bit), cb = b | (1u << bit);
+    uint32_t sa = 0u, sb = 0u;
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      sa += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(va[i] >= ca));
+      sb += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(vb[i] >= cb));
+    }
+    if (sa >= na) a = ca;
+    if (sb >= nb) b = cb;
+  }
+  *ta = a;
+  *tb = b;
+}
+
+// Local filter edges of unit u for a wave's two rows (keys k[i] = position
+// 64(16u+i) + lane).  A unit keeps every key >= its edge: at least its
+// quota of keys (all of them when it has no more than the quota).  With a
+// quota of at most 192 the search runs over each lane's three largest keys,
+// a subset that holds the unit's quota largest keys unless a lane holds
+// more than three of them (then the edge is lower and more keys are kept).
+constexpr uint32_t kTop3Quota = 3 * 64;
+__device__ __forceinline__ void tile_edges(const Params& P, int u, bool la, int ta, int npa,
+                                           const uint32_t (&ka)[kUnitPages], bool lb, int tb,
+                                           int npb, const uint32_t (&kb)[kUnitPages],
+                                           uint32_t* ea, uint32_t* eb) {
+  const int pg0 = kUnitPages * u;
+  const int ga = min(npa, pg0 + kUnitPages) - pg0, gb = min(npb, pg0 + kUnitPages) - pg0;
+  const uint32_t qa = unit_quota(ta, P.topk), qb = unit_quota(tb, P.topk);
+  // need = ~0: no filtering for that row (edge 0)
+  const uint32_t na = la && ga > 0 && qa < (uint32_t)(ga * kPage) ? qa : 0xFFFFFFFFu;
+  const uint32_t nb = lb && gb > 0 && qb < (uint32_t)(gb * kPage) ? qb : 0xFFFFFFFFu;
+  *ea = *eb = 0u;
+  if (na == 0xFFFFFFFFu && nb == 0xFFFFFFFFu) return;
+  if ((na <= kTop3Quota || na == 0xFFFFFFFFu) && (nb <= kTop3Quota || nb == 0xFFFFFFFFu)) {
+    uint32_t ma[3], mb[3];
+    lane_top3(ka, ma);
+    lane_top3(kb, mb);
+    key_floor2<3>(ma, mb, na, nb, ea, eb);
+  } else {
+    key_floor2<kUnitPages>(ka, kb, na, nb, ea, eb);
+  }
+}
+
+// Candidates of unit u of one row: keys >= edge, in position order, then
+// the unit's count and edge.  Every call issues exactly kTileStores buffer
+// stores (lanes with nothing to write address out of range), so the page
+// loop can count them in its waits.
 constexpr int kTileStores = kUnitPages + 2;
-__device__ __forceinline__ void filter_wave(const Params& P, TileSmem& S, int wv, int row, bool live_row,
-                                            int t, int np_row, int u, const uint32_t (&k)[kUnitPages]) {
+__device__ __forceinline__ void emit_wave(const Params& P, int row, bool live_row, int np_row, int u,
+                                          const uint32_t (&k)[kUnitPages], uint32_t edge) {
   const int lane = threadIdx.x & 63;
   const int pg0 = kUnitPages * u;
-  const int npg = min(np_row, pg0 + kUnitPages) - pg0;
-  const bool live = live_row && npg > 0;
-  uint32_t edge = 0;
-  const uint32_t quota = unit_quota(t, P.topk);
-  if (live && quota < (uint32_t)(npg * kPage)) {
-#pragma unroll
-    for (int i = 0; i < kUnitPages; ++i)
-      if (k[i]) atomicAdd(&S.hist[wv][k[i] >> 24], 1u);
-    uint32_t b1, above;
-    if (wave_hist_find(S, wv, quota, &b1, &above)) {   // else: fewer than quota keys, keep all
-#pragma unroll
-      for (int i = 0; i < kUnitPages; ++i)
-        if (k[i] && (k[i] >> 24) == b1) atomicAdd(&S.hist[wv][(k[i] >> 16) & 0xFFu], 1u);
-      uint32_t b2, above2;
-      wave_hist_find(S, wv, quota - above, &b2, &above2);
-      edge = (b1 << 24) | (b2 << 16);
-    }
-  }
+  const bool live = live_row && np_row > pg0;
   const int64_t slice = ((int64_t)(live ? row : 0) * P.bt_stride + pg0) * kPage;
   const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
       P.cand + slice, (short)0, live ? kUnitTok * 8 : 0, kRawBufferWord3);
-  const uint64_t below = lanemask_lt();
+  // one compare per key: key 0 (no candidate) is below every threshold >= 1,
+  // and no finite score's key reaches 0xFFFFFFFF
+  const uint32_t thr = live ? max(edge, 1u) : 0xFFFFFFFFu;
+  const uint32_t pos0 = (uint32_t)(pg0 * kPage + lane);
   uint32_t cnt = 0;
 #pragma unroll
   for (int i = 0; i < kUnitPages; ++i) {
-    const bool kept = live && k[i] != 0u && k[i] >= edge;
+    const bool kept = k[i] >= thr;
     const uint64_t m = __builtin_amdgcn_ballot_w64(kept);
-    const uint32_t off = cnt + (uint32_t)__builtin_popcountll(m & below);
-    const v2u v = {k[i], (uint32_t)((pg0 + i) * kPage + lane)};
+    // cnt + the number of kept lanes below this one
+    const uint32_t off = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, cnt));
+    const v2u v = {k[i], pos0 + (uint32_t)(i * kPage)};
     __builtin_amdgcn_raw_buffer_store_b64(v, rc, kept ? off * 8u : 0x7FFFFFF0u, 0, 0);
     cnt += (uint32_t)__builtin_popcountll(m);
   }
@@ -1319,30 +1366,12 @@ __device__ __forceinline__ void filter_wave(const Params& P, TileSmem& S, int wv
   __builtin_amdgcn_raw_buffer_store_b32(edge, re, uoff, 0, 0);
 }
 
-// One row's per-lane share of the score of a token tile, before the sum over
-// the four rows (the per-row scan's score_half for one jj).
-template <int NHT>
-__device__ __forceinline__ float tile_part(const QOperand<NHT>& Q, const v8i& kb, int ks) {
-  float part = 0.f;
-#pragma unroll
-  for (int i = 0; i < NHT; ++i) {
-    const v4f zero = {0.f, 0.f, 0.f, 0.f};
-    const v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Q.a[i], kb, zero, 0, 0, 0,
-                                                                      Q.s[i], 0, ks);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) part = __builtin_fmaf(Q.w[i][c], relu(acc[c]), part);
-  }
-  return part;
-}
-
 template <int NHT>
 __global__ __launch_bounds__(kThreads, 2) void indexer_tile_kernel(Params P) {
   __shared__ __attribute__((aligned(16))) TileSmem S;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hr = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) S.hist[wv][lane + 64 * i] = 0;
   const uint32_t ring0 = lds_addr(S.ring), junk = lds_addr(S.junk);
   const int ntiles = (P.R + kTileRows - 1) / kTileRows;
   bool bad = false;
@@ -1425,17 +1454,42 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_tile_kernel(Params P) {
         if (p >= npt) continue;                                    // uniform: past the tile
         const uint8_t* pg = S.ring[L % kPgRing];
         const bool pok = S.pt[p] >= 0;
-        float pa[4], pb[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        // Token tile j's key operand: two 16-byte reads and a scale byte.
+        auto operand = [&](int j, v8i& kv, int& ks) {
           const uint8_t* tok = pg + (16 * j + hr) * (16 * kTokGran) + 16 * g;
           const uint4 lo = *reinterpret_cast<const uint4*>(tok);
           const uint4 hi = *reinterpret_cast<const uint4*>(tok + 64);
-          const int ks = (int)pg[16 * kScaleGran0 + (16 * j + hr) * 4 + g];
-          const v8i kv = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-          pa[j] = tile_part<NHT>(Qa, kv, ks);
-          pb[j] = tile_part<NHT>(Qb, kv, ks);
+          ks = (int)pg[16 * kScaleGran0 + (16 * j + hr) * 4 + g];
+          kv = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                   (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        };
+        // 2*NHT MFMAs per token tile (m < NHT: row a's head tile m, else row
+        // b's head tile m - NHT), software-pipelined: MFMA m+1, or the next
+        // token tile's first, is issued before the FMA chain reads MFMA m,
+        // so the matrix unit works while the vector unit consumes.  Per row
+        // and token tile the chain is head_part's.
+        constexpr int kM = 2 * NHT;
+        float pa[4], pb[4];
+        v8i kc, kn;
+        int sc, sn = 0;
+        operand(0, kc, sc);
+        v4f cur = head_mfma(Qa, 0, kc, sc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          pa[j] = pb[j] = 0.f;
+          if (j + 1 < 4) operand(j + 1, kn, sn);
+#pragma unroll
+          for (int m = 0; m < kM; ++m) {
+            v4f nxt = cur;
+            if (m + 1 < NHT) nxt = head_mfma(Qa, m + 1, kc, sc);
+            else if (m + 1 < kM) nxt = head_mfma(Qb, m + 1 - NHT, kc, sc);
+            else if (j + 1 < 4) nxt = head_mfma(Qa, 0, kn, sn);
+            if (m < NHT) pa[j] = head_acc(Qa, m, cur, pa[j]);
+            else pb[j] = head_acc(Qb, m - NHT, cur, pb[j]);
+            cur = nxt;
+          }
+          kc = kn;
+          sc = sn;
         }
         // lane group g receives token tile g: lane l holds position 64p + l
         const float sa = rows_sum_scatter(pa), sb = rows_sum_scatter(pb);
@@ -1443,8 +1497,10 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_tile_kernel(Params P) {
         ka[pi] = pok && pos <= ta ? score_key(sa) : 0u;
         kb[pi] = pok && pos <= tb ? score_key(sb) : 0u;
       }
-      filter_wave(P, S, wv, ra, la, ta, npa, u, ka);
-      filter_wave(P, S, wv, rb, lb, tb, npb, u, kb);
+      uint32_t ea, eb;
+      tile_edges(P, u, la, ta, npa, ka, lb, tb, npb, kb, &ea, &eb);
+      emit_wave(P, ra, la, npa, u, ka, ea);
+      emit_wave(P, rb, lb, npb, u, kb, eb);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // the padding copies past the tile have landed
   }
