@@ -15,12 +15,14 @@
 //     their E8M0 block scales applied by the instruction, fp32 accumulation)
 //     against the resident query heads, applies ReLU and the head weights in
 //     fp32 and keeps the unit's
-//     scores as order-preserving 32-bit keys in LDS.  A local filter (two
-//     8-bit LDS histogram passes) finds the edge e_u of the 16-bit key bin
-//     that holds the unit's quota-th largest key (quota: about the unit's
-//     expected share of the Top-K plus four standard deviations); the unit
-//     writes every key >= e_u with its position, in position order, to its
-//     slice of the candidate workspace and records e_u.
+//     scores as order-preserving 32-bit keys in LDS.  A local filter (a
+//     bitwise search with ballot counts over each lane's largest keys) finds
+//     an edge e_u with zero low 16 bits that at least the unit's quota of
+//     keys reach (quota: about the unit's expected share of the Top-K plus
+//     four standard deviations), so e_u never exceeds the unit's quota-th
+//     largest key; the unit writes every key >= e_u with its position, in
+//     position order, to its slice of the candidate workspace and records
+//     e_u.
 //  2. select: one workgroup per row gathers the row's candidates into LDS,
 //     finds the exact K-th key T among those >= max_u e_u with up to three
 //     radix passes over the occupied key range, and writes the kept
@@ -42,9 +44,13 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnitPages = 16;
 constexpr int kUnitTok = kUnitPages * kPage;           // 1024 keys per unit
-constexpr int kHalvesPerWave = 2 * kUnitPages / kWaves;  // 8 half pages per wave
+constexpr int kHalvesPerWave = 2 * kUnitPages / kWaves;  // 8 half pages per wave (unit rescoring)
+// The per-row scan: two work-groups of four waves per CU (measured faster
+// than one of eight).
+constexpr int kScanThreads = 256;
+constexpr int kScanWaves = kScanThreads / 64;
+constexpr int kScanHalves = 2 * kUnitPages / kScanWaves;  // 4 half pages per wave and unit
 constexpr int kRing = 4;                               // half pages in flight per wave
-constexpr int kFBins = 256;                            // filter histogram (8-bit passes)
 constexpr int kBins = 4096;                            // select histogram (12-bit passes)
 constexpr int kCandPer = 24;                           // select: candidates per thread
 constexpr int kChunk = kCandPer * kThreads;            // candidates held in registers at once
@@ -55,8 +61,8 @@ constexpr int kSelThreads = 1024;                      // select workgroup
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kFastUnits = 128;                        // select fast path: units per row
 constexpr int kFastPer = kFastUnits / kSelWaves;       // units per wave
-static_assert(kFBins == kThreads, "one filter bin per thread");
 static_assert(kHalvesPerWave % kRing == 0, "the ring wraps at unit boundaries");
+static_assert(kScanHalves % kRing == 0, "the scan ring wraps at unit boundaries");
 
 // Buffer descriptor word 3 for raw (untyped) buffer access on gfx9-class
 // GPUs: 32-bit data format, no swizzle.
@@ -90,12 +96,10 @@ struct Params {
 
 struct ScanSmem {
   uint32_t keys[kUnitTok];            // scores of the current unit as keys
-  uint32_t hist[kFBins];
   uint32_t rowpre[kMaxRows + 1];      // exclusive prefix of units per row
   int32_t rowt[kMaxRows];             // row_pos of every row
   int32_t rowseq[kMaxRows];           // row_seq of every row
-  uint32_t red[2 * kWaves + 2];
-  uint32_t misc[16];
+  uint32_t red[2 * kScanWaves + 2];
 };
 
 struct SelSmem {
@@ -139,7 +143,9 @@ __device__ __forceinline__ uint32_t wave_incl_max(uint32_t x) {
   return x;
 }
 
-// Exclusive prefix of v over the block; *total receives the block sum.
+// Exclusive prefix of v over the block of NT threads; *total receives the
+// block sum.
+template <int NT = kThreads>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* red, uint32_t* total) {
   const int wv = threadIdx.x >> 6;
   const uint32_t x = wave_incl_scan(v);
@@ -147,7 +153,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* red, u
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
+  for (int i = 0; i < NT / 64; ++i) {
     const uint32_t t = red[i];
     before += i < wv ? t : 0;
     tot += t;
@@ -183,10 +189,11 @@ __device__ __forceinline__ int row_units(int t, int bt_stride) {
   return (row_pages(t, bt_stride) + kUnitPages - 1) / kUnitPages;
 }
 
+template <int NT>
 __device__ __forceinline__ void plan_rows(const Params& P, ScanSmem& S) {
   uint32_t* rowpre = S.rowpre;
   uint32_t* red = S.red;
-  const int per = (P.R + kThreads - 1) / kThreads;
+  const int per = (P.R + NT - 1) / NT;
   const int r0 = threadIdx.x * per;
   uint32_t lu = 0;
   for (int i = 0; i < per; ++i) {
@@ -198,7 +205,7 @@ __device__ __forceinline__ void plan_rows(const Params& P, ScanSmem& S) {
     }
   }
   uint32_t total;
-  uint32_t run = block_excl_scan(lu, red, &total);
+  uint32_t run = block_excl_scan<NT>(lu, red, &total);
   for (int i = 0; i < per; ++i) {
     if (r0 + i < P.R) {
       rowpre[r0 + i] = run;
@@ -249,6 +256,7 @@ __device__ __forceinline__ Unit row_unit(const Params& P, int row, int t, int ui
 // ---- scoring ---------------------------------------------------------------
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 template <int NHT>
 struct QOperand {
@@ -267,26 +275,31 @@ struct QOperand {
 template <int NHT>
 __device__ __forceinline__ void load_q(const Params& P, int row, QOperand<NHT>& Q) {
   const int lane = threadIdx.x & 63, hr = lane & 15, g = lane >> 4;
-  // every load is issued unconditionally (heads beyond H read head 0 and are
-  // zeroed afterwards) so the compiler's wait counting sees a fixed number
-  // of loads on every path
+  // Buffer loads over the row's q codes, scales and weights: a head beyond H
+  // reads out of range, which returns zeros.  No value is selected after
+  // its load, so nothing here waits for the loads; every path issues the
+  // same loads, so the compiler's wait counting sees a fixed number.
+  row = __builtin_amdgcn_readfirstlane(row);
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(P.q + (int64_t)row * P.H * kIdxDim), (short)0, P.H * kIdxDim, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(P.qs + (int64_t)row * P.H * 4), (short)0, P.H * 4, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(P.w + (int64_t)row * P.H), (short)0, P.H * 4, kRawBufferWord3);
+  constexpr uint32_t kOut = 0x7FFFFFF0u;
 #pragma unroll
   for (int i = 0; i < NHT; ++i) {
     const int h = 16 * i + hr;
     const bool live = h < P.H;
-    const int hs = live ? h : 0;
-    const uint8_t* src = P.q + ((int64_t)row * P.H + hs) * kIdxDim;
-    const uint4 a = *reinterpret_cast<const uint4*>(src + 16 * g);
-    const uint4 b = *reinterpret_cast<const uint4*>(src + 64 + 16 * g);
-    Q.a[i] = v8i{(int)(live ? a.x : 0u), (int)(live ? a.y : 0u), (int)(live ? a.z : 0u),
-                 (int)(live ? a.w : 0u), (int)(live ? b.x : 0u), (int)(live ? b.y : 0u),
-                 (int)(live ? b.z : 0u), (int)(live ? b.w : 0u)};
-    Q.s[i] = (int)P.qs[((int64_t)row * P.H + hs) * 4 + g];
+    const uint32_t oq = live ? (uint32_t)(h * kIdxDim + 16 * g) : kOut;
+    const v4u a = __builtin_amdgcn_raw_buffer_load_b128(rq, oq, 0, 0);
+    const v4u b = __builtin_amdgcn_raw_buffer_load_b128(rq, live ? oq + 64u : kOut, 0, 0);
+    Q.a[i] = v8i{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+    Q.s[i] = (int)__builtin_amdgcn_raw_buffer_load_b8(rs, live ? (uint32_t)(h * 4 + g) : kOut, 0, 0);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int hh = 16 * i + 4 * g + c;
-      const float wv = P.w[(int64_t)row * P.H + (hh < P.H ? hh : 0)];
-      Q.w[i][c] = hh < P.H ? wv : 0.f;
+      Q.w[i][c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, hh < P.H ? (uint32_t)hh * 4u : kOut, 0, 0));
     }
   }
 }
@@ -494,77 +507,116 @@ __device__ __forceinline__ uint32_t unit_quota(int t, int topk) {
   return (uint32_t)fminf(ceilf(m), (float)kUnitTok);
 }
 
-// Wave 0 walks the 256-bin histogram from the top bin down and finds the bin
-// b where the count of keys in bins >= b first reaches `need`; it clears
-// every bin it read.  misc[0] = b, misc[1] = count in bins > b, misc[2] = 1
-// if found.  Ends with a block barrier.
-__device__ __forceinline__ void filter_threshold(uint32_t* hist, uint32_t need, uint32_t* misc) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const int top = kFBins - 1 - 4 * lane;          // this lane's bins: top .. top-3
-    uint32_t c[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      c[i] = hist[top - i];
-      hist[top - i] = 0;
-    }
-    const uint32_t mine = c[0] + c[1] + c[2] + c[3];
-    const uint32_t incl = wave_incl_scan(mine);
-    uint32_t run = incl - mine;                      // keys in bins above this lane's
-    if (lane == 0) misc[2] = 0;
-    if (run < need && incl >= need) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (run < need && run + c[i] >= need) {
-          misc[0] = (uint32_t)(top - i);
-          misc[1] = run;
-          misc[2] = 1;
-        }
-        run += c[i];
-      }
-    }
-  }
-  __syncthreads();
+__device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
+  return max(min(a, b), min(max(a, b), c));   // one v_med3_u32
 }
 
-// Local filter of a scored unit: the edge is the lower end of the 16-bit key
-// bin holding the unit's quota-th largest key (two 8-bit LDS histogram
-// passes); keys at or above it are emitted, so every key left out is below
-// the recorded edge.  The histogram is all zero on entry and on exit.
+// The three largest of a lane's keys, m[0] >= m[1] >= m[2] (0 = none).
+__device__ __forceinline__ void lane_top3(const uint32_t (&k)[kUnitPages], uint32_t (&m)[3]) {
+  m[0] = m[1] = m[2] = 0u;
+#pragma unroll
+  for (int i = 0; i < kUnitPages; ++i) {
+    m[2] = umed3(m[1], m[2], k[i]);
+    m[1] = umed3(m[0], m[1], k[i]);
+    m[0] = max(m[0], k[i]);
+  }
+}
+
+// Edges of two rows' units (values va, vb: D per lane over the wave): the
+// largest key T with zero low 16 bits such that at least `need` of the
+// values are >= T, found bit by bit from the top with ballot counts (no
+// memory traffic, no atomics); 0 when fewer than `need` values reach
+// 2^16.  The values are the unit's keys or a subset of them, so at least
+// `need` of the unit's keys are >= T: T never exceeds the unit's need-th
+// largest key.
+template <int D>
+__device__ __forceinline__ void key_floor2(const uint32_t (&va)[D], const uint32_t (&vb)[D],
+                                           uint32_t na, uint32_t nb, uint32_t* ta, uint32_t* tb) {
+  uint32_t a = 0u, b = 0u;
+#pragma unroll
+  for (int bit = 31; bit >= 16; --bit) {
+    const uint32_t ca = a | (1u << bit), cb = b | (1u << bit);
+    uint32_t sa = 0u, sb = 0u;
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      sa += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(va[i] >= ca));
+      sb += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(vb[i] >= cb));
+    }
+    if (sa >= na) a = ca;
+    if (sb >= nb) b = cb;
+  }
+  *ta = a;
+  *tb = b;
+}
+
+// key_floor2 for one row.
+template <int D>
+__device__ __forceinline__ uint32_t key_floor(const uint32_t (&v)[D], uint32_t need) {
+  uint32_t a = 0u;
+#pragma unroll
+  for (int bit = 31; bit >= 16; --bit) {
+    const uint32_t ca = a | (1u << bit);
+    uint32_t sa = 0u;
+#pragma unroll
+    for (int i = 0; i < D; ++i) sa += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(v[i] >= ca));
+    if (sa >= need) a = ca;
+  }
+  return a;
+}
+
+// The per-lane top three suffice for the edge search when the quota is at
+// most this (three keys of each of 64 lanes).
+constexpr uint32_t kTop3Quota = 3 * 64;
+
+// Local filter of a scored unit (keys of unit-local position 64i + lane in
+// S.keys).  Every wave reads all 1024 keys and finds the same edge: the
+// largest 16-bit-prefix key that at least `quota` keys reach, searched over
+// each lane's three largest keys (a subset, so the edge never exceeds the
+// unit's quota-th largest key), or over all keys for quotas above 192.
+// Keys at or above the edge are emitted in position order: wave w writes
+// its share of the pages (16 / waves), at offsets from the per-page ballot counts that every
+// wave holds.  No atomics; one barrier, once every wave holds the keys in
+// registers, so the next unit may overwrite them.
 __device__ __forceinline__ void filter_unit(const Params& P, ScanSmem& S, const Unit& U) {
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint32_t k[kUnitPages];
+#pragma unroll
+  for (int i = 0; i < kUnitPages; ++i) k[i] = S.keys[kPage * i + lane];
+  __syncthreads();
   const int ntok = (U.pg1 - U.pg0) * kPage;
   const uint32_t quota = unit_quota(U.t, P.topk);
-  const uint4 kv = *reinterpret_cast<const uint4*>(&S.keys[4 * tid]);
-  const uint32_t k[4] = {kv.x, kv.y, kv.z, kv.w};
   uint32_t edge = 0;
   if (quota < (uint32_t)ntok) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (k[j]) atomicAdd(&S.hist[k[j] >> 24], 1u);
-    __syncthreads();
-    filter_threshold(S.hist, quota, S.misc);
-    if (S.misc[2]) {   // else: fewer than quota keys, keep them all
-      const uint32_t b1 = S.misc[0], need = quota - S.misc[1];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (k[j] && (k[j] >> 24) == b1) atomicAdd(&S.hist[(k[j] >> 16) & 0xFFu], 1u);
-      __syncthreads();
-      filter_threshold(S.hist, need, S.misc + 4);
-      edge = (b1 << 24) | (S.misc[4] << 16);
+    if (quota <= kTop3Quota) {
+      uint32_t m[3];
+      lane_top3(k, m);
+      edge = key_floor<3>(m, quota);
+    } else {
+      edge = key_floor<kUnitPages>(k, quota);
     }
   }
-  uint32_t cnt = 0;
+  const uint32_t thr = max(edge, 1u);   // key 0 (no candidate) is never kept
+  uint32_t before = 0, total = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) cnt += (k[j] != 0u && k[j] >= edge) ? 1u : 0u;
-  uint32_t total;
-  uint32_t off = block_excl_scan(cnt, S.red, &total);
-  uint2* dst = P.cand + ((int64_t)U.row * P.bt_stride + U.pg0) * kPage;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (k[j] != 0u && k[j] >= edge) dst[off++] = make_uint2(k[j], (uint32_t)(U.pg0 * kPage + 4 * tid + j));
+  for (int i = 0; i < kUnitPages; ++i) {
+    const uint32_t c = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(k[i] >= thr));
+    before += i < kUnitPages / kScanWaves * wv ? c : 0u;
+    total += c;
   }
-  if (tid == 0) {
+  const int64_t slice = ((int64_t)U.row * P.bt_stride + U.pg0) * kPage;
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(P.cand + slice, (short)0, kUnitTok * 8, kRawBufferWord3);
+#pragma unroll
+  for (int i = 0; i < kUnitPages; ++i) {
+    if (i / (kUnitPages / kScanWaves) != wv) continue;   // uniform
+    const bool kept = k[i] >= thr;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(kept);
+    const uint32_t off = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, before));
+    const v2u v = {k[i], (uint32_t)(U.pg0 * kPage + kPage * i + lane)};
+    __builtin_amdgcn_raw_buffer_store_b64(v, rc, kept ? off * 8u : 0x7FFFFFF0u, 0, 0);
+    before += (uint32_t)__builtin_popcountll(m);
+  }
+  if (threadIdx.x == 0) {
     const int64_t slot = (int64_t)U.row * P.upr + U.uir;
     P.ucount[slot] = total;
     P.uedge[slot] = edge;
@@ -577,10 +629,9 @@ __device__ __forceinline__ void filter_unit(const Params& P, ScanSmem& S, const 
 // the next unit are already requested, so they are in flight during the
 // local filter and the memory system never idles at a unit boundary.
 template <int NHT>
-__global__ __launch_bounds__(kThreads, 2) void indexer_scan_kernel(Params P) {
+__global__ __launch_bounds__(kScanThreads, 2) void indexer_scan_kernel(Params P) {
   __shared__ ScanSmem S;
-  S.hist[threadIdx.x] = 0;
-  plan_rows(P, S);   // ends with a barrier
+  plan_rows<kScanThreads>(P, S);   // ends with a barrier
   const uint32_t U_total = S.rowpre[P.R];
   const uint32_t per = (U_total + gridDim.x - 1) / gridDim.x;
   uint32_t u = blockIdx.x * per;
@@ -596,7 +647,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_scan_kernel(Params P) {
   HalfRegs b[kRing];
   bool ok[kRing];
 #pragma unroll
-  for (int k = 0; k < kRing; ++k) ok[k] = fetch_half(P, U, pid, wv + kWaves * k, b[k], &bad);
+  for (int k = 0; k < kRing; ++k) ok[k] = fetch_half(P, U, pid, wv + kScanWaves * k, b[k], &bad);
   for (;;) {
     const bool more = u + 1 < uend;
     // the next unit (the current one again when there is none: its ring
@@ -606,16 +657,16 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_scan_kernel(Params P) {
     Unit Vf = V;          // the ring's view of the next unit: no pages when there is none
     if (!more) Vf.t = -1;
 #pragma unroll
-    for (int k = 0; k < kHalvesPerWave; ++k) {
-      consume_half<NHT, false>(P, U, Q, wv + kWaves * k, b[k % kRing], ok[k % kRing], S.keys);
+    for (int k = 0; k < kScanHalves; ++k) {
+      consume_half<NHT, false>(P, U, Q, wv + kScanWaves * k, b[k % kRing], ok[k % kRing], S.keys);
       const int kn = k + kRing;
-      if (kn < kHalvesPerWave)
-        ok[k % kRing] = fetch_half(P, U, pid, wv + kWaves * kn, b[k % kRing], &bad);
+      if (kn < kScanHalves)
+        ok[k % kRing] = fetch_half(P, U, pid, wv + kScanWaves * kn, b[k % kRing], &bad);
       else
-        ok[k % kRing] = fetch_half(P, Vf, pidn, wv + kWaves * (kn - kHalvesPerWave), b[k % kRing], &bad);
+        ok[k % kRing] = fetch_half(P, Vf, pidn, wv + kScanWaves * (kn - kScanHalves), b[k % kRing], &bad);
     }
     __syncthreads();
-    filter_unit(P, S, U);   // its last barrier orders the key reads before the next unit's writes
+    filter_unit(P, S, U);   // its barrier orders the key reads before the next unit's writes
     if (!more) break;
     if (V.row != qrow) {
       load_q<NHT>(P, V.row, Q);
@@ -632,7 +683,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_scan_kernel(Params P) {
 template <int NHT>
 __global__ __launch_bounds__(kThreads, 2) void indexer_dump_kernel(Params P) {
   __shared__ ScanSmem S;
-  plan_rows(P, S);
+  plan_rows<kThreads>(P, S);
   const uint32_t U_total = S.rowpre[P.R];
   for (uint32_t u = blockIdx.x; u < U_total; u += gridDim.x) {
     const Unit U = decode_unit(P, S, u);
@@ -902,7 +953,6 @@ __device__ __forceinline__ void seg_emit_all(const Params& P, const Seg& sg, int
 // global-address-space pointers, which cannot alias LDS.
 typedef __attribute__((address_space(1))) int32_t gint32;
 typedef __attribute__((address_space(1))) float gfloat;
-typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 // Bin of rank `need` from the top of histogram H (kBins bins) and the count
 // of keys in the bins above it; false when H holds fewer than `need` keys.
@@ -1258,55 +1308,12 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
                : "memory", "m0");
 }
 
-__device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
-  return max(min(a, b), min(max(a, b), c));   // one v_med3_u32
-}
-
-// The three largest of a lane's keys, m[0] >= m[1] >= m[2] (0 = none).
-__device__ __forceinline__ void lane_top3(const uint32_t (&k)[kUnitPages], uint32_t (&m)[3]) {
-  m[0] = m[1] = m[2] = 0u;
-#pragma unroll
-  for (int i = 0; i < kUnitPages; ++i) {
-    m[2] = umed3(m[1], m[2], k[i]);
-    m[1] = umed3(m[0], m[1], k[i]);
-    m[0] = max(m[0], k[i]);
-  }
-}
-
-// Edges of two rows' units (values va, vb: D per lane over the wave): the
-// largest key T with zero low 16 bits such that at least `need` of the
-// values are >= T, found bit by bit from the top with ballot counts (no
-// memory traffic, no atomics); 0 when fewer than `need` values reach
-// 2^16.  The values are the unit's keys or a subset of them, so at least
-// `need` of the unit's keys are >= T: T never exceeds the unit's need-th
-// largest key.
-template <int D>
-__device__ __forceinline__ void key_floor2(const uint32_t (&va)[D], const uint32_t (&vb)[D],
-                                           uint32_t na, uint32_t nb, uint32_t* ta, uint32_t* tb) {
-  uint32_t a = 0u, b = 0u;
-#pragma unroll
-  for (int bit = 31; bit >= 16; --bit) {
-    const uint32_t ca = a | (1u << bit), cb = b | (1u << bit);
-    uint32_t sa = 0u, sb = 0u;
-#pragma unroll
-    for (int i = 0; i < D; ++i) {
-      sa += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(va[i] >= ca));
-      sb += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(vb[i] >= cb));
-    }
-    if (sa >= na) a = ca;
-    if (sb >= nb) b = cb;
-  }
-  *ta = a;
-  *tb = b;
-}
-
 // Local filter edges of unit u for a wave's two rows (keys k[i] = position
 // 64(16u+i) + lane).  A unit keeps every key >= its edge: at least its
 // quota of keys (all of them when it has no more than the quota).  With a
 // quota of at most 192 the search runs over each lane's three largest keys,
 // a subset that holds the unit's quota largest keys unless a lane holds
 // more than three of them (then the edge is lower and more keys are kept).
-constexpr uint32_t kTop3Quota = 3 * 64;
 __device__ __forceinline__ void tile_edges(const Params& P, int u, bool la, int ta, int npa,
                                            const uint32_t (&ka)[kUnitPages], bool lb, int tb,
                                            int npb, const uint32_t (&kb)[kUnitPages],
@@ -1553,7 +1560,7 @@ void* pick_tile_kernel(int nht) {
 }
 
 // resident workgroups of a kernel on the current device (cached per device)
-int resident_capacity(void* fn, int slot) {
+int resident_capacity(void* fn, int slot, int threads) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
   static int cached[64][16];
@@ -1563,7 +1570,7 @@ int resident_capacity(void* fn, int slot) {
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return -1;
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn),
-                                                   kThreads, 0) != hipSuccess)
+                                                   threads, 0) != hipSuccess)
     return -1;
   const int cap = std::max(1, per_cu) * prop.multiProcessorCount;
   if (dev < 64) { cached[dev][slot] = cap; have[dev][slot] = true; }
@@ -1585,7 +1592,8 @@ int run(Params P, bool dump, hipStream_t stream) {
   const KernelKind kind = dump ? kDump : kScan;
   void* scan = pick_kernel(nht, kind);
   void* sel = pick_kernel(nht, kSelect);
-  const int cap = resident_capacity(scan, (nht - 1) * 3 + (int)kind);
+  const int scan_threads = dump ? kThreads : kScanThreads;
+  const int cap = resident_capacity(scan, (nht - 1) * 3 + (int)kind, scan_threads);
   if (cap <= 0) return DSA_ERR_HIP;
   const int R = P.R;
   const int upr = units_stride(P.bt_stride);
@@ -1606,7 +1614,7 @@ int run(Params P, bool dump, hipStream_t stream) {
     }
     const int64_t G = std::min<int64_t>((int64_t)cap, (int64_t)rn * upr);
     void* args[] = {&Q};
-    if (hipLaunchKernel(scan, dim3((unsigned)G), dim3(kThreads), args, 0, stream) != hipSuccess)
+    if (hipLaunchKernel(scan, dim3((unsigned)G), dim3(scan_threads), args, 0, stream) != hipSuccess)
       return DSA_ERR_HIP;
     if (!dump && hipLaunchKernel(sel, dim3((unsigned)rn), dim3(kSelThreads), args, 0, stream) != hipSuccess)
       return DSA_ERR_HIP;
@@ -1730,7 +1738,7 @@ extern "C" int dsa_indexer_topk_seq(const void* q_fp8, const void* q_e8m0, const
   const int nht = (H_I + 15) / 16;
   void* tk = pick_tile_kernel(nht);
   void* sel = pick_kernel(nht, kSelect);
-  const int cap = resident_capacity(tk, 12 + nht - 1);
+  const int cap = resident_capacity(tk, 12 + nht - 1, kThreads);
   if (cap <= 0) return DSA_ERR_HIP;
   for (int r0 = 0; r0 < R; r0 += kSeqChunkRows) {
     const int rn = std::min(kSeqChunkRows, R - r0);
