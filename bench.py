@@ -10,7 +10,9 @@ One step = the whole hot path for one decode token of each sequence:
   dsa_decode_prolog (in one launch: mxfp8_quant of the indexer q, the new
   indexer k into the K cache, kv_fp8_quant_paged_write of the new KV row)
   -> dsa_indexer_topk -> dsa_sparse_attn
-(--separate-prolog runs the three quantisations as three launches instead).
+(--separate-prolog runs the three quantisations as three launches instead;
+--graph captures the step once per cache replica in a HIP graph and times
+graph replays instead of eager launches).
 Caches are replicated (default 4 replicas, about 3.3 GB) and rotated per step
 so that the 256 MB Infinity Cache cannot serve one step's reads from the
 previous step.
@@ -55,6 +57,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate-prolog", action="store_true",
                     help="quantise q, k and kv with three launches instead of dsa_decode_prolog")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the step once per cache replica in a HIP graph and time graph replays")
     ap.add_argument("--profile-steps", action="store_true",
                     help="only warm up and run the timed steps (for profiler runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -67,6 +71,9 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the DSA decode path here has no multi-GPU mode "
               "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.graph and args.separate_prolog:
+        print("--graph captures the fused prolog; drop --separate-prolog", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -155,11 +162,30 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    run_step = step
+    if args.graph:
+        # one graph per replica, its launches recorded on a capture stream
+        cap = torch.cuda.Stream()
+        cap_h = P(cap.cuda_stream)
+        graphs = []
+        for j in range(args.replicas):
+            aj = {k: tuple(cap_h if x is stream else x for x in v) for k, v in steps_args[j].items()}
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                st = L.dsa_decode_prolog(*aj["pro"]) | L.dsa_indexer_topk(*aj["idx"]) | L.dsa_sparse_attn(*aj["sfa"])
+            if st:
+                raise RuntimeError(f"library call failed during capture (status bits {st})")
+            graphs.append(g)
+        torch.cuda.synchronize()
+        run_step = lambda i: graphs[i % args.replicas].replay()
+        for i in range(args.warmup):
+            run_step(i)
+        torch.cuda.synchronize()
     K_steps = args.steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K_steps):
-        step(i)
+        run_step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     if args.profile_steps:
@@ -213,7 +239,8 @@ def main():
         "config": {"workload": cfg.name, "batch": B, "context": int(lens.max()), "query_rows": R,
                    "h_index": H_I, "h_attn": H, "topk": K, "page_tokens": 64,
                    "cache_replicas_rotated": args.replicas, "parallelism": "single GPU",
-                   "prolog": "three launches" if args.separate_prolog else "dsa_decode_prolog (one launch)"},
+                   "prolog": "three launches" if args.separate_prolog else "dsa_decode_prolog (one launch)",
+                   "launch": "hipGraph replay per step" if args.graph else "eager launches"},
         "hbm_gbs_step": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "algorithmic_bytes_step": step_bytes,
         "kernel_ms": {"dsa_indexer_topk": round(idx_avg, 5),

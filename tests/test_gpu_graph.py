@@ -1,0 +1,70 @@
+"""The decode step (dsa_decode_prolog, dsa_indexer_topk, dsa_sparse_attn)
+captured once in a HIP graph and replayed: every replay returns the eager
+step's bits.  Between replays the outputs are cleared by eager work and the
+device is synchronised, so each replay has to recompute them."""
+import pytest
+import torch
+
+from sparse_attention_decode_topk_amd import ops, synth
+from tests.dsa_state import DeviceState, bf16_tensor, say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replay_matches_eager(need_gpu):
+    say("[graph] decode_8k_needles: prolog + indexer + sparse attention")
+    inp = synth.make("decode_8k_needles")
+    st = DeviceState(inp)
+    dev = st.dev
+    R, K = st.R, st.topk
+    new_tok = inp["seq_starts"] + inp["seq_lens"] - 1
+    k_new = bf16_tensor(inp["k_idx"][new_tok], dev)
+    kv_new = bf16_tensor(inp["kv"][new_tok], dev)
+    slots = torch.from_numpy(inp["slot_mapping"][new_tok]).to(dev)
+    q_bf = bf16_tensor(inp["q_idx"], dev)
+    q_fp8 = torch.empty_like(st.q_fp8)
+    q_e8 = torch.empty_like(st.q_e8m0)
+    out_idx = torch.empty((R, K), dtype=torch.int32, device=dev)
+    out_sc = torch.empty((R, K), dtype=torch.float32, device=dev)
+    out = torch.empty((R, st.H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((R, st.H), dtype=torch.float32, device=dev)
+    ws_i = ops.indexer_workspace(R, st.block_table.shape[1], st.H_I, K, dev)
+    ws_s = ops.sparse_attn_workspace(R, st.H, K, dev)
+    outs = (out_idx, out_sc, out, lse)
+
+    def step():
+        ops.decode_prolog(q_bf, k_new, kv_new, slots, st.k_pool, st.kv_pool, q_out=(q_fp8, q_e8))
+        ops.dsa_indexer_topk(q_fp8, q_e8, st.w, st.k_pool, st.block_table, st.row_seq, st.row_pos, K,
+                             out_idx=out_idx, out_score=out_sc, workspace=ws_i)
+        ops.dsa_sparse_attn(st.q_sfa, st.kv_pool, st.block_table, st.row_seq, out_idx,
+                            out=out, lse=lse, workspace=ws_s)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    assert int((ref[0] >= 0).sum()) == R * K
+
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        step()   # once on the capture stream before capture
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in outs:
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("idx", "score", "out", "lse"), outs, ref):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager step"
+        say(f"[graph] replay {rep} equal to eager")
+    # eager again after the replays: the same bits
+    step()
+    torch.cuda.synchronize()
+    for a, b in zip(outs, ref):
+        assert torch.equal(a, b)
