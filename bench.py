@@ -26,7 +26,11 @@ calls, each bracketed by HIP events; the indexer's average is the roofline
 duration.  `traffic` is filled from the committed FETCH_SIZE/WRITE_SIZE
 summary when it was taken on the current indexer source.
 
-Prints one JSON line.  `value` is decode tokens/s (batch * steps / seconds).
+Prints one JSON line.  `value` is query tokens/s (rows * steps / seconds;
+for decode one row per sequence).  --config prefill_chunk_8k_of_128k times
+the chunked-prefill step instead (8192 query rows of one sequence through
+dsa_indexer_topk_seq), whose roofline is the MFMA one of its longer entry
+point; `mfma_rooflines` gives both entry points' scaled-MFMA rates.
 """
 from __future__ import annotations
 
@@ -41,7 +45,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "LI+SFA decode tokens/s and achieved HBM GB/s at 128K ctx, batch 8, 1 GPU"
+METRIC_PREFILL = "LI+SFA chunked-prefill query tokens/s and MFMA utilisation, 8K rows of a 128K context, 1 GPU"
 HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFS = 5000.0          # dense fp8 MFMA
+BF16_PEAK_TFS = 2500.0         # dense bf16 / fp16 MFMA
 IDX_BYTES_PER_TOKEN = 132      # 128 E4M3 + 4 E8M0 per history token (one query row)
 SFA_BYTES_PER_ENTRY = 656      # one latent record per selected position
 
@@ -106,10 +113,14 @@ def main():
     q_idx = bf16(inp["q_idx"])
     w = torch.from_numpy(inp["w"]).to(dev)
     q_sfa = bf16(inp["q_sfa"])
-    new_tok = starts + lens - 1                       # the decode token of each sequence
+    # the token of every query row (decode: the last token of its sequence;
+    # chunked prefill: the chunk's tokens), written into the caches by the prolog
+    new_tok = starts[inp["row_seq"]].astype(np.int64) + inp["row_pos"].astype(np.int64)
     k_new = bf16(inp["k_idx"][new_tok])
     kv_new = bf16(inp["kv"][new_tok])
     slots_new = torch.from_numpy(inp["slot_mapping"][new_tok]).to(dev)
+    # rows of one sequence (a prefill chunk) take the row-tiled indexer entry
+    one_seq = len(np.unique(inp["row_seq"])) == 1 and R > B
     k0 = torch.zeros((npages, ops.K_PAGE_BYTES), dtype=torch.uint8, device=dev)
     kv0 = torch.zeros((npages, ops.KV_PAGE_BYTES), dtype=torch.uint8, device=dev)
     slots_all = torch.from_numpy(inp["slot_mapping"]).to(dev)
@@ -124,7 +135,11 @@ def main():
     out_sc = torch.empty((R, K), dtype=torch.float32, device=dev)
     out = torch.empty((R, H, 512), dtype=torch.float32, device=dev)
     lse = torch.empty((R, H), dtype=torch.float32, device=dev)
-    ws_i = ops.indexer_workspace(R, block_table.shape[1], H_I, K, dev)
+    if one_seq:
+        bt_row = block_table[int(inp["row_seq"][0])].contiguous()
+        ws_i = ops.indexer_seq_workspace(R, bt_row.numel(), H_I, K, dev)
+    else:
+        ws_i = ops.indexer_workspace(R, block_table.shape[1], H_I, K, dev)
     ws_s = ops.sparse_attn_workspace(R, H, K, dev)
     torch.cuda.synchronize()
 
@@ -137,16 +152,21 @@ def main():
     for j in range(args.replicas):
         steps_args.append(dict(
             qq=(ptr(q_idx), R * H_I, 128, ptr(q_fp8), ptr(q_e8), None, None, 0, stream),
-            kq=(ptr(k_new), B, 128, None, None, ptr(k_pools[j]), ptr(slots_new), npages, stream),
-            kvq=(ptr(kv_new), B, ptr(slots_new), ptr(kv_pools[j]), npages, stream),
-            pro=(ptr(q_idx), R * H_I, 128, ptr(q_fp8), ptr(q_e8), ptr(k_new), ptr(kv_new), B,
+            kq=(ptr(k_new), R, 128, None, None, ptr(k_pools[j]), ptr(slots_new), npages, stream),
+            kvq=(ptr(kv_new), R, ptr(slots_new), ptr(kv_pools[j]), npages, stream),
+            pro=(ptr(q_idx), R * H_I, 128, ptr(q_fp8), ptr(q_e8), ptr(k_new), ptr(kv_new), R,
                  ptr(slots_new), ptr(k_pools[j]), ptr(kv_pools[j]), npages, stream),
-            idx=(ptr(q_fp8), ptr(q_e8), ptr(w), ptr(k_pools[j]), npages, ptr(block_table),
-                 block_table.shape[1], ptr(row_seq), ptr(row_pos), R, H_I, K, ptr(out_idx),
-                 ptr(out_sc), ptr(ws_i), ws_i.numel(), stream),
+            idx=((ptr(q_fp8), ptr(q_e8), ptr(w), ptr(k_pools[j]), npages, ptr(bt_row),
+                  bt_row.numel(), ptr(row_pos), R, H_I, K, ptr(out_idx), ptr(out_sc), ptr(ws_i),
+                  ws_i.numel(), stream) if one_seq else
+                 (ptr(q_fp8), ptr(q_e8), ptr(w), ptr(k_pools[j]), npages, ptr(block_table),
+                  block_table.shape[1], ptr(row_seq), ptr(row_pos), R, H_I, K, ptr(out_idx),
+                  ptr(out_sc), ptr(ws_i), ws_i.numel(), stream)),
             sfa=(ptr(q_sfa), ptr(kv_pools[j]), npages, ptr(block_table), block_table.shape[1],
                  ptr(row_seq), ptr(out_idx), R, H, K, ctypes.c_float(ops.DEFAULT_SCALE),
                  ptr(out), ptr(lse), ptr(ws_s), ws_s.numel(), stream)))
+
+    indexer_call = L.dsa_indexer_topk_seq if one_seq else L.dsa_indexer_topk
 
     def step(i):
         a = steps_args[i % args.replicas]
@@ -154,7 +174,7 @@ def main():
             st = L.mxfp8_quant(*a["qq"]) | L.mxfp8_quant(*a["kq"]) | L.kv_fp8_quant_paged_write(*a["kvq"])
         else:
             st = L.dsa_decode_prolog(*a["pro"])
-        st |= L.dsa_indexer_topk(*a["idx"])
+        st |= indexer_call(*a["idx"])
         st |= L.dsa_sparse_attn(*a["sfa"])
         if st:
             raise RuntimeError(f"library call failed (status bits {st})")
@@ -172,7 +192,7 @@ def main():
             aj = {k: tuple(cap_h if x is stream else x for x in v) for k, v in steps_args[j].items()}
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
-                st = L.dsa_decode_prolog(*aj["pro"]) | L.dsa_indexer_topk(*aj["idx"]) | L.dsa_sparse_attn(*aj["sfa"])
+                st = L.dsa_decode_prolog(*aj["pro"]) | indexer_call(*aj["idx"]) | L.dsa_sparse_attn(*aj["sfa"])
             if st:
                 raise RuntimeError(f"library call failed during capture (status bits {st})")
             graphs.append(g)
@@ -204,10 +224,10 @@ def main():
         torch.cuda.synchronize()
         return ev[0].elapsed_time(ev[1]) / K_steps
 
-    idx_avg = timed_calls(L.dsa_indexer_topk, "idx")
+    idx_avg = timed_calls(indexer_call, "idx")
     sfa_avg = timed_calls(L.dsa_sparse_attn, "sfa")
     ms_per_step = elapsed * 1e3 / K_steps
-    tokens_per_s = B * K_steps / elapsed
+    tokens_per_s = R * K_steps / elapsed   # query tokens (decode: one per sequence)
 
     hist_tokens = int((inp["row_pos"].astype(np.int64) + 1).sum())
     idx_bytes = hist_tokens * IDX_BYTES_PER_TOKEN
@@ -216,6 +236,12 @@ def main():
     sfa_bytes = n_sel * SFA_BYTES_PER_ENTRY
     step_bytes = idx_bytes + sfa_bytes
     achieved = idx_bytes / (idx_avg * 1e-3) / 1e9
+    # scaled-MFMA work: the indexer's q.k contraction and the attention's
+    # logits and P.V products
+    idx_flop = hist_tokens * H_I * 128 * 2
+    sfa_flop = n_sel * H * (576 + 512) * 2
+    idx_tf = idx_flop / (idx_avg * 1e-3) / 1e12
+    sfa_tf = sfa_flop / (sfa_avg * 1e-3) / 1e12
     err_word = int(ws_i[8:12].view(torch.int32).item())
     traffic = measured_traffic(cfg.name)
 
@@ -223,8 +249,25 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, args.cpu_rows)
 
+    idx_name = "dsa_indexer_topk_seq" if one_seq else "dsa_indexer_topk"
+    mfma = {idx_name: {"achieved": round(idx_tf, 1), "peak": FP8_PEAK_TFS, "unit": "TFLOP/s",
+                       "frac": round(idx_tf / FP8_PEAK_TFS, 4), "flop": idx_flop,
+                       "dtype": "fp8 e4m3 x e4m3, E8M0 block scales"},
+            "dsa_sparse_attn": {"achieved": round(sfa_tf, 1), "peak": BF16_PEAK_TFS, "unit": "TFLOP/s",
+                                "frac": round(sfa_tf / BF16_PEAK_TFS, 4), "flop": sfa_flop,
+                                "dtype": "bf16 logits, f16 P.V"}}
+    if one_seq:
+        # a prefill chunk is MFMA-bound: the longer of the two entry points
+        kname = idx_name if idx_avg >= sfa_avg else "dsa_sparse_attn"
+        m = mfma[kname]
+        roofline = {"bound": "mfma", "kernel": kname, "achieved": m["achieved"], "peak": m["peak"],
+                    "unit": "TFLOP/s", "frac": m["frac"], "traffic": None, "flop": m["flop"]}
+    else:
+        roofline = {"bound": "hbm", "kernel": idx_name, "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": traffic, "algorithmic_bytes": idx_bytes}
     rec = {
-        "metric": METRIC,
+        "metric": METRIC if not one_seq else METRIC_PREFILL,
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -243,11 +286,10 @@ def main():
                    "launch": "hipGraph replay per step" if args.graph else "eager launches"},
         "hbm_gbs_step": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "algorithmic_bytes_step": step_bytes,
-        "kernel_ms": {"dsa_indexer_topk": round(idx_avg, 5),
+        "kernel_ms": {idx_name: round(idx_avg, 5),
                       "dsa_sparse_attn": round(sfa_avg, 5)},
-        "roofline": {"bound": "hbm", "kernel": "dsa_indexer_topk", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes": idx_bytes},
+        "roofline": roofline,
+        "mfma_rooflines": mfma,
         "cpu_baseline": cpu,
         "indexer_error_word": err_word,
         "input_gen_s": round(t_gen, 1),
@@ -311,7 +353,7 @@ def cpu_baseline(inp, rows):
         o.sfa(r, res["idx"])
     dt = time.perf_counter() - t0
     return {"value": round(rows / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{rows} of {len(inp['row_seq'])} decode rows (indexer+Top-K+SFA per row, "
+            "sample": f"{rows} of {len(inp['row_seq'])} query rows (indexer+Top-K+SFA per row, "
                       f"fp64 numpy), {dt:.1f} s"}
 
 
