@@ -432,7 +432,8 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
   const int64_t ph = ((int64_t)row * P.H + head) * P.S + sp;
   float4* po = reinterpret_cast<float4*>(P.part_o + ph * kLatent) + 64 * dh;
 #pragma unroll
-  for (int d = 0; d < 16; ++d) po[4 * d + g] = make_float4(o[d][0], o[d][1], o[d][2], o[d][3]);
+  for (int d = 0; d < 16; ++d)
+    __builtin_nontemporal_store(v4f{o[d][0], o[d][1], o[d][2], o[d][3]}, reinterpret_cast<v4f*>(po + 4 * d + g));
   if (g == 0 && dh == 0) {
     P.part_ml[2 * ph] = m_ref;
     P.part_ml[2 * ph + 1] = l_run;
