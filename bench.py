@@ -31,6 +31,10 @@ for decode one row per sequence).  --config prefill_chunk_8k_of_128k times
 the chunked-prefill step instead (8192 query rows of one sequence through
 dsa_indexer_topk_seq), whose roofline is the MFMA one of its longer entry
 point; `mfma_rooflines` gives both entry points' scaled-MFMA rates.
+--config decode_mtp4_128k_b8 times multi-query decode (4 query tokens per
+sequence, as in the verification of drafted tokens) through
+dsa_indexer_topk_mq, which reads each sequence's K once for its 4 rows; its
+roofline counts those bytes once per sequence.
 """
 from __future__ import annotations
 
@@ -45,6 +49,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "LI+SFA decode tokens/s and achieved HBM GB/s at 128K ctx, batch 8, 1 GPU"
+METRIC_MQ = ("LI+SFA multi-query decode query tokens/s and achieved HBM GB/s at 128K ctx, "
+             "batch 8 x 4 query tokens, 1 GPU")
 METRIC_PREFILL = "LI+SFA chunked-prefill query tokens/s and MFMA utilisation, 8K rows of a 128K context, 1 GPU"
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFS = 5000.0          # dense fp8 MFMA
@@ -121,6 +127,9 @@ def main():
     slots_new = torch.from_numpy(inp["slot_mapping"][new_tok]).to(dev)
     # rows of one sequence (a prefill chunk) take the row-tiled indexer entry
     one_seq = len(np.unique(inp["row_seq"])) == 1 and R > B
+    # several query rows per sequence (multi-query decode) take the entry
+    # point that reads each sequence's K once for its group of rows
+    mq = cfg.q_per_seq if (not one_seq and cfg.q_per_seq > 1) else 0
     k0 = torch.zeros((npages, ops.K_PAGE_BYTES), dtype=torch.uint8, device=dev)
     kv0 = torch.zeros((npages, ops.KV_PAGE_BYTES), dtype=torch.uint8, device=dev)
     slots_all = torch.from_numpy(inp["slot_mapping"]).to(dev)
@@ -160,13 +169,17 @@ def main():
                   bt_row.numel(), ptr(row_pos), R, H_I, K, ptr(out_idx), ptr(out_sc), ptr(ws_i),
                   ws_i.numel(), stream) if one_seq else
                  (ptr(q_fp8), ptr(q_e8), ptr(w), ptr(k_pools[j]), npages, ptr(block_table),
+                  block_table.shape[1], ptr(row_seq), ptr(row_pos), R, mq, H_I, K, ptr(out_idx),
+                  ptr(out_sc), ptr(ws_i), ws_i.numel(), stream) if mq else
+                 (ptr(q_fp8), ptr(q_e8), ptr(w), ptr(k_pools[j]), npages, ptr(block_table),
                   block_table.shape[1], ptr(row_seq), ptr(row_pos), R, H_I, K, ptr(out_idx),
                   ptr(out_sc), ptr(ws_i), ws_i.numel(), stream)),
             sfa=(ptr(q_sfa), ptr(kv_pools[j]), npages, ptr(block_table), block_table.shape[1],
                  ptr(row_seq), ptr(out_idx), R, H, K, ctypes.c_float(ops.DEFAULT_SCALE),
                  ptr(out), ptr(lse), ptr(ws_s), ws_s.numel(), stream)))
 
-    indexer_call = L.dsa_indexer_topk_seq if one_seq else L.dsa_indexer_topk
+    indexer_call = (L.dsa_indexer_topk_seq if one_seq else
+                    L.dsa_indexer_topk_mq if mq else L.dsa_indexer_topk)
 
     def step(i):
         a = steps_args[i % args.replicas]
@@ -230,7 +243,12 @@ def main():
     tokens_per_s = R * K_steps / elapsed   # query tokens (decode: one per sequence)
 
     hist_tokens = int((inp["row_pos"].astype(np.int64) + 1).sum())
-    idx_bytes = hist_tokens * IDX_BYTES_PER_TOKEN
+    if mq:
+        # K is read once per group of a sequence's rows: its longest history
+        groups = (inp["row_pos"].astype(np.int64) + 1).reshape(-1, mq).max(axis=1)
+        idx_bytes = int(groups.sum()) * IDX_BYTES_PER_TOKEN
+    else:
+        idx_bytes = hist_tokens * IDX_BYTES_PER_TOKEN
     sel = out_idx.cpu().numpy()
     n_sel = int((sel >= 0).sum())
     sfa_bytes = n_sel * SFA_BYTES_PER_ENTRY
@@ -249,7 +267,8 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, args.cpu_rows)
 
-    idx_name = "dsa_indexer_topk_seq" if one_seq else "dsa_indexer_topk"
+    idx_name = ("dsa_indexer_topk_seq" if one_seq else
+                "dsa_indexer_topk_mq" if mq else "dsa_indexer_topk")
     mfma = {idx_name: {"achieved": round(idx_tf, 1), "peak": FP8_PEAK_TFS, "unit": "TFLOP/s",
                        "frac": round(idx_tf / FP8_PEAK_TFS, 4), "flop": idx_flop,
                        "dtype": "fp8 e4m3 x e4m3, E8M0 block scales"},
@@ -267,7 +286,7 @@ def main():
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": traffic, "algorithmic_bytes": idx_bytes}
     rec = {
-        "metric": METRIC if not one_seq else METRIC_PREFILL,
+        "metric": METRIC_PREFILL if one_seq else METRIC_MQ if mq else METRIC,
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,

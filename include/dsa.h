@@ -207,6 +207,37 @@ int dsa_indexer_topk_seq(const void* q_fp8, const void* q_e8m0, const float* w,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * dsa_indexer_topk for multi-query decode: each of B sequences brings
+ * q_per_seq consecutive query rows, as when the target model verifies
+ * several drafted tokens in one pass (speculative decoding: "Deep Dive into
+ * Sparse Attention", section "3. Decoding Phase Optimization"; Day0 page,
+ * "System-Level Coordination").  Rows
+ * r = b*q_per_seq .. b*q_per_seq + q_per_seq - 1 form one tile whose K pages
+ * are read once for all of them; each row keeps its own causal limit
+ * row_pos[r] and its own Top-K.  A tile's pages are dealt to work-groups in
+ * chunks of 16-page units.
+ *
+ *   R          B * q_per_seq (a multiple of q_per_seq, else
+ *              DSA_ERR_INVALID_ARG);  q_per_seq 1..8
+ *   row_seq    [R] int32; the rows of one tile must name the same sequence
+ *              (the tile reads the pages of its first row's sequence; a tile
+ *              whose rows differ sets status bit 4 and is scored against
+ *              those pages)
+ *   bt_stride  <= 4096 pages (256K tokens)
+ *   other arguments, outputs, status bits and workspace (sized by
+ *   dsa_indexer_topk_workspace_size) as for dsa_indexer_topk.
+ * Scores are computed with the same operations in the same order as
+ * dsa_indexer_topk, so both entry points return identical bits.
+ */
+int dsa_indexer_topk_mq(const void* q_fp8, const void* q_e8m0, const float* w,
+                        const void* k_pool, int64_t pool_pages,
+                        const int32_t* block_table, int32_t bt_stride,
+                        const int32_t* row_seq, const int32_t* row_pos, int32_t R,
+                        int32_t q_per_seq, int32_t H_I, int32_t topk,
+                        int32_t* out_idx, float* out_score,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * TEST ONLY: the full score rows of dsa_indexer_topk, computed by the same
  * device code: out_scores[r*ld + s] = I(t,s) for s <= t, -inf for
  * t < s < ld.  Requires ld >= max(row_pos)+1 (positions beyond ld are not

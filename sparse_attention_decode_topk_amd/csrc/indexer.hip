@@ -68,7 +68,7 @@ static_assert(kScanHalves % kRing == 0, "the scan ring wraps at unit boundaries"
 // GPUs: 32-bit data format, no swizzle.
 constexpr int kRawBufferWord3 = 0x00020000;
 
-enum : uint32_t { kErrBadPage = 4u, kErrFallback = 8u };
+enum : uint32_t { kErrBadPage = 4u, kErrFallback = 8u, kErrMixedTile = 16u };
 
 struct Params {
   const uint8_t* q;      // [R, H, 128] E4M3
@@ -84,6 +84,8 @@ struct Params {
   int32_t H;
   int32_t topk;
   int32_t upr;           // units-per-row stride of ucount / uedge
+  int32_t tile_rows;     // row-tiled path: rows per tile (<= kTileRows), all of one sequence
+  int32_t chunk_units;   // row-tiled path: units per work item (0 = the whole tile)
   int32_t* out_idx;
   float* out_score;
   float* dump;           // score rows (test entry point only)
@@ -1273,6 +1275,13 @@ constexpr int kTileRows = 8;
 constexpr int kTileRowsPerWave = kTileRows / kWaves;   // 2
 constexpr int kPgRing = 4;                             // page buffers
 constexpr int kPgAhead = kPgRing - 1;                  // pages copied ahead
+// vmcnt of the page loop's waits (immediates of its inline assembly): a
+// page's copies have landed once only the younger pages' copies remain, plus,
+// for the first pages after a unit's filter, the filter's stores
+#define DSA_PG_WAIT 6
+#define DSA_PG_WAIT_AFTER_FILTER 42
+#define DSA_STR2(x) #x
+#define DSA_STR(x) DSA_STR2(x)
 // A page in LDS: token rows of 144 bytes (128 code bytes + 16 bytes of
 // padding, so that the 16 token rows one MFMA operand reads fall on distinct
 // banks), then the 256 scale bytes.  Counted in 16-byte granules:
@@ -1373,53 +1382,75 @@ __device__ __forceinline__ void emit_wave(const Params& P, int row, bool live_ro
   __builtin_amdgcn_raw_buffer_store_b32(edge, re, uoff, 0, 0);
 }
 
-template <int NHT>
+// TWO: two rows per wave (tiles of up to 8 rows); otherwise one row per wave
+// (tiles of up to 4 rows), so that every wave of a small tile scores a row.
+template <int NHT, bool TWO>
 __global__ __launch_bounds__(kThreads, 2) void indexer_tile_kernel(Params P) {
   __shared__ __attribute__((aligned(16))) TileSmem S;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hr = lane & 15, g = lane >> 4;
   const uint32_t ring0 = lds_addr(S.ring), junk = lds_addr(S.junk);
-  const int ntiles = (P.R + kTileRows - 1) / kTileRows;
-  bool bad = false;
+  const int TR = P.tile_rows;
+  const int ntiles = (P.R + TR - 1) / TR;
+  // work items: (tile, chunk of chunk_units units), or whole tiles
+  const int nchunks = P.chunk_units > 0 ? (P.upr + P.chunk_units - 1) / P.chunk_units : 1;
+  const int nitems = ntiles * nchunks;
+  bool bad = false, mixed = false;
   for (int round = 0;; ++round) {
     const int slot = round * (int)gridDim.x +
                      ((round & 1) ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x);
-    if (slot >= ntiles) break;
-    const int r0 = (ntiles - 1 - slot) * kTileRows;   // longest (last) tiles first
-    // rows of the tile: lane i < 8 holds row r0+i's position and page count
-    const bool rin = lane < kTileRows && r0 + lane < P.R;
+    if (slot >= nitems) break;
+    const int tslot = slot / nchunks, chunk = slot - tslot * nchunks;
+    const int r0 = (ntiles - 1 - tslot) * TR;   // longest (last) tiles first
+    // rows of the tile: lane i < TR holds row r0+i's position and page count;
+    // the tile's pages are those of the sequence of its first row
+    const bool rin = lane < TR && r0 + lane < P.R;
     const int t_l = rin ? P.row_pos[r0 + lane] : -1;
     const int np_l = rin ? row_pages(t_l, P.bt_stride) : 0;
     const int npt = __builtin_amdgcn_readlane((int)wave_incl_max((uint32_t)np_l), 63);
-    const int ra = r0 + kTileRowsPerWave * wv, rb = ra + 1;
-    const bool la = ra < P.R, lb = rb < P.R;
-    const int ta = __builtin_amdgcn_readlane(t_l, kTileRowsPerWave * wv);
-    const int tb = __builtin_amdgcn_readlane(t_l, kTileRowsPerWave * wv + 1);
-    const int npa = __builtin_amdgcn_readlane(np_l, kTileRowsPerWave * wv);
-    const int npb = __builtin_amdgcn_readlane(np_l, kTileRowsPerWave * wv + 1);
-    // every wave is done with the previous tile's ring and page ids
+    int seq = 0;
+    if (P.row_seq) {
+      seq = __builtin_amdgcn_readfirstlane(P.row_seq[r0]);
+      const int s_l = rin ? P.row_seq[r0 + lane] : seq;
+      mixed |= __builtin_amdgcn_ballot_w64(s_l != seq) != 0;
+    }
+    const int32_t* btrow = P.bt + (int64_t)seq * P.bt_stride;
+    constexpr int RPW = TWO ? 2 : 1;   // rows per wave
+    const int ra = r0 + RPW * wv, rb = ra + 1;
+    const bool la = RPW * wv < TR && ra < P.R;
+    const bool lb = TWO && RPW * wv + 1 < TR && rb < P.R;
+    const int ta = __builtin_amdgcn_readlane(t_l, RPW * wv);
+    const int tb = __builtin_amdgcn_readlane(t_l, RPW * wv + RPW - 1);
+    const int npa = __builtin_amdgcn_readlane(np_l, RPW * wv);
+    const int npb = __builtin_amdgcn_readlane(np_l, RPW * wv + RPW - 1);
+    // the chunk's units [cu0, cu0 + nun) of the tile's ceil(npt / 16)
+    const int nun_t = (npt + kUnitPages - 1) / kUnitPages;
+    const int cu0 = P.chunk_units > 0 ? chunk * P.chunk_units : 0;
+    const int nun = P.chunk_units > 0 ? min(P.chunk_units, nun_t - cu0) : nun_t;
+    if (nun <= 0) continue;   // uniform: the chunk lies past this tile's pages
+    const int pg_lo = kUnitPages * cu0, pg_hi = min(npt, kUnitPages * (cu0 + nun));
+    // every wave is done with the previous item's ring and page ids
     __syncthreads();
-    for (int p = tid; p < npt; p += kThreads) {
-      const int32_t id = P.bt[p];
+    for (int p = pg_lo + tid; p < pg_hi; p += kThreads) {
+      const int32_t id = btrow[p];
       const bool ok = id >= 0 && (int64_t)id < P.pool_pages;
       bad |= !ok;
       S.pt[p] = ok ? id : -1;
     }
     QOperand<NHT> Qa, Qb;
     load_q<NHT>(P, la ? ra : r0, Qa);
-    load_q<NHT>(P, lb ? rb : r0, Qb);
+    if (TWO) load_q<NHT>(P, lb ? rb : r0, Qb);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): nothing but page copies outstanding below
     __syncthreads();
     // Units are visited in rotated order, starting at a phase that depends on
     // the work-group's index within its XCD: the 64 work-groups of an XCD then
     // stream 8 different pages at any time instead of all hammering the same
-    // L2 lines.  Logical page q is page 16*((q/16 + u0) % nun) + q%16.
-    const int nun = (npt + kUnitPages - 1) / kUnitPages;
+    // L2 lines.  Logical page q is page 16*(cu0 + (q/16 + u0) % nun) + q%16.
     const int u0 = (int)(((blockIdx.x >> 3) & 7) * (uint32_t)nun / 8u);
     auto phys = [&](int q) {
       const int uq = q / kUnitPages + u0;
-      return kUnitPages * (uq >= nun ? uq - nun : uq) + q % kUnitPages;
+      return kUnitPages * (cu0 + (uq >= nun ? uq - nun : uq)) + q % kUnitPages;
     };
     auto issue_page = [&](int q) {
       const int pq = phys(q);
@@ -1441,7 +1472,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_tile_kernel(Params P) {
 #pragma unroll
     for (int q = 0; q < kPgAhead; ++q) issue_page(q);
     for (int uu = 0; uu < nun; ++uu) {
-      const int u = uu + u0 >= nun ? uu + u0 - nun : uu + u0;   // physical unit
+      const int u = cu0 + (uu + u0 >= nun ? uu + u0 - nun : uu + u0);   // physical unit
       uint32_t ka[kUnitPages], kb[kUnitPages];
 #pragma unroll
       for (int pi = 0; pi < kUnitPages; ++pi) {
@@ -1454,11 +1485,12 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_tile_kernel(Params P) {
         // Every logical page takes this step, present or not, so that each
         // step consumes exactly one page's copies.
         if (uu > 0 && pi < kPgAhead)
-          asm volatile("s_waitcnt vmcnt(42)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          asm volatile("s_waitcnt vmcnt(" DSA_STR(DSA_PG_WAIT_AFTER_FILTER) ")\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         else
-          asm volatile("s_waitcnt vmcnt(6)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          asm volatile("s_waitcnt vmcnt(" DSA_STR(DSA_PG_WAIT) ")\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         issue_page(L + kPgAhead);
         if (p >= npt) continue;                                    // uniform: past the tile
+        if (!la && !lb) continue;                                  // uniform: a wave without rows
         const uint8_t* pg = S.ring[L % kPgRing];
         const bool pok = S.pt[p] >= 0;
         // Token tile j's key operand: two 16-byte reads and a scale byte.
@@ -1475,7 +1507,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_tile_kernel(Params P) {
         // token tile's first, is issued before the FMA chain reads MFMA m,
         // so the matrix unit works while the vector unit consumes.  Per row
         // and token tile the chain is head_part's.
-        constexpr int kM = 2 * NHT;
+        constexpr int kM = TWO ? 2 * NHT : NHT;
         float pa[4], pb[4];
         v8i kc, kn;
         int sc, sn = 0;
@@ -1499,10 +1531,10 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_tile_kernel(Params P) {
           sc = sn;
         }
         // lane group g receives token tile g: lane l holds position 64p + l
-        const float sa = rows_sum_scatter(pa), sb = rows_sum_scatter(pb);
+        const float sa = rows_sum_scatter(pa), sb = TWO ? rows_sum_scatter(pb) : 0.f;
         const int pos = p * kPage + lane;
         ka[pi] = pok && pos <= ta ? score_key(sa) : 0u;
-        kb[pi] = pok && pos <= tb ? score_key(sb) : 0u;
+        kb[pi] = TWO && pok && pos <= tb ? score_key(sb) : 0u;
       }
       uint32_t ea, eb;
       tile_edges(P, u, la, ta, npa, ka, lb, tb, npb, kb, &ea, &eb);
@@ -1512,10 +1544,12 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_tile_kernel(Params P) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // the padding copies past the tile have landed
   }
   if (bad && tid == 0) flag_error(P.hdr, kErrBadPage);
+  if (mixed && tid == 0) flag_error(P.hdr, kErrMixedTile);
 }
-static_assert(kTileRowsPerWave * kTileStores + kPgDmaPerWave * (kPgAhead - 1) == 42,
+static_assert(kTileRowsPerWave * kTileStores + kPgDmaPerWave * (kPgAhead - 1) == DSA_PG_WAIT_AFTER_FILTER,
               "the page loop's wait after a filter");
-static_assert(kPgDmaPerWave * (kPgAhead - 1) == 6, "the page loop's wait");
+static_assert(kPgDmaPerWave * (kPgAhead - 1) == DSA_PG_WAIT, "the page loop's wait");
+static_assert(DSA_PG_WAIT_AFTER_FILTER < 64, "vmcnt holds 6 bits");
 
 // ---- host side ----------------------------------------------------------------
 
@@ -1550,12 +1584,12 @@ void* pick_kernel(int nht, KernelKind kind) {
   }
 }
 
-void* pick_tile_kernel(int nht) {
+void* pick_tile_kernel(int nht, bool two) {
   switch (nht) {
-    case 1: return (void*)&indexer_tile_kernel<1>;
-    case 2: return (void*)&indexer_tile_kernel<2>;
-    case 3: return (void*)&indexer_tile_kernel<3>;
-    default: return (void*)&indexer_tile_kernel<4>;
+    case 1: return two ? (void*)&indexer_tile_kernel<1, true> : (void*)&indexer_tile_kernel<1, false>;
+    case 2: return two ? (void*)&indexer_tile_kernel<2, true> : (void*)&indexer_tile_kernel<2, false>;
+    case 3: return two ? (void*)&indexer_tile_kernel<3, true> : (void*)&indexer_tile_kernel<3, false>;
+    default: return two ? (void*)&indexer_tile_kernel<4, true> : (void*)&indexer_tile_kernel<4, false>;
   }
 }
 
@@ -1563,8 +1597,8 @@ void* pick_tile_kernel(int nht) {
 int resident_capacity(void* fn, int slot, int threads) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
-  static int cached[64][16];
-  static bool have[64][16];
+  static int cached[64][20];
+  static bool have[64][20];
   if (dev < 64 && have[dev][slot]) return cached[dev][slot];
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return -1;
@@ -1642,6 +1676,8 @@ Params base_params(const void* q_fp8, const void* q_e8m0, const float* w, const 
   P.R = R;
   P.H = H_I;
   P.upr = units_stride(bt_stride);
+  P.tile_rows = kTileRows;
+  P.chunk_units = 0;
   return P;
 }
 
@@ -1736,7 +1772,7 @@ extern "C" int dsa_indexer_topk_seq(const void* q_fp8, const void* q_e8m0, const
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   hipStream_t s = dsa_host::as_stream(stream);
   const int nht = (H_I + 15) / 16;
-  void* tk = pick_tile_kernel(nht);
+  void* tk = pick_tile_kernel(nht, true);
   void* sel = pick_kernel(nht, kSelect);
   const int cap = resident_capacity(tk, 12 + nht - 1, kThreads);
   if (cap <= 0) return DSA_ERR_HIP;
@@ -1756,6 +1792,65 @@ extern "C" int dsa_indexer_topk_seq(const void* q_fp8, const void* q_e8m0, const
     P.cand = reinterpret_cast<uint2*>(ws + L.cand);
     const int ntiles = (rn + kTileRows - 1) / kTileRows;
     const int G = std::min(cap, ntiles);
+    void* args[] = {&P};
+    if (hipLaunchKernel(tk, dim3((unsigned)G), dim3(kThreads), args, 0, s) != hipSuccess)
+      return DSA_ERR_HIP;
+    if (hipLaunchKernel(sel, dim3((unsigned)rn), dim3(kSelThreads), args, 0, s) != hipSuccess)
+      return DSA_ERR_HIP;
+  }
+  return DSA_OK;
+}
+
+extern "C" int dsa_indexer_topk_mq(const void* q_fp8, const void* q_e8m0, const float* w,
+                                   const void* k_pool, int64_t pool_pages,
+                                   const int32_t* block_table, int32_t bt_stride,
+                                   const int32_t* row_seq, const int32_t* row_pos, int32_t R,
+                                   int32_t q_per_seq, int32_t H_I, int32_t topk,
+                                   int32_t* out_idx, float* out_score, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  int st = validate(q_fp8, q_e8m0, w, k_pool, pool_pages, block_table, bt_stride, row_seq, row_pos,
+                    R, H_I);
+  if (st != DSA_OK) return st;
+  if (out_idx == nullptr) return DSA_ERR_INVALID_ARG;
+  if (q_per_seq < 1 || q_per_seq > kTileRows) return DSA_ERR_UNSUPPORTED;
+  if (R % q_per_seq != 0) return DSA_ERR_INVALID_ARG;
+  if (bt_stride > kTileMaxPages) return DSA_ERR_UNSUPPORTED;
+  if (topk < 1 || topk > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
+  if (R == 0) return DSA_OK;
+  const int64_t rows = std::min<int64_t>(R, kMaxRows);
+  const Layout L = layout_for(rows, bt_stride);
+  if (workspace == nullptr || workspace_bytes < L.total) return DSA_ERR_WORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipStream_t s = dsa_host::as_stream(stream);
+  const int nht = (H_I + 15) / 16;
+  const bool two = q_per_seq > kWaves;   // more rows per tile than waves
+  void* tk = pick_tile_kernel(nht, two);
+  void* sel = pick_kernel(nht, kSelect);
+  const int cap = resident_capacity(tk, (two ? 12 : 16) + nht - 1, kThreads);
+  if (cap <= 0) return DSA_ERR_HIP;
+  const int upr = units_stride(bt_stride);
+  const int step = kMaxRows - kMaxRows % q_per_seq;   // whole sequences per launch
+  for (int r0 = 0; r0 < R; r0 += step) {
+    const int rn = std::min(step, R - r0);
+    Params P = base_params(q_fp8, q_e8m0, w, k_pool, pool_pages, block_table, bt_stride,
+                           row_seq + r0, row_pos + r0, rn, H_I);
+    P.q += (int64_t)r0 * H_I * kIdxDim;
+    P.qs += (int64_t)r0 * H_I * 4;
+    P.w += (int64_t)r0 * H_I;
+    P.topk = topk;
+    P.out_idx = out_idx + (int64_t)r0 * topk;
+    P.out_score = out_score ? out_score + (int64_t)r0 * topk : nullptr;
+    P.hdr = reinterpret_cast<uint32_t*>(ws + L.hdr);
+    P.ucount = reinterpret_cast<uint32_t*>(ws + L.ucount);
+    P.uedge = reinterpret_cast<uint32_t*>(ws + L.uedge);
+    P.cand = reinterpret_cast<uint2*>(ws + L.cand);
+    // one tile per sequence, its units dealt in chunks so that about one
+    // work item per resident workgroup exists
+    const int64_t ntiles = rn / q_per_seq;
+    P.tile_rows = q_per_seq;
+    P.chunk_units = (int)std::max<int64_t>(1, (ntiles * upr + cap - 1) / cap);
+    const int64_t nitems = ntiles * ((upr + P.chunk_units - 1) / P.chunk_units);
+    const int64_t G = std::min<int64_t>(cap, nitems);
     void* args[] = {&P};
     if (hipLaunchKernel(tk, dim3((unsigned)G), dim3(kThreads), args, 0, s) != hipSuccess)
       return DSA_ERR_HIP;

@@ -47,6 +47,8 @@ SIGNATURES = {
     "dsa_indexer_topk_seq_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
     "dsa_indexer_topk_seq": (_c.c_int, [_P, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32,
                                         _P, _P, _P, _SZ, _P]),
+    "dsa_indexer_topk_mq": (_c.c_int, [_P, _P, _P, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _I32,
+                                       _I32, _P, _P, _P, _SZ, _P]),
     "dsa_indexer_scores": (_c.c_int, [_P, _P, _P, _P, _I64, _P, _I32, _P, _P, _I32, _I32,
                                       _P, _I64, _P]),
     "dsa_sparse_attn_workspace_size": (_SZ, [_I32, _I32, _I32]),
@@ -206,6 +208,34 @@ def dsa_indexer_topk_seq(q_fp8, q_e8m0, w, k_pool, block_table_row, row_pos, top
                                       _ptr(block_table_row), n_pages, _ptr(row_pos), R, H, topk,
                                       _ptr(out_idx), _ptr(out_score), _ptr(workspace),
                                       workspace.numel(), _stream()), "dsa_indexer_topk_seq")
+    return out_idx, out_score
+
+
+def dsa_indexer_topk_mq(q_fp8, q_e8m0, w, k_pool, block_table, row_seq, row_pos, q_per_seq: int,
+                        topk: int, out_idx=None, out_score=None, workspace=None,
+                        with_scores: bool = True):
+    """Multi-query decode: rows come in groups of q_per_seq consecutive rows of
+    one sequence whose K pages are read once per group; same results as
+    dsa_indexer_topk."""
+    R, H = q_fp8.shape[0], q_fp8.shape[1]
+    for t, dt, n in ((q_fp8, torch.uint8, "q_fp8"), (q_e8m0, torch.uint8, "q_e8m0"),
+                     (w, torch.float32, "w"), (k_pool, torch.uint8, "k_pool"),
+                     (block_table, torch.int32, "block_table"), (row_seq, torch.int32, "row_seq"),
+                     (row_pos, torch.int32, "row_pos")):
+        _need(t, dt, n)
+    dev = q_fp8.device
+    if out_idx is None:
+        out_idx = torch.empty((R, topk), dtype=torch.int32, device=dev)
+    if out_score is None and with_scores:
+        out_score = torch.empty((R, topk), dtype=torch.float32, device=dev)
+    bt_stride = block_table.shape[1]
+    if workspace is None:
+        workspace = indexer_workspace(R, bt_stride, H, topk, dev)
+    _check(lib().dsa_indexer_topk_mq(_ptr(q_fp8), _ptr(q_e8m0), _ptr(w), _ptr(k_pool), k_pool.shape[0],
+                                     _ptr(block_table), bt_stride, _ptr(row_seq), _ptr(row_pos), R,
+                                     q_per_seq, H, topk, _ptr(out_idx), _ptr(out_score),
+                                     _ptr(workspace), workspace.numel(), _stream()),
+           "dsa_indexer_topk_mq")
     return out_idx, out_score
 
 

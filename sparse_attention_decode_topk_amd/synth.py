@@ -57,6 +57,7 @@ class Config:
     # query rows: "last" = one decode row per sequence at t = L-1,
     # "all" = every position of sequence 0, or an explicit (first, count) range
     rows: object = "last"
+    q_per_seq: int = 1         # with rows="last": query rows per sequence, t = L-q .. L-1
     needles: int = 0
     identity_pages: bool = False
     description: str = ""
@@ -83,6 +84,12 @@ CONFIGS: Dict[str, Config] = {
                                        rows=(131072 - 8192, 8192),
                                        description="1 seq, 8192 query rows t=122880..131071 "
                                                    "against a 131072-token cache"),
+    # multi-query decode (speculative verification of drafted tokens): the
+    # long-context decode batch with 4 query tokens per sequence
+    "decode_mtp4_128k_b8": Config(6, "decode_mtp4_128k_b8", batch=8, h_index=64, h_attn=128,
+                                  topk=2048, ctx=131072, q_per_seq=4,
+                                  description="B=8 x 4 query tokens t=L-4..L-1, L=131072, "
+                                              "shuffled pages"),
 }
 CONFIG_ORDER: List[str] = list(CONFIGS)
 
@@ -137,7 +144,10 @@ def lengths(cfg: Config) -> np.ndarray:
 def rows_of(cfg: Config, seq_lens: np.ndarray):
     """Query rows as (row_seq, row_pos) with row_pos the causal limit t."""
     if cfg.rows == "last":
-        return (np.arange(cfg.batch, dtype=np.int32), (seq_lens - 1).astype(np.int32))
+        q = cfg.q_per_seq
+        row_seq = np.repeat(np.arange(cfg.batch, dtype=np.int32), q)
+        row_pos = (seq_lens.astype(np.int64)[:, None] - q + np.arange(q)[None, :]).reshape(-1)
+        return row_seq, row_pos.astype(np.int32)
     if cfg.rows == "all":
         L = int(seq_lens[0])
         return np.zeros(L, dtype=np.int32), np.arange(L, dtype=np.int32)

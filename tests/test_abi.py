@@ -120,3 +120,27 @@ def test_sparse_attn_argument_errors(lib):
     assert _sfa_call(lib, ws=None) == 3
     assert _sfa_call(lib, wsb=8) == 3
     assert _sfa_call(lib, R=0) == 0
+
+
+def _mq_call(lib, **kw):
+    a = dict(q=FAKE, qs=FAKE, w=FAKE, kpool=FAKE, pages=100, bt=FAKE, bts=4, rs=FAKE, rp=FAKE,
+             R=8, qps=4, H=64, K=2048, oi=FAKE, osc=None, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.dsa_indexer_topk_mq(a["q"], a["qs"], a["w"], a["kpool"], a["pages"], a["bt"],
+                                   a["bts"], a["rs"], a["rp"], a["R"], a["qps"], a["H"], a["K"],
+                                   a["oi"], a["osc"], a["ws"], a["wsb"], None)
+
+
+def test_multi_query_indexer_argument_errors(lib):
+    assert _mq_call(lib, q=None) == 1
+    assert _mq_call(lib, rs=None) == 1
+    assert _mq_call(lib, oi=None) == 1
+    assert _mq_call(lib, qps=0) == 2
+    assert _mq_call(lib, qps=9) == 2
+    assert _mq_call(lib, R=6) == 1          # not a multiple of q_per_seq
+    assert _mq_call(lib, bts=4097) == 2     # tiles hold at most 4096 page ids
+    assert _mq_call(lib, H=65) == 2
+    assert _mq_call(lib, K=2049) == 2
+    assert _mq_call(lib, ws=None) == 3
+    assert _mq_call(lib, wsb=16) == 3
+    assert _mq_call(lib, R=0) == 0

@@ -256,3 +256,77 @@ def test_seq_path_exact_fallback(need_gpu):
     torch.cuda.synchronize()
     assert torch.equal(a_idx, b_idx) and torch.equal(a_sc, b_sc)
     assert (int(ws.view(torch.int32)[2].item()) & 8) != 0
+
+
+def _mq_topk(st, q_per_seq, topk=None, row_pos=None, workspace=None):
+    return ops.dsa_indexer_topk_mq(st.q_fp8, st.q_e8m0, st.w, st.k_pool, st.block_table, st.row_seq,
+                                   st.row_pos if row_pos is None else row_pos, q_per_seq,
+                                   st.topk if topk is None else topk, workspace=workspace)
+
+
+def test_multi_query_decode_parity(need_gpu):
+    """Multi-query decode at 128K (8 sequences x 4 query tokens): the
+    multi-query entry point returns the per-row entry point's bits on every
+    row, and sampled rows pass the oracle rule."""
+    st = state("decode_mtp4_128k_b8")
+    say(f"[indexer mq] decode_mtp4_128k_b8 R={st.R}")
+    ws = ops.indexer_workspace(st.R, st.block_table.shape[1], st.H_I, st.topk)
+    a_idx, a_sc = st.indexer()
+    b_idx, b_sc = _mq_topk(st, 4, workspace=ws)
+    c_idx, c_sc = _mq_topk(st, 4, workspace=ws)   # workspace reuse
+    torch.cuda.synchronize()
+    assert torch.equal(a_idx, b_idx) and torch.equal(a_sc, b_sc)
+    assert torch.equal(b_idx, c_idx) and torch.equal(b_sc, c_sc)
+    assert int(ws.view(torch.int32)[2].item()) & 4 == 0
+    o = Oracle(st.inp)
+    b_idx, b_sc = b_idx.cpu().numpy(), b_sc.cpu().numpy()
+    for r in (0, 3, 13, 31):
+        check_topk_row(b_idx[r], b_sc[r], o.topk(r), st.topk, int(st.inp["row_pos"][r]))
+    o.drop_cache()
+
+
+@pytest.mark.parametrize("q_per_seq", [1, 3, 8])
+def test_multi_query_ragged(need_gpu, q_per_seq):
+    """Ragged histories, rows of a group with different limits (short ones,
+    t < 0, t beyond the group's longest), several Top-K sizes: bit-equal to
+    the per-row entry point, and the oracle rule on every row."""
+    B = 5
+    cfg = synth.Config(92, "mq_ragged", batch=B, h_index=64, h_attn=16, topk=2048,
+                       ragged=(100, 9000), q_per_seq=q_per_seq)
+    inp = synth.make(cfg, with_sfa=False)
+    rng = np.random.default_rng(q_per_seq)
+    pos = inp["row_pos"].copy()
+    lens = inp["seq_lens"]
+    for r in range(len(pos)):
+        b = r // q_per_seq
+        pos[r] = rng.integers(-1, int(lens[b]))
+    pos[0] = -1
+    pos[-1] = int(lens[B - 1]) - 1
+    inp["row_pos"] = pos.astype(np.int32)
+    st = DeviceState(inp, with_sfa=False)
+    say(f"[indexer mq] ragged q_per_seq={q_per_seq} R={st.R}")
+    o = Oracle(inp)
+    for K in (2048, 1, 300):
+        a_idx, a_sc = st.indexer(topk=K)
+        b_idx, b_sc = _mq_topk(st, q_per_seq, topk=K)
+        torch.cuda.synchronize()
+        assert torch.equal(a_idx, b_idx), f"K={K}"
+        assert torch.equal(a_sc, b_sc), f"K={K}"
+        b_idx, b_sc = b_idx.cpu().numpy(), b_sc.cpu().numpy()
+        for r in range(st.R):
+            t = int(pos[r])
+            if t < 0:
+                assert np.all(b_idx[r] == -1)
+                continue
+            check_topk_row(b_idx[r], b_sc[r], o.topk(r, K), K, t)
+    o.drop_cache()
+
+
+def test_multi_query_mixed_group_flagged(need_gpu):
+    """A group whose rows name different sequences sets status bit 4."""
+    st = state("decode_ragged_b32")
+    say("[indexer mq] mixed group flag")
+    ws = ops.indexer_workspace(st.R, st.block_table.shape[1], st.H_I, st.topk)
+    _mq_topk(st, 2, workspace=ws)   # rows 2b, 2b+1 belong to different sequences
+    torch.cuda.synchronize()
+    assert int(ws.view(torch.int32)[2].item()) & 16 != 0
