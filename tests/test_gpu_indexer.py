@@ -285,13 +285,14 @@ def test_multi_query_decode_parity(need_gpu):
     o.drop_cache()
 
 
-@pytest.mark.parametrize("q_per_seq", [1, 3, 8])
-def test_multi_query_ragged(need_gpu, q_per_seq):
+@pytest.mark.parametrize("q_per_seq,h_index", [(1, 64), (3, 64), (8, 64), (2, 20)])
+def test_multi_query_ragged(need_gpu, q_per_seq, h_index):
     """Ragged histories, rows of a group with different limits (short ones,
-    t < 0, t beyond the group's longest), several Top-K sizes: bit-equal to
-    the per-row entry point, and the oracle rule on every row."""
+    t < 0, t beyond the group's longest), several Top-K sizes, a head count
+    that is not a multiple of 16: bit-equal to the per-row entry point, and
+    the oracle rule on every row."""
     B = 5
-    cfg = synth.Config(92, "mq_ragged", batch=B, h_index=64, h_attn=16, topk=2048,
+    cfg = synth.Config(92, "mq_ragged", batch=B, h_index=h_index, h_attn=16, topk=2048,
                        ragged=(100, 9000), q_per_seq=q_per_seq)
     inp = synth.make(cfg, with_sfa=False)
     rng = np.random.default_rng(q_per_seq)
