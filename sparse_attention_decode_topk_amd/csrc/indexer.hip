@@ -513,13 +513,16 @@ __device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
   return max(min(a, b), min(max(a, b), c));   // one v_med3_u32
 }
 
-// The three largest of a lane's keys, m[0] >= m[1] >= m[2] (0 = none).
-__device__ __forceinline__ void lane_top3(const uint32_t (&k)[kUnitPages], uint32_t (&m)[3]) {
-  m[0] = m[1] = m[2] = 0u;
+// The N largest of a lane's keys, m[0] >= ... >= m[N-1] (0 = none): each
+// key is inserted by clamping it between neighbours, from the bottom up.
+template <int N>
+__device__ __forceinline__ void lane_top(const uint32_t (&k)[kUnitPages], uint32_t (&m)[N]) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) m[j] = 0u;
 #pragma unroll
   for (int i = 0; i < kUnitPages; ++i) {
-    m[2] = umed3(m[1], m[2], k[i]);
-    m[1] = umed3(m[0], m[1], k[i]);
+#pragma unroll
+    for (int j = N - 1; j > 0; --j) m[j] = umed3(m[j - 1], m[j], k[i]);
     m[0] = max(m[0], k[i]);
   }
 }
@@ -566,15 +569,22 @@ __device__ __forceinline__ uint32_t key_floor(const uint32_t (&v)[D], uint32_t n
   return a;
 }
 
-// The per-lane top three suffice for the edge search when the quota is at
-// most this (three keys of each of 64 lanes).
-constexpr uint32_t kTop3Quota = 3 * 64;
+// The edge search runs over each lane's three largest keys when the quota
+// is at most 64 (one key per lane on average), over its five largest up to
+// 320, and over all keys above.  The subset must hold about the quota
+// largest keys: a lane that holds more of them than the subset keeps makes
+// the edge lower and the unit keeps more candidates (a Binomial(16, q/1024)
+// count per lane exceeds 3 for q = 192 often enough to add a hundred
+// candidates; 5 rarely).
+constexpr uint32_t kTop3Quota = 64;
+constexpr uint32_t kTop5Quota = 5 * 64;
 
 // Local filter of a scored unit (keys of unit-local position 64i + lane in
 // S.keys).  Every wave reads all 1024 keys and finds the same edge: the
 // largest 16-bit-prefix key that at least `quota` keys reach, searched over
-// each lane's three largest keys (a subset, so the edge never exceeds the
-// unit's quota-th largest key), or over all keys for quotas above 192.
+// each lane's three or five largest keys (a subset, so the edge never
+// exceeds the unit's quota-th largest key), or over all keys for quotas
+// above 320.
 // Keys at or above the edge are emitted in position order: wave w writes
 // its share of the pages (16 / waves), at offsets from the per-page ballot counts that every
 // wave holds.  No atomics; one barrier, once every wave holds the keys in
@@ -592,8 +602,12 @@ __device__ __forceinline__ void filter_unit(const Params& P, ScanSmem& S, const 
   if (quota < (uint32_t)ntok) {
     if (quota <= kTop3Quota) {
       uint32_t m[3];
-      lane_top3(k, m);
+      lane_top<3>(k, m);
       edge = key_floor<3>(m, quota);
+    } else if (quota <= kTop5Quota) {
+      uint32_t m[5];
+      lane_top<5>(k, m);
+      edge = key_floor<5>(m, quota);
     } else {
       edge = key_floor<kUnitPages>(k, quota);
     }
@@ -1002,23 +1016,31 @@ __device__ __forceinline__ bool fast_find(SelSmem& S, const uint32_t* H, uint32_
   return true;
 }
 
-// Returns false, having written nothing, when the row does not fit the path
-// (more than kFastUnits units, or a unit with more than 64 candidates) or
-// when fewer than K candidates reach the largest unit edge; the caller then
-// takes the general path.  Block-uniform.
-__device__ __forceinline__ bool select_fast(const Params& P, SelSmem& S, int row) {
+// Layout J (1, 2, 4 or 8): wave w owns units (8/J)w .. (8/J)w + 8/J - 1 and
+// holds slots lane, lane + 64, ..., lane + 64(J-1) of each, eight keys per
+// lane in position order (unit, then slot); so the path takes rows of up to
+// 128/J units of up to 64J candidates.
+// Returns 1 when the row is done.  Otherwise nothing was written and it
+// returns the layout that would fit the row (2, 4 or 8, only from layout 1:
+// the row has a unit with more than 64J candidates but few enough units),
+// or 0: the row fits no layout, or fewer than K candidates reach the
+// largest unit edge; the caller then takes the general path.  Block-uniform.
+template <int J>
+__device__ __forceinline__ int select_fast(const Params& P, SelSmem& S, int row) {
+  constexpr int UPW = kFastPer / J;           // units per wave
+  constexpr int kUnits = kFastUnits / J;      // units per row
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int u0 = kFastPer * wv;
+  const int u0 = UPW * wv;
   const int K = P.topk;
-  const int nu = min(P.upr, kFastUnits);   // units whose slices exist in the workspace
-  // loads: row position; count and edge of unit u0 + lane (lanes < 8);
-  // slot `lane` of each of the wave's units
+  const int nu = min(P.upr, kUnits);   // units whose slices exist in the workspace
+  // loads: row position; count and edge of unit u0 + lane (lanes < UPW);
+  // slot lane + 64j of each of the wave's units
   const int t = P.row_pos[row];
   const int64_t ub = (int64_t)row * P.upr;
   const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(P.ucount + ub, (short)0, nu * 4, kRawBufferWord3);
   const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(P.uedge + ub, (short)0, nu * 4, kRawBufferWord3);
-  const uint32_t uoff = lane < kFastPer ? (uint32_t)(u0 + lane) * 4u : (uint32_t)nu * 4u;
+  const uint32_t uoff = lane < UPW ? (uint32_t)(u0 + lane) * 4u : (uint32_t)nu * 4u;
   uint32_t cnt_l = __builtin_amdgcn_raw_buffer_load_b32(rc, uoff, 0, 0);
   uint32_t edge_l = __builtin_amdgcn_raw_buffer_load_b32(re, uoff, 0, 0);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -1026,7 +1048,9 @@ __device__ __forceinline__ bool select_fast(const Params& P, SelSmem& S, int row
   uint32_t k[kFastPer], p[kFastPer];
 #pragma unroll
   for (int i = 0; i < kFastPer; ++i) {
-    const v2u v = __builtin_amdgcn_raw_buffer_load_b64(rk, (uint32_t)(((u0 + i) * kUnitTok + lane) * 8), 0, 0);
+    const int a = i / J, jj = i % J;
+    const v2u v = __builtin_amdgcn_raw_buffer_load_b64(
+        rk, (uint32_t)(((u0 + a) * kUnitTok + lane + 64 * jj) * 8), 0, 0);
     k[i] = v[0];
     p[i] = v[1];
   }
@@ -1037,17 +1061,17 @@ __device__ __forceinline__ bool select_fast(const Params& P, SelSmem& S, int row
     for (int i = 0; i < 2 * kBins / 4 / kSelThreads; ++i) h4[threadIdx.x + i * kSelThreads] = make_uint4(0, 0, 0, 0);
   }
   const int units_r = row_units(t, P.bt_stride);
-  if (units_r > kFastUnits) return false;
+  if (units_r > kUnits) return 0;
   const bool take_all = t < 0 || unit_quota(t, K) == 0xFFFFFFFFu;   // at most K positions
-  const bool uin = lane < kFastPer && u0 + lane < units_r;
+  const bool uin = lane < UPW && u0 + lane < units_r;
   cnt_l = uin ? cnt_l : 0u;
   edge_l = uin ? edge_l : 0u;
   const uint32_t csum_l = wave_incl_scan(cnt_l);   // lane i: candidates of units u0 .. u0+i
   uint32_t km = 0;
 #pragma unroll
   for (int i = 0; i < kFastPer; ++i) {
-    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)cnt_l, i);
-    if ((uint32_t)lane >= c) k[i] = 0u;
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)cnt_l, i / J);
+    if ((uint32_t)(lane + 64 * (i % J)) >= c) k[i] = 0u;
     km = max(km, k[i]);
   }
   const uint32_t cmax_w = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_max(cnt_l), 63);
@@ -1066,16 +1090,23 @@ __device__ __forceinline__ bool select_fast(const Params& P, SelSmem& S, int row
     emax = max(emax, x.z);
     kmax = max(kmax, x.w);
   }
-  if (cmax > 64u) return false;
+  if (cmax > 64u * J) {
+    // a layout with more slots per unit, if the row has few enough units
+    if (J > 1) return 0;
+    for (int jn = 2; jn <= kFastPer; jn *= 2)
+      if (cmax <= 64u * jn && units_r <= kFastUnits / jn) return jn;
+    return 0;
+  }
   gint32* oidx = (gint32*)(P.out_idx + (int64_t)row * K);
   gfloat* osc = P.out_score ? (gfloat*)(P.out_score + (int64_t)row * K) : nullptr;
   if (take_all) {
     // every candidate is kept: unit u0+i's slot j goes to its flat index
 #pragma unroll
     for (int i = 0; i < kFastPer; ++i) {
-      const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)cnt_l, i);
-      const uint32_t f = wbase + (uint32_t)__builtin_amdgcn_readlane((int)csum_l, i) - c + lane;
-      if ((uint32_t)lane < c && f < (uint32_t)K) {
+      const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)cnt_l, i / J);
+      const uint32_t sl = (uint32_t)(lane + 64 * (i % J));
+      const uint32_t f = wbase + (uint32_t)__builtin_amdgcn_readlane((int)csum_l, i / J) - c + sl;
+      if (sl < c && f < (uint32_t)K) {
         oidx[f] = (int32_t)p[i];
         if (osc) osc[f] = key_score(k[i]);
       }
@@ -1084,12 +1115,12 @@ __device__ __forceinline__ bool select_fast(const Params& P, SelSmem& S, int row
       oidx[f] = -1;
       if (osc) osc[f] = -__builtin_huge_valf();
     }
-    return true;
+    return 1;
   }
   // radix passes over [lo, kmax]: pass p bins the keys of [base, base + span)
   // by (key - base) >> shift into histogram p & 1
   const uint32_t lo = max(emax, 1u);
-  if (kmax < lo) return false;
+  if (kmax < lo) return 0;
   int shift = range_shift(kmax - lo);
   uint64_t span = (uint64_t)(kmax - lo) + 1;
   uint32_t base = lo, need = (uint32_t)K;
@@ -1105,7 +1136,7 @@ __device__ __forceinline__ bool select_fast(const Params& P, SelSmem& S, int row
       if (k[i] >= base && (uint64_t)(k[i] - base) < span) atomicAdd(&H[(k[i] - base) >> shift], 1u);
     __syncthreads();
     uint32_t bin, above;
-    if (!fast_find(S, H, S.wsum[pass & 1], need, &bin, &above)) return false;   // pass 0 only
+    if (!fast_find(S, H, S.wsum[pass & 1], need, &bin, &above)) return 0;   // pass 0 only
     base += bin << shift;
     need -= above;
     if (shift == 0) break;
@@ -1152,7 +1183,7 @@ __device__ __forceinline__ bool select_fast(const Params& P, SelSmem& S, int row
     gt_before += (uint32_t)__builtin_popcountll(gb);
     eq_before += (uint32_t)__builtin_popcountll(eb);
   }
-  return true;
+  return 1;
 }
 
 // Rescore unit u of the row in full and publish all of its keys.
@@ -1183,7 +1214,13 @@ template <int NHT>
 __global__ __launch_bounds__(kSelThreads, 1) void indexer_select_kernel(Params P) {
   __shared__ SelSmem S;
   const int row = blockIdx.x;
-  if (select_fast(P, S, row)) return;
+  int fast = select_fast<1>(P, S, row);
+  if (fast > 1) {
+    __syncthreads();   // every wave has read the first attempt's LDS results
+    fast = fast == 2 ? select_fast<2>(P, S, row) : fast == 4 ? select_fast<4>(P, S, row)
+                                                             : select_fast<8>(P, S, row);
+  }
+  if (fast == 1) return;
   // general path: waves 0..3 (a barrier first, so that no wave still reads
   // what the fast path left in LDS; waves that have ended no longer count
   // at a barrier)
@@ -1319,10 +1356,10 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
 
 // Local filter edges of unit u for a wave's two rows (keys k[i] = position
 // 64(16u+i) + lane).  A unit keeps every key >= its edge: at least its
-// quota of keys (all of them when it has no more than the quota).  With a
-// quota of at most 192 the search runs over each lane's three largest keys,
-// a subset that holds the unit's quota largest keys unless a lane holds
-// more than three of them (then the edge is lower and more keys are kept).
+// quota of keys (all of them when it has no more than the quota).  The
+// search runs over each lane's three or five largest keys (kTop3Quota,
+// kTop5Quota), a subset that holds the unit's quota largest keys unless a
+// lane holds more of them (then the edge is lower and more keys are kept).
 __device__ __forceinline__ void tile_edges(const Params& P, int u, bool la, int ta, int npa,
                                            const uint32_t (&ka)[kUnitPages], bool lb, int tb,
                                            int npb, const uint32_t (&kb)[kUnitPages],
@@ -1337,9 +1374,14 @@ __device__ __forceinline__ void tile_edges(const Params& P, int u, bool la, int 
   if (na == 0xFFFFFFFFu && nb == 0xFFFFFFFFu) return;
   if ((na <= kTop3Quota || na == 0xFFFFFFFFu) && (nb <= kTop3Quota || nb == 0xFFFFFFFFu)) {
     uint32_t ma[3], mb[3];
-    lane_top3(ka, ma);
-    lane_top3(kb, mb);
+    lane_top<3>(ka, ma);
+    lane_top<3>(kb, mb);
     key_floor2<3>(ma, mb, na, nb, ea, eb);
+  } else if ((na <= kTop5Quota || na == 0xFFFFFFFFu) && (nb <= kTop5Quota || nb == 0xFFFFFFFFu)) {
+    uint32_t ma[5], mb[5];
+    lane_top<5>(ka, ma);
+    lane_top<5>(kb, mb);
+    key_floor2<5>(ma, mb, na, nb, ea, eb);
   } else {
     key_floor2<kUnitPages>(ka, kb, na, nb, ea, eb);
   }
