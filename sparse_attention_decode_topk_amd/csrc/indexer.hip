@@ -1016,10 +1016,12 @@ __device__ __forceinline__ bool fast_find(SelSmem& S, const uint32_t* H, uint32_
   return true;
 }
 
-// Layout J (1, 2, 4 or 8): wave w owns units (8/J)w .. (8/J)w + 8/J - 1 and
-// holds slots lane, lane + 64, ..., lane + 64(J-1) of each, eight keys per
-// lane in position order (unit, then slot); so the path takes rows of up to
-// 128/J units of up to 64J candidates.
+// Layout J (1, 2, 4, 8 or 16): for J <= 8 wave w owns units (8/J)w ..
+// (8/J)w + 8/J - 1 and holds slots lane, lane + 64, ..., lane + 64(J-1) of
+// each; for J = 16 waves 2u and 2u+1 share unit u, slots lane + 64j and
+// 512 + lane + 64j (j < 8).  Eight keys per lane in position order (unit,
+// then slot); the path takes rows of up to 128/J units of up to 64J
+// candidates.
 // Returns 1 when the row is done.  Otherwise nothing was written and it
 // returns the layout that would fit the row (2, 4 or 8, only from layout 1:
 // the row has a unit with more than 64J candidates but few enough units),
@@ -1027,11 +1029,14 @@ __device__ __forceinline__ bool fast_find(SelSmem& S, const uint32_t* H, uint32_
 // largest unit edge; the caller then takes the general path.  Block-uniform.
 template <int J>
 __device__ __forceinline__ int select_fast(const Params& P, SelSmem& S, int row) {
-  constexpr int UPW = kFastPer / J;           // units per wave
-  constexpr int kUnits = kFastUnits / J;      // units per row
+  constexpr int WPU = J > kFastPer ? J / kFastPer : 1;   // waves per unit
+  constexpr int UPW = J > kFastPer ? 1 : kFastPer / J;   // units per wave
+  constexpr int JW = J / WPU;                            // 64-slot groups a wave holds per unit
+  constexpr int kUnits = kFastUnits / J;                 // units per row
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int u0 = UPW * wv;
+  const int u0 = UPW * (wv / WPU);
+  const uint32_t sbase = (uint32_t)(64 * JW * (wv % WPU));   // first slot this wave holds
   const int K = P.topk;
   const int nu = min(P.upr, kUnits);   // units whose slices exist in the workspace
   // loads: row position; count and edge of unit u0 + lane (lanes < UPW);
@@ -1048,9 +1053,9 @@ __device__ __forceinline__ int select_fast(const Params& P, SelSmem& S, int row)
   uint32_t k[kFastPer], p[kFastPer];
 #pragma unroll
   for (int i = 0; i < kFastPer; ++i) {
-    const int a = i / J, jj = i % J;
+    const int a = i / JW, jj = i % JW;
     const v2u v = __builtin_amdgcn_raw_buffer_load_b64(
-        rk, (uint32_t)(((u0 + a) * kUnitTok + lane + 64 * jj) * 8), 0, 0);
+        rk, (uint32_t)(((u0 + a) * kUnitTok + sbase + lane + 64 * jj) * 8), 0, 0);
     k[i] = v[0];
     p[i] = v[1];
   }
@@ -1066,18 +1071,24 @@ __device__ __forceinline__ int select_fast(const Params& P, SelSmem& S, int row)
   const bool uin = lane < UPW && u0 + lane < units_r;
   cnt_l = uin ? cnt_l : 0u;
   edge_l = uin ? edge_l : 0u;
-  const uint32_t csum_l = wave_incl_scan(cnt_l);   // lane i: candidates of units u0 .. u0+i
+  // candidates of unit u0+a in this wave's slots, and before them in the wave
+  uint32_t vis[UPW], vpre[UPW], tot_w = 0;
+#pragma unroll
+  for (int a = 0; a < UPW; ++a) {
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)cnt_l, a);
+    vis[a] = min(c > sbase ? c - sbase : 0u, (uint32_t)(64 * JW));
+    vpre[a] = tot_w;
+    tot_w += vis[a];
+  }
   uint32_t km = 0;
 #pragma unroll
   for (int i = 0; i < kFastPer; ++i) {
-    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)cnt_l, i / J);
-    if ((uint32_t)(lane + 64 * (i % J)) >= c) k[i] = 0u;
+    if ((uint32_t)(lane + 64 * (i % JW)) >= vis[i / JW]) k[i] = 0u;
     km = max(km, k[i]);
   }
   const uint32_t cmax_w = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_max(cnt_l), 63);
   const uint32_t emax_w = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_max(edge_l), 63);
   const uint32_t kmax_w = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_max(km), 63);
-  const uint32_t tot_w = (uint32_t)__builtin_amdgcn_readlane((int)csum_l, 63);
   if (lane == 0) *reinterpret_cast<uint4*>(S.wred[wv]) = make_uint4(tot_w, cmax_w, emax_w, kmax_w);
   __syncthreads();
   uint32_t n_c = 0, cmax = 0, emax = 0, kmax = 0, wbase = 0;
@@ -1093,7 +1104,7 @@ __device__ __forceinline__ int select_fast(const Params& P, SelSmem& S, int row)
   if (cmax > 64u * J) {
     // a layout with more slots per unit, if the row has few enough units
     if (J > 1) return 0;
-    for (int jn = 2; jn <= kFastPer; jn *= 2)
+    for (int jn = 2; jn <= 2 * kFastPer; jn *= 2)
       if (cmax <= 64u * jn && units_r <= kFastUnits / jn) return jn;
     return 0;
   }
@@ -1103,10 +1114,9 @@ __device__ __forceinline__ int select_fast(const Params& P, SelSmem& S, int row)
     // every candidate is kept: unit u0+i's slot j goes to its flat index
 #pragma unroll
     for (int i = 0; i < kFastPer; ++i) {
-      const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)cnt_l, i / J);
-      const uint32_t sl = (uint32_t)(lane + 64 * (i % J));
-      const uint32_t f = wbase + (uint32_t)__builtin_amdgcn_readlane((int)csum_l, i / J) - c + sl;
-      if (sl < c && f < (uint32_t)K) {
+      const uint32_t sl = (uint32_t)(lane + 64 * (i % JW));   // relative to sbase
+      const uint32_t f = wbase + vpre[i / JW] + sl;
+      if (sl < vis[i / JW] && f < (uint32_t)K) {
         oidx[f] = (int32_t)p[i];
         if (osc) osc[f] = key_score(k[i]);
       }
@@ -1218,7 +1228,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void indexer_select_kernel(Params P
   if (fast > 1) {
     __syncthreads();   // every wave has read the first attempt's LDS results
     fast = fast == 2 ? select_fast<2>(P, S, row) : fast == 4 ? select_fast<4>(P, S, row)
-                                                             : select_fast<8>(P, S, row);
+         : fast == 8 ? select_fast<8>(P, S, row) : select_fast<16>(P, S, row);
   }
   if (fast == 1) return;
   // general path: waves 0..3 (a barrier first, so that no wave still reads
