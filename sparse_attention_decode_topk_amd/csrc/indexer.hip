@@ -1071,15 +1071,15 @@ __device__ __forceinline__ int select_fast(const Params& P, SelSmem& S, int row)
   const bool uin = lane < UPW && u0 + lane < units_r;
   cnt_l = uin ? cnt_l : 0u;
   edge_l = uin ? edge_l : 0u;
-  // candidates of unit u0+a in this wave's slots, and before them in the wave
-  uint32_t vis[UPW], vpre[UPW], tot_w = 0;
+  // candidates of unit u0+a (vis) and of the wave's units before it (vpre)
+  const uint32_t csum_l = wave_incl_scan(cnt_l);   // lane i: candidates of units u0 .. u0+i
+  uint32_t vis[UPW], vpre[UPW];
 #pragma unroll
   for (int a = 0; a < UPW; ++a) {
-    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)cnt_l, a);
-    vis[a] = min(c > sbase ? c - sbase : 0u, (uint32_t)(64 * JW));
-    vpre[a] = tot_w;
-    tot_w += vis[a];
+    vis[a] = (uint32_t)__builtin_amdgcn_readlane((int)cnt_l, a);
+    vpre[a] = (uint32_t)__builtin_amdgcn_readlane((int)csum_l, a) - vis[a];
   }
+  const uint32_t tot_w = (uint32_t)__builtin_amdgcn_readlane((int)csum_l, 63);
   uint32_t km = 0;
 #pragma unroll
   for (int i = 0; i < kFastPer; ++i) {
@@ -1196,6 +1196,171 @@ __device__ __forceinline__ int select_fast(const Params& P, SelSmem& S, int row)
   return 1;
 }
 
+// select_fast with the layout J (2, 4, 8 or 16) a runtime value: one copy of
+// the code for all wide layouts.
+__device__ __forceinline__ int select_fast_rt(const Params& P, SelSmem& S, int row, int J) {
+  J = __builtin_amdgcn_readfirstlane(J);
+  const int WPU = J > kFastPer ? J / kFastPer : 1;       // waves per unit
+  const int UPW = J > kFastPer ? 1 : kFastPer / J;       // units per wave
+  const int JW = J / WPU;                                // 64-slot groups a wave holds per unit
+  const int lgJW = 31 - __builtin_clz(JW);
+  const int kUnits = kFastUnits / J;                     // units per row
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int u0 = UPW * (wv / WPU);
+  const uint32_t sbase = (uint32_t)(64 * JW * (wv % WPU));   // first slot this wave holds
+  const int K = P.topk;
+  const int nu = min(P.upr, kUnits);   // units whose slices exist in the workspace
+  // loads: row position; count and edge of unit u0 + lane (lanes < UPW);
+  // slot lane + 64j of each of the wave's units
+  const int t = P.row_pos[row];
+  const int64_t ub = (int64_t)row * P.upr;
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(P.ucount + ub, (short)0, nu * 4, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(P.uedge + ub, (short)0, nu * 4, kRawBufferWord3);
+  const uint32_t uoff = lane < UPW ? (uint32_t)(u0 + lane) * 4u : (uint32_t)nu * 4u;
+  uint32_t cnt_l = __builtin_amdgcn_raw_buffer_load_b32(rc, uoff, 0, 0);
+  uint32_t edge_l = __builtin_amdgcn_raw_buffer_load_b32(re, uoff, 0, 0);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      P.cand + (int64_t)row * P.bt_stride * kPage, (short)0, nu * kUnitTok * 8, kRawBufferWord3);
+  uint32_t k[kFastPer], p[kFastPer];
+#pragma unroll
+  for (int i = 0; i < kFastPer; ++i) {
+    const int a = i >> lgJW, jj = i & (JW - 1);
+    const v2u v = __builtin_amdgcn_raw_buffer_load_b64(
+        rk, (uint32_t)(((u0 + a) * kUnitTok + sbase + lane + 64 * jj) * 8), 0, 0);
+    k[i] = v[0];
+    p[i] = v[1];
+  }
+  // clear both radix histograms (ordered before any add by the first barrier)
+  {
+    uint4* h4 = reinterpret_cast<uint4*>(S.hist);
+#pragma unroll
+    for (int i = 0; i < 2 * kBins / 4 / kSelThreads; ++i) h4[threadIdx.x + i * kSelThreads] = make_uint4(0, 0, 0, 0);
+  }
+  const int units_r = row_units(t, P.bt_stride);
+  if (units_r > kUnits) return 0;
+  const bool take_all = t < 0 || unit_quota(t, K) == 0xFFFFFFFFu;   // at most K positions
+  const bool uin = lane < UPW && u0 + lane < units_r;
+  cnt_l = uin ? cnt_l : 0u;
+  edge_l = uin ? edge_l : 0u;
+  // candidates of unit u0+a in this wave's slots: vis_l in lane a, their
+  // prefix within the wave in vsc_l
+  const uint32_t vis_l = min(cnt_l > sbase ? cnt_l - sbase : 0u, (uint32_t)(64 * JW));
+  const uint32_t vsc_l = wave_incl_scan(vis_l);
+  const uint32_t tot_w = (uint32_t)__builtin_amdgcn_readlane((int)vsc_l, 63);
+  uint32_t km = 0;
+#pragma unroll
+  for (int i = 0; i < kFastPer; ++i) {
+    const uint32_t vis = (uint32_t)__builtin_amdgcn_readlane((int)vis_l, i >> lgJW);
+    if ((uint32_t)(lane + 64 * (i & (JW - 1))) >= vis) k[i] = 0u;
+    km = max(km, k[i]);
+  }
+  const uint32_t cmax_w = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_max(cnt_l), 63);
+  const uint32_t emax_w = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_max(edge_l), 63);
+  const uint32_t kmax_w = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_max(km), 63);
+  if (lane == 0) *reinterpret_cast<uint4*>(S.wred[wv]) = make_uint4(tot_w, cmax_w, emax_w, kmax_w);
+  __syncthreads();
+  uint32_t n_c = 0, cmax = 0, emax = 0, kmax = 0, wbase = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    const uint4 x = *reinterpret_cast<const uint4*>(S.wred[w]);
+    wbase += w < wv ? x.x : 0u;
+    n_c += x.x;
+    cmax = max(cmax, x.y);
+    emax = max(emax, x.z);
+    kmax = max(kmax, x.w);
+  }
+  if (cmax > 64u * J) return 0;
+  gint32* oidx = (gint32*)(P.out_idx + (int64_t)row * K);
+  gfloat* osc = P.out_score ? (gfloat*)(P.out_score + (int64_t)row * K) : nullptr;
+  if (take_all) {
+    // every candidate is kept: unit u0+i's slot j goes to its flat index
+#pragma unroll
+    for (int i = 0; i < kFastPer; ++i) {
+      const int a = i >> lgJW;
+      const uint32_t sl = (uint32_t)(lane + 64 * (i & (JW - 1)));   // relative to sbase
+      const uint32_t vis = (uint32_t)__builtin_amdgcn_readlane((int)vis_l, a);
+      const uint32_t f = wbase + (uint32_t)__builtin_amdgcn_readlane((int)vsc_l, a) - vis + sl;
+      if (sl < vis && f < (uint32_t)K) {
+        oidx[f] = (int32_t)p[i];
+        if (osc) osc[f] = key_score(k[i]);
+      }
+    }
+    for (uint32_t f = n_c + threadIdx.x; f < (uint32_t)K; f += kSelThreads) {
+      oidx[f] = -1;
+      if (osc) osc[f] = -__builtin_huge_valf();
+    }
+    return 1;
+  }
+  // radix passes over [lo, kmax]: pass p bins the keys of [base, base + span)
+  // by (key - base) >> shift into histogram p & 1
+  const uint32_t lo = max(emax, 1u);
+  if (kmax < lo) return 0;
+  int shift = range_shift(kmax - lo);
+  uint64_t span = (uint64_t)(kmax - lo) + 1;
+  uint32_t base = lo, need = (uint32_t)K;
+  for (int pass = 0;; ++pass) {
+    uint32_t* H = S.hist + (pass & 1) * kBins;
+    if (pass >= 2) {
+      // every wave finished reading this histogram before the last barrier
+      reinterpret_cast<uint4*>(H)[threadIdx.x] = make_uint4(0, 0, 0, 0);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < kFastPer; ++i)
+      if (k[i] >= base && (uint64_t)(k[i] - base) < span) atomicAdd(&H[(k[i] - base) >> shift], 1u);
+    __syncthreads();
+    uint32_t bin, above;
+    if (!fast_find(S, H, S.wsum[pass & 1], need, &bin, &above)) return 0;   // pass 0 only
+    base += bin << shift;
+    need -= above;
+    if (shift == 0) break;
+    span = 1ull << shift;   // the keys of the chosen bin
+    shift = max(0, shift - 12);
+  }
+  const uint32_t T = base, ties = need;   // T >= lo >= 1, so empty slots never equal it
+  // emission: per-wave (greater, equal) totals, then every kept key's
+  // position from the units' running sums and ballots
+  uint32_t gt_w = 0, eq_w = 0;
+#pragma unroll
+  for (int i = 0; i < kFastPer; ++i) {
+    gt_w += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(k[i] > T));
+    eq_w += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(k[i] == T));
+  }
+  if (lane == 0) S.wtot[wv] = (eq_w << 16) | gt_w;
+  __syncthreads();
+  uint32_t gt_before = 0, eq_before = 0;
+#pragma unroll
+  for (int w4 = 0; w4 < kSelWaves / 4; ++w4) {
+    const uint4 x = *reinterpret_cast<const uint4*>(&S.wtot[4 * w4]);
+    const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t v = 4 * w4 + j < wv ? xs[j] : 0u;
+      gt_before += v & 0xFFFFu;
+      eq_before += v >> 16;
+    }
+  }
+  const uint64_t below = lanemask_lt();
+#pragma unroll
+  for (int i = 0; i < kFastPer; ++i) {
+    const bool gt = k[i] > T, eq = k[i] == T;
+    const uint64_t gb = __builtin_amdgcn_ballot_w64(gt);
+    const uint64_t eb = __builtin_amdgcn_ballot_w64(eq);
+    const uint32_t erank = eq_before + (uint32_t)__builtin_popcountll(eb & below);
+    const bool kept = gt || (eq && erank < ties);
+    const uint64_t kb = __builtin_amdgcn_ballot_w64(kept);
+    const uint32_t opos = gt_before + min(eq_before, ties) + (uint32_t)__builtin_popcountll(kb & below);
+    if (kept && opos < (uint32_t)K) {
+      oidx[opos] = (int32_t)p[i];
+      if (osc) osc[opos] = key_score(k[i]);
+    }
+    gt_before += (uint32_t)__builtin_popcountll(gb);
+    eq_before += (uint32_t)__builtin_popcountll(eb);
+  }
+  return 1;
+}
+
 // Rescore unit u of the row in full and publish all of its keys.
 template <int NHT>
 __device__ __forceinline__ void rescore_unit(const Params& P, SelSmem& S, int row, int t, int u) {
@@ -1227,8 +1392,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void indexer_select_kernel(Params P
   int fast = select_fast<1>(P, S, row);
   if (fast > 1) {
     __syncthreads();   // every wave has read the first attempt's LDS results
-    fast = fast == 2 ? select_fast<2>(P, S, row) : fast == 4 ? select_fast<4>(P, S, row)
-         : fast == 8 ? select_fast<8>(P, S, row) : select_fast<16>(P, S, row);
+    fast = select_fast_rt(P, S, row, fast);
   }
   if (fast == 1) return;
   // general path: waves 0..3 (a barrier first, so that no wave still reads

@@ -22,6 +22,10 @@ __device__ __forceinline__ void mxfp8_quant_range(
   const int64_t per_row = cols / 8;
   const int64_t total = rows * per_row;
   for (int64_t i = first; i < total; i += nthreads) {
+    // the slot (paged mode) is loaded together with the data, not after the
+    // conversion, so the two loads' latencies overlap
+    const int64_t row = i / per_row;
+    const int64_t slot = kpool != nullptr ? slots[row] : 0;
     const uint4 raw = *reinterpret_cast<const uint4*>(x + i * 8);
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
     float v[8];
@@ -47,9 +51,7 @@ __device__ __forceinline__ void mxfp8_quant_range(
       *reinterpret_cast<uint2*>(out + i * 8) = make_uint2(lo, hi);
       if ((i & 3) == 0) out_scale[i >> 2] = sbyte;
     } else {
-      const int64_t row = i / per_row;
       const int c8 = (int)(i - row * per_row);  // 0..15
-      const int64_t slot = slots[row];
       if (slot < 0 || slot >= pool_slots) continue;
       uint8_t* page = kpool + (slot >> 6) * (int64_t)kKPageBytes;
       const int off = (int)(slot & 63);
@@ -75,10 +77,13 @@ __device__ __forceinline__ void kv_quant_range(
     const int64_t* __restrict__ slots, uint8_t* __restrict__ pool, int64_t pool_slots) {
   const int lane = threadIdx.x & 63;
   for (int64_t tok = first; tok < n; tok += waves) {
+    // the token's data is loaded together with its slot (its address does
+    // not depend on the slot), so the two loads' latencies overlap
     const int64_t slot = slots[tok];
-    if (slot < 0 || slot >= pool_slots) continue;  // uniform across the wave
     const uint16_t* src = kv + tok * kQK;
     const uint4 raw = *reinterpret_cast<const uint4*>(src + lane * 8);
+    const uint4 rope = *reinterpret_cast<const uint4*>(src + kLatent + (lane & 7) * 8);
+    if (slot < 0 || slot >= pool_slots) continue;  // uniform across the wave
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
     float v[8];
     float amax = 0.f;
@@ -99,10 +104,7 @@ __device__ __forceinline__ void kv_quant_range(
     uint8_t* rec = pool + slot * (int64_t)kRec;
     *reinterpret_cast<uint2*>(rec + lane * 8) = make_uint2(lo, hi);
     if ((lane & 15) == 0) *reinterpret_cast<float*>(rec + kRecScaleOff + (lane >> 4) * 4) = scale;
-    if (lane < 8) {
-      const uint4 r = *reinterpret_cast<const uint4*>(src + kLatent + lane * 8);
-      *reinterpret_cast<uint4*>(rec + kRecRopeOff + lane * 16) = r;
-    }
+    if (lane < 8) *reinterpret_cast<uint4*>(rec + kRecRopeOff + lane * 16) = rope;
   }
 }
 
