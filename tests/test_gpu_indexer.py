@@ -331,3 +331,36 @@ def test_multi_query_mixed_group_flagged(need_gpu):
     _mq_topk(st, 2, workspace=ws)   # rows 2b, 2b+1 belong to different sequences
     torch.cuda.synchronize()
     assert int(ws.view(torch.int32)[2].item()) & 16 != 0
+
+
+def test_select_layouts(need_gpu):
+    """Rows whose units keep many candidates (short histories relative to
+    K) take the select's wider register layouts (up to 1024 candidates in
+    a unit, two waves per unit): the oracle rule and bit-exact equality with
+    the exact Top-K of the kernel's own scores, for several K."""
+    say("[indexer] select layouts")
+    lens = np.array([2100, 3000, 4100, 5000, 9000, 17000, 26000, 40000], dtype=np.int32)
+    cfg = synth.Config(93, "layouts", batch=len(lens), h_index=64, h_attn=16, topk=2048,
+                       ragged=(int(lens.min()), int(lens.max())))
+    rng = np.random.default_rng(5)
+    bt, slots, starts, npages = synth.page_tables(cfg, lens, rng)
+    R = len(lens)
+    inp = dict(seq_lens=lens, block_table=bt, slot_mapping=slots, seq_starts=starts,
+               total_pages=np.int64(npages), topk=np.int32(2048),
+               row_seq=np.arange(R, dtype=np.int32), row_pos=(lens - 1).astype(np.int32),
+               q_idx=synth.f32_to_bf16_bits(rng.standard_normal((R, 64, 128)).astype(np.float32)),
+               k_idx=synth.f32_to_bf16_bits(rng.standard_normal((int(lens.sum()), 128)).astype(np.float32)),
+               w=(rng.standard_normal((R, 64)) / 8).astype(np.float32))
+    st = DeviceState(inp, with_sfa=False)
+    o = Oracle(inp)
+    scores = st.scores().cpu().numpy()
+    for K in (2048, 1024, 300):
+        ws = ops.indexer_workspace(R, st.block_table.shape[1], st.H_I, K)
+        idx, sc = st.indexer(topk=K, workspace=ws)
+        idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+        for r in range(R):
+            t = int(inp["row_pos"][r])
+            check_topk_row(idx[r], sc[r], o.topk(r, K), K, t)
+            assert np.array_equal(idx[r][:min(K, t + 1)], exact_topk_of(scores[r], K)), f"row {r} K={K}"
+        assert int(ws.view(torch.int32)[2].item()) & 4 == 0
+    o.drop_cache()
