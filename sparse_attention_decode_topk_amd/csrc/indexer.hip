@@ -10,7 +10,7 @@
 // Two launches on the caller's stream:
 //  1. scan: every row's causal history is cut into units of 16 pages (1024
 //     positions); workgroups take units in row-major order.  For a unit, each
-//     wave streams eight half pages through a three-deep register ring and
+//     wave streams eight half pages through a four-deep register ring and
 //     runs v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 codes of both operands,
 //     their E8M0 block scales applied by the instruction, fp32 accumulation)
 //     against the resident query heads, applies ReLU and the head weights in
@@ -23,9 +23,11 @@
 //     largest key; the unit writes every key >= e_u with its position, in
 //     position order, to its slice of the candidate workspace and records
 //     e_u.
-//  2. select: one workgroup per row gathers the row's candidates into LDS,
-//     finds the exact K-th key T among those >= max_u e_u with up to three
-//     radix passes over the occupied key range, and writes the kept
+//  2. select: one workgroup per row holds the row's candidates in registers
+//     (eight per lane in position order, in one of five layouts by the
+//     size of the row's largest unit; rows that fit none are gathered into
+//     LDS), finds the exact K-th key T among those >= max_u e_u with radix
+//     passes over the occupied key range, and writes the kept
 //     positions in ascending order.  Every key a unit left out is below its
 //     e_u <= T, so the result is the exact Top-K.  When fewer than K
 //     candidates reach max_u e_u, the units whose edge could hide a Top-K key
@@ -49,7 +51,7 @@ constexpr int kHalvesPerWave = 2 * kUnitPages / kWaves;  // 8 half pages per wav
 // than one of eight).
 constexpr int kScanThreads = 256;
 constexpr int kScanWaves = kScanThreads / 64;
-constexpr int kScanHalves = 2 * kUnitPages / kScanWaves;  // 4 half pages per wave and unit
+constexpr int kScanHalves = 2 * kUnitPages / kScanWaves;  // 8 half pages per wave and unit
 constexpr int kRing = 4;                               // half pages in flight per wave
 constexpr int kBins = 4096;                            // select histogram (12-bit passes)
 constexpr int kCandPer = 24;                           // select: candidates per thread
