@@ -507,7 +507,12 @@ __device__ __forceinline__ uint32_t unit_quota(int t, int topk) {
   const int64_t n = (int64_t)t + 1;
   if (n <= topk) return 0xFFFFFFFFu;
   const float e = (float)topk * (float)kUnitTok / (float)n;
-  const float m = e + 4.0f * sqrtf(e) + 8.0f;
+  float m = e + 4.0f * sqrtf(e) + 8.0f;
+  // A row of more than 64 units can only take the select's first layout (64
+  // slots per unit): keep the quota, and so the edge's few surplus keys,
+  // below that.  There e < 32 (topk <= 2048), so 56 is still more than four
+  // standard deviations above the unit's expected share.
+  if (n > (int64_t)64 * kUnitTok) m = fminf(m, 56.0f);
   return (uint32_t)fminf(ceilf(m), (float)kUnitTok);
 }
 

@@ -339,7 +339,8 @@ def test_select_layouts(need_gpu):
     a unit, two waves per unit): the oracle rule and bit-exact equality with
     the exact Top-K of the kernel's own scores, for several K."""
     say("[indexer] select layouts")
-    lens = np.array([2100, 3000, 4100, 5000, 9000, 17000, 26000, 40000], dtype=np.int32)
+    lens = np.array([2100, 3000, 4100, 5000, 9000, 17000, 26000, 40000, 65600, 70000],
+                    dtype=np.int32)
     cfg = synth.Config(93, "layouts", batch=len(lens), h_index=64, h_attn=16, topk=2048,
                        ragged=(int(lens.min()), int(lens.max())))
     rng = np.random.default_rng(5)
