@@ -440,22 +440,31 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
   }
 }
 
-// Combines the S partials of every (row, head) in split order: thread t of a
-// block handles head 4*blockIdx.y + t/64, dims 8*(t%64) .. +7.
+// Combines the S partials of every (row, head) in split order.  A thread takes
+// V consecutive dims of one head (512/V threads per head), so a block of 256
+// threads covers 2 heads for V = 4 and 4 heads for V = 8.  V = 4 is used when
+// the V = 8 grid would have fewer blocks than the chip has CUs (one row of
+// 128 heads: 32 blocks): twice the blocks put more loads in flight
+// (measured 23.1 -> 22.7 us per call at 8K, batch 1); with a block per CU
+// the two measure the same.  The arithmetic per element is the same for both.
+template <int V>
 __global__ __launch_bounds__(kCombineThreads) void sfa_combine_kernel(Params P) {
-  const int row = blockIdx.x, h = 4 * blockIdx.y + (threadIdx.x >> 6), c = threadIdx.x & 63;
+  constexpr int kF4 = V / 4;                          // float4 per thread
+  constexpr int kTPH = kLatent / V;                   // threads per head
+  const int row = blockIdx.x, h = (kCombineThreads / kTPH) * blockIdx.y + threadIdx.x / kTPH;
+  const int c = threadIdx.x % kTPH;
   if (h >= P.H) return;
   const int64_t ph0 = ((int64_t)row * P.H + h) * P.S;
   // every split's loads first (S <= kMaxSplits), then the fixed-order sums
   float2 ml[kMaxSplits];
-  float4 x[kMaxSplits][2];
+  float4 x[kMaxSplits][kF4];
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
     if (s < P.S) {
       ml[s] = reinterpret_cast<const float2*>(P.part_ml)[ph0 + s];
-      const float4* src = reinterpret_cast<const float4*>(P.part_o + (ph0 + s) * kLatent) + 2 * c;
-      x[s][0] = src[0];
-      x[s][1] = src[1];
+      const float4* src = reinterpret_cast<const float4*>(P.part_o + (ph0 + s) * kLatent) + kF4 * c;
+#pragma unroll
+      for (int f = 0; f < kF4; ++f) x[s][f] = src[f];
     }
   }
   float M = -__builtin_huge_valf();
@@ -463,20 +472,26 @@ __global__ __launch_bounds__(kCombineThreads) void sfa_combine_kernel(Params P) 
   for (int s = 0; s < kMaxSplits; ++s)
     if (s < P.S) M = fmaxf(M, ml[s].x);
   float L = 0.f;
-  float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
+  float4 a[kF4];
+#pragma unroll
+  for (int f = 0; f < kF4; ++f) a[f] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
     if (s >= P.S) continue;
     const float m = ml[s].x;
     const float w = (M == -__builtin_huge_valf() || m == -__builtin_huge_valf()) ? 0.f : exp2f(m - M);
     L += w * ml[s].y;
-    a0.x += w * x[s][0].x; a0.y += w * x[s][0].y; a0.z += w * x[s][0].z; a0.w += w * x[s][0].w;
-    a1.x += w * x[s][1].x; a1.y += w * x[s][1].y; a1.z += w * x[s][1].z; a1.w += w * x[s][1].w;
+#pragma unroll
+    for (int f = 0; f < kF4; ++f) {
+      a[f].x += w * x[s][f].x; a[f].y += w * x[s][f].y;
+      a[f].z += w * x[s][f].z; a[f].w += w * x[s][f].w;
+    }
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
-  float4* dst = reinterpret_cast<float4*>(P.out + ((int64_t)row * P.H + h) * kLatent) + 2 * c;
-  dst[0] = make_float4(a0.x * inv, a0.y * inv, a0.z * inv, a0.w * inv);
-  dst[1] = make_float4(a1.x * inv, a1.y * inv, a1.z * inv, a1.w * inv);
+  float4* dst = reinterpret_cast<float4*>(P.out + ((int64_t)row * P.H + h) * kLatent) + kF4 * c;
+#pragma unroll
+  for (int f = 0; f < kF4; ++f)
+    dst[f] = make_float4(a[f].x * inv, a[f].y * inv, a[f].z * inv, a[f].w * inv);
   if (P.lse && c == 0)
     P.lse[(int64_t)row * P.H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -__builtin_huge_valf();
 }
@@ -568,7 +583,11 @@ extern "C" int dsa_sparse_attn(const void* q_bf16, const void* kv_pool, int64_t 
   hipLaunchKernelGGL(sfa_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, P);
   if (hipGetLastError() != hipSuccess) return DSA_ERR_HIP;
   if (pl.S > 1) {
-    hipLaunchKernelGGL(sfa_combine_kernel, dim3((unsigned)R, (unsigned)((H + 3) / 4)), dim3(kCombineThreads), 0, s, P);
+    const bool wide = (int64_t)R * ((H + 3) / 4) >= 256;   // a block per CU at V = 8
+    if (wide)
+      hipLaunchKernelGGL(sfa_combine_kernel<8>, dim3((unsigned)R, (unsigned)((H + 3) / 4)), dim3(kCombineThreads), 0, s, P);
+    else
+      hipLaunchKernelGGL(sfa_combine_kernel<4>, dim3((unsigned)R, (unsigned)((H + 1) / 2)), dim3(kCombineThreads), 0, s, P);
     if (hipGetLastError() != hipSuccess) return DSA_ERR_HIP;
   }
   return DSA_OK;
