@@ -144,3 +144,27 @@ def test_multi_query_indexer_argument_errors(lib):
     assert _mq_call(lib, ws=None) == 3
     assert _mq_call(lib, wsb=16) == 3
     assert _mq_call(lib, R=0) == 0
+
+
+def _prolog_call(lib, **kw):
+    a = dict(q=FAKE, rows=8, cols=128, qf=FAKE, qs=FAKE, k=FAKE, kv=FAKE, n=8, slots=FAKE,
+             kpool=FAKE, kvpool=FAKE, pages=100)
+    a.update(kw)
+    return lib.dsa_decode_prolog(a["q"], a["rows"], a["cols"], a["qf"], a["qs"], a["k"], a["kv"],
+                                 a["n"], a["slots"], a["kpool"], a["kvpool"], a["pages"], None)
+
+
+def test_decode_prolog_argument_errors(lib):
+    assert _prolog_call(lib, q=None) == 1
+    assert _prolog_call(lib, qf=None) == 1
+    assert _prolog_call(lib, qs=None) == 1
+    assert _prolog_call(lib, rows=-1) == 1
+    assert _prolog_call(lib, cols=0) == 1
+    assert _prolog_call(lib, cols=100) == 2      # not a multiple of the 32-element block
+    assert _prolog_call(lib, n=-1) == 1
+    for name in ("k", "kv", "slots", "kpool", "kvpool"):
+        assert _prolog_call(lib, **{name: None}) == 1, name
+    assert _prolog_call(lib, pages=0) == 1
+    # no new tokens: the cache arguments may be absent
+    assert _prolog_call(lib, rows=0, n=0, k=None, kv=None, slots=None, kpool=None, kvpool=None,
+                        pages=0) == 0
