@@ -124,3 +124,20 @@ def test_sfa_split_path_with_holes(need_gpu):
     idx[K - 37:] = -1               # ragged tail of the last split
     out, lse = _compare(st, o, idx[None, :], [0], "split path with holes")
     assert np.all(np.isfinite(out[0]))
+
+
+def test_sfa_ragged_batch(need_gpu):
+    """32 sequences of 4K-64K tokens, 128 heads: two splits per row and the
+    combine launch.  Every row's list is 2048 distinct seeded positions of
+    its own history (fewer for short rows), with -1 holes."""
+    st = state("decode_ragged_b32")
+    o = Oracle(st.inp)
+    rng = np.random.default_rng(21)
+    idx = np.full((st.R, st.topk), -1, dtype=np.int32)
+    for r in range(st.R):
+        t = int(st.inp["row_pos"][r])
+        n = min(st.topk, t + 1)
+        idx[r, :n] = rng.choice(t + 1, n, replace=False)
+    idx[:, ::9] = -1
+    _compare(st, o, idx, list(range(st.R)), "ragged batch")
+    o.drop_cache()
