@@ -141,3 +141,24 @@ def test_sfa_ragged_batch(need_gpu):
     idx[:, ::9] = -1
     _compare(st, o, idx, list(range(st.R)), "ragged batch")
     o.drop_cache()
+
+
+def test_sfa_prefill_chunk_sampled_rows(need_gpu):
+    """The chunked-prefill shape as bench.py launches it: 8192 query rows of
+    128 heads against a 131072-token cache, one split per row (the direct
+    output path, 32768 work-groups).  Sampled rows carry 2048 distinct
+    seeded positions of their causal history; every other row is empty and
+    must come out as zeros with lse -inf."""
+    st = state("prefill_chunk_8k_of_128k")
+    o = Oracle(st.inp)
+    R = st.R
+    rng = np.random.default_rng(23)
+    rows = sorted(set([0, 1, R // 2, R - 1] + rng.choice(R, 8, replace=False).tolist()))
+    idx = np.full((R, st.topk), -1, dtype=np.int32)
+    for r in rows:
+        t = int(st.inp["row_pos"][r])
+        idx[r] = rng.choice(t + 1, st.topk, replace=False)
+    out, lse = _compare(st, o, idx, rows, "prefill chunk, sampled rows")
+    empty = [r for r in (2, R // 3, R - 2) if r not in rows]
+    assert np.all(out[empty] == 0) and np.all(np.isneginf(lse[empty]))
+    o.drop_cache()
