@@ -365,3 +365,41 @@ def test_select_layouts(need_gpu):
             assert np.array_equal(idx[r][:min(K, t + 1)], exact_topk_of(scores[r], K)), f"row {r} K={K}"
         assert int(ws.view(torch.int32)[2].item()) & 4 == 0
     o.drop_cache()
+
+
+def test_long_context_rows(need_gpu):
+    """Rows past the select's fast layouts (more than 128 units of 1024
+    keys): a 1M-token row at the block table's maximum width (16384 pages),
+    a 256K row and a 200001-token row.  Against the oracle, and bit-exact
+    against the exact Top-K of the kernel's own scores."""
+    say("[indexer] long rows: 1048576, 262144, 200001 tokens")
+    lens = np.array([1048576, 262144, 200001], dtype=np.int32)
+    cfg = synth.Config(94, "long", batch=len(lens), h_index=64, h_attn=16, topk=2048,
+                       ragged=(int(lens.min()), int(lens.max())))
+    rng = np.random.default_rng(7)
+    bt, slots, starts, npages = synth.page_tables(cfg, lens, rng)
+    assert bt.shape[1] == 16384
+    R = len(lens)
+    inp = dict(seq_lens=lens, block_table=bt, slot_mapping=slots, seq_starts=starts,
+               total_pages=np.int64(npages), topk=np.int32(2048),
+               row_seq=np.arange(R, dtype=np.int32), row_pos=(lens - 1).astype(np.int32),
+               q_idx=synth.f32_to_bf16_bits(rng.standard_normal((R, 64, 128)).astype(np.float32)),
+               k_idx=synth.f32_to_bf16_bits(rng.standard_normal((int(lens.sum()), 128)).astype(np.float32)),
+               w=(rng.standard_normal((R, 64)) / 8).astype(np.float32))
+    st = DeviceState(inp, with_sfa=False)
+    o = Oracle(inp)
+    scores = st.scores().cpu().numpy()
+    for K in (2048, 300):
+        ws = ops.indexer_workspace(R, st.block_table.shape[1], st.H_I, K)
+        idx, sc = st.indexer(topk=K, workspace=ws)
+        idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+        for r in range(R):
+            t = int(inp["row_pos"][r])
+            assert np.array_equal(idx[r][:min(K, t + 1)], exact_topk_of(scores[r], K)), f"row {r} K={K}"
+            ora = o.topk(r, K)
+            gs = scores[r, :t + 1]
+            assert np.all(np.abs(gs.astype(np.float64) - ora["scores"]) <= 1e-4 * ora["maxabs"]), f"row {r}"
+            check_topk_row(idx[r], sc[r], ora, K, t)
+        assert int(ws.view(torch.int32)[2].item()) & 4 == 0
+        say(f"[indexer] long rows K={K} ok")
+    o.drop_cache()
