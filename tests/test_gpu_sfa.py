@@ -162,3 +162,15 @@ def test_sfa_prefill_chunk_sampled_rows(need_gpu):
     empty = [r for r in (2, R // 3, R - 2) if r not in rows]
     assert np.all(out[empty] == 0) and np.all(np.isneginf(lse[empty]))
     o.drop_cache()
+
+
+@pytest.mark.parametrize("K", [1, 100, 1000, 2047])
+def test_sfa_list_lengths(need_gpu, K):
+    """Index lists whose length is not a multiple of the 64-entry step (and
+    for 1000 and 2047 not a whole number of splits either)."""
+    st = state("decode_8k_needles")
+    o = Oracle(st.inp)
+    t = int(st.inp["row_pos"][0])
+    rng = np.random.default_rng(31 + K)
+    idx = rng.choice(t + 1, K, replace=False).astype(np.int32)[None, :]
+    _compare(st, o, idx, [0], f"list of {K}")
