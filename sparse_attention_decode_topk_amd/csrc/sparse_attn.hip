@@ -55,7 +55,8 @@ constexpr int kSlotBytes = kDmaPerTile * 1024;  // 21504: 32 records + padding
 constexpr int kRingSteps = 3;
 constexpr int kRingBytes = kRingSteps * 2 * kSlotBytes;   // 129024
 constexpr int kMaxEntries = DSA_MAX_TOPK;     // entries of one split
-constexpr int kMaxSplits = 8;
+constexpr int kMaxSplits = 16;                // a row of 2048 entries: two 64-entry steps per split
+constexpr int kWideSplits = 8;                // splits the eight-dim combine holds in registers
 constexpr int kTargetWgs = 256;
 constexpr int kZeroBytes = 1024;              // zero record in the workspace
 constexpr int kMargin = 6;                    // logits may exceed the softmax reference by 2^6
@@ -447,7 +448,9 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
 // 128 heads: 32 blocks): twice the blocks put more loads in flight
 // (measured 23.1 -> 22.7 us per call at 8K, batch 1); with a block per CU
 // the two measure the same.  The arithmetic per element is the same for both.
-template <int V>
+// SMAX is the most splits the block holds in registers (8, or 16 for a batch
+// of a few rows whose lists are cut into two steps per split).
+template <int V, int SMAX>
 __global__ __launch_bounds__(kCombineThreads) void sfa_combine_kernel(Params P) {
   constexpr int kF4 = V / 4;                          // float4 per thread
   constexpr int kTPH = kLatent / V;                   // threads per head
@@ -455,11 +458,11 @@ __global__ __launch_bounds__(kCombineThreads) void sfa_combine_kernel(Params P) 
   const int c = threadIdx.x % kTPH;
   if (h >= P.H) return;
   const int64_t ph0 = ((int64_t)row * P.H + h) * P.S;
-  // every split's loads first (S <= kMaxSplits), then the fixed-order sums
-  float2 ml[kMaxSplits];
-  float4 x[kMaxSplits][kF4];
+  // every split's loads first (S <= SMAX), then the fixed-order sums
+  float2 ml[SMAX];
+  float4 x[SMAX][kF4];
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
+  for (int s = 0; s < SMAX; ++s) {
     if (s < P.S) {
       ml[s] = reinterpret_cast<const float2*>(P.part_ml)[ph0 + s];
       const float4* src = reinterpret_cast<const float4*>(P.part_o + (ph0 + s) * kLatent) + kF4 * c;
@@ -469,14 +472,14 @@ __global__ __launch_bounds__(kCombineThreads) void sfa_combine_kernel(Params P) 
   }
   float M = -__builtin_huge_valf();
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s)
+  for (int s = 0; s < SMAX; ++s)
     if (s < P.S) M = fmaxf(M, ml[s].x);
   float L = 0.f;
   float4 a[kF4];
 #pragma unroll
   for (int f = 0; f < kF4; ++f) a[f] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
+  for (int s = 0; s < SMAX; ++s) {
     if (s >= P.S) continue;
     const float m = ml[s].x;
     const float w = (M == -__builtin_huge_valf() || m == -__builtin_huge_valf()) ? 0.f : exp2f(m - M);
@@ -583,11 +586,17 @@ extern "C" int dsa_sparse_attn(const void* q_bf16, const void* kv_pool, int64_t 
   hipLaunchKernelGGL(sfa_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, P);
   if (hipGetLastError() != hipSuccess) return DSA_ERR_HIP;
   if (pl.S > 1) {
-    const bool wide = (int64_t)R * ((H + 3) / 4) >= 256;   // a block per CU at V = 8
+    // V = 8 needs a block per CU and at most 8 splits; more than 8 splits
+    // only arise with fewer than 32 (row, head group) pairs, where V = 4
+    // is the faster form anyway
+    const bool wide = (int64_t)R * ((H + 3) / 4) >= 256 && pl.S <= kWideSplits;
+    const dim3 g4((unsigned)R, (unsigned)((H + 1) / 2));
     if (wide)
-      hipLaunchKernelGGL(sfa_combine_kernel<8>, dim3((unsigned)R, (unsigned)((H + 3) / 4)), dim3(kCombineThreads), 0, s, P);
+      hipLaunchKernelGGL((sfa_combine_kernel<8, kWideSplits>), dim3((unsigned)R, (unsigned)((H + 3) / 4)), dim3(kCombineThreads), 0, s, P);
+    else if (pl.S <= kWideSplits)
+      hipLaunchKernelGGL((sfa_combine_kernel<4, kWideSplits>), g4, dim3(kCombineThreads), 0, s, P);
     else
-      hipLaunchKernelGGL(sfa_combine_kernel<4>, dim3((unsigned)R, (unsigned)((H + 1) / 2)), dim3(kCombineThreads), 0, s, P);
+      hipLaunchKernelGGL((sfa_combine_kernel<4, kMaxSplits>), g4, dim3(kCombineThreads), 0, s, P);
     if (hipGetLastError() != hipSuccess) return DSA_ERR_HIP;
   }
   return DSA_OK;
