@@ -445,9 +445,10 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
 // V consecutive dims of one head (512/V threads per head), so a block of 256
 // threads covers 2 heads for V = 4 and 4 heads for V = 8.  V = 4 is used when
 // the V = 8 grid would have fewer blocks than the chip has CUs (one row of
-// 128 heads: 32 blocks): twice the blocks put more loads in flight
-// (measured 23.1 -> 22.7 us per call at 8K, batch 1); with a block per CU
-// the two measure the same.  The arithmetic per element is the same for both.
+// 128 heads: 32 blocks): twice the blocks put more loads in flight (0.4 us
+// less per call for one row of 128 heads in eight splits); with a block per
+// CU the two measure the same.  The arithmetic per element is the same for
+// both.
 // SMAX is the most splits the block holds in registers (8, or 16 for a batch
 // of a few rows whose lists are cut into two steps per split).
 template <int V, int SMAX>
