@@ -88,6 +88,7 @@ struct Params {
   int32_t upr;           // units-per-row stride of ucount / uedge
   int32_t tile_rows;     // row-tiled path: rows per tile (<= kTileRows), all of one sequence
   int32_t chunk_units;   // row-tiled path: units per work item (0 = the whole tile)
+  int32_t j_start;       // select: the first layout tried (slots per unit / 64)
   int32_t* out_idx;
   float* out_score;
   float* dump;           // score rows (test entry point only)
@@ -503,7 +504,7 @@ __device__ __forceinline__ void score_unit(const Params& P, const Unit& U, uint3
 // Keys a unit keeps: its expected share E of the Top-K (about
 // topk * 1024 / (t+1)) plus four standard deviations and a margin; every key
 // when the row has no more than topk positions.
-__device__ __forceinline__ uint32_t unit_quota(int t, int topk) {
+__host__ __device__ __forceinline__ uint32_t unit_quota(int t, int topk) {
   const int64_t n = (int64_t)t + 1;
   if (n <= topk) return 0xFFFFFFFFu;
   const float e = (float)topk * (float)kUnitTok / (float)n;
@@ -1204,7 +1205,9 @@ __device__ __forceinline__ int select_fast(const Params& P, SelSmem& S, int row)
 }
 
 // select_fast with the layout J (2, 4, 8 or 16) a runtime value: one copy of
-// the code for all wide layouts.
+// the code for all wide layouts.  With RETRY, a layout too small for the row
+// returns the larger one to try instead of giving up.
+template <bool RETRY>
 __device__ __forceinline__ int select_fast_rt(const Params& P, SelSmem& S, int row, int J) {
   J = __builtin_amdgcn_readfirstlane(J);
   const int WPU = J > kFastPer ? J / kFastPer : 1;       // waves per unit
@@ -1277,7 +1280,13 @@ __device__ __forceinline__ int select_fast_rt(const Params& P, SelSmem& S, int r
     emax = max(emax, x.z);
     kmax = max(kmax, x.w);
   }
-  if (cmax > 64u * J) return 0;
+  if (cmax > 64u * J) {
+    // a layout with more slots per unit, if the row has few enough units
+    if (RETRY)
+      for (int jn = 2 * J; jn <= 2 * kFastPer; jn *= 2)
+        if (cmax <= 64u * jn && units_r <= kFastUnits / jn) return jn;
+    return 0;
+  }
   gint32* oidx = (gint32*)(P.out_idx + (int64_t)row * K);
   gfloat* osc = P.out_score ? (gfloat*)(P.out_score + (int64_t)row * K) : nullptr;
   if (take_all) {
@@ -1392,14 +1401,28 @@ __device__ __forceinline__ void rescore_unit(const Params& P, SelSmem& S, int ro
   }
 }
 
-template <int NHT>
+template <int NHT, bool SHORT>
 __global__ __launch_bounds__(kSelThreads, 1) void indexer_select_kernel(Params P) {
   __shared__ SelSmem S;
   const int row = blockIdx.x;
-  int fast = select_fast<1>(P, S, row);
-  if (fast > 1) {
-    __syncthreads();   // every wave has read the first attempt's LDS results
-    fast = select_fast_rt(P, S, row, fast);
+  int fast;
+  if (SHORT) {
+    // every row of the launch is short enough to need a layout with more
+    // slots per unit (chosen on the host); one too small for a row names a
+    // larger one, tried next
+    fast = P.j_start;
+    bool tried = false;
+    while (fast > 1) {
+      if (tried) __syncthreads();   // every wave has read the last attempt's LDS results
+      tried = true;
+      fast = select_fast_rt<true>(P, S, row, fast);
+    }
+  } else {
+    fast = select_fast<1>(P, S, row);
+    if (fast > 1) {
+      __syncthreads();   // every wave has read the first attempt's LDS results
+      fast = select_fast_rt<false>(P, S, row, fast);
+    }
   }
   if (fast == 1) return;
   // general path: waves 0..3 (a barrier first, so that no wave still reads
@@ -1796,14 +1819,14 @@ Layout layout_for(int64_t rows, int64_t bt_stride) {
   return L;
 }
 
-enum KernelKind { kScan = 0, kSelect = 1, kDump = 2 };
+enum KernelKind { kScan = 0, kSelect = 1, kDump = 2, kSelectShort = 3 };
 
 void* pick_kernel(int nht, KernelKind kind) {
   switch (nht) {
-    case 1: return kind == kScan ? (void*)&indexer_scan_kernel<1> : kind == kSelect ? (void*)&indexer_select_kernel<1> : (void*)&indexer_dump_kernel<1>;
-    case 2: return kind == kScan ? (void*)&indexer_scan_kernel<2> : kind == kSelect ? (void*)&indexer_select_kernel<2> : (void*)&indexer_dump_kernel<2>;
-    case 3: return kind == kScan ? (void*)&indexer_scan_kernel<3> : kind == kSelect ? (void*)&indexer_select_kernel<3> : (void*)&indexer_dump_kernel<3>;
-    default: return kind == kScan ? (void*)&indexer_scan_kernel<4> : kind == kSelect ? (void*)&indexer_select_kernel<4> : (void*)&indexer_dump_kernel<4>;
+    case 1: return kind == kScan ? (void*)&indexer_scan_kernel<1> : kind == kSelect ? (void*)&indexer_select_kernel<1, false> : kind == kSelectShort ? (void*)&indexer_select_kernel<1, true> : (void*)&indexer_dump_kernel<1>;
+    case 2: return kind == kScan ? (void*)&indexer_scan_kernel<2> : kind == kSelect ? (void*)&indexer_select_kernel<2, false> : kind == kSelectShort ? (void*)&indexer_select_kernel<2, true> : (void*)&indexer_dump_kernel<2>;
+    case 3: return kind == kScan ? (void*)&indexer_scan_kernel<3> : kind == kSelect ? (void*)&indexer_select_kernel<3, false> : kind == kSelectShort ? (void*)&indexer_select_kernel<3, true> : (void*)&indexer_dump_kernel<3>;
+    default: return kind == kScan ? (void*)&indexer_scan_kernel<4> : kind == kSelect ? (void*)&indexer_select_kernel<4, false> : kind == kSelectShort ? (void*)&indexer_select_kernel<4, true> : (void*)&indexer_dump_kernel<4>;
   }
 }
 
@@ -1848,7 +1871,7 @@ int run(Params P, bool dump, hipStream_t stream) {
   const int nht = (P.H + 15) / 16;
   const KernelKind kind = dump ? kDump : kScan;
   void* scan = pick_kernel(nht, kind);
-  void* sel = pick_kernel(nht, kSelect);
+  void* sel = pick_kernel(nht, P.j_start > 1 ? kSelectShort : kSelect);
   const int scan_threads = dump ? kThreads : kScanThreads;
   const int cap = resident_capacity(scan, (nht - 1) * 3 + (int)kind, scan_threads);
   if (cap <= 0) return DSA_ERR_HIP;
@@ -1901,7 +1924,29 @@ Params base_params(const void* q_fp8, const void* q_e8m0, const float* w, const 
   P.upr = units_stride(bt_stride);
   P.tile_rows = kTileRows;
   P.chunk_units = 0;
+  P.j_start = 1;
   return P;
+}
+
+// The select's first layout for rows of up to bt_stride pages: every such
+// row keeps at least min(quota, unit size) candidates in its fullest unit,
+// and the quota only grows as rows get shorter, so the longest possible
+// row's quota is a lower bound for all of them; smaller layouts would be
+// tried and abandoned.  Taken only when that bound already asks for 8 or
+// more 64-slot groups per unit (rows of up to about 10K positions at
+// K = 2048: decode 8K, batch 1, 25.4 -> 23.8 us per call).  With a looser
+// bound most rows still need a larger layout than the first one tried, and
+// a failed runtime-layout attempt costs more than a failed first-layout one
+// (ragged decode of 4K-64K rows, bound 2: 47.2 -> 47.7 us), so those
+// launches keep the regular order (returns 1).
+int select_j_start(int32_t bt_stride, int32_t topk) {
+  const int64_t n_max = (int64_t)bt_stride * kPage;
+  if (n_max <= topk) return 1;
+  const uint32_t q = unit_quota((int)(n_max - 1), topk);
+  int J = 1;
+  while (64u * (uint32_t)J < q && J < 2 * kFastPer) J *= 2;
+  const int64_t units = (n_max + kUnitTok - 1) / kUnitTok;
+  return (J >= 8 && 64u * (uint32_t)J >= q && units <= kFastUnits / J) ? J : 1;
 }
 
 }  // namespace
@@ -1940,6 +1985,7 @@ extern "C" int dsa_indexer_topk(const void* q_fp8, const void* q_e8m0, const flo
   P.ucount = reinterpret_cast<uint32_t*>(ws + L.ucount);
   P.uedge = reinterpret_cast<uint32_t*>(ws + L.uedge);
   P.cand = reinterpret_cast<uint2*>(ws + L.cand);
+  P.j_start = select_j_start(bt_stride, topk);
   return run(P, false, dsa_host::as_stream(stream));
 }
 
