@@ -57,10 +57,6 @@ def bf16_decode(bits) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
-def f32_bits(x) -> np.ndarray:
-    return np.asarray(x, dtype=np.float32).view(np.uint32)
-
-
 def e4m3_encode_nearest(y) -> np.ndarray:
     """Reference encoder by exhaustive search: the finite E4M3 value nearest
     to |y|; on an exact tie the code with an even mantissa (even code) wins;

@@ -8,8 +8,10 @@ MXFP8 (E4M3, one E8M0 scale per 32 elements) is reported to cost under 0.1%
 of accuracy on the page's long-context benchmark.  That benchmark and the
 model weights are not available here, so this module measures the quantity
 the claim rests on, on the seeded synthetic inputs: how far the Top-K
-positions chosen from MXFP8 scores (this package's indexer definition, which
-the HIP path reproduces bit for bit) agree with the Top-K of the same
+positions chosen from MXFP8 scores (this package's fp64 indexer on the
+dequantised MXFP8 q and k; the HIP path computes the same scores in fp32 on
+the scaled fp8 MFMA, within 1e-4 of the row's largest score, and may swap
+positions whose scores lie that close to the K-th) agree with the Top-K of the same
 indexer evaluated in fp64 on the unquantised bf16 q and k.
 
 Per query row r with history t (n = min(K, t + 1) positions kept):

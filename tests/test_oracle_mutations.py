@@ -17,6 +17,8 @@ import oracle.quant as quant
 from tests import test_oracle_attention as TA
 from tests import test_oracle_formats as TF
 from tests import test_oracle_indexer as TI
+from tests import test_oracle_pipeline as TP
+from oracle.pipeline import Oracle
 from tests import test_oracle_quant as TQ
 
 
@@ -84,6 +86,18 @@ def _sfa_dedup(q, lat, rope, idx, scale=attention.DEFAULT_SCALE):
     return _orig["sparse_attn"](q, lat, rope, np.unique(idx[idx >= 0]), scale)
 
 
+def _k_index_no_offset(self, b):
+    # the sequence's keys taken from token 0 instead of its own start
+    L = int(self.inp["seq_lens"][b])
+    codes, e8 = quant.mxfp8_quant(self.inp["k_idx"][:L])
+    return quant.mxfp8_dequant(codes, e8)
+
+
+def _kv_rows_no_offset(self, b, positions):
+    rec = quant.kv_quant(self.inp["kv"][np.asarray(positions, dtype=np.int64)])
+    return quant.kv_dequant(rec)
+
+
 _orig = dict(indexer_scores=indexer.indexer_scores, sparse_attn=attention.sparse_attn)
 
 CASES = [
@@ -109,6 +123,10 @@ CASES = [
      [TA.test_all_positions_equal_torch_sdpa, TA.test_single_index_returns_latent_row]),
     ("duplicates collapsed", attention, "sparse_attn", _sfa_dedup,
      [TA.test_duplicates_count_and_empty_list]),
+    ("indexer keys without the sequence offset", Oracle, "k_index", _k_index_no_offset,
+     [TP.test_scores_of_every_sequence_through_the_k_pool]),
+    ("KV rows without the sequence offset", Oracle, "kv_rows", _kv_rows_no_offset,
+     [TP.test_attention_of_every_sequence_through_the_kv_pool]),
 ]
 
 

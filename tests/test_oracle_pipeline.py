@@ -1,0 +1,96 @@
+"""Pins of the end-to-end oracle (oracle/pipeline.py) on inputs with several
+sequences.
+
+The pipeline works in logical token order: sequence b's tokens are rows
+seq_starts[b] .. seq_starts[b] + L_b - 1 of the drawn tensors.  The paged
+caches the kernels read are written out separately (oracle/pools.py), token s
+of sequence b at slot block_table[b][s // 64] * 64 + s % 64 ("Deep Dive into
+Sparse Attention ...", section 2.1: the indexer reads the paged K cache
+directly; "Adapting and Optimizing Kimi K3.1 Pro ...", section 2: SFA gathers
+cache entries by index; indices are logical positions of the sequence).
+These tests check the pipeline's scores and attention for rows of every
+sequence, including sequences that start deep inside the token arrays,
+against the same definitions evaluated on bytes gathered from the paged
+pools through each sequence's own block-table row.  A wrong sequence offset,
+a page/offset mix-up or a row of the wrong sequence fails them."""
+import numpy as np
+
+from oracle import attention, formats, indexer, pools, quant
+from oracle.pipeline import Oracle
+from sparse_attention_decode_topk_amd import synth
+
+
+def _ragged_input():
+    # four sequences of lengths that end mid-page, shuffled pages, two query
+    # rows per sequence (t = L-2, L-1)
+    cfg = synth.Config(97, "multi_seq", batch=4, h_index=4, h_attn=8, topk=16,
+                       ragged=(70, 260), q_per_seq=2)
+    inp = synth.make(cfg)
+    assert len(np.unique(inp["seq_starts"])) == 4 and inp["seq_starts"][3] > 0
+    return inp
+
+
+def test_scores_of_every_sequence_through_the_k_pool():
+    inp = _ragged_input()
+    o = Oracle(inp)
+    npages = int(inp["total_pages"])
+    codes, e8 = quant.mxfp8_quant(inp["k_idx"])
+    pool = pools.k_pool_write(codes, e8, inp["slot_mapping"], npages)
+    for r in range(len(inp["row_seq"])):
+        b = int(inp["row_seq"][r])
+        t = int(inp["row_pos"][r])
+        L = int(inp["seq_lens"][b])
+        c, x = pools.k_pool_read(pool, inp["block_table"][b], L)
+        k = quant.mxfp8_dequant(c, x)
+        qc, qe = quant.mxfp8_quant(inp["q_idx"][r])
+        q = quant.mxfp8_dequant(qc, qe)
+        ref = indexer.indexer_scores(q, k, inp["w"][r].astype(np.float64), t)
+        got = o.scores(r)
+        assert got.shape == (t + 1,)
+        assert np.array_equal(got, ref), f"row {r} (sequence {b})"
+
+
+def test_attention_of_every_sequence_through_the_kv_pool():
+    inp = _ragged_input()
+    o = Oracle(inp)
+    npages = int(inp["total_pages"])
+    rec = quant.kv_quant(inp["kv"])
+    pool = pools.kv_pool_write(rec, inp["slot_mapping"], npages)
+    rng = np.random.default_rng(12)
+    for r in range(len(inp["row_seq"])):
+        b = int(inp["row_seq"][r])
+        t = int(inp["row_pos"][r])
+        idx = rng.integers(0, t + 1, size=24)
+        idx[3] = -1
+        valid = idx[idx >= 0]
+        lat, rope = quant.kv_dequant(pools.kv_pool_read(pool, inp["block_table"][b], valid))
+        q = formats.bf16_decode(inp["q_sfa"][r])
+        ref_o, ref_l = attention.sparse_attn(q, lat, rope, np.arange(len(valid)))
+        got_o, got_l = o.sfa(r, idx)
+        assert np.allclose(got_o, ref_o, rtol=0, atol=1e-12 * np.abs(ref_o).max())
+        assert np.allclose(got_l, ref_l, rtol=0, atol=1e-12)
+
+
+def test_kv_pool_read_hand_example():
+    # block-table row [3, 0, 2]: position 70 is page row entry 1 (page 0),
+    # offset 6 -> slot 6; position 130 is entry 2 (page 2), offset 2 -> slot
+    # 130; position 5 is entry 0 (page 3), offset 5 -> slot 197
+    pool = np.zeros((4 * 64, quant.RECORD_BYTES), dtype=np.uint8)
+    for s in range(4 * 64):
+        pool[s, 0] = s & 0xFF
+        pool[s, 1] = s >> 8
+    got = pools.kv_pool_read(pool, np.array([3, 0, 2], dtype=np.int32), np.array([70, 130, 5]))
+    slots = got[:, 0].astype(np.int64) + (got[:, 1].astype(np.int64) << 8)
+    assert slots.tolist() == [6, 130, 197]
+
+
+def test_k_pool_read_hand_example():
+    # the K page stores codes token-major, then 4 scale bytes per token:
+    # position 65 of block-table row [1, 0] is page 0, offset 1 -> code bytes
+    # [128, 256) and scale bytes [8196, 8200) of page 0
+    pool = np.zeros((2, pools.K_PAGE_BYTES), dtype=np.uint8)
+    pool[0, 128:256] = 7
+    pool[0, 8192 + 4:8192 + 8] = [120, 121, 122, 123]
+    c, x = pools.k_pool_read(pool, np.array([1, 0], dtype=np.int32), 66)
+    assert np.all(c[65] == 7) and x[65].tolist() == [120, 121, 122, 123]
+    assert np.all(c[:64] == 0) and np.all(x[:64] == 0)

@@ -16,29 +16,71 @@ def bf16(x):
     return synth.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
 
 
+def _golden(kind):
+    """Data lines of tests/golden/quant_examples.txt: name -> {key: int}."""
+    out = {}
+    with open(os.path.join(GOLDEN, "quant_examples.txt")) as f:
+        for line in f:
+            parts = line.split()
+            if not parts or parts[0].startswith("#") or parts[0] != kind:
+                continue
+            out[parts[1]] = {k: int(v, 0) for k, v in (p.split("=") for p in parts[2:])}
+    return out
+
+
+# the input group / tile each golden line describes (its comment block)
+def _mx_input(name):
+    g = np.ones(32, dtype=np.float32)
+    if name == "ones_with_3_at_5":
+        g[5] = 3.0
+    elif name == "zeros":
+        g[:] = 0.0
+    elif name == "all_448":
+        g[:] = 448.0
+    elif name == "all_0.875":
+        g[:] = 0.875
+    else:
+        raise KeyError(name)
+    return g
+
+
+def _kv_input(name):
+    t = np.full(576, 0.25, dtype=np.float32)
+    if name == "half_with_minus7_at_9":
+        t[:128] = 0.5
+        t[9] = -7.0
+    elif name == "zeros":
+        t[:] = 0.0
+    else:
+        raise KeyError(name)
+    return t
+
+
 def test_mx_golden_examples():
-    g = np.ones(32, dtype=np.float32); g[5] = 3.0
-    codes, e8 = quant.mxfp8_quant(bf16(g)[None])
-    assert e8[0, 0] == 120 and codes[0, 5] == 0x7C
-    assert np.all(np.delete(codes[0], 5) == 0x70)
-    codes, e8 = quant.mxfp8_quant(bf16(np.zeros(32))[None])
-    assert e8[0, 0] == 127 and np.all(codes == 0)
-    codes, e8 = quant.mxfp8_quant(bf16(np.full(32, 448.0))[None])
-    assert e8[0, 0] == 127 and np.all(codes == 0x7E)
-    codes, e8 = quant.mxfp8_quant(bf16(np.full(32, 0.875))[None])
-    assert e8[0, 0] == 118 and np.all(codes == 0x7E)
+    gold = _golden("mx_group")
+    assert set(gold) == {"ones_with_3_at_5", "zeros", "all_448", "all_0.875"}
+    for name, exp in gold.items():
+        codes, e8 = quant.mxfp8_quant(bf16(_mx_input(name))[None])
+        assert e8[0, 0] == exp["e8m0"], name
+        if name == "ones_with_3_at_5":
+            assert codes[0, 5] == exp["code_three"]
+            assert np.all(np.delete(codes[0], 5) == exp["code_one"])
+        else:
+            assert np.all(codes == exp["code"]), name
 
 
 def test_kv_golden_examples():
-    t = np.full(576, 0.25, dtype=np.float32)
-    t[:128] = 0.5; t[9] = -7.0
-    rec = quant.kv_quant(bf16(t)[None])[0]
-    assert rec[512:516].tobytes() == bytes([0x00, 0x00, 0x80, 0x3C])
-    assert rec[9] == 0xFE and np.all(np.delete(rec[:128], 9) == 0x60)
-    z = np.zeros(576, dtype=np.float32)
-    rec = quant.kv_quant(bf16(z)[None])[0]
-    assert rec[512:516].tobytes() == np.float32(1.0).tobytes()
-    assert np.all(rec[:512] == 0)
+    gold = _golden("kv_tile")
+    assert set(gold) == {"half_with_minus7_at_9", "zeros"}
+    for name, exp in gold.items():
+        rec = quant.kv_quant(bf16(_kv_input(name))[None])[0]
+        scale_bits = int(np.frombuffer(rec[512:516].tobytes(), dtype="<u4")[0])
+        assert scale_bits == exp["scale_bits"], name
+        if name == "half_with_minus7_at_9":
+            assert rec[9] == exp["code_m7"]
+            assert np.all(np.delete(rec[:128], 9) == exp["code_half"])
+        else:
+            assert np.all(rec[:512] == exp["code"])
 
 
 def _random_bf16(rng, shape, spread=True):
