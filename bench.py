@@ -26,6 +26,16 @@ calls, each bracketed by HIP events; the indexer's average is the roofline
 duration.  `traffic` is filled from the committed FETCH_SIZE/WRITE_SIZE
 summary when it was taken on the current indexer source.
 
+Further fields: `per_call` (p10/median/p90 of every step and entry point
+from an event pair around each call, in a region of its own),
+`stream_read_gbs` (a plain streaming read of 4 GiB by the library's probe
+kernel in the same process: the practical read ceiling next to the 8 TB/s
+datasheet peak), `step_roofline` (the whole step's algorithmic bytes over
+its event-free time), `cpu_model`, and `parity`: the oracle rows timed for
+`cpu_baseline` also gate the timed kernels' outputs (Top-K pass rule and
+scores within 1e-4 max|I|, SFA on the GPU's own indices within 1e-3
+max|oracle|); a failing workload prints `value: null`.
+
 Prints one JSON line.  `value` is query tokens/s (rows * steps / seconds;
 for decode one row per sequence).  --config prefill_chunk_8k_of_128k times
 the chunked-prefill step instead (8192 query rows of one sequence through
@@ -239,6 +249,35 @@ def main():
 
     idx_avg = timed_calls(indexer_call, "idx")
     sfa_avg = timed_calls(L.dsa_sparse_attn, "sfa")
+
+    # per-call distributions: an event pair around every call (the events
+    # themselves cost a little, so `value` comes from the event-free region)
+    def per_call(fn_step, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(evs):
+            a.record()
+            fn_step(i)
+            b.record()
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+        return {"p10_us": round(float(np.percentile(t, 10)), 2),
+                "median_us": round(float(np.median(t)), 2),
+                "p90_us": round(float(np.percentile(t, 90)), 2), "calls": n}
+
+    def call_idx(i):
+        if indexer_call(*steps_args[i % args.replicas]["idx"]):
+            raise RuntimeError("indexer call failed")
+
+    def call_sfa(i):
+        if L.dsa_sparse_attn(*steps_args[i % args.replicas]["sfa"]):
+            raise RuntimeError("sparse attention call failed")
+
+    n_pc = max(50, min(K_steps, 200))
+    dist = {"step": per_call(run_step, n_pc), idx_name_of(one_seq, mq): per_call(call_idx, n_pc),
+            "dsa_sparse_attn": per_call(call_sfa, n_pc)}
+    stream_gbs = stream_read_gbs(ops, dev) if not args.profile_steps else None
     ms_per_step = elapsed * 1e3 / K_steps
     tokens_per_s = R * K_steps / elapsed   # query tokens (decode: one per sequence)
 
@@ -263,12 +302,13 @@ def main():
     err_word = int(ws_i[8:12].view(torch.int32).item())
     traffic = measured_traffic(cfg.name)
 
-    cpu = None
+    cpu, parity = None, None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, args.cpu_rows)
+        res_idx, res_sc = out_idx.cpu().numpy(), out_sc.cpu().numpy()
+        res_out = out.cpu().numpy()
+        cpu, parity = cpu_baseline(inp, args.cpu_rows, res_idx, res_sc, res_out)
 
-    idx_name = ("dsa_indexer_topk_seq" if one_seq else
-                "dsa_indexer_topk_mq" if mq else "dsa_indexer_topk")
+    idx_name = idx_name_of(one_seq, mq)
     mfma = {idx_name: {"achieved": round(idx_tf, 1), "peak": FP8_PEAK_TFS, "unit": "TFLOP/s",
                        "frac": round(idx_tf / FP8_PEAK_TFS, 4), "flop": idx_flop,
                        "dtype": "fp8 e4m3 x e4m3, E8M0 block scales"},
@@ -285,9 +325,11 @@ def main():
         roofline = {"bound": "hbm", "kernel": idx_name, "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": traffic, "algorithmic_bytes": idx_bytes}
+    step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     rec = {
         "metric": METRIC_PREFILL if one_seq else METRIC_MQ if mq else METRIC,
-        "value": round(tokens_per_s, 1),
+        # a workload whose sampled rows fail the parity rules reports no value
+        "value": round(tokens_per_s, 1) if (parity is None or parity["pass"]) else None,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K_steps,
@@ -303,8 +345,18 @@ def main():
                    "cache_replicas_rotated": args.replicas, "parallelism": "single GPU",
                    "prolog": "three launches" if args.separate_prolog else "dsa_decode_prolog (one launch)",
                    "launch": "hipGraph replay per step" if args.graph else "eager launches"},
-        "hbm_gbs_step": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "hbm_gbs_step": round(step_gbs, 1),
         "algorithmic_bytes_step": step_bytes,
+        # the whole step (every launch of the hot path) against HBM: indexer
+        # K scan + SFA gather bytes over the event-free step time
+        "step_roofline": {"bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                          "frac_of_stream_read": (round(step_gbs / stream_gbs, 4)
+                                                  if stream_gbs else None)},
+        "stream_read_gbs": round(stream_gbs, 1) if stream_gbs else None,
+        "per_call": dist,
+        "parity": parity,
+        "cpu_model": cpu_model(),
         "kernel_ms": {idx_name: round(idx_avg, 5),
                       "dsa_sparse_attn": round(sfa_avg, 5)},
         "roofline": roofline,
@@ -314,6 +366,46 @@ def main():
         "input_gen_s": round(t_gen, 1),
     }
     print(json.dumps(rec))
+
+
+def idx_name_of(one_seq, mq):
+    return "dsa_indexer_topk_seq" if one_seq else "dsa_indexer_topk_mq" if mq else "dsa_indexer_topk"
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def stream_read_gbs(ops, dev, nbytes=4 << 30, iters=20):
+    """Plain streaming read of a 4 GiB buffer (16 times the 256 MB Infinity
+    Cache) with the library's probe kernel; best-of and median GB/s over
+    `iters` back-to-back reads, each between its own event pair."""
+    import numpy as np
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    grid = 256 * 16
+    out = torch.empty(grid, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        ops.probe_stream_read(src, out, grid)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        ops.probe_stream_read(src, out, grid)
+        b.record()
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    del src
+    return float(nbytes / (np.median(ms) * 1e-3) / 1e9)
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "dsa_indexer_topk_decode_128k_b8_traffic.txt")
@@ -354,9 +446,17 @@ def copy_probe(nbytes):
     print(json.dumps({"copy_probe_bytes": nbytes}))
 
 
-def cpu_baseline(inp, rows):
-    """The fp64 oracle (as it stands) on the first `rows` decode rows of the
-    same inputs: indexer scores, Top-K and sparse attention per row."""
+def cpu_baseline(inp, rows, gpu_idx, gpu_sc, gpu_out):
+    """The fp64 oracle (as it stands) on the first `rows` query rows of the
+    same inputs: indexer scores, Top-K and sparse attention per row, timed.
+    The same oracle results then gate the GPU's outputs of the timed steps
+    on those rows (outside the timed CPU region):
+      * Top-K: |S| = min(K, t+1) unique ascending positions in [0, t], -1
+        padding; every position where the GPU and the oracle differ has an
+        oracle score within 1e-4 * max|I| of the oracle's K-th score;
+      * the GPU's reported scores within 1e-4 * max|I| of the oracle's;
+      * SFA over the GPU's own indices: max abs error <= 1e-3 * max|oracle|
+        over the checked rows."""
     import numpy as np
 
     from oracle.pipeline import Oracle
@@ -367,13 +467,48 @@ def cpu_baseline(inp, rows):
         cores = len(os.sched_getaffinity(0))
     o = Oracle(inp)
     t0 = time.perf_counter()
+    ora = []
     for r in range(rows):
         res = o.topk(r)
         o.sfa(r, res["idx"])
+        ora.append(res)
     dt = time.perf_counter() - t0
-    return {"value": round(rows / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{rows} of {len(inp['row_seq'])} query rows (indexer+Top-K+SFA per row, "
-                      f"fp64 numpy), {dt:.1f} s"}
+    cpu = {"value": round(rows / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": f"{rows} of {len(inp['row_seq'])} query rows (indexer+Top-K+SFA per row, "
+                     f"fp64 numpy), {dt:.1f} s"}
+    K = int(inp["topk"])
+    fails, swaps, worst_idx, worst_sfa = [], 0, 0.0, 0.0
+    ref_max, err_max = 0.0, 0.0
+    for r, res in enumerate(ora):
+        t = int(inp["row_pos"][r])
+        n = min(K, t + 1)
+        g = gpu_idx[r]
+        sel = g[:n]
+        I, tol = res["scores"], 1e-4 * res["maxabs"]
+        ok = (np.all(g[n:] == -1) and np.all(sel >= 0) and np.all(sel <= t)
+              and np.all(np.diff(sel) > 0))
+        if ok:
+            diff = np.setxor1d(sel, res["idx"][:n])
+            swaps += len(diff)
+            if len(diff) and not np.all(np.abs(I[diff] - res["kth"]) <= tol):
+                ok = False
+            e = float(np.abs(gpu_sc[r][:n] - I[sel]).max()) if n else 0.0
+            worst_idx = max(worst_idx, e / res["maxabs"] if res["maxabs"] > 0 else 0.0)
+            ok = ok and e <= tol
+        if not ok:
+            fails.append(f"row {r}: Top-K rule")
+            continue
+        ref, _ = o.sfa(r, g)
+        ref_max = max(ref_max, float(np.abs(ref).max()))
+        err_max = max(err_max, float(np.abs(gpu_out[r] - ref).max()))
+    if ref_max > 0:
+        worst_sfa = err_max / ref_max
+        if err_max > 1e-3 * ref_max:
+            fails.append(f"SFA error {worst_sfa:.2e} of max|oracle|")
+    parity = {"pass": not fails, "rows": rows, "tolerated_swaps": swaps,
+              "score_err_frac_max": float(f"{worst_idx:.3g}"), "score_bar": 1e-4,
+              "sfa_err_frac": float(f"{worst_sfa:.3g}"), "sfa_bar": 1e-3, "failures": fails[:4]}
+    return cpu, parity
 
 
 if __name__ == "__main__":

@@ -286,6 +286,18 @@ int dsa_sparse_attn(const void* q_bf16, const void* kv_pool, int64_t pool_pages,
                     float* out, float* lse,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Measurement utility (not part of the hot path): reads `bytes` (a multiple
+ * of 16) from the device buffer `src` once with streaming 16-byte loads on
+ * `grid` work-groups of 256 threads and writes one folded word per
+ * work-group to out[grid] (device, caller-owned).  Its duration gives the
+ * plain streaming-read bandwidth of the GPU, the practical ceiling next to
+ * the HBM datasheet figure for the indexer's K-cache scan ("Adapting and
+ * Optimizing Kimi K3.1 Pro for Long-Sequence Inference", section 3: memory
+ * bandwidth is one of the primary bottlenecks of long sequences).
+ */
+int dsa_probe_stream_read(const void* src, size_t bytes, uint32_t* out, int32_t grid, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

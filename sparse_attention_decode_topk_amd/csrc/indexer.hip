@@ -35,6 +35,7 @@
 //     taken).  Ties are broken by the lower position.
 // No floating-point atomics are used, so results are deterministic.
 #include <algorithm>
+#include <atomic>
 
 #include "common.hpp"
 
@@ -1024,6 +1025,15 @@ __device__ __forceinline__ bool fast_find(SelSmem& S, const uint32_t* H, uint32_
   return true;
 }
 
+// Candidate slots of a row's first nu units that lie inside the row's region
+// of the workspace (bt_stride * 64 slots): the last unit of a block table
+// whose width is not a multiple of 16 pages has a shorter slice, and a
+// layout's loads past it must read nothing (out-of-range buffer loads return
+// 0) rather than the next row's region or memory past the workspace.
+__device__ __forceinline__ int row_slots(const Params& P, int nu) {
+  return min(nu * kUnitTok, P.bt_stride * kPage);
+}
+
 // Layout J (1, 2, 4, 8 or 16): for J <= 8 wave w owns units (8/J)w ..
 // (8/J)w + 8/J - 1 and holds slots lane, lane + 64, ..., lane + 64(J-1) of
 // each; for J = 16 waves 2u and 2u+1 share unit u, slots lane + 64j and
@@ -1057,7 +1067,7 @@ __device__ __forceinline__ int select_fast(const Params& P, SelSmem& S, int row)
   uint32_t cnt_l = __builtin_amdgcn_raw_buffer_load_b32(rc, uoff, 0, 0);
   uint32_t edge_l = __builtin_amdgcn_raw_buffer_load_b32(re, uoff, 0, 0);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      P.cand + (int64_t)row * P.bt_stride * kPage, (short)0, nu * kUnitTok * 8, kRawBufferWord3);
+      P.cand + (int64_t)row * P.bt_stride * kPage, (short)0, row_slots(P, nu) * 8, kRawBufferWord3);
   uint32_t k[kFastPer], p[kFastPer];
 #pragma unroll
   for (int i = 0; i < kFastPer; ++i) {
@@ -1231,7 +1241,7 @@ __device__ __forceinline__ int select_fast_rt(const Params& P, SelSmem& S, int r
   uint32_t cnt_l = __builtin_amdgcn_raw_buffer_load_b32(rc, uoff, 0, 0);
   uint32_t edge_l = __builtin_amdgcn_raw_buffer_load_b32(re, uoff, 0, 0);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      P.cand + (int64_t)row * P.bt_stride * kPage, (short)0, nu * kUnitTok * 8, kRawBufferWord3);
+      P.cand + (int64_t)row * P.bt_stride * kPage, (short)0, row_slots(P, nu) * 8, kRawBufferWord3);
   uint32_t k[kFastPer], p[kFastPer];
 #pragma unroll
   for (int i = 0; i < kFastPer; ++i) {
@@ -1839,13 +1849,22 @@ void* pick_tile_kernel(int nht, bool two) {
   }
 }
 
-// resident workgroups of a kernel on the current device (cached per device)
+// resident workgroups of a kernel on the current device, cached per device
+// and kernel slot.  Entries are atomics: two host threads that miss at the
+// same time both compute the same value and store it, so no lock is needed
+// and a reader never sees a torn value (0 = not computed yet).
+constexpr int kCapDevices = 64;
+constexpr int kCapSlots = 20;
+std::atomic<int> g_capacity[kCapDevices][kCapSlots];
+
 int resident_capacity(void* fn, int slot, int threads) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
-  static int cached[64][20];
-  static bool have[64][20];
-  if (dev < 64 && have[dev][slot]) return cached[dev][slot];
+  const bool cache = dev >= 0 && dev < kCapDevices && slot >= 0 && slot < kCapSlots;
+  if (cache) {
+    const int c = g_capacity[dev][slot].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return -1;
   int per_cu = 0;
@@ -1853,7 +1872,7 @@ int resident_capacity(void* fn, int slot, int threads) {
                                                    threads, 0) != hipSuccess)
     return -1;
   const int cap = std::max(1, per_cu) * prop.multiProcessorCount;
-  if (dev < 64) { cached[dev][slot] = cap; have[dev][slot] = true; }
+  if (cache) g_capacity[dev][slot].store(cap, std::memory_order_relaxed);
   return cap;
 }
 

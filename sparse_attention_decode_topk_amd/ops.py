@@ -54,6 +54,7 @@ SIGNATURES = {
     "dsa_sparse_attn_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "dsa_sparse_attn": (_c.c_int, [_P, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _I32, _F,
                                    _P, _P, _P, _SZ, _P]),
+    "dsa_probe_stream_read": (_c.c_int, [_P, _SZ, _P, _I32, _P]),
 }
 
 
@@ -276,3 +277,18 @@ def dsa_sparse_attn(q, kv_pool, block_table, row_seq, idx, softmax_scale: float 
                                  float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                                  workspace.numel(), _stream()), "dsa_sparse_attn")
     return out, lse
+
+
+# ------------------------------------------------------------- measurement
+
+def probe_stream_read(src: torch.Tensor, out: torch.Tensor, grid: int):
+    """Streaming read of every byte of `src` (device, contiguous, size a
+    multiple of 16); one folded word per work-group into out (int32 [grid])."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise TypeError("src: expected a contiguous device tensor")
+    _need(out, torch.int32, "out")
+    if out.numel() < grid:
+        raise ValueError("out needs one word per work-group")
+    nbytes = src.numel() * src.element_size()
+    _check(lib().dsa_probe_stream_read(_ptr(src), nbytes, _ptr(out), grid, _stream()),
+           "dsa_probe_stream_read")

@@ -168,3 +168,36 @@ def test_decode_prolog_argument_errors(lib):
     # no new tokens: the cache arguments may be absent
     assert _prolog_call(lib, rows=0, n=0, k=None, kv=None, slots=None, kpool=None, kvpool=None,
                         pages=0) == 0
+
+
+def test_probe_argument_errors(lib):
+    assert lib.dsa_probe_stream_read(None, 1 << 20, FAKE, 256, None) == 1
+    assert lib.dsa_probe_stream_read(FAKE, 1 << 20, None, 256, None) == 1
+    assert lib.dsa_probe_stream_read(FAKE, 1000, FAKE, 256, None) == 1   # not a multiple of 16
+    assert lib.dsa_probe_stream_read(FAKE, 1 << 20, FAKE, 0, None) == 1
+
+
+def test_concurrent_first_calls_from_host_threads(lib):
+    """Many host threads enter the indexer entry points at once, the first
+    calls of the process included: the per-device occupancy cache they all
+    consult is filled without a lock.  Without a GPU every call gets past
+    validation and stops at the device query with DSA_ERR_HIP; every thread
+    must see the same status and nothing may crash."""
+    import threading
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("the device query succeeds on a GPU host; covered by the GPU tests")
+    results = []
+    lock = threading.Lock()
+
+    def worker():
+        st = [_idx_call(lib) for _ in range(20)] + [_mq_call(lib) for _ in range(20)]
+        with lock:
+            results.extend(st)
+
+    threads = [threading.Thread(target=worker) for _ in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert len(results) == 8 * 40 and set(results) == {4}

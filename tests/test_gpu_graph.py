@@ -5,8 +5,11 @@ device is synchronised, so each replay has to recompute them."""
 import pytest
 import torch
 
+import numpy as np
+
+from oracle.pipeline import Oracle
 from sparse_attention_decode_topk_amd import ops, synth
-from tests.dsa_state import DeviceState, bf16_tensor, say
+from tests.dsa_state import DeviceState, bf16_tensor, check_topk_row, say
 
 pytestmark = pytest.mark.gpu
 
@@ -63,6 +66,20 @@ def test_graph_replay_matches_eager(need_gpu):
         for name, a, b in zip(("idx", "score", "out", "lse"), outs, ref):
             assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager step"
         say(f"[graph] replay {rep} equal to eager")
+    # the last replay's results against the oracle: the Top-K rule, and the
+    # attention over the replay's own indices
+    o = Oracle(inp)
+    gi, gs = outs[0].cpu().numpy(), outs[1].cpu().numpy()
+    for r in range(R):
+        ora = o.topk(r)
+        check_topk_row(gi[r], gs[r], ora, K, int(inp["row_pos"][r]))
+        ref_o, ref_l = o.sfa(r, gi[r])
+        got = outs[2][r].cpu().numpy()
+        err = float(np.abs(got - ref_o).max())
+        bar = 1e-3 * float(np.abs(ref_o).max())
+        assert err <= bar, f"row {r}: SFA error {err:.3g} above {bar:.3g}"
+        assert np.all(np.abs(outs[3][r].cpu().numpy() - ref_l) <= 1e-3)
+    say("[graph] replay results pass the oracle checks")
     # eager again after the replays: the same bits
     step()
     torch.cuda.synchronize()

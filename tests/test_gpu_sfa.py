@@ -97,17 +97,22 @@ def test_sfa_deterministic(need_gpu):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-def test_end_to_end_decode(need_gpu):
-    """GPU indexer -> GPU SFA; rows whose selection equals the oracle's are
-    compared end to end."""
-    st = state("decode_8k_needles")
+@pytest.mark.parametrize("cfg", ["decode_8k_needles", "decode_ragged_b32", "decode_128k_b8"])
+def test_end_to_end_decode(need_gpu, cfg):
+    """GPU indexer -> GPU SFA on every row: the selection follows the Top-K
+    pass rule, and the attention over the GPU's own indices (which may
+    differ from the oracle's by tolerated near-tie swaps) matches the
+    oracle's attention over those same indices."""
+    st = state(cfg)
     o = Oracle(st.inp)
     idx, sc = st.indexer()
-    gi = idx.cpu().numpy()
-    ora = o.topk(0)
-    check_topk_row(gi[0], sc.cpu().numpy()[0], ora, st.topk, int(st.inp["row_pos"][0]))
-    if np.array_equal(gi[0], ora["idx"]):
-        _compare(st, o, gi, [0], "end to end")
+    gi, gs = idx.cpu().numpy(), sc.cpu().numpy()
+    swaps = 0
+    for r in range(st.R):
+        swaps += check_topk_row(gi[r], gs[r], o.topk(r), st.topk, int(st.inp["row_pos"][r]))
+    say(f"[e2e] {cfg}: {st.R} rows pass the Top-K rule ({swaps} tolerated swaps)")
+    _compare(st, o, gi, list(range(st.R)), f"end to end {cfg}")
+    o.drop_cache()
 
 
 def test_sfa_split_path_with_holes(need_gpu):
@@ -143,25 +148,35 @@ def test_sfa_ragged_batch(need_gpu):
     o.drop_cache()
 
 
-def test_sfa_prefill_chunk_sampled_rows(need_gpu):
+def test_sfa_prefill_chunk_every_64th_row(need_gpu):
     """The chunked-prefill shape as bench.py launches it: 8192 query rows of
     128 heads against a 131072-token cache, one split per row (the direct
-    output path, 32768 work-groups).  Sampled rows carry 2048 distinct
-    seeded positions of their causal history; every other row is empty and
-    must come out as zeros with lse -inf."""
+    output path, 32768 work-groups).  Every 64th row (and the last) carries
+    the GPU indexer's own selection, checked against the Top-K rule and then
+    through SFA against the oracle's attention over the same indices; the
+    rows in between are emptied and must come out as zeros with lse -inf."""
     st = state("prefill_chunk_8k_of_128k")
     o = Oracle(st.inp)
     R = st.R
-    rng = np.random.default_rng(23)
-    rows = sorted(set([0, 1, R // 2, R - 1] + rng.choice(R, 8, replace=False).tolist()))
-    idx = np.full((R, st.topk), -1, dtype=np.int32)
+    rows = sorted(set(range(0, R, 64)) | {R - 1})
+    gi, gs = _seq_topk_all(st)
     for r in rows:
-        t = int(st.inp["row_pos"][r])
-        idx[r] = rng.choice(t + 1, st.topk, replace=False)
-    out, lse = _compare(st, o, idx, rows, "prefill chunk, sampled rows")
+        check_topk_row(gi[r], gs[r], o.topk(r), st.topk, int(st.inp["row_pos"][r]))
+    say(f"[sfa] prefill chunk: {len(rows)} rows pass the Top-K rule")
+    idx = np.full((R, st.topk), -1, dtype=np.int32)
+    idx[rows] = gi[rows]
+    out, lse = _compare(st, o, idx, rows, f"prefill chunk, {len(rows)} rows")
     empty = [r for r in (2, R // 3, R - 2) if r not in rows]
     assert np.all(out[empty] == 0) and np.all(np.isneginf(lse[empty]))
     o.drop_cache()
+
+
+def _seq_topk_all(st):
+    bt_row = st.block_table[int(st.inp["row_seq"][0])].contiguous()
+    idx, sc = ops.dsa_indexer_topk_seq(st.q_fp8, st.q_e8m0, st.w, st.k_pool, bt_row, st.row_pos,
+                                       st.topk)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), sc.cpu().numpy()
 
 
 @pytest.mark.parametrize("K", [1, 100, 1000, 2047])
