@@ -174,6 +174,30 @@ int dsa_indexer_topk(const void* q_fp8, const void* q_e8m0, const float* w,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * dsa_indexer_topk without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It computes exactly what dsa_indexer_topk
+ * computes (the same kernels) and allocates nothing: its workspace is a
+ * 64 MiB array inside the library, one per GPU, held until the process ends.
+ *   - Limit: the workspace dsa_indexer_topk_workspace_size(R, bt_stride, ...)
+ *     reports must be at most 64 MiB (e.g. 32 rows of 1024 pages, or 8 rows
+ *     of 2048 pages, need 16.8 MB / 8.4 MB); larger launches return
+ *     DSA_ERR_WORKSPACE before any device work.
+ *   - Every call on a GPU shares that GPU's array: calls that overlap on one
+ *     GPU (two streams, two host threads) race and must be serialised by the
+ *     caller.  Nothing in the array has to start at zero; the status bits of
+ *     dsa_indexer_topk's workspace word are kept there and not reported.
+ *   - The first call on each device looks up the array's device address
+ *     (no allocation) and returns DSA_ERR_HIP if that fails.
+ */
+int dsa_indexer_topk_noalloc(const void* q_fp8, const void* q_e8m0, const float* w,
+                             const void* k_pool, int64_t pool_pages,
+                             const int32_t* block_table, int32_t bt_stride,
+                             const int32_t* row_seq, const int32_t* row_pos, int32_t R,
+                             int32_t H_I, int32_t topk, int32_t* out_idx, float* out_score,
+                             void* stream);
+
+/*
  * Bytes of zero-initialised workspace dsa_indexer_topk_seq needs for R query
  * rows of a sequence of n_pages pages.
  */

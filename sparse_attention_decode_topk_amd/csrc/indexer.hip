@@ -36,6 +36,7 @@
 // No floating-point atomics are used, so results are deterministic.
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "common.hpp"
 
@@ -1979,22 +1980,15 @@ extern "C" size_t dsa_indexer_topk_workspace_size(int32_t R, int32_t bt_stride, 
   return layout_for(rows, bt_stride).total;
 }
 
-extern "C" int dsa_indexer_topk(const void* q_fp8, const void* q_e8m0, const float* w,
-                                const void* k_pool, int64_t pool_pages, const int32_t* block_table,
-                                int32_t bt_stride, const int32_t* row_seq, const int32_t* row_pos,
-                                int32_t R, int32_t H_I, int32_t topk, int32_t* out_idx,
-                                float* out_score, void* workspace, size_t workspace_bytes,
-                                void* stream) {
-  int st = validate(q_fp8, q_e8m0, w, k_pool, pool_pages, block_table, bt_stride, row_seq, row_pos,
-                    R, H_I);
-  if (st != DSA_OK) return st;
-  if (out_idx == nullptr) return DSA_ERR_INVALID_ARG;
-  if (topk < 1 || topk > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
-  if (R == 0) return DSA_OK;
-  const int64_t rows = std::min<int64_t>(R, kMaxRows);
-  const Layout L = layout_for(rows, bt_stride);
-  if (workspace == nullptr || workspace_bytes < L.total) return DSA_ERR_WORKSPACE;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
+namespace {
+
+// dsa_indexer_topk after argument validation, on a workspace of `ws_bytes`
+// bytes (from the caller, or the library's static scratch array).
+int indexer_topk_on(const void* q_fp8, const void* q_e8m0, const float* w, const void* k_pool,
+                    int64_t pool_pages, const int32_t* block_table, int32_t bt_stride,
+                    const int32_t* row_seq, const int32_t* row_pos, int32_t R, int32_t H_I,
+                    int32_t topk, int32_t* out_idx, float* out_score, uint8_t* ws,
+                    const Layout& L, void* stream) {
   Params P = base_params(q_fp8, q_e8m0, w, k_pool, pool_pages, block_table, bt_stride, row_seq,
                          row_pos, R, H_I);
   P.topk = topk;
@@ -2006,6 +2000,83 @@ extern "C" int dsa_indexer_topk(const void* q_fp8, const void* q_e8m0, const flo
   P.cand = reinterpret_cast<uint2*>(ws + L.cand);
   P.j_start = select_j_start(bt_stride, topk);
   return run(P, false, dsa_host::as_stream(stream));
+}
+
+int indexer_topk_checks(const void* q_fp8, const void* q_e8m0, const float* w, const void* k_pool,
+                        int64_t pool_pages, const int32_t* block_table, int32_t bt_stride,
+                        const int32_t* row_seq, const int32_t* row_pos, int32_t R, int32_t H_I,
+                        int32_t topk, const int32_t* out_idx) {
+  const int st = validate(q_fp8, q_e8m0, w, k_pool, pool_pages, block_table, bt_stride, row_seq,
+                          row_pos, R, H_I);
+  if (st != DSA_OK) return st;
+  if (out_idx == nullptr) return DSA_ERR_INVALID_ARG;
+  if (topk < 1 || topk > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
+}
+
+// ---- the allocation-free variant's workspace ---------------------------------
+//
+// A file-scope device array holds the workspace of dsa_indexer_topk_noalloc:
+// each GPU the library runs on holds its own copy until the process ends.
+// Host code must not use the array's name as a device address (it is a
+// host-side stand-in); the device address comes from hipGetSymbolAddress,
+// taken once per device with that device current, and is kept per device.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kScratchDevices = 64;
+std::once_flag g_scratch_once[kScratchDevices];
+void* g_scratch_ptr[kScratchDevices];
+
+// Device address of this device's scratch array (nullptr if the lookup
+// failed or the device index is out of range).
+void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = e == hipSuccess ? ptr : nullptr;
+  });
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int dsa_indexer_topk(const void* q_fp8, const void* q_e8m0, const float* w,
+                                const void* k_pool, int64_t pool_pages, const int32_t* block_table,
+                                int32_t bt_stride, const int32_t* row_seq, const int32_t* row_pos,
+                                int32_t R, int32_t H_I, int32_t topk, int32_t* out_idx,
+                                float* out_score, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  const int st = indexer_topk_checks(q_fp8, q_e8m0, w, k_pool, pool_pages, block_table, bt_stride,
+                                     row_seq, row_pos, R, H_I, topk, out_idx);
+  if (st != DSA_OK) return st;
+  if (R == 0) return DSA_OK;
+  const Layout L = layout_for(std::min<int64_t>(R, kMaxRows), bt_stride);
+  if (workspace == nullptr || workspace_bytes < L.total) return DSA_ERR_WORKSPACE;
+  return indexer_topk_on(q_fp8, q_e8m0, w, k_pool, pool_pages, block_table, bt_stride, row_seq,
+                         row_pos, R, H_I, topk, out_idx, out_score, static_cast<uint8_t*>(workspace),
+                         L, stream);
+}
+
+extern "C" int dsa_indexer_topk_noalloc(const void* q_fp8, const void* q_e8m0, const float* w,
+                                        const void* k_pool, int64_t pool_pages,
+                                        const int32_t* block_table, int32_t bt_stride,
+                                        const int32_t* row_seq, const int32_t* row_pos, int32_t R,
+                                        int32_t H_I, int32_t topk, int32_t* out_idx,
+                                        float* out_score, void* stream) {
+  const int st = indexer_topk_checks(q_fp8, q_e8m0, w, k_pool, pool_pages, block_table, bt_stride,
+                                     row_seq, row_pos, R, H_I, topk, out_idx);
+  if (st != DSA_OK) return st;
+  if (R == 0) return DSA_OK;
+  const Layout L = layout_for(std::min<int64_t>(R, kMaxRows), bt_stride);
+  if (L.total > kNoAllocScratchBytes) return DSA_ERR_WORKSPACE;
+  void* ptr = scratch_on_current_device();
+  if (ptr == nullptr) return DSA_ERR_HIP;
+  return indexer_topk_on(q_fp8, q_e8m0, w, k_pool, pool_pages, block_table, bt_stride, row_seq,
+                         row_pos, R, H_I, topk, out_idx, out_score, static_cast<uint8_t*>(ptr), L,
+                         stream);
 }
 
 extern "C" int dsa_indexer_scores(const void* q_fp8, const void* q_e8m0, const float* w,

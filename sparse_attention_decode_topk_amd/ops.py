@@ -44,6 +44,8 @@ SIGNATURES = {
     "dsa_indexer_topk_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
     "dsa_indexer_topk": (_c.c_int, [_P, _P, _P, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _I32,
                                     _P, _P, _P, _SZ, _P]),
+    "dsa_indexer_topk_noalloc": (_c.c_int, [_P, _P, _P, _P, _I64, _P, _I32, _P, _P, _I32, _I32,
+                                            _I32, _P, _P, _P]),
     "dsa_indexer_topk_seq_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
     "dsa_indexer_topk_seq": (_c.c_int, [_P, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32,
                                         _P, _P, _P, _SZ, _P]),
@@ -179,6 +181,28 @@ def dsa_indexer_topk(q_fp8, q_e8m0, w, k_pool, block_table, row_seq, row_pos, to
                                   _ptr(block_table), bt_stride, _ptr(row_seq), _ptr(row_pos), R, H,
                                   topk, _ptr(out_idx), _ptr(out_score), _ptr(workspace),
                                   workspace.numel(), _stream()), "dsa_indexer_topk")
+    return out_idx, out_score
+
+
+def dsa_indexer_topk_noalloc(q_fp8, q_e8m0, w, k_pool, block_table, row_seq, row_pos, topk: int,
+                             out_idx=None, out_score=None, with_scores: bool = True):
+    """dsa_indexer_topk on the library's own per-GPU scratch array (no
+    workspace; calls on one GPU must not overlap)."""
+    R, H = q_fp8.shape[0], q_fp8.shape[1]
+    for t, dt, n in ((q_fp8, torch.uint8, "q_fp8"), (q_e8m0, torch.uint8, "q_e8m0"),
+                     (w, torch.float32, "w"), (k_pool, torch.uint8, "k_pool"),
+                     (block_table, torch.int32, "block_table"), (row_seq, torch.int32, "row_seq"),
+                     (row_pos, torch.int32, "row_pos")):
+        _need(t, dt, n)
+    dev = q_fp8.device
+    if out_idx is None:
+        out_idx = torch.empty((R, topk), dtype=torch.int32, device=dev)
+    if out_score is None and with_scores:
+        out_score = torch.empty((R, topk), dtype=torch.float32, device=dev)
+    _check(lib().dsa_indexer_topk_noalloc(_ptr(q_fp8), _ptr(q_e8m0), _ptr(w), _ptr(k_pool),
+                                          k_pool.shape[0], _ptr(block_table), block_table.shape[1],
+                                          _ptr(row_seq), _ptr(row_pos), R, H, topk, _ptr(out_idx),
+                                          _ptr(out_score), _stream()), "dsa_indexer_topk_noalloc")
     return out_idx, out_score
 
 
