@@ -7,10 +7,12 @@ latent cache (FP8 latent with per-128 tile scales + bf16 rope), 64-token
 pages under a shuffled block table; seeded synthetic N(0,1) data.
 
 One step = the whole hot path for one decode token of each sequence:
-  dsa_decode_prolog (in one launch: mxfp8_quant of the indexer q, the new
-  indexer k into the K cache, kv_fp8_quant_paged_write of the new KV row)
-  -> dsa_indexer_topk -> dsa_sparse_attn
-(--separate-prolog runs the three quantisations as three launches instead;
+  dsa_decode_indexer_topk (the indexer with the quantisation prolog folded
+  into its launches: mxfp8 quantisation of the indexer q inside the scan, the
+  new indexer k and the new KV record written into the caches by the scan)
+  -> dsa_sparse_attn
+(--unfused-prolog runs dsa_decode_prolog, one launch, then dsa_indexer_topk;
+--separate-prolog runs the three quantisations as three launches instead;
 --graph captures the step once per cache replica in a HIP graph and times
 graph replays instead of eager launches).
 Caches are replicated (default 4 replicas, about 3.3 GB) and rotated per step
@@ -80,6 +82,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate-prolog", action="store_true",
                     help="quantise q, k and kv with three launches instead of dsa_decode_prolog")
+    ap.add_argument("--unfused-prolog", action="store_true",
+                    help="decode: dsa_decode_prolog then dsa_indexer_topk instead of dsa_decode_indexer_topk")
     ap.add_argument("--graph", action="store_true",
                     help="capture the step once per cache replica in a HIP graph and time graph replays")
     ap.add_argument("--profile-steps", action="store_true",
@@ -184,20 +188,29 @@ def main():
                  (ptr(q_fp8), ptr(q_e8), ptr(w), ptr(k_pools[j]), npages, ptr(block_table),
                   block_table.shape[1], ptr(row_seq), ptr(row_pos), R, H_I, K, ptr(out_idx),
                   ptr(out_sc), ptr(ws_i), ws_i.numel(), stream)),
+            dec=(ptr(q_idx), ptr(w), ptr(k_new), ptr(kv_new), ptr(slots_new), ptr(k_pools[j]),
+                 ptr(kv_pools[j]), npages, ptr(block_table), block_table.shape[1], ptr(row_seq),
+                 ptr(row_pos), R, H_I, K, ptr(out_idx), ptr(out_sc), ptr(ws_i), ws_i.numel(), stream),
             sfa=(ptr(q_sfa), ptr(kv_pools[j]), npages, ptr(block_table), block_table.shape[1],
                  ptr(row_seq), ptr(out_idx), R, H, K, ctypes.c_float(ops.DEFAULT_SCALE),
                  ptr(out), ptr(lse), ptr(ws_s), ws_s.numel(), stream)))
 
+    # decode with one query row per sequence folds the prolog into the
+    # indexer's launches (dsa_decode_indexer_topk)
+    fused = not one_seq and not mq and not args.separate_prolog and not args.unfused_prolog
     indexer_call = (L.dsa_indexer_topk_seq if one_seq else
-                    L.dsa_indexer_topk_mq if mq else L.dsa_indexer_topk)
+                    L.dsa_indexer_topk_mq if mq else
+                    L.dsa_decode_indexer_topk if fused else L.dsa_indexer_topk)
+    idx_key = "dec" if fused else "idx"
 
     def step(i):
         a = steps_args[i % args.replicas]
+        st = 0
         if args.separate_prolog:
             st = L.mxfp8_quant(*a["qq"]) | L.mxfp8_quant(*a["kq"]) | L.kv_fp8_quant_paged_write(*a["kvq"])
-        else:
+        elif not fused:
             st = L.dsa_decode_prolog(*a["pro"])
-        st |= indexer_call(*a["idx"])
+        st |= indexer_call(*a[idx_key])
         st |= L.dsa_sparse_attn(*a["sfa"])
         if st:
             raise RuntimeError(f"library call failed (status bits {st})")
@@ -215,7 +228,8 @@ def main():
             aj = {k: tuple(cap_h if x is stream else x for x in v) for k, v in steps_args[j].items()}
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
-                st = L.dsa_decode_prolog(*aj["pro"]) | indexer_call(*aj["idx"]) | L.dsa_sparse_attn(*aj["sfa"])
+                st = 0 if fused else L.dsa_decode_prolog(*aj["pro"])
+                st |= indexer_call(*aj[idx_key]) | L.dsa_sparse_attn(*aj["sfa"])
             if st:
                 raise RuntimeError(f"library call failed during capture (status bits {st})")
             graphs.append(g)
@@ -247,7 +261,7 @@ def main():
         torch.cuda.synchronize()
         return ev[0].elapsed_time(ev[1]) / K_steps
 
-    idx_avg = timed_calls(indexer_call, "idx")
+    idx_avg = timed_calls(indexer_call, idx_key)
     sfa_avg = timed_calls(L.dsa_sparse_attn, "sfa")
 
     # per-call distributions: an event pair around every call (the events
@@ -267,7 +281,7 @@ def main():
                 "p90_us": round(float(np.percentile(t, 90)), 2), "calls": n}
 
     def call_idx(i):
-        if indexer_call(*steps_args[i % args.replicas]["idx"]):
+        if indexer_call(*steps_args[i % args.replicas][idx_key]):
             raise RuntimeError("indexer call failed")
 
     def call_sfa(i):
@@ -275,7 +289,7 @@ def main():
             raise RuntimeError("sparse attention call failed")
 
     n_pc = max(50, min(K_steps, 200))
-    dist = {"step": per_call(run_step, n_pc), idx_name_of(one_seq, mq): per_call(call_idx, n_pc),
+    dist = {"step": per_call(run_step, n_pc), idx_name_of(one_seq, mq, fused): per_call(call_idx, n_pc),
             "dsa_sparse_attn": per_call(call_sfa, n_pc)}
     stream_gbs = stream_read_gbs(ops, dev) if not args.profile_steps else None
     ms_per_step = elapsed * 1e3 / K_steps
@@ -308,7 +322,7 @@ def main():
         res_out = out.cpu().numpy()
         cpu, parity = cpu_baseline(inp, args.cpu_rows, res_idx, res_sc, res_out)
 
-    idx_name = idx_name_of(one_seq, mq)
+    idx_name = idx_name_of(one_seq, mq, fused)
     mfma = {idx_name: {"achieved": round(idx_tf, 1), "peak": FP8_PEAK_TFS, "unit": "TFLOP/s",
                        "frac": round(idx_tf / FP8_PEAK_TFS, 4), "flop": idx_flop,
                        "dtype": "fp8 e4m3 x e4m3, E8M0 block scales"},
@@ -343,7 +357,9 @@ def main():
         "config": {"workload": cfg.name, "batch": B, "context": int(lens.max()), "query_rows": R,
                    "h_index": H_I, "h_attn": H, "topk": K, "page_tokens": 64,
                    "cache_replicas_rotated": args.replicas, "parallelism": "single GPU",
-                   "prolog": "three launches" if args.separate_prolog else "dsa_decode_prolog (one launch)",
+                   "prolog": ("three launches" if args.separate_prolog else
+                              "folded into dsa_decode_indexer_topk" if fused else
+                              "dsa_decode_prolog (one launch)"),
                    "launch": "hipGraph replay per step" if args.graph else "eager launches"},
         "hbm_gbs_step": round(step_gbs, 1),
         "algorithmic_bytes_step": step_bytes,
@@ -368,8 +384,9 @@ def main():
     print(json.dumps(rec))
 
 
-def idx_name_of(one_seq, mq):
-    return "dsa_indexer_topk_seq" if one_seq else "dsa_indexer_topk_mq" if mq else "dsa_indexer_topk"
+def idx_name_of(one_seq, mq, fused):
+    return ("dsa_indexer_topk_seq" if one_seq else "dsa_indexer_topk_mq" if mq else
+            "dsa_decode_indexer_topk" if fused else "dsa_indexer_topk")
 
 
 def cpu_model():

@@ -198,6 +198,44 @@ int dsa_indexer_topk_noalloc(const void* q_fp8, const void* q_e8m0, const float*
                              void* stream);
 
 /*
+ * One decode step's indexer with the quantisation prolog folded into the
+ * same launch ("Lightning Indexer Three-Stream Coordination" and "System-
+ * Level Coordination", Kimi K3.1 Pro Day0 page: Q quantisation feeds the
+ * scoring directly, and the KV-cache writes of the new token happen during
+ * the step instead of as a serial prolog).  Row r brings its new token: the
+ * bf16 indexer key k_new[r], the bf16 KV row kv_new[r] and its cache slot
+ * slot_mapping[r] (int64).  The call computes exactly what
+ *   dsa_decode_prolog(q_bf16, R*H_I, 128, q_fp8, q_e8m0, k_new, kv_new, R,
+ *                     slot_mapping, k_pool, kv_pool, pool_pages)
+ *   dsa_indexer_topk(q_fp8, q_e8m0, w, k_pool, ...)
+ * computes (same cache bytes written, same indices and scores bit for bit),
+ * in the launches of dsa_indexer_topk alone:
+ *   - the queries are quantised to MXFP8 inside the scan (no q_fp8 array);
+ *   - the new keys and KV records are written into the caches by the scan
+ *     (read by later launches), and each row's new key is scored from the
+ *     launch's own copy.
+ * Preconditions: slot_mapping[r] is the slot of position row_pos[r] of
+ * sequence row_seq[r] (the decode token at the row's causal limit), and the
+ * rows name distinct sequences (multi-query groups and prefill chunks use
+ * dsa_decode_prolog and dsa_indexer_topk_mq / _seq).  A slot < 0 or >=
+ * pool_pages*64 means the row writes nothing and position row_pos[r] is
+ * scored from the cache as it is.
+ *
+ *   q_bf16       [R, H_I, 128] bf16 indexer queries
+ *   k_new_bf16   [R, 128] bf16;  kv_new_bf16 [R, 576] bf16 (latent | rope)
+ *   k_pool, kv_pool  the two caches (pool_pages pages each), written
+ *   other arguments, outputs and status bits as for dsa_indexer_topk; the
+ *   workspace is sized by dsa_indexer_topk_workspace_size.
+ */
+int dsa_decode_indexer_topk(const void* q_bf16, const float* w, const void* k_new_bf16,
+                            const void* kv_new_bf16, const int64_t* slot_mapping,
+                            void* k_pool, void* kv_pool, int64_t pool_pages,
+                            const int32_t* block_table, int32_t bt_stride,
+                            const int32_t* row_seq, const int32_t* row_pos, int32_t R,
+                            int32_t H_I, int32_t topk, int32_t* out_idx, float* out_score,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of zero-initialised workspace dsa_indexer_topk_seq needs for R query
  * rows of a sequence of n_pages pages.
  */

@@ -58,6 +58,18 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float y) {
   return code | sign;
 }
 
+// Four E4M3 codes of values already inside [-448, 448], packed little-end
+// first, by the hardware conversion v_cvt_pk_fp8_f32 (gfx950: OCP E4M3FN,
+// round to nearest even under the default mode).  On that domain it returns
+// exactly e4m3_rne_sat's code: an exhaustive run over every bf16 value with
+// |v| <= 448 found no difference (bf16 inputs scaled by a power of two, as
+// MXFP8 produces them, are bf16 values).  Above 464 it returns NaN instead
+// of saturating, so callers whose values may exceed 448 use e4m3_rne_sat.
+__device__ __forceinline__ uint32_t e4m3x4_in_range(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
 // MXFP8 scale exponent of a group: smallest e with amax <= 448 * 2^e,
 // clamped to [-127, 127]; 0 for an all-zero group.  amax is a bf16 value.
 __device__ __forceinline__ int mx_exponent(float amax) {

@@ -35,10 +35,11 @@
 //     taken).  Ties are broken by the lower position.
 // No floating-point atomics are used, so results are deterministic.
 #include <algorithm>
+#include <type_traits>
 #include <atomic>
 #include <mutex>
 
-#include "common.hpp"
+#include "quant_dev.hpp"
 
 namespace {
 
@@ -99,6 +100,16 @@ struct Params {
   uint32_t* ucount;      // [R][upr] candidates emitted per unit
   uint32_t* uedge;       // [R][upr] every key a unit left out is below this
   uint2* cand;           // [R][bt_stride * 64] (key, position)
+  // decode prolog folded into the scan (dsa_decode_indexer_topk only)
+  const uint16_t* q_bf16;  // [R, H, 128] bf16 queries (quantised in LDS; q / qs unused)
+  const uint16_t* k_new;   // [R, 128] bf16 new indexer key of each row
+  const uint16_t* kv_new;  // [R, 576] bf16 new KV row of each row
+  const int64_t* new_slot; // [R] slot of each row's new token (< 0: none)
+  uint8_t* kpool_w;        // the K pool, written with the new keys
+  uint8_t* kvpool_w;       // the KV pool, written with the new records
+  uint8_t* q_ws;           // [R, H, 128] the quantised queries, written for the select (== q)
+  uint8_t* qs_ws;          // [R, H, 4] their scales (== qs)
+  int32_t extra_wgs;       // work-groups after the scan's that write the new tokens
 };
 
 struct ScanSmem {
@@ -649,17 +660,203 @@ __device__ __forceinline__ void filter_unit(const Params& P, ScanSmem& S, const 
   }
 }
 
+// ---- the decode prolog folded into the scan ----------------------------------
+//
+// dsa_decode_indexer_topk hands the scan bf16 queries and each row's new
+// token (indexer key, KV row, slot).  A work-group quantises its current
+// row's queries and new key into LDS with the quantisers' own arithmetic
+// (so the codes are the bytes mxfp8_quant writes) and takes its query operand
+// from there.  The new token's own score is computed from the LDS copy of its
+// key with the same instruction and operand layout as a key read from the
+// cache, and replaces the score of position t, whose cache slot this launch
+// writes concurrently (so the page read may hold either bytes).  The cache
+// writes themselves (the new keys and KV records) are spread over the grid;
+// later launches read them.
+
+struct FusedSmem {
+  alignas(16) uint8_t qc[DSA_MAX_INDEX_HEADS * kIdxDim];   // query codes [h][128]
+  uint8_t qsc[DSA_MAX_INDEX_HEADS * 4];                     // query scales [h][4]
+  alignas(16) uint8_t kc[kIdxDim];                          // new key codes
+  uint8_t ksc[4];                                           // new key scales
+};
+struct NoSmem {};
+
+// Whether row `row` brings a new token this launch writes (slot in the pool).
+__device__ __forceinline__ bool has_new_token(const Params& P, int row) {
+  const int64_t sl = P.new_slot[row];
+  return sl >= 0 && sl < P.pool_pages * kPage;
+}
+
+// MXFP8 codes of 32 consecutive bf16 values (one E8M0 group, as 16 packed
+// words): the same amax, exponent and rounding as mxfp8_quant_range.
+__device__ __forceinline__ uint32_t quant_group32(const uint32_t (&w)[16], uint32_t (&codes)[8]) {
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(w[j] & 0xFFFFu)), fabsf(bf16_bits_to_f32(w[j] >> 16))));
+  const int e = mx_exponent(amax);
+  const float inv = pow2f(-e);
+  // |x * inv| <= 448 by the scale rule: the hardware conversion applies
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    const uint32_t a = w[2 * d], b = w[2 * d + 1];
+    codes[d] = e4m3x4_in_range(bf16_bits_to_f32(a & 0xFFFFu) * inv, bf16_bits_to_f32(a >> 16) * inv,
+                               bf16_bits_to_f32(b & 0xFFFFu) * inv, bf16_bits_to_f32(b >> 16) * inv);
+  }
+  return (uint32_t)(e + 127);
+}
+
+// A thread's raw bf16 inputs of a row: its query group (head t/4, dims
+// 32(t%4)..+31) and, for threads 0..3, a group of the row's new key.  Loaded
+// before the ring's first loads so that waiting for them never waits for the
+// ring; quantised while the ring is in flight.
+struct RowIn {
+  uint32_t q[16];
+  uint32_t k[16];
+  bool qlive, knew;
+};
+
+__device__ __forceinline__ void load_words32(const uint16_t* src, uint32_t (&w)[16]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(src + 8 * j);
+    w[4 * j] = raw.x; w[4 * j + 1] = raw.y; w[4 * j + 2] = raw.z; w[4 * j + 3] = raw.w;
+  }
+}
+
+__device__ __forceinline__ void row_in_load(const Params& P, int row, RowIn& in) {
+  const int t = threadIdx.x, h = t >> 2, grp = t & 3;
+  in.qlive = h < P.H;
+  if (in.qlive) load_words32(P.q_bf16 + ((int64_t)row * P.H + h) * kIdxDim + 32 * grp, in.q);
+  in.knew = t < 4 && has_new_token(P, row);
+  if (in.knew) load_words32(P.k_new + (int64_t)row * kIdxDim + 32 * t, in.k);
+}
+
+// The row's query codes and scales (heads >= H: zeros, as the out-of-range
+// loads of load_q return) and new key into LDS.  No barrier.
+__device__ __forceinline__ void row_in_store(const RowIn& in, FusedSmem& F) {
+  const int t = threadIdx.x, h = t >> 2, grp = t & 3;
+  uint32_t codes[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const uint32_t sb = in.qlive ? quant_group32(in.q, codes) : 0u;
+  uint4* dst = reinterpret_cast<uint4*>(F.qc + h * kIdxDim + 32 * grp);
+  dst[0] = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+  dst[1] = make_uint4(codes[4], codes[5], codes[6], codes[7]);
+  F.qsc[h * 4 + grp] = (uint8_t)sb;
+  if (in.knew) {
+    uint32_t kc[8];
+    const uint32_t ks = quant_group32(in.k, kc);
+    uint4* kd = reinterpret_cast<uint4*>(F.kc + 32 * t);
+    kd[0] = make_uint4(kc[0], kc[1], kc[2], kc[3]);
+    kd[1] = make_uint4(kc[4], kc[5], kc[6], kc[7]);
+    F.ksc[t] = (uint8_t)ks;
+  }
+}
+
+// The head weights of the query operand (global loads, issued early).
+template <int NHT>
+__device__ __forceinline__ void load_w(const Params& P, int row, QOperand<NHT>& Q) {
+  const int g = (threadIdx.x & 63) >> 4;
+  row = __builtin_amdgcn_readfirstlane(row);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(P.w + (int64_t)row * P.H), (short)0, P.H * 4, kRawBufferWord3);
+  constexpr uint32_t kOut = 0x7FFFFFF0u;
+#pragma unroll
+  for (int i = 0; i < NHT; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int hh = 16 * i + 4 * g + c;
+      Q.w[i][c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, hh < P.H ? (uint32_t)hh * 4u : kOut, 0, 0));
+    }
+}
+
+// The query codes and scales of the operand from LDS (load_q's layout).
+template <int NHT>
+__device__ __forceinline__ void load_q_codes_lds(const FusedSmem& F, QOperand<NHT>& Q) {
+  const int lane = threadIdx.x & 63, hr = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < NHT; ++i) {
+    const int h = 16 * i + hr;
+    const uint4 a = *reinterpret_cast<const uint4*>(F.qc + h * kIdxDim + 16 * g);
+    const uint4 b = *reinterpret_cast<const uint4*>(F.qc + h * kIdxDim + 64 + 16 * g);
+    Q.a[i] = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+    Q.s[i] = (int)F.qsc[h * 4 + g];
+  }
+}
+
+// Score of the row's new key (every lane holds it): the key operand of a
+// token tile whose 16 columns all carry the new key, through head_part and
+// rows_sum as in score_half, so the bits equal the score of that key read
+// from the cache.
+template <int NHT>
+__device__ __forceinline__ float new_token_score(const QOperand<NHT>& Q, const FusedSmem& F) {
+  const int g = (threadIdx.x & 63) >> 4;
+  const uint4 lo = *reinterpret_cast<const uint4*>(F.kc + 16 * g);
+  const uint4 hi = *reinterpret_cast<const uint4*>(F.kc + 64 + 16 * g);
+  const v8i kb = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  return rows_sum(head_part<NHT>(Q, kb, (int)F.ksc[g]));
+}
+
+// Fused path, at the first unit of a row (its inputs loaded by row_in_load
+// and the head weights by load_w): the row's queries and new key into LDS,
+// then the query operand; the work-group that holds the row's first unit
+// also writes the row's query codes and scales to the workspace for the
+// select's rescoring path.  Ends after a barrier.
+template <int NHT>
+__device__ __forceinline__ void fused_row(const Params& P, int row, int uir, const RowIn& in,
+                                          FusedSmem& F, QOperand<NHT>& Q) {
+  row_in_store(in, F);
+  __syncthreads();
+  load_q_codes_lds<NHT>(F, Q);
+  if (uir == 0) {
+    const int t = threadIdx.x;
+    if (t * 32 < P.H * kIdxDim) {
+      uint4* dst = reinterpret_cast<uint4*>(P.q_ws + (int64_t)row * P.H * kIdxDim + t * 32);
+      const uint4* src = reinterpret_cast<const uint4*>(F.qc + t * 32);
+      dst[0] = src[0];
+      dst[1] = src[1];
+    }
+    if (t < P.H * 4) P.qs_ws[(int64_t)row * P.H * 4 + t] = F.qsc[t];
+  }
+}
+
 // A workgroup takes a contiguous run of units (usually of one row, so the
 // query operand stays resident).  The half-page ring runs across the units:
 // while a unit's last half pages are scored, the first kRing half pages of
 // the next unit are already requested, so they are in flight during the
 // local filter and the memory system never idles at a unit boundary.
-template <int NHT>
+//
+// FUSED (dsa_decode_indexer_topk): the decode prolog is folded in.  The new
+// tokens' cache writes are spread over the grid; the queries come from bf16
+// and are quantised per row into LDS (after the first ring loads are
+// issued); the work-group holding a row's first unit also writes the row's
+// quantised queries to the workspace for the select's rescoring path; and
+// the new token's score is computed from its LDS copy.
+template <int NHT, bool FUSED>
 __global__ __launch_bounds__(kScanThreads, 2) void indexer_scan_kernel(Params P) {
   __shared__ ScanSmem S;
+  __shared__ typename std::conditional<FUSED, FusedSmem, NoSmem>::type F;
+  // fused: the last P.extra_wgs work-groups write the step's new indexer
+  // keys and KV records into the caches, one token per wave (later launches
+  // read them; the scan scores each new key from its own LDS copy).  They
+  // come last in the grid, so they never hold a slot a scan work-group waits
+  // for at the start.
+  const int scan_wgs = (int)gridDim.x - (FUSED ? P.extra_wgs : 0);
+  if constexpr (FUSED) {
+    if ((int)blockIdx.x >= scan_wgs) {
+      const int lane = threadIdx.x & 63;
+      const int r = ((int)blockIdx.x - scan_wgs) * kScanWaves + (int)(threadIdx.x >> 6);
+      if (r < P.R) {
+        const int64_t pool_slots = P.pool_pages * kPage;
+        mxfp8_quant_range(lane < 16 ? lane : 16, 16, P.k_new + (int64_t)r * kIdxDim, 1, kIdxDim,
+                          nullptr, nullptr, P.kpool_w, P.new_slot + r, pool_slots);
+        kv_quant_range(0, 1, P.kv_new + (int64_t)r * kQK, 1, P.new_slot + r, P.kvpool_w, pool_slots);
+      }
+      return;
+    }
+  }
   plan_rows<kScanThreads>(P, S);   // ends with a barrier
   const uint32_t U_total = S.rowpre[P.R];
-  const uint32_t per = (U_total + gridDim.x - 1) / gridDim.x;
+  const uint32_t per = (U_total + scan_wgs - 1) / scan_wgs;
   uint32_t u = blockIdx.x * per;
   const uint32_t uend = min(U_total, u + per);
   if (u >= uend) return;
@@ -668,12 +865,19 @@ __global__ __launch_bounds__(kScanThreads, 2) void indexer_scan_kernel(Params P)
   Unit U = decode_unit(P, S, u);
   int32_t pid = unit_pages(P, U, S.rowseq[U.row]);
   QOperand<NHT> Q;
-  load_q<NHT>(P, U.row, Q);
+  RowIn in;
+  if constexpr (FUSED) {
+    row_in_load(P, U.row, in);
+    load_w<NHT>(P, U.row, Q);
+  } else {
+    load_q<NHT>(P, U.row, Q);
+  }
   int qrow = U.row;
   HalfRegs b[kRing];
   bool ok[kRing];
 #pragma unroll
   for (int k = 0; k < kRing; ++k) ok[k] = fetch_half(P, U, pid, wv + kScanWaves * k, b[k], &bad);
+  if constexpr (FUSED) fused_row<NHT>(P, U.row, U.uir, in, F, Q);
   for (;;) {
     const bool more = u + 1 < uend;
     // the next unit (the current one again when there is none: its ring
@@ -691,11 +895,31 @@ __global__ __launch_bounds__(kScanThreads, 2) void indexer_scan_kernel(Params P)
       else
         ok[k % kRing] = fetch_half(P, Vf, pidn, wv + kScanWaves * (kn - kScanHalves), b[k % kRing], &bad);
     }
+    if constexpr (FUSED) {
+      // the new token's key, when it lies in this unit, from its LDS copy:
+      // written by the lane that wrote the cache-read key (half h of wave
+      // h % 4, lane tok % 16), so program order puts it last; a key of 0
+      // (the page is absent) stays 0
+      const int tl = U.t - U.pg0 * kPage;
+      if (tl >= 0 && U.t < U.pg1 * kPage && has_new_token(P, U.row)) {
+        const float ns = new_token_score<NHT>(Q, F);
+        if (wv == ((tl >> 5) & (kScanWaves - 1)) && (threadIdx.x & 63) == (tl & 15) &&
+            S.keys[tl] != 0u)
+          S.keys[tl] = score_key(ns);
+      }
+    }
     __syncthreads();
     filter_unit(P, S, U);   // its barrier orders the key reads before the next unit's writes
     if (!more) break;
     if (V.row != qrow) {
-      load_q<NHT>(P, V.row, Q);
+      if constexpr (FUSED) {
+        row_in_load(P, V.row, in);
+        load_w<NHT>(P, V.row, Q);
+        __syncthreads();   // every wave has read the previous row's LDS operands
+        fused_row<NHT>(P, V.row, V.uir, in, F, Q);
+      } else {
+        load_q<NHT>(P, V.row, Q);
+      }
       qrow = V.row;
     }
     U = V;
@@ -1811,7 +2035,7 @@ static_assert(DSA_PG_WAIT_AFTER_FILTER < 64, "vmcnt holds 6 bits");
 // ---- host side ----------------------------------------------------------------
 
 struct Layout {
-  size_t hdr, ucount, uedge, cand, total;
+  size_t hdr, ucount, uedge, cand, qcodes, qscales, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -1826,18 +2050,33 @@ Layout layout_for(int64_t rows, int64_t bt_stride) {
   L.ucount = off; off += align256((size_t)rows * upr * 4);
   L.uedge = off; off += align256((size_t)rows * upr * 4);
   L.cand = off; off += align256((size_t)rows * bt_stride * kPage * 8);
+  // the quantised queries of the fused-prolog entry point (for the select's
+  // rescoring path), sized for the largest head count
+  L.qcodes = off; off += align256((size_t)rows * DSA_MAX_INDEX_HEADS * kIdxDim);
+  L.qscales = off; off += align256((size_t)rows * DSA_MAX_INDEX_HEADS * 4);
   L.total = off;
   return L;
 }
 
-enum KernelKind { kScan = 0, kSelect = 1, kDump = 2, kSelectShort = 3 };
+enum KernelKind { kScan = 0, kSelect = 1, kDump = 2, kSelectShort = 3, kScanFused = 4 };
+
+template <int NHT>
+void* pick_kernel_t(KernelKind kind) {
+  switch (kind) {
+    case kScan: return (void*)&indexer_scan_kernel<NHT, false>;
+    case kScanFused: return (void*)&indexer_scan_kernel<NHT, true>;
+    case kSelect: return (void*)&indexer_select_kernel<NHT, false>;
+    case kSelectShort: return (void*)&indexer_select_kernel<NHT, true>;
+    default: return (void*)&indexer_dump_kernel<NHT>;
+  }
+}
 
 void* pick_kernel(int nht, KernelKind kind) {
   switch (nht) {
-    case 1: return kind == kScan ? (void*)&indexer_scan_kernel<1> : kind == kSelect ? (void*)&indexer_select_kernel<1, false> : kind == kSelectShort ? (void*)&indexer_select_kernel<1, true> : (void*)&indexer_dump_kernel<1>;
-    case 2: return kind == kScan ? (void*)&indexer_scan_kernel<2> : kind == kSelect ? (void*)&indexer_select_kernel<2, false> : kind == kSelectShort ? (void*)&indexer_select_kernel<2, true> : (void*)&indexer_dump_kernel<2>;
-    case 3: return kind == kScan ? (void*)&indexer_scan_kernel<3> : kind == kSelect ? (void*)&indexer_select_kernel<3, false> : kind == kSelectShort ? (void*)&indexer_select_kernel<3, true> : (void*)&indexer_dump_kernel<3>;
-    default: return kind == kScan ? (void*)&indexer_scan_kernel<4> : kind == kSelect ? (void*)&indexer_select_kernel<4, false> : kind == kSelectShort ? (void*)&indexer_select_kernel<4, true> : (void*)&indexer_dump_kernel<4>;
+    case 1: return pick_kernel_t<1>(kind);
+    case 2: return pick_kernel_t<2>(kind);
+    case 3: return pick_kernel_t<3>(kind);
+    default: return pick_kernel_t<4>(kind);
   }
 }
 
@@ -1855,7 +2094,7 @@ void* pick_tile_kernel(int nht, bool two) {
 // same time both compute the same value and store it, so no lock is needed
 // and a reader never sees a torn value (0 = not computed yet).
 constexpr int kCapDevices = 64;
-constexpr int kCapSlots = 20;
+constexpr int kCapSlots = 24;
 std::atomic<int> g_capacity[kCapDevices][kCapSlots];
 
 int resident_capacity(void* fn, int slot, int threads) {
@@ -1887,13 +2126,14 @@ int validate(const void* q, const void* qs, const float* w, const void* kpool, i
   return DSA_OK;
 }
 
-int run(Params P, bool dump, hipStream_t stream) {
+int run(Params P, bool dump, hipStream_t stream, bool fused = false) {
   const int nht = (P.H + 15) / 16;
-  const KernelKind kind = dump ? kDump : kScan;
+  const KernelKind kind = dump ? kDump : fused ? kScanFused : kScan;
   void* scan = pick_kernel(nht, kind);
   void* sel = pick_kernel(nht, P.j_start > 1 ? kSelectShort : kSelect);
   const int scan_threads = dump ? kThreads : kScanThreads;
-  const int cap = resident_capacity(scan, (nht - 1) * 3 + (int)kind, scan_threads);
+  const int cap = resident_capacity(scan, fused ? 20 + nht - 1 : (nht - 1) * 3 + (int)kind,
+                                    scan_threads);
   if (cap <= 0) return DSA_ERR_HIP;
   const int R = P.R;
   const int upr = units_stride(P.bt_stride);
@@ -1906,6 +2146,14 @@ int run(Params P, bool dump, hipStream_t stream) {
     Q.w = P.w + (int64_t)r0 * P.H;
     Q.row_seq = P.row_seq + r0;
     Q.row_pos = P.row_pos + r0;
+    if (fused) {
+      Q.q_bf16 = P.q_bf16 + (int64_t)r0 * P.H * kIdxDim;
+      Q.k_new = P.k_new + (int64_t)r0 * kIdxDim;
+      Q.kv_new = P.kv_new + (int64_t)r0 * kQK;
+      Q.new_slot = P.new_slot + r0;
+      Q.q_ws = P.q_ws + (int64_t)r0 * P.H * kIdxDim;
+      Q.qs_ws = P.qs_ws + (int64_t)r0 * P.H * 4;
+    }
     if (dump) {
       Q.dump = P.dump + (int64_t)r0 * P.ld;
     } else {
@@ -1913,8 +2161,9 @@ int run(Params P, bool dump, hipStream_t stream) {
       Q.out_score = P.out_score ? P.out_score + (int64_t)r0 * P.topk : nullptr;
     }
     const int64_t G = std::min<int64_t>((int64_t)cap, (int64_t)rn * upr);
+    Q.extra_wgs = fused ? (rn + kScanWaves - 1) / kScanWaves : 0;
     void* args[] = {&Q};
-    if (hipLaunchKernel(scan, dim3((unsigned)G), dim3(scan_threads), args, 0, stream) != hipSuccess)
+    if (hipLaunchKernel(scan, dim3((unsigned)(G + Q.extra_wgs)), dim3(scan_threads), args, 0, stream) != hipSuccess)
       return DSA_ERR_HIP;
     if (!dump && hipLaunchKernel(sel, dim3((unsigned)rn), dim3(kSelThreads), args, 0, stream) != hipSuccess)
       return DSA_ERR_HIP;
@@ -2077,6 +2326,46 @@ extern "C" int dsa_indexer_topk_noalloc(const void* q_fp8, const void* q_e8m0, c
   return indexer_topk_on(q_fp8, q_e8m0, w, k_pool, pool_pages, block_table, bt_stride, row_seq,
                          row_pos, R, H_I, topk, out_idx, out_score, static_cast<uint8_t*>(ptr), L,
                          stream);
+}
+
+extern "C" int dsa_decode_indexer_topk(const void* q_bf16, const float* w, const void* k_new_bf16,
+                                       const void* kv_new_bf16, const int64_t* slot_mapping,
+                                       void* k_pool, void* kv_pool, int64_t pool_pages,
+                                       const int32_t* block_table, int32_t bt_stride,
+                                       const int32_t* row_seq, const int32_t* row_pos, int32_t R,
+                                       int32_t H_I, int32_t topk, int32_t* out_idx,
+                                       float* out_score, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  if (!q_bf16 || !k_new_bf16 || !kv_new_bf16 || !slot_mapping || !kv_pool)
+    return DSA_ERR_INVALID_ARG;
+  // (q_bf16 stands in for the quantised-query arguments in the shared checks)
+  const int st = indexer_topk_checks(q_bf16, q_bf16, w, k_pool, pool_pages, block_table, bt_stride,
+                                     row_seq, row_pos, R, H_I, topk, out_idx);
+  if (st != DSA_OK) return st;
+  if (pool_pages > (int64_t(1) << 25)) return DSA_ERR_UNSUPPORTED;   // slots fit the kernels' int math
+  if (R == 0) return DSA_OK;
+  const Layout L = layout_for(std::min<int64_t>(R, kMaxRows), bt_stride);
+  if (workspace == nullptr || workspace_bytes < L.total) return DSA_ERR_WORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  Params P = base_params(ws + L.qcodes, ws + L.qscales, w, k_pool, pool_pages, block_table,
+                         bt_stride, row_seq, row_pos, R, H_I);
+  P.topk = topk;
+  P.out_idx = out_idx;
+  P.out_score = out_score;
+  P.hdr = reinterpret_cast<uint32_t*>(ws + L.hdr);
+  P.ucount = reinterpret_cast<uint32_t*>(ws + L.ucount);
+  P.uedge = reinterpret_cast<uint32_t*>(ws + L.uedge);
+  P.cand = reinterpret_cast<uint2*>(ws + L.cand);
+  P.j_start = select_j_start(bt_stride, topk);
+  P.q_bf16 = static_cast<const uint16_t*>(q_bf16);
+  P.k_new = static_cast<const uint16_t*>(k_new_bf16);
+  P.kv_new = static_cast<const uint16_t*>(kv_new_bf16);
+  P.new_slot = slot_mapping;
+  P.kpool_w = static_cast<uint8_t*>(k_pool);
+  P.kvpool_w = static_cast<uint8_t*>(kv_pool);
+  P.q_ws = ws + L.qcodes;
+  P.qs_ws = ws + L.qscales;
+  return run(P, false, dsa_host::as_stream(stream), true);
 }
 
 extern "C" int dsa_indexer_scores(const void* q_fp8, const void* q_e8m0, const float* w,

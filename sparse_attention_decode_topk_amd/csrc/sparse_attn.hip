@@ -125,11 +125,32 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hr = lane & 15, g = lane >> 4;
   const int grp = wv >> 2, ht = wv & 1, dh = (wv >> 1) & 1;
-  // blockIdx -> (head group, row, split): the head groups of one (row, split)
-  // are R*S blocks apart, a multiple of 8 when R*S is, so they share an XCD
-  const int pairs = P.R * P.S;
-  const int pair = blockIdx.x % pairs, hg = blockIdx.x / pairs;
-  const int row = pair / P.S, sp = pair % P.S;
+  // blockIdx -> (row, head group, split).  Work-groups are dealt to the 8
+  // XCDs round-robin (block b to XCD b % 8).  When the rows divide evenly
+  // among the XCDs, every work-group of a row goes to one XCD (row r to XCD
+  // r % 8): the row's records and its split partials then stay in that
+  // XCD's L2, where the combine launch (whose blocks of row r also run on
+  // XCD r % 8) reads them.  Otherwise the head groups of one (row, split)
+  // are R*S blocks apart, a multiple of 8 when R*S is, so at least the
+  // records they share come from one L2.
+  int row, hg, sp;
+  {
+    const int per_row = P.HGn * P.S;
+    const int b = blockIdx.x;
+    if ((P.R & 7) == 0) {
+      const int x = b & 7, j = b >> 3;
+      row = x + 8 * (j / per_row);
+      const int rem = j % per_row;
+      hg = rem / P.S;
+      sp = rem % P.S;
+    } else {
+      const int pairs = P.R * P.S;
+      const int pair = b % pairs;
+      hg = b / pairs;
+      row = pair / P.S;
+      sp = pair % P.S;
+    }
+  }
   const int seq = P.row_seq[row];
   const int j0 = sp * P.per_split;
   const int jend = min(P.topk, j0 + P.per_split);

@@ -46,6 +46,8 @@ SIGNATURES = {
                                     _P, _P, _P, _SZ, _P]),
     "dsa_indexer_topk_noalloc": (_c.c_int, [_P, _P, _P, _P, _I64, _P, _I32, _P, _P, _I32, _I32,
                                             _I32, _P, _P, _P]),
+    "dsa_decode_indexer_topk": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _I64, _P, _I32, _P, _P,
+                                           _I32, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "dsa_indexer_topk_seq_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
     "dsa_indexer_topk_seq": (_c.c_int, [_P, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32,
                                         _P, _P, _P, _SZ, _P]),
@@ -203,6 +205,38 @@ def dsa_indexer_topk_noalloc(q_fp8, q_e8m0, w, k_pool, block_table, row_seq, row
                                           k_pool.shape[0], _ptr(block_table), block_table.shape[1],
                                           _ptr(row_seq), _ptr(row_pos), R, H, topk, _ptr(out_idx),
                                           _ptr(out_score), _stream()), "dsa_indexer_topk_noalloc")
+    return out_idx, out_score
+
+
+def dsa_decode_indexer_topk(q_bf16, w, k_new, kv_new, slot_mapping, k_pool, kv_pool, block_table,
+                            row_seq, row_pos, topk: int, out_idx=None, out_score=None,
+                            workspace=None, with_scores: bool = True):
+    """The decode prolog (q quantisation, new key / KV record writes) and
+    dsa_indexer_topk in the indexer's launches; q_bf16 [R, H_I, 128],
+    k_new [R, 128], kv_new [R, 576] bf16, slot_mapping int64 [R]."""
+    R, H = q_bf16.shape[0], q_bf16.shape[1]
+    for t, dt, n in ((q_bf16, torch.bfloat16, "q_bf16"), (w, torch.float32, "w"),
+                     (k_new, torch.bfloat16, "k_new"), (kv_new, torch.bfloat16, "kv_new"),
+                     (slot_mapping, torch.int64, "slot_mapping"), (k_pool, torch.uint8, "k_pool"),
+                     (kv_pool, torch.uint8, "kv_pool"), (block_table, torch.int32, "block_table"),
+                     (row_seq, torch.int32, "row_seq"), (row_pos, torch.int32, "row_pos")):
+        _need(t, dt, n)
+    if k_pool.shape[0] != kv_pool.shape[0]:
+        raise ValueError("k_pool and kv_pool must have the same number of pages")
+    dev = q_bf16.device
+    if out_idx is None:
+        out_idx = torch.empty((R, topk), dtype=torch.int32, device=dev)
+    if out_score is None and with_scores:
+        out_score = torch.empty((R, topk), dtype=torch.float32, device=dev)
+    bt_stride = block_table.shape[1]
+    if workspace is None:
+        workspace = indexer_workspace(R, bt_stride, H, topk, dev)
+    _check(lib().dsa_decode_indexer_topk(_ptr(q_bf16), _ptr(w), _ptr(k_new), _ptr(kv_new),
+                                         _ptr(slot_mapping), _ptr(k_pool), _ptr(kv_pool),
+                                         k_pool.shape[0], _ptr(block_table), bt_stride,
+                                         _ptr(row_seq), _ptr(row_pos), R, H, topk, _ptr(out_idx),
+                                         _ptr(out_score), _ptr(workspace), workspace.numel(),
+                                         _stream()), "dsa_decode_indexer_topk")
     return out_idx, out_score
 
 
