@@ -150,3 +150,32 @@ def test_decode_prolog_no_new_tokens(need_gpu):
     assert np.array_equal(codes.cpu().numpy(), c_ref)
     assert np.array_equal(scales.cpu().numpy(), s_ref)
     assert int(kpool.sum()) == 0 and int(kvpool.sum()) == 0
+
+
+def test_mxfp8_every_in_range_bf16_value(need_gpu):
+    """Every finite bf16 value v with |v| <= 448 is quantised in a group whose
+    scale is 2^0 (each group of 32 holds 448 in its first element), so its
+    E4M3 code is the code of v itself: all of them against the oracle's
+    encoder.  This covers the whole input domain of the element conversion
+    of MXFP8 (a bf16 value times a power of two is a bf16 value, and the
+    scale rule keeps it within 448)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = (bits.astype(np.uint32) << 16).view(np.float32)
+    keep = np.isfinite(vals) & (np.abs(vals) <= 448.0)
+    dom = bits[keep]
+    per = 31
+    n_groups = (len(dom) + per - 1) // per
+    grid = np.zeros((n_groups, 32), dtype=np.uint16)
+    grid[:, 0] = synth.f32_to_bf16_bits(np.array([448.0], dtype=np.float32))[0]
+    flat = np.zeros(n_groups * per, dtype=np.uint16)
+    flat[:len(dom)] = dom
+    grid[:, 1:] = flat.reshape(n_groups, per)
+    x = grid.reshape(-1, 128) if (n_groups % 4 == 0) else np.concatenate(
+        [grid, np.zeros((4 - n_groups % 4, 32), dtype=np.uint16)]).reshape(-1, 128)
+    codes, e8 = ops.mxfp8_quant(bf16_tensor(x, "cuda"))
+    torch.cuda.synchronize()
+    ref_c, ref_e = quant.mxfp8_quant(x)
+    assert np.array_equal(e8.cpu().numpy(), ref_e)
+    assert np.all(ref_e.reshape(-1)[:n_groups] == 127)
+    assert np.array_equal(codes.cpu().numpy(), ref_c)
+    say(f"[quant] {len(dom)} in-range bf16 values: codes equal to the oracle's")
