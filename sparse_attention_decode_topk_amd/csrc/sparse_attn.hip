@@ -94,6 +94,7 @@ struct Smem {
   uint8_t junk[1024];                  // target of padding DMA instructions
   int32_t slot[kMaxEntries];           // record slot per entry of the split, -1 = none
   float zx[2][2][2][8 * 64];           // partial logits [group][ht][dh], swapped between partners
+  uint32_t vmask[kMaxEntries / 32];   // entry validity, one bit per entry of the split
 };
 
 __device__ __forceinline__ void flag(uint32_t* err, uint32_t bits) {
@@ -112,6 +113,34 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
                :
                : "v"(src), "s"(lds_base)
                : "memory", "m0");
+}
+
+// Maximum / sum of a value over the four 16-lane rows of a wave (every lane
+// receives it), by v_permlane16_swap / v_permlane32_swap instead of LDS
+// round trips.  The sum is (row0 + row1) + (row2 + row3) in every lane, as
+// the pairwise exchange by lane xor 16 then 32 gives up to the order of
+// each (commutative) addition.
+__device__ __forceinline__ float rows_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const unsigned v = __float_as_uint(m);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ uint32_t rows_umax(uint32_t u) {
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const uint32_t m = max((uint32_t)a[0], (uint32_t)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+  return max((uint32_t)b[0], (uint32_t)b[1]);
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const unsigned v = __float_as_uint(s);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // The tokens of a tile in the order of the P.V contraction: k = 8g + i is
@@ -203,6 +232,13 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
           flag(P.err, 1u);
       }
       if (e < nsteps * kStepTok) S.slot[e] = s;
+      // validity of the wave's 64 consecutive entries, one bit per entry
+      const uint64_t vb = __builtin_amdgcn_ballot_w64(s >= 0);
+      const int e0 = (tid & ~63) + i * kThreads;
+      if (lane == 0 && e0 < nsteps * kStepTok) {
+        S.vmask[e0 >> 5] = (uint32_t)vb;
+        S.vmask[(e0 >> 5) + 1] = (uint32_t)(vb >> 32);
+      }
     }
   }
   __syncthreads();
@@ -317,11 +353,12 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     float z[8];
+    const uint32_t tmask = S.vmask[eq0 >> 5];   // validity of the tile's 32 entries
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float own = zx[i * 64 + lane], other = zpart[i * 64 + lane];
       const float v = dh ? other + own : own + other;   // half 0 first in both partners
-      z[i] = S.slot[eq0 + ktok(g, i)] >= 0 ? v * P.scale_log2 : -__builtin_huge_valf();
+      z[i] = (tmask >> ktok(g, i)) & 1u ? v * P.scale_log2 : -__builtin_huge_valf();
     }
     uint32_t smax[2] = {0u, 0u};
 #pragma unroll
@@ -334,15 +371,13 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
     float zm = z[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) zm = fmaxf(zm, z[i]);
-    zm = fmaxf(zm, __shfl_xor(zm, 16));
-    zm = fmaxf(zm, __shfl_xor(zm, 32));
+    zm = rows_max(zm);
     int et[2];
     bool egrow = false;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       uint32_t b = smax[t];
-      b = max(b, (uint32_t)__shfl_xor((int)b, 16));
-      b = max(b, (uint32_t)__shfl_xor((int)b, 32));
+      b = rows_umax(b);
       et[t] = (b & 0x7FFFFFFFu) ? (int)((b >> 23) & 0xFF) - 127 : -1000;
       egrow |= et[t] > eref[t];
     }
@@ -374,8 +409,7 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
       pr[i] = z[i] == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(z[i] - m_ref);   // <= 2^kMargin
       ps += pr[i];
     }
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
+    ps = rows_sum(ps);
     l_run += ps;
 
     // ---- O^T += V^T P'^T over the tile (one k-step of 32 tokens) ----
