@@ -129,6 +129,8 @@ struct SelSmem {
   alignas(16) uint32_t wtot[kSelWaves];     // fast path: per-wave (equal, greater) counts
   uint32_t red[2 * kWaves + 2];
   uint32_t misc[16];
+  uint32_t rcount;                    // fast path: keys of a small bin collected so far
+  uint32_t rlist[64];                 // fast path: the keys of a small bin (any order)
 };
 
 __device__ __forceinline__ void flag_error(uint32_t* hdr, uint32_t bits) {
@@ -1259,6 +1261,37 @@ __device__ __forceinline__ int row_slots(const Params& P, int nu) {
   return min(nu * kUnitTok, P.bt_stride * kPage);
 }
 
+// A radix bin holding at most kSmallBin keys: instead of a further radix
+// pass, its keys are collected in LDS (in any order) and every wave ranks
+// them directly.  Returns the key T of rank `need` from the top within the
+// bin and the number of keys equal to T that are kept (need minus the keys
+// above T), the same result the remaining passes give.  One barrier.
+// S.rcount must be zero (cleared with the histograms).
+constexpr uint32_t kSmallBin = 64;
+
+template <int NK>
+__device__ __forceinline__ void small_bin_resolve(SelSmem& S, const uint32_t (&k)[NK], uint32_t lo,
+                                                  uint64_t span, uint32_t need, uint32_t* T,
+                                                  uint32_t* ties) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < NK; ++i)
+    if (k[i] >= lo && (uint64_t)(k[i] - lo) < span) S.rlist[atomicAdd(&S.rcount, 1u)] = k[i];
+  __syncthreads();
+  const uint32_t c = __builtin_amdgcn_readfirstlane(S.rcount);
+  const uint32_t v = (uint32_t)lane < c ? S.rlist[lane] : 0u;
+  uint32_t gt = 0, eq = 0;
+  for (uint32_t j = 0; j < c; ++j) {
+    const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)v, (int)j);
+    gt += kj > v ? 1u : 0u;
+    eq += kj == v ? 1u : 0u;
+  }
+  const uint64_t hit = __builtin_amdgcn_ballot_w64((uint32_t)lane < c && gt < need && gt + eq >= need);
+  const int src = __builtin_ctzll(hit);
+  *T = (uint32_t)__builtin_amdgcn_readlane((int)v, src);
+  *ties = need - (uint32_t)__builtin_amdgcn_readlane((int)gt, src);
+}
+
 // Layout J (1, 2, 4, 8 or 16): for J <= 8 wave w owns units (8/J)w ..
 // (8/J)w + 8/J - 1 and holds slots lane, lane + 64, ..., lane + 64(J-1) of
 // each; for J = 16 waves 2u and 2u+1 share unit u, slots lane + 64j and
@@ -1307,6 +1340,7 @@ __device__ __forceinline__ int select_fast(const Params& P, SelSmem& S, int row)
     uint4* h4 = reinterpret_cast<uint4*>(S.hist);
 #pragma unroll
     for (int i = 0; i < 2 * kBins / 4 / kSelThreads; ++i) h4[threadIdx.x + i * kSelThreads] = make_uint4(0, 0, 0, 0);
+    if (threadIdx.x == 0) S.rcount = 0;
   }
   const int units_r = row_units(t, P.bt_stride);
   if (units_r > kUnits) return 0;
@@ -1394,6 +1428,13 @@ __device__ __forceinline__ int select_fast(const Params& P, SelSmem& S, int row)
     need -= above;
     if (shift == 0) break;
     span = 1ull << shift;   // the keys of the chosen bin
+    if (H[bin] <= kSmallBin) {   // uniform: every wave reads the complete histogram
+      uint32_t T0, t0;
+      small_bin_resolve(S, k, base, span, need, &T0, &t0);
+      base = T0;
+      need = t0;
+      break;
+    }
     shift = max(0, shift - 12);
   }
   const uint32_t T = base, ties = need;   // T >= lo >= 1, so empty slots never equal it
@@ -1481,6 +1522,7 @@ __device__ __forceinline__ int select_fast_rt(const Params& P, SelSmem& S, int r
     uint4* h4 = reinterpret_cast<uint4*>(S.hist);
 #pragma unroll
     for (int i = 0; i < 2 * kBins / 4 / kSelThreads; ++i) h4[threadIdx.x + i * kSelThreads] = make_uint4(0, 0, 0, 0);
+    if (threadIdx.x == 0) S.rcount = 0;
   }
   const int units_r = row_units(t, P.bt_stride);
   if (units_r > kUnits) return 0;
@@ -1567,6 +1609,13 @@ __device__ __forceinline__ int select_fast_rt(const Params& P, SelSmem& S, int r
     need -= above;
     if (shift == 0) break;
     span = 1ull << shift;   // the keys of the chosen bin
+    if (H[bin] <= kSmallBin) {   // uniform: every wave reads the complete histogram
+      uint32_t T0, t0;
+      small_bin_resolve(S, k, base, span, need, &T0, &t0);
+      base = T0;
+      need = t0;
+      break;
+    }
     shift = max(0, shift - 12);
   }
   const uint32_t T = base, ties = need;   // T >= lo >= 1, so empty slots never equal it
