@@ -128,17 +128,23 @@ int dsa_decode_prolog(const void* q_bf16, int64_t q_rows, int32_t q_cols,
                       int64_t pool_pages, void* stream);
 
 /*
- * Bytes of zero-initialised workspace dsa_indexer_topk needs for R query
- * rows whose block tables have bt_stride entries.
+ * Bytes of workspace dsa_indexer_topk needs for R query rows whose block
+ * tables have bt_stride entries.
  */
 size_t dsa_indexer_topk_workspace_size(int32_t R, int32_t bt_stride,
                                        int32_t H_I, int32_t topk);
 
 /*
- * Lightning Indexer with fused head weighting and Top-K, one launch, no
- * score matrix in HBM ("Deep Dive into Sparse Attention", section "1.
- * Computation Optimization: ... DSA Fused Kernel"; Kimi K3.1 Pro Day0 page,
- * "Lightning Indexer Three-Stream Coordination"):
+ * Lightning Indexer with fused head weighting and Top-K, no score matrix in
+ * HBM ("Deep Dive into Sparse Attention", section "1. Computation
+ * Optimization: ... DSA Fused Kernel"; Kimi K3.1 Pro Day0 page, "Lightning
+ * Indexer Three-Stream Coordination").  Two launches per 1024 rows on the
+ * caller's stream: a scan that scores the K pages and keeps each 1024-position
+ * unit's candidates (keys at or above a per-unit edge), then a select that
+ * takes the exact Top-K of every row from them.  The second launch starts
+ * when the first has drained (at 8 rows of 128K positions: about 33 us of
+ * scan, then about 7 us of select); no work-group waits on another inside a
+ * launch.
  *
  *   I(t,s) = sum_h w[r,h] * max(0, q[r,h] . k[s]),  0 <= s <= t = row_pos[r]
  *
@@ -155,12 +161,13 @@ size_t dsa_indexer_topk_workspace_size(int32_t R, int32_t bt_stride,
  *   out_idx    [R, topk] int32 ascending positions, then -1
  *   out_score  [R, topk] fp32 scores aligned with out_idx (-inf padding);
  *              may be NULL
- *   workspace  >= dsa_indexer_topk_workspace_size(...) bytes, zero-filled
- *              once by the caller before first use; each call returns its
- *              counters to zero for the next call.  Bytes [8,12) hold a
- *              sticky status word the caller may read and clear: bit 2 = a
- *              page id outside [0, pool_pages) was skipped, bit 3 = a row
- *              needed the exact rescoring path (informational).
+ *   workspace  >= dsa_indexer_topk_workspace_size(...) bytes.  Its
+ *              contents need no initialisation: every call writes what it
+ *              reads.  Bytes [8,12) hold a sticky status word that the
+ *              kernels only OR bits into (the caller clears it to start
+ *              afresh and reads it after the call): bit 2 = a page id
+ *              outside [0, pool_pages) was skipped, bit 3 = a row needed
+ *              the exact rescoring path (informational).
  * Results are exact and deterministic (no floating-point atomics).  A page id
  * outside [0, pool_pages) or a row with row_pos < 0 contributes no positions.
  * block_table widths up to 16384 pages (1M tokens) are supported.
@@ -236,7 +243,7 @@ int dsa_decode_indexer_topk(const void* q_bf16, const float* w, const void* k_ne
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Bytes of zero-initialised workspace dsa_indexer_topk_seq needs for R query
+ * Bytes of workspace dsa_indexer_topk_seq needs for R query
  * rows of a sequence of n_pages pages.
  */
 size_t dsa_indexer_topk_seq_workspace_size(int32_t R, int32_t n_pages,

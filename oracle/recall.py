@@ -18,7 +18,16 @@ Per query row r with history t (n = min(K, t + 1) positions kept):
   recall       |TopK_mx ∩ TopK_ref| / n
   mass recall  sum of I_ref over TopK_mx / sum of I_ref over TopK_ref (how
                much of the reference selection's score the quantised
-               selection keeps; 1 when the sets agree)
+               selection keeps; 1 when the sets agree).  Read as a fraction
+               only where the reference selection's scores are positive: the
+               head weights may be negative, and a row whose K-th largest
+               score is below zero makes the ratio depend on where zero lies
+  score loss   (mean of I_ref over TopK_ref - mean of I_ref over TopK_mx) /
+               standard deviation of I_ref over the row's history: the
+               average score given up per kept position, in units of the
+               row's spread; unchanged by a shift or a positive scale of the
+               scores, never negative (TopK_ref has the largest sum), 0 when
+               the sets agree
   needles      of the planted needle positions that the reference keeps,
                the fraction the MXFP8 selection keeps too
 
@@ -57,6 +66,9 @@ def row_recall(I_mx: np.ndarray, I_ref: np.ndarray, K: int,
     out = dict(recall=common / n)
     ref_mass = float(I_ref[sel_ref].sum())
     out["mass_recall"] = float(I_ref[sel_mx].sum()) / ref_mass if ref_mass != 0.0 else 1.0
+    sd = float(I_ref.std())
+    gap = float(I_ref[sel_ref].sum() - I_ref[sel_mx].sum()) / n
+    out["score_loss"] = gap / sd if sd > 0.0 else 0.0
     if needles is not None and len(needles):
         kept_ref = np.intersect1d(needles, sel_ref)
         out["needles_ref"] = int(kept_ref.size)
@@ -84,7 +96,8 @@ def study(inp: Dict[str, np.ndarray], rows: Optional[Iterable[int]] = None) -> D
     summary = dict(rows=len(per),
                    recall_mean=float(np.mean([p["recall"] for p in per])),
                    recall_min=float(np.min([p["recall"] for p in per])),
-                   mass_recall_min=float(np.min([p["mass_recall"] for p in per])))
+                   mass_recall_min=float(np.min([p["mass_recall"] for p in per])),
+                   score_loss_max=float(np.max([p["score_loss"] for p in per])))
     if per and "needle_recall" in per[0]:
         summary["needles_in_ref_topk"] = int(sum(p["needles_ref"] for p in per))
         summary["needle_recall_min"] = float(np.min([p["needle_recall"] for p in per]))
@@ -103,7 +116,7 @@ def main(argv) -> int:
     names = argv or ["decode_8k_needles", "decode_ragged_b32", "decode_128k_b8",
                      "prefill_chunk_8k_of_128k"]
     print(f"{'config':28s} {'rows':>4s} {'recall mean':>11s} {'recall min':>10s} "
-          f"{'mass min':>9s} {'needles':>8s} {'secs':>6s}")
+          f"{'mass min':>9s} {'loss max':>9s} {'needles':>8s} {'secs':>6s}")
     for name in names:
         cfg = synth.config(name)
         R = len(synth.make(cfg, with_sfa=False, with_index=False)["row_seq"])
@@ -114,7 +127,7 @@ def main(argv) -> int:
         nd = ("%d/%.3f" % (s["needles_in_ref_topk"], s["needle_recall_min"])
               if "needle_recall_min" in s else "-")
         print(f"{name:28s} {s['rows']:4d} {s['recall_mean']:11.4f} {s['recall_min']:10.4f} "
-              f"{s['mass_recall_min']:9.5f} {nd:>8s} {time.perf_counter() - t0:6.1f}", flush=True)
+              f"{s['mass_recall_min']:9.5f} {s['score_loss_max']:9.5f} {nd:>8s} {time.perf_counter() - t0:6.1f}", flush=True)
     return 0
 
 

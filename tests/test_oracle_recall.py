@@ -3,7 +3,7 @@
 Pins: on inputs that MXFP8 represents exactly (every value on the E4M3 grid,
 every 32-group holding 448 so that its scale is 2^0) the quantised and the
 unquantised indexers are the same function, so recall and mass recall are
-exactly 1 for every row and K; a position list shifted by one, a wrong row
+exactly 1 and the score loss exactly 0 for every row and K; a position list shifted by one, a wrong row
 or a dropped head would break that.  On the needle workload the study's
 figures are checked against bounds taken from its measured values."""
 import numpy as np
@@ -47,6 +47,7 @@ def test_lossless_recall_is_one(K):
     inp["topk"] = np.int32(K)
     s = recall.study(inp)
     assert s["recall_min"] == 1.0 and s["mass_recall_min"] == 1.0
+    assert s["score_loss_max"] == 0.0
 
 
 def test_row_recall_counts_overlap():
@@ -55,9 +56,21 @@ def test_row_recall_counts_overlap():
     r = recall.row_recall(I_mx, I_ref, 3, needles=np.array([0, 2]))
     assert r["recall"] == pytest.approx(2 / 3)
     assert r["mass_recall"] == pytest.approx((5 + 4 + 1) / (5 + 4 + 3))
+    assert r["score_loss"] == pytest.approx(((5 + 4 + 3) - (5 + 4 + 1)) / 3 / np.sqrt(2.0))
     assert r["needles_ref"] == 2 and r["needle_recall"] == 0.5
     # K beyond the history keeps everything
     assert recall.row_recall(I_mx, I_ref, 99)["recall"] == 1.0
+
+
+def test_score_loss_ignores_shift_and_scale():
+    rng = np.random.default_rng(3)
+    I_ref = rng.standard_normal(500)
+    I_mx = I_ref + 0.3 * rng.standard_normal(500)
+    a = recall.row_recall(I_mx, I_ref, 40)
+    b = recall.row_recall(2.5 * I_mx - 7.0, 2.5 * I_ref - 7.0, 40)
+    assert a["score_loss"] > 0.0
+    assert b["score_loss"] == pytest.approx(a["score_loss"], rel=1e-12)
+    assert b["recall"] == a["recall"]
 
 
 def test_needle_workload_recall():
