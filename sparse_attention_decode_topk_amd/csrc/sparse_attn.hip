@@ -291,6 +291,14 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
 
   issue_step(0);
   issue_step(1);
+  // Group 1 runs one barrier behind group 0: every s_barrier of the loop is
+  // then group 0's step-top barrier and group 1's mid-step barrier or the
+  // reverse, so one group computes logits while the other runs the softmax
+  // and P.V (the two waves sharing a SIMD are in different phases).  A
+  // group's ring slots, partial logits and DMA are its own, so only its own
+  // waves' ordering matters; the counts match through one extra barrier of
+  // group 0 after the loop.
+  if (grp == 1) __builtin_amdgcn_s_barrier();
   for (int k = 0; k < nsteps; ++k) {
     // this step's copies are complete once only the next step's remain; the
     // barrier also releases the slots of step k-1
@@ -438,6 +446,7 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
   // no copy may still be landing in LDS when the ring is reused or the
   // workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (grp == 0) __builtin_amdgcn_s_barrier();
 
   // ---- true O relative to m_ref: o * 2^(eref - kPBias) ----
 #pragma unroll
