@@ -243,8 +243,11 @@ int dsa_decode_indexer_topk(const void* q_bf16, const float* w, const void* k_ne
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Bytes of workspace dsa_indexer_topk_seq needs for R query
- * rows of a sequence of n_pages pages.
+ * Bytes of workspace dsa_indexer_topk_seq needs for R query rows of a
+ * sequence of n_pages pages.  The rows are taken in launches of at most 4096
+ * rows, and of few enough that a launch's candidate region (8 bytes per
+ * history slot of every row) stays within 512 MiB: about 537 MB at 2048
+ * pages (512 rows per launch), whatever R is.
  */
 size_t dsa_indexer_topk_seq_workspace_size(int32_t R, int32_t n_pages,
                                            int32_t H_I, int32_t topk);

@@ -1817,7 +1817,16 @@ constexpr int kPgBlocks = (kPgGran + 63) / 64;         // 10 one-KB copy blocks 
 constexpr int kPgDmaPerWave = (kPgBlocks + kWaves - 1) / kWaves;   // 3
 constexpr int kPgBytes = kPgBlocks * 1024;
 constexpr int kTileMaxPages = 4096;                    // page ids of a tile held in LDS
-constexpr int kSeqChunkRows = 4096;                    // rows per launch of the tiled path
+constexpr int kSeqChunkRows = 4096;                    // rows per launch of the tiled path (most)
+// The candidate region of a launch holds 8 bytes per history slot of every
+// row (a unit's slice has room for all 1024 of its keys, which the exact
+// rescoring path may write).  A chunked prefill over a long context takes
+// fewer rows per launch so that the region stays within this size (at 2048
+// pages: 512 rows, 512 MiB, instead of 4 GiB for 4096 rows); the units of
+// its tiles are then dealt in chunks so that the launch still has work for
+// every resident work-group.  Measured at 8192 rows of a 128K context: 256
+// MiB (32 launches) costs 4% of the indexer's time, 512 MiB 0.6%.
+constexpr int64_t kSeqCandBytes = int64_t(512) << 20;
 static_assert(kTileRowsPerWave == 2, "two rows per wave");
 static_assert(kPgDmaPerWave * kWaves >= kPgBlocks, "the copy blocks cover a page");
 static_assert(kUnitPages == 16, "16 pages per unit: one key per lane and page");
@@ -2441,13 +2450,20 @@ extern "C" int dsa_indexer_scores(const void* q_fp8, const void* q_e8m0, const f
   return run(P, true, s);
 }
 
+// Rows per launch of dsa_indexer_topk_seq: at most kSeqChunkRows, a multiple
+// of the tile height, and within kSeqCandBytes of candidate region.
+int seq_rows_per_launch(int64_t R, int64_t n_pages) {
+  const int64_t per_row = n_pages * kPage * 8;
+  const int64_t fit = std::max<int64_t>(kTileRows, kSeqCandBytes / per_row / kTileRows * kTileRows);
+  return (int)std::min<int64_t>(std::min<int64_t>(R, kSeqChunkRows), fit);
+}
+
 extern "C" size_t dsa_indexer_topk_seq_workspace_size(int32_t R, int32_t n_pages, int32_t H_I,
                                                       int32_t topk) {
   (void)H_I;
   (void)topk;
   if (R <= 0 || n_pages <= 0) return 256;
-  const int64_t rows = std::min<int64_t>(R, kSeqChunkRows);
-  return layout_for(rows, n_pages).total;
+  return layout_for(seq_rows_per_launch(R, n_pages), n_pages).total;
 }
 
 extern "C" int dsa_indexer_topk_seq(const void* q_fp8, const void* q_e8m0, const float* w,
@@ -2463,8 +2479,8 @@ extern "C" int dsa_indexer_topk_seq(const void* q_fp8, const void* q_e8m0, const
   if (n_pages > kTileMaxPages) return DSA_ERR_UNSUPPORTED;
   if (topk < 1 || topk > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
   if (R == 0) return DSA_OK;
-  const int64_t rows = std::min<int64_t>(R, kSeqChunkRows);
-  const Layout L = layout_for(rows, n_pages);
+  const int per_launch = seq_rows_per_launch(R, n_pages);
+  const Layout L = layout_for(per_launch, n_pages);
   if (workspace == nullptr || workspace_bytes < L.total) return DSA_ERR_WORKSPACE;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   hipStream_t s = dsa_host::as_stream(stream);
@@ -2473,8 +2489,9 @@ extern "C" int dsa_indexer_topk_seq(const void* q_fp8, const void* q_e8m0, const
   void* sel = pick_kernel(nht, kSelect);
   const int cap = resident_capacity(tk, 12 + nht - 1, kThreads);
   if (cap <= 0) return DSA_ERR_HIP;
-  for (int r0 = 0; r0 < R; r0 += kSeqChunkRows) {
-    const int rn = std::min(kSeqChunkRows, R - r0);
+  const int64_t upr = units_stride(n_pages);
+  for (int r0 = 0; r0 < R; r0 += per_launch) {
+    const int rn = std::min(per_launch, R - r0);
     Params P = base_params(q_fp8, q_e8m0, w, k_pool, pool_pages, block_table_row, n_pages, nullptr,
                            row_pos + r0, rn, H_I);
     P.q += (int64_t)r0 * H_I * kIdxDim;
@@ -2487,8 +2504,15 @@ extern "C" int dsa_indexer_topk_seq(const void* q_fp8, const void* q_e8m0, const
     P.ucount = reinterpret_cast<uint32_t*>(ws + L.ucount);
     P.uedge = reinterpret_cast<uint32_t*>(ws + L.uedge);
     P.cand = reinterpret_cast<uint2*>(ws + L.cand);
-    const int ntiles = (rn + kTileRows - 1) / kTileRows;
-    const int G = std::min(cap, ntiles);
+    const int64_t ntiles = (rn + kTileRows - 1) / kTileRows;
+    // whole tiles when there are two per resident work-group; otherwise
+    // the tiles' units in chunks, about two work items per work-group
+    P.chunk_units = ntiles >= 2 * (int64_t)cap
+                        ? 0
+                        : (int)std::max<int64_t>(1, (ntiles * upr + 2 * cap - 1) / (2 * cap));
+    const int64_t nitems = P.chunk_units > 0 ? ntiles * ((upr + P.chunk_units - 1) / P.chunk_units)
+                                             : ntiles;
+    const int64_t G = std::min<int64_t>(cap, nitems);
     void* args[] = {&P};
     if (hipLaunchKernel(tk, dim3((unsigned)G), dim3(kThreads), args, 0, s) != hipSuccess)
       return DSA_ERR_HIP;

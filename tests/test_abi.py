@@ -58,6 +58,23 @@ def test_workspace_sizes_are_host_only(lib):
     assert lib.dsa_sparse_attn_workspace_size(512, 8, 64) == small
 
 
+def test_chunked_prefill_workspace_is_bounded(lib):
+    # the row-tiled prefill path keeps a launch's candidate region (8 bytes
+    # per history slot of every row) within 512 MiB by taking fewer rows per
+    # launch: 8192 rows of a 2048-page sequence need 512 rows' worth, not
+    # 4096 rows' (4 GiB)
+    per_row = 2048 * 64 * 8
+    big = lib.dsa_indexer_topk_seq_workspace_size(8192, 2048, 64, 2048)
+    assert 512 * per_row <= big < 600 * 2**20
+    assert lib.dsa_indexer_topk_seq_workspace_size(4096, 2048, 64, 2048) == big
+    # short contexts keep up to 4096 rows per launch; a small R needs only its own rows
+    short = lib.dsa_indexer_topk_seq_workspace_size(8192, 64, 64, 2048)
+    assert short >= 4096 * 64 * 64 * 8
+    assert lib.dsa_indexer_topk_seq_workspace_size(16, 2048, 64, 2048) < 17 * per_row
+    # the longest sequence (4096 pages) still fits: one tile height of rows at least
+    assert lib.dsa_indexer_topk_seq_workspace_size(8192, 4096, 64, 2048) < 600 * 2**20
+
+
 P = ctypes.c_void_p
 FAKE = P(0x1000)   # never dereferenced: every call below fails validation first
 
