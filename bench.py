@@ -13,8 +13,10 @@ One step = the whole hot path for one decode token of each sequence:
   -> dsa_sparse_attn
 (--unfused-prolog runs dsa_decode_prolog, one launch, then dsa_indexer_topk;
 --separate-prolog runs the three quantisations as three launches instead;
---graph captures the step once per cache replica in a HIP graph and times
-graph replays instead of eager launches).
+--graph captures the step in HIP graphs, one per cache replica, and times
+graph replays instead of eager launches; --graph-steps N puts N consecutive
+steps (on rotating replicas) in every graph, as a model would capture the
+DSA calls of several layers in one graph).
 Caches are replicated (default 4 replicas, about 3.3 GB) and rotated per step
 so that the 256 MB Infinity Cache cannot serve one step's reads from the
 previous step.
@@ -86,6 +88,8 @@ def parse():
                     help="decode: dsa_decode_prolog then dsa_indexer_topk instead of dsa_decode_indexer_topk")
     ap.add_argument("--graph", action="store_true",
                     help="capture the step once per cache replica in a HIP graph and time graph replays")
+    ap.add_argument("--graph-steps", type=int, default=1, metavar="N",
+                    help="with --graph: N consecutive steps per graph (steps must be a multiple of N)")
     ap.add_argument("--profile-steps", action="store_true",
                     help="only warm up and run the timed steps (for profiler runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -101,6 +105,9 @@ def main():
         sys.exit(2)
     if args.graph and args.separate_prolog:
         print("--graph captures the fused prolog; drop --separate-prolog", file=sys.stderr)
+        sys.exit(2)
+    if args.graph_steps < 1 or args.steps % args.graph_steps or args.warmup % args.graph_steps:
+        print("--graph-steps must divide --steps and --warmup", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -218,31 +225,40 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    run_step = step
+    # run_block(b) runs steps b*G .. b*G + G - 1 (G = 1 unless graphs hold
+    # several steps)
+    G = args.graph_steps if args.graph else 1
+    run_block = step
     if args.graph:
-        # one graph per replica, its launches recorded on a capture stream
+        # graph j holds steps on replicas (j*G + s) % replicas, s < G, so that
+        # replaying graph b % replicas for block b continues the rotation;
+        # launches recorded on a capture stream
         cap = torch.cuda.Stream()
         cap_h = P(cap.cuda_stream)
         graphs = []
         for j in range(args.replicas):
-            aj = {k: tuple(cap_h if x is stream else x for x in v) for k, v in steps_args[j].items()}
             g = torch.cuda.CUDAGraph()
+            st = 0
             with torch.cuda.graph(g, stream=cap):
-                st = 0 if fused else L.dsa_decode_prolog(*aj["pro"])
-                st |= indexer_call(*aj[idx_key]) | L.dsa_sparse_attn(*aj["sfa"])
+                for sidx in range(G):
+                    r = (j * G + sidx) % args.replicas
+                    aj = {k: tuple(cap_h if x is stream else x for x in v) for k, v in steps_args[r].items()}
+                    if not fused:
+                        st |= L.dsa_decode_prolog(*aj["pro"])
+                    st |= indexer_call(*aj[idx_key]) | L.dsa_sparse_attn(*aj["sfa"])
             if st:
                 raise RuntimeError(f"library call failed during capture (status bits {st})")
             graphs.append(g)
         torch.cuda.synchronize()
-        run_step = lambda i: graphs[i % args.replicas].replay()
-        for i in range(args.warmup):
-            run_step(i)
+        run_block = lambda b: graphs[b % args.replicas].replay()
+        for b in range(args.warmup // G):
+            run_block(b)
         torch.cuda.synchronize()
     K_steps = args.steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K_steps):
-        run_step(i)
+    for b in range(K_steps // G):
+        run_block(b)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     if args.profile_steps:
@@ -289,7 +305,10 @@ def main():
             raise RuntimeError("sparse attention call failed")
 
     n_pc = max(50, min(K_steps, 200))
-    dist = {"step": per_call(run_step, n_pc), idx_name_of(one_seq, mq, fused): per_call(call_idx, n_pc),
+    step_dist = per_call(run_block, max(1, n_pc // G))
+    if G > 1:   # a block of G steps per event pair: per step
+        step_dist = {k: (round(v / G, 2) if k != "calls" else v * G) for k, v in step_dist.items()}
+    dist = {"step": step_dist, idx_name_of(one_seq, mq, fused): per_call(call_idx, n_pc),
             "dsa_sparse_attn": per_call(call_sfa, n_pc)}
     stream_gbs = stream_read_gbs(ops, dev) if not args.profile_steps else None
     ms_per_step = elapsed * 1e3 / K_steps
@@ -360,7 +379,7 @@ def main():
                    "prolog": ("three launches" if args.separate_prolog else
                               "folded into dsa_decode_indexer_topk" if fused else
                               "dsa_decode_prolog (one launch)"),
-                   "launch": "hipGraph replay per step" if args.graph else "eager launches"},
+                   "launch": (f"hipGraph replay per {G} step(s)" if args.graph else "eager launches")},
         "hbm_gbs_step": round(step_gbs, 1),
         "algorithmic_bytes_step": step_bytes,
         # the whole step (every launch of the hot path) against HBM: indexer
