@@ -94,6 +94,8 @@ def parse():
                     help="only warm up and run the timed steps (for profiler runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES between two device buffers (counter calibration)")
+    ap.add_argument("--stream-probe", type=int, nargs="+", default=None, metavar="BYTES",
+                    help="only time plain streaming reads of each size at several grid sizes")
     return ap.parse_args()
 
 
@@ -114,6 +116,9 @@ def main():
 
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.stream_probe:
+        stream_probe(args.stream_probe)
         return
     from sparse_attention_decode_topk_amd import ops, synth
 
@@ -333,7 +338,7 @@ def main():
     idx_tf = idx_flop / (idx_avg * 1e-3) / 1e12
     sfa_tf = sfa_flop / (sfa_avg * 1e-3) / 1e12
     err_word = int(ws_i[8:12].view(torch.int32).item())
-    traffic = measured_traffic(cfg.name)
+    traffic = measured_traffic(cfg.name, idx_name_of(one_seq, mq, fused))
 
     cpu, parity = None, None
     if not args.no_cpu_baseline:
@@ -419,39 +424,63 @@ def cpu_model():
     return None
 
 
-def stream_read_gbs(ops, dev, nbytes=4 << 30, iters=20):
-    """Plain streaming read of a 4 GiB buffer (16 times the 256 MB Infinity
-    Cache) with the library's probe kernel; best-of and median GB/s over
-    `iters` back-to-back reads, each between its own event pair."""
+def stream_read_times(ops, dev, nbytes, grids=(512, 1024, 4096), iters=20):
+    """Median time (us) of a plain streaming read of `nbytes` with the
+    library's probe kernel, per grid size (work-groups of 256 threads), over
+    `iters` back-to-back reads, each between its own event pair.  Reads
+    rotate over enough buffers (at least 2 GiB in all) that the 256 MB
+    Infinity Cache cannot serve a repeat."""
     import numpy as np
     import torch
-    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    src.fill_(1)
-    grid = 256 * 16
-    out = torch.empty(grid, dtype=torch.int32, device=dev)
-    for _ in range(3):
-        ops.probe_stream_read(src, out, grid)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(iters)]
-    torch.cuda.synchronize()
-    for a, b in evs:
-        a.record()
-        ops.probe_stream_read(src, out, grid)
-        b.record()
-    torch.cuda.synchronize()
-    ms = np.array([a.elapsed_time(b) for a, b in evs])
-    del src
-    return float(nbytes / (np.median(ms) * 1e-3) / 1e9)
+    nbuf = max(1, min(8, (2 << 30) // nbytes))
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+    res = {}
+    for grid in grids:
+        out = torch.empty(grid, dtype=torch.int32, device=dev)
+        for i in range(4):
+            ops.probe_stream_read(bufs[i % nbuf], out, grid)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(iters)]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(evs):
+            a.record()
+            ops.probe_stream_read(bufs[i % nbuf], out, grid)
+            b.record()
+        torch.cuda.synchronize()
+        res[grid] = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
+    del bufs
+    return res
 
 
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "dsa_indexer_topk_decode_128k_b8_traffic.txt")
+def stream_read_gbs(ops, dev, nbytes=4 << 30):
+    """The practical read ceiling: a streaming read of 4 GiB (16 times the
+    Infinity Cache), GB/s of the fastest grid size."""
+    t = stream_read_times(ops, dev, nbytes)
+    return nbytes / (min(t.values()) * 1e-6) / 1e9
+
+
+def stream_probe(sizes):
+    """Streaming-read times per size and grid (one JSON line per size)."""
+    import torch
+    from sparse_attention_decode_topk_amd import ops
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    for n in sizes:
+        t = stream_read_times(ops, dev, n)
+        print(json.dumps({"stream_probe_bytes": n,
+                          "us_by_grid": {str(g): round(v, 2) for g, v in t.items()},
+                          "best_gbs": round(n / (min(t.values()) * 1e-6) / 1e9, 1)}), flush=True)
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "dsa_decode_indexer_topk_decode_128k_b8_traffic.txt")
 INDEXER_SOURCE = os.path.join(ROOT, "sparse_attention_decode_topk_amd", "csrc", "indexer.hip")
 
 
-def measured_traffic(workload):
-    """HBM bytes per dsa_indexer_topk call from the committed counter summary
-    (calibrated FETCH_SIZE + WRITE_SIZE), or None when the summary is missing,
-    for another workload, or was taken on a different indexer source."""
+def measured_traffic(workload, kernel):
+    """HBM bytes per call of the indexer entry point `kernel` from the
+    committed counter summary (calibrated FETCH_SIZE + WRITE_SIZE), or None
+    when the summary is missing, for another workload or entry point, or was
+    taken on a different indexer source."""
     import hashlib
     try:
         fields = {}
@@ -462,7 +491,8 @@ def measured_traffic(workload):
                     fields[k.strip()] = v.strip()
         with open(INDEXER_SOURCE, "rb") as f:
             sha = hashlib.sha256(f.read()).hexdigest()
-        if fields.get("indexer_source_sha256") != sha or fields.get("workload") != workload:
+        if (fields.get("indexer_source_sha256") != sha or fields.get("workload") != workload
+                or fields.get("kernel") != kernel):
             return None
         return int(fields["traffic_bytes_per_call"])
     except (OSError, KeyError, ValueError):
