@@ -28,8 +28,14 @@
  * Cache layouts (one block table of physical page ids serves both caches;
  * token s of sequence b lives in page block_table[b*bt_stride + s/64] at
  * offset s%64):
- *  - indexer K page, DSA_K_PAGE_BYTES = 8448 bytes:
- *      [64 tokens x 128 E4M3 codes][64 tokens x 4 E8M0 scale bytes]
+ *  - indexer K page, DSA_K_PAGE_BYTES = 8448 bytes, in tiles of 16 tokens:
+ *      bytes [0, 8192): codes, tile j (tokens 16j..16j+15) at 2048j; code d
+ *        of the tile's token n at 1024*(d/64) + 256*((d%64)/16) + 16*n + d%16
+ *        (16-byte pieces of the 16 tokens side by side, dims 0-15, 16-31,
+ *        32-47, 48-63, then the same for dims 64-127);
+ *      bytes [8192, 8448): E8M0 scales, tile j at 8192 + 64j; byte b (dims
+ *        32b..32b+31) of the tile's token n at 16*b + n.
+ *    (A 16-token MFMA operand then reads one contiguous kilobyte per load.)
  *  - SFA KV record, DSA_KV_RECORD_BYTES = 656 bytes per token (slot p*64+o
  *    at byte offset (p*64+o)*656 of the pool):
  *      [512 E4M3 latent codes][4 x fp32 tile scales][64 x bf16 rope]

@@ -10,8 +10,16 @@ Readings taken:
   * pages hold 64 tokens; one block table [B, pages] of physical page ids is
     shared by both caches, and token s of sequence b is in page
     block_table[b][s // 64] at offset s % 64;
-  * indexer K page (8448 bytes): 64 x 128 E4M3 codes (token-major), then
-    64 x 4 E8M0 bytes (token-major);
+  * indexer K page (8448 bytes): the 64 tokens' 128 E4M3 codes in four
+    tiles of 16 tokens (bytes 2048j .. 2048j + 2047 for tokens 16j .. 16j+15),
+    then their 4 E8M0 bytes in four 64-byte tiles.  Inside a code tile, code d
+    of the tile's token n sits at 1024*(d // 64) + 256*((d % 64) // 16)
+    + 16*n + d % 16: sixteen-byte pieces of the tile's tokens side by side,
+    the pieces of dims 0-15 first, then 16-31, 32-47, 48-63 (1 KB), then the
+    same for dims 64-127.  Inside a scale tile, byte b of token n sits at
+    16*b + n.  (Any byte order inside a page serves the method; this one
+    lets a reader take one piece per token and dim range from contiguous
+    memory.)
   * SFA KV page (41984 bytes): 64 records of 656 bytes (layout in quant.py),
     i.e. record of slot p*64+o at byte (p*64+o)*656 of the pool.
 """
@@ -24,6 +32,33 @@ from .quant import RECORD_BYTES
 PAGE = 64
 D_I = 128
 K_PAGE_BYTES = PAGE * D_I + PAGE * (D_I // 32)   # 8448
+K_TILE = 16                                      # tokens per K-page tile
+
+
+def _k_code_offsets() -> np.ndarray:
+    """[64, 128]: byte offset in a K page of code d of the token at offset o."""
+    off = np.empty((PAGE, D_I), dtype=np.int64)
+    for o in range(PAGE):
+        tile, n = divmod(o, K_TILE)
+        for d in range(D_I):
+            half, rest = divmod(d, 64)
+            piece, byte = divmod(rest, 16)
+            off[o, d] = tile * K_TILE * D_I + half * 1024 + piece * 256 + n * 16 + byte
+    return off
+
+
+def _k_scale_offsets() -> np.ndarray:
+    """[64, 4]: byte offset in a K page of E8M0 byte b of the token at offset o."""
+    off = np.empty((PAGE, D_I // 32), dtype=np.int64)
+    for o in range(PAGE):
+        tile, n = divmod(o, K_TILE)
+        for b in range(D_I // 32):
+            off[o, b] = PAGE * D_I + tile * 64 + b * K_TILE + n
+    return off
+
+
+K_CODE_OFF = _k_code_offsets()
+K_SCALE_OFF = _k_scale_offsets()
 
 
 def k_pool_write(codes: np.ndarray, e8m0: np.ndarray, slots: np.ndarray,
@@ -35,8 +70,8 @@ def k_pool_write(codes: np.ndarray, e8m0: np.ndarray, slots: np.ndarray,
         if slot < 0:
             continue
         p, o = divmod(int(slot), PAGE)
-        pool[p, o * D_I:(o + 1) * D_I] = codes[i]
-        pool[p, PAGE * D_I + o * 4:PAGE * D_I + (o + 1) * 4] = e8m0[i]
+        pool[p, K_CODE_OFF[o]] = codes[i]
+        pool[p, K_SCALE_OFF[o]] = e8m0[i]
     return pool
 
 
@@ -47,8 +82,8 @@ def k_pool_read(pool: np.ndarray, bt_row: np.ndarray, n_tokens: int):
     for s in range(0, n_tokens, PAGE):
         n = min(PAGE, n_tokens - s)
         page = pool[int(bt_row[s // PAGE])]
-        codes[s:s + n] = page[:PAGE * D_I].reshape(PAGE, D_I)[:n]
-        e8[s:s + n] = page[PAGE * D_I:].reshape(PAGE, 4)[:n]
+        codes[s:s + n] = page[K_CODE_OFF[:n]]
+        e8[s:s + n] = page[K_SCALE_OFF[:n]]
     return codes, e8
 
 

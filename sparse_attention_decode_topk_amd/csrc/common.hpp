@@ -12,6 +12,24 @@ constexpr int kPage = DSA_PAGE_TOKENS;          // tokens per page
 constexpr int kIdxDim = DSA_INDEX_DIM;          // indexer head dim
 constexpr int kKPageBytes = DSA_K_PAGE_BYTES;   // 64*128 codes + 64*4 scales
 constexpr int kKScaleOff = kPage * kIdxDim;     // scale bytes start in a K page
+constexpr int kKTileTok = 16;                   // tokens per K-page tile
+constexpr int kKTileBytes = kKTileTok * kIdxDim;   // 2048 code bytes per tile
+
+// K page byte of code d (0..127) of the token at page offset o: tile j = o/16
+// holds its tokens' codes as [d/64][(d%64)/16][o%16][d%16], so the 16-byte
+// chunk that lane n + 16g of a token-tile MFMA operand holds (dims 16g..+15,
+// or 64+16g..+15) sits at 16 * lane of a contiguous kilobyte.
+__host__ __device__ constexpr int k_code_off(int o, int d) {
+  return kKTileBytes * (o / kKTileTok) + 1024 * (d / 64) + 256 * ((d % 64) / 16) +
+         16 * (o % kKTileTok) + d % 16;
+}
+// K page byte of E8M0 scale b (dims 32b..32b+31) of the token at offset o:
+// [tile][b][o%16] after the codes.
+__host__ __device__ constexpr int k_scale_off(int o, int b) {
+  return kKScaleOff + 64 * (o / kKTileTok) + kKTileTok * b + o % kKTileTok;
+}
+static_assert(k_code_off(63, 127) == kKScaleOff - 1 && k_scale_off(63, 3) == kKPageBytes - 1,
+              "the K page layout fills the page");
 constexpr int kLatent = DSA_LATENT_DIM;
 constexpr int kRope = DSA_ROPE_DIM;
 constexpr int kQK = kLatent + kRope;            // 576

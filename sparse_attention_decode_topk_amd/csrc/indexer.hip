@@ -213,15 +213,25 @@ template <int NT>
 __device__ __forceinline__ void plan_rows(const Params& P, ScanSmem& S) {
   uint32_t* rowpre = S.rowpre;
   uint32_t* red = S.red;
+  constexpr int kPerMax = (kMaxRows + NT - 1) / NT;
   const int per = (P.R + NT - 1) / NT;
   const int r0 = threadIdx.x * per;
+  // every load is issued before the first store to LDS (a store through a
+  // generic pointer would otherwise keep the next load behind it)
+  int tv[kPerMax], sv[kPerMax];
+#pragma unroll
+  for (int i = 0; i < kPerMax; ++i) {
+    const bool in = i < per && r0 + i < P.R;
+    tv[i] = in ? P.row_pos[r0 + i] : 0;
+    sv[i] = in && P.row_seq ? P.row_seq[r0 + i] : 0;
+  }
   uint32_t lu = 0;
-  for (int i = 0; i < per; ++i) {
-    if (r0 + i < P.R) {
-      const int t = P.row_pos[r0 + i];
-      S.rowt[r0 + i] = t;
-      S.rowseq[r0 + i] = P.row_seq ? P.row_seq[r0 + i] : 0;
-      lu += (uint32_t)row_units(t, P.bt_stride);
+#pragma unroll
+  for (int i = 0; i < kPerMax; ++i) {
+    if (i < per && r0 + i < P.R) {
+      S.rowt[r0 + i] = tv[i];
+      S.rowseq[r0 + i] = sv[i];
+      lu += (uint32_t)row_units(tv[i], P.bt_stride);
     }
   }
   uint32_t total;
@@ -335,19 +345,19 @@ struct HalfRegs {
 
 // Loads half `half` of the page behind `rsrc` (a raw buffer descriptor
 // covering the page, or with zero records when the half is absent: then
-// every load is out of range, reads nothing and returns 0).  off_d / off_s
-// are the lane's fixed byte offsets of its first code bytes and scale byte.
-__device__ __forceinline__ void load_half(__amdgpu_buffer_rsrc_t rsrc, int half, uint32_t off_d,
-                                          uint32_t off_s, HalfRegs& hr) {
-  const uint32_t od = off_d + (uint32_t)half * 32 * kIdxDim;
-  const uint32_t os = off_s + (uint32_t)(kKScaleOff + half * 128);
+// every load is out of range, reads nothing and returns 0).  The page's
+// tile layout makes each of the four code loads one contiguous kilobyte
+// (16 bytes at 16 * lane) and each scale load 64 contiguous bytes.
+__device__ __forceinline__ void load_half(__amdgpu_buffer_rsrc_t rsrc, int half, HalfRegs& hr) {
+  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int jj = 0; jj < 2; ++jj) {
-    const v4u a = __builtin_amdgcn_raw_buffer_load_b128(rsrc, od + jj * 16 * kIdxDim, 0, 0);
-    const v4u b = __builtin_amdgcn_raw_buffer_load_b128(rsrc, od + jj * 16 * kIdxDim + 64, 0, 0);
+    const int o = 32 * half + 16 * jj + r;   // the lane's token in the page
+    const v4u a = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (uint32_t)k_code_off(o, 16 * g), 0, 0);
+    const v4u b = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (uint32_t)k_code_off(o, 64 + 16 * g), 0, 0);
     hr.d[2 * jj] = make_uint4(a[0], a[1], a[2], a[3]);
     hr.d[2 * jj + 1] = make_uint4(b[0], b[1], b[2], b[3]);
-    hr.s[jj] = __builtin_amdgcn_raw_buffer_load_b8(rsrc, os + jj * 64, 0, 0);
+    hr.s[jj] = __builtin_amdgcn_raw_buffer_load_b8(rsrc, (uint32_t)k_scale_off(o, g), 0, 0);
   }
 }
 
@@ -452,7 +462,6 @@ __device__ __forceinline__ int32_t unit_pages(const Params& P, const Unit& U, in
 // whether the half exists.
 __device__ __forceinline__ bool fetch_half(const Params& P, const Unit& U, int32_t pid, int h,
                                            HalfRegs& b, bool* bad) {
-  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const bool want = h < 2 * (U.pg1 - U.pg0) && U.t >= 0;
   const int32_t raw = __builtin_amdgcn_readlane(pid, (h >> 1) & 63);
   const bool inpool = raw >= 0 && (int64_t)raw < P.pool_pages;
@@ -462,7 +471,7 @@ __device__ __forceinline__ bool fetch_half(const Params& P, const Unit& U, int32
   const uint8_t* page = P.kpool + (int64_t)(ok ? id : 0) * kKPageBytes;
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(page), (short)0, ok ? kKPageBytes : 0, kRawBufferWord3);
-  load_half(rsrc, h & 1, (uint32_t)(r * kIdxDim + 16 * g), (uint32_t)(r * 4 + g), b);
+  load_half(rsrc, h & 1, b);
   return ok;
 }
 
@@ -715,6 +724,7 @@ __device__ __forceinline__ uint32_t quant_group32(const uint32_t (&w)[16], uint3
 struct RowIn {
   uint32_t q[16];
   uint32_t k[16];
+  int64_t slot;        // the row's new-token slot
   bool qlive, knew;
 };
 
@@ -726,12 +736,29 @@ __device__ __forceinline__ void load_words32(const uint16_t* src, uint32_t (&w)[
   }
 }
 
+// Every load is unconditional (threads without a query group or key group
+// address past a buffer descriptor's end and read zeros), so the compiler's
+// wait counting stays exact and waiting for these never waits for younger
+// loads.
 __device__ __forceinline__ void row_in_load(const Params& P, int row, RowIn& in) {
   const int t = threadIdx.x, h = t >> 2, grp = t & 3;
+  row = __builtin_amdgcn_readfirstlane(row);
   in.qlive = h < P.H;
-  if (in.qlive) load_words32(P.q_bf16 + ((int64_t)row * P.H + h) * kIdxDim + 32 * grp, in.q);
-  in.knew = t < 4 && has_new_token(P, row);
-  if (in.knew) load_words32(P.k_new + (int64_t)row * kIdxDim + 32 * t, in.k);
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(P.q_bf16 + (int64_t)row * P.H * kIdxDim), (short)0, P.H * kIdxDim * 2, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(P.k_new + (int64_t)row * kIdxDim), (short)0, kIdxDim * 2, kRawBufferWord3);
+  const uint32_t oq = in.qlive ? (uint32_t)((h * kIdxDim + 32 * grp) * 2) : 0x7FFFF000u;
+  const uint32_t ok = t < 4 ? (uint32_t)(64 * t) : 0x7FFFF000u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const v4u a = __builtin_amdgcn_raw_buffer_load_b128(rq, oq + 16 * j, 0, 0);
+    const v4u b = __builtin_amdgcn_raw_buffer_load_b128(rk, ok + 16 * j, 0, 0);
+    in.q[4 * j] = a[0]; in.q[4 * j + 1] = a[1]; in.q[4 * j + 2] = a[2]; in.q[4 * j + 3] = a[3];
+    in.k[4 * j] = b[0]; in.k[4 * j + 1] = b[1]; in.k[4 * j + 2] = b[2]; in.k[4 * j + 3] = b[3];
+  }
+  in.slot = P.new_slot[row];
+  in.knew = t < 4 && in.slot >= 0 && in.slot < P.pool_pages * kPage;
 }
 
 // The row's query codes and scales (heads >= H: zeros, as the out-of-range
@@ -833,26 +860,30 @@ __device__ __forceinline__ void fused_row(const Params& P, int row, int uir, con
 // issued); the work-group holding a row's first unit also writes the row's
 // quantised queries to the workspace for the select's rescoring path; and
 // the new token's score is computed from its LDS copy.
+// Fused launches: the last P.extra_wgs work-groups write the step's new
+// indexer keys and KV records into the caches, one token per wave (later
+// launches read them; the scan scores each new key from its own copy).  They
+// come last in the grid, so they never hold a slot a scan work-group waits
+// for at the start.
+__device__ __forceinline__ void write_new_tokens(const Params& P, int scan_wgs) {
+  const int lane = threadIdx.x & 63;
+  const int r = ((int)blockIdx.x - scan_wgs) * kScanWaves + (int)(threadIdx.x >> 6);
+  if (r < P.R) {
+    const int64_t pool_slots = P.pool_pages * kPage;
+    mxfp8_quant_range(lane < 16 ? lane : 16, 16, P.k_new + (int64_t)r * kIdxDim, 1, kIdxDim,
+                      nullptr, nullptr, P.kpool_w, P.new_slot + r, pool_slots);
+    kv_quant_range(0, 1, P.kv_new + (int64_t)r * kQK, 1, P.new_slot + r, P.kvpool_w, pool_slots);
+  }
+}
+
 template <int NHT, bool FUSED>
 __global__ __launch_bounds__(kScanThreads, 2) void indexer_scan_kernel(Params P) {
   __shared__ ScanSmem S;
   __shared__ typename std::conditional<FUSED, FusedSmem, NoSmem>::type F;
-  // fused: the last P.extra_wgs work-groups write the step's new indexer
-  // keys and KV records into the caches, one token per wave (later launches
-  // read them; the scan scores each new key from its own LDS copy).  They
-  // come last in the grid, so they never hold a slot a scan work-group waits
-  // for at the start.
   const int scan_wgs = (int)gridDim.x - (FUSED ? P.extra_wgs : 0);
   if constexpr (FUSED) {
     if ((int)blockIdx.x >= scan_wgs) {
-      const int lane = threadIdx.x & 63;
-      const int r = ((int)blockIdx.x - scan_wgs) * kScanWaves + (int)(threadIdx.x >> 6);
-      if (r < P.R) {
-        const int64_t pool_slots = P.pool_pages * kPage;
-        mxfp8_quant_range(lane < 16 ? lane : 16, 16, P.k_new + (int64_t)r * kIdxDim, 1, kIdxDim,
-                          nullptr, nullptr, P.kpool_w, P.new_slot + r, pool_slots);
-        kv_quant_range(0, 1, P.kv_new + (int64_t)r * kQK, 1, P.new_slot + r, P.kvpool_w, pool_slots);
-      }
+      write_new_tokens(P, scan_wgs);
       return;
     }
   }
@@ -903,7 +934,7 @@ __global__ __launch_bounds__(kScanThreads, 2) void indexer_scan_kernel(Params P)
       // h % 4, lane tok % 16), so program order puts it last; a key of 0
       // (the page is absent) stays 0
       const int tl = U.t - U.pg0 * kPage;
-      if (tl >= 0 && U.t < U.pg1 * kPage && has_new_token(P, U.row)) {
+      if (tl >= 0 && U.t < U.pg1 * kPage && in.slot >= 0 && in.slot < P.pool_pages * kPage) {
         const float ns = new_token_score<NHT>(Q, F);
         if (wv == ((tl >> 5) & (kScanWaves - 1)) && (threadIdx.x & 63) == (tl & 15) &&
             S.keys[tl] != 0u)
@@ -1774,9 +1805,10 @@ __global__ __launch_bounds__(kSelThreads, 1) void indexer_select_kernel(Params P
 //
 // The rows of a chunked prefill (or the several query tokens of one sequence)
 // read the same K pages.  A work-group takes a tile of kTileRows consecutive
-// rows; each page is copied once into an LDS ring (global_load_lds, kPgRing
-// pages, kPgAhead ahead; each lane's 16-byte source is chosen so that token
-// rows land 144 bytes apart) and every wave scores it for its two rows, whose
+// rows; each page is copied once, as it is in the cache, into an LDS ring
+// (global_load_lds, kPgRing pages, kPgAhead ahead; the page's tile layout
+// puts every operand chunk a lane reads at 16 * lane of a contiguous
+// kilobyte, free of bank conflicts) and every wave scores it for its two rows, whose
 // query operands stay in registers.  Lane l ends a page with the key of
 // position 64p + l of each of its rows, so after the 16 pages of a unit a
 // row's 1024 keys sit 16 per lane in position order: the wave runs the
@@ -1807,13 +1839,9 @@ constexpr int kPgAhead = kPgRing - 1;                  // pages copied ahead
 #define DSA_PG_WAIT_AFTER_FILTER 42
 #define DSA_STR2(x) #x
 #define DSA_STR(x) DSA_STR2(x)
-// A page in LDS: token rows of 144 bytes (128 code bytes + 16 bytes of
-// padding, so that the 16 token rows one MFMA operand reads fall on distinct
-// banks), then the 256 scale bytes.  Counted in 16-byte granules:
-constexpr int kTokGran = kIdxDim / 16 + 1;             // 9 per token row
-constexpr int kScaleGran0 = kPage * kTokGran;          // 576: first scale granule
-constexpr int kPgGran = kScaleGran0 + kPage * 4 / 16;  // 592
-constexpr int kPgBlocks = (kPgGran + 63) / 64;         // 10 one-KB copy blocks per page
+// A page in LDS: its 8448 bytes as in the cache, counted in 16-byte granules
+constexpr int kPgGran = kKPageBytes / 16;              // 528
+constexpr int kPgBlocks = (kPgGran + 63) / 64;         // 9 one-KB copy blocks per page
 constexpr int kPgDmaPerWave = (kPgBlocks + kWaves - 1) / kWaves;   // 3
 constexpr int kPgBytes = kPgBlocks * 1024;
 constexpr int kTileMaxPages = 4096;                    // page ids of a tile held in LDS
@@ -2000,12 +2028,9 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_tile_kernel(Params P) {
 #pragma unroll
       for (int m = 0; m < kPgDmaPerWave; ++m) {
         const int j = wv + kWaves * m;                             // copy block
-        const int gs = 64 * j + lane;                              // LDS granule of this lane
-        const int tok = gs / kTokGran, c = gs - tok * kTokGran;
-        // source granule: a code granule, a scale granule, or (padding) any
-        const int src_g = gs < kScaleGran0 ? (c < kIdxDim / 16 ? tok * (kIdxDim / 16) + c : 0)
-                                           : (gs < kPgGran ? kKScaleOff / 16 + (gs - kScaleGran0) : 0);
-        dma16(page + 16 * src_g, live && j < kPgBlocks ? base + (uint32_t)(j * 1024) : junk);
+        const int gs = 64 * j + lane;                              // granule of this lane
+        // past the page's end (the last block's padding lanes): any granule
+        dma16(page + 16 * (gs < kPgGran ? gs : 0), live && j < kPgBlocks ? base + (uint32_t)(j * 1024) : junk);
       }
     };
 #pragma unroll
@@ -2034,10 +2059,10 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_tile_kernel(Params P) {
         const bool pok = S.pt[p] >= 0;
         // Token tile j's key operand: two 16-byte reads and a scale byte.
         auto operand = [&](int j, v8i& kv, int& ks) {
-          const uint8_t* tok = pg + (16 * j + hr) * (16 * kTokGran) + 16 * g;
-          const uint4 lo = *reinterpret_cast<const uint4*>(tok);
-          const uint4 hi = *reinterpret_cast<const uint4*>(tok + 64);
-          ks = (int)pg[16 * kScaleGran0 + (16 * j + hr) * 4 + g];
+          const int o = 16 * j + hr;
+          const uint4 lo = *reinterpret_cast<const uint4*>(pg + k_code_off(o, 16 * g));
+          const uint4 hi = *reinterpret_cast<const uint4*>(pg + k_code_off(o, 64 + 16 * g));
+          ks = (int)pg[k_scale_off(o, g)];
           kv = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         };
@@ -2090,6 +2115,315 @@ static_assert(kTileRowsPerWave * kTileStores + kPgDmaPerWave * (kPgAhead - 1) ==
 static_assert(kPgDmaPerWave * (kPgAhead - 1) == DSA_PG_WAIT, "the page loop's wait");
 static_assert(DSA_PG_WAIT_AFTER_FILTER < 64, "vmcnt holds 6 bits");
 
+// ---- per-row scan, one wave per unit ---------------------------------------------
+//
+// The launch form for many units (long contexts or large batches: more units
+// than the work-group scan above has resident work-groups).  Every wave takes
+// its own contiguous run of units and scores all 16 pages of a unit by itself
+// through a four-deep register ring of half pages that runs across unit
+// boundaries.  Per page, the partial head sums of its four token tiles are
+// combined by rows_sum_scatter (associated as rows_sum, so the keys are the
+// work-group scan's bits) so that lane l ends with the key of position
+// 64p + l; after the unit's 16 pages the wave runs the local filter on its
+// registers (wave_edge) and writes the candidates, count and edge
+// (emit_wave).  No LDS and no work-group barrier after the row plan, and each
+// unit's filter runs once, on the wave that scored it.
+//
+// FUSED: each wave quantises the queries of its row and the row's new key in
+// registers.  A lane holds, per operand row, the 16-dim pieces 16g..16g+15 and
+// 64+16g..64+16g+15; the other half of each 32-dim group lies 16 lanes away
+// and the group whose scale the lane supplies to the MFMA (dims 32g..32g+31)
+// was reduced 32 lanes away for g = 1, 2.  Exponent and conversion are the
+// quantisers', so the codes are the bytes mxfp8_quant writes.
+
+// The unit's edge: the work-group scan's filter_unit search on a wave's keys.
+__device__ __forceinline__ uint32_t wave_edge(const Params& P, const Unit& U,
+                                              const uint32_t (&k)[kUnitPages]) {
+  const int ntok = (U.pg1 - U.pg0) * kPage;
+  const uint32_t quota = unit_quota(U.t, P.topk);
+  if (quota >= (uint32_t)ntok) return 0u;
+  if (quota <= kTop3Quota) {
+    uint32_t m[3];
+    lane_top<3>(k, m);
+    return key_floor<3>(m, quota);
+  }
+  if (quota <= kTop5Quota) {
+    uint32_t m[5];
+    lane_top<5>(k, m);
+    return key_floor<5>(m, quota);
+  }
+  return key_floor<kUnitPages>(k, quota);
+}
+
+// MXFP8 codes (MFMA operand order) and the E8M0 byte of dims 32g..32g+31 of
+// one operand row whose 32 bf16 values this lane holds as pieces: w[0..7]
+// dims 16g..16g+15, w[8..15] dims 64+16g..64+16g+15 (g = lane/16).  Every
+// lane of the wave must take part.  A row that is not live gets zero codes
+// and scale byte 0.
+__device__ __forceinline__ void quant_operand_row(const uint32_t (&w)[16], bool live, v8i& codes,
+                                                  int& sbyte) {
+  const int g = (threadIdx.x & 63) >> 4;
+  int e[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(w[8 * p + j] & 0xFFFFu)),
+                               fabsf(bf16_bits_to_f32(w[8 * p + j] >> 16))));
+    // piece p is half of group p ? 2 + g/2 : g/2; the other half is 16 lanes away
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    e[p] = mx_exponent(amax);
+  }
+  // the lane supplies group g: lanes g = 0 and 3 reduced it themselves
+  // (piece 0 and piece 1); g = 1 takes group 1 from g = 3 (its piece 0) and
+  // g = 2 takes group 2 from g = 0 (its piece 1), 32 lanes away
+  const int send = g < 2 ? e[1] : e[0];
+  const int recv = __shfl_xor(send, 32);
+  const int eg = g == 0 ? e[0] : (g == 3 ? e[1] : recv);
+  sbyte = live ? eg + 127 : 0;
+  int c[8];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const float inv = pow2f(-e[p]);
+    // |v * inv| <= 448 by the scale rule: the hardware conversion applies
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t a = w[8 * p + 2 * d], b = w[8 * p + 2 * d + 1];
+      const uint32_t q = e4m3x4_in_range(bf16_bits_to_f32(a & 0xFFFFu) * inv, bf16_bits_to_f32(a >> 16) * inv,
+                                         bf16_bits_to_f32(b & 0xFFFFu) * inv, bf16_bits_to_f32(b >> 16) * inv);
+      c[4 * p + d] = live ? (int)q : 0;
+    }
+  }
+  codes = v8i{c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[7]};
+}
+
+// The lane's two 16-dim pieces of a 128-dim bf16 row at byte offset `off` of
+// the buffer behind `rsrc` (out of range: zeros).
+__device__ __forceinline__ void load_pieces(__amdgpu_buffer_rsrc_t rsrc, uint32_t off, uint32_t (&w)[16]) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + (uint32_t)(2 * (64 * p + 16 * g) + 16 * j), 0, 0);
+      w[8 * p + 4 * j] = v[0]; w[8 * p + 4 * j + 1] = v[1];
+      w[8 * p + 4 * j + 2] = v[2]; w[8 * p + 4 * j + 3] = v[3];
+    }
+}
+
+// Fused path, at the first unit of a row: the row's query operand from its
+// bf16 queries, the head weights, and the row's new key as the key operand of
+// a token tile whose 16 columns all carry it.  The wave holding the row's
+// first unit writes the quantised queries to the workspace for the select's
+// rescoring path.  Returns whether the row brings a new token.
+template <int NHT>
+__device__ __forceinline__ bool fused_row_regs(const Params& P, int row, int uir, QOperand<NHT>& Q,
+                                               v8i& kn, int& ksn) {
+  const int lane = threadIdx.x & 63, hr = lane & 15, g = lane >> 4;
+  row = __builtin_amdgcn_readfirstlane(row);
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(P.q_bf16 + (int64_t)row * P.H * kIdxDim), (short)0, P.H * kIdxDim * 2, kRawBufferWord3);
+  const bool knew = has_new_token(P, row);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(P.k_new + (int64_t)row * kIdxDim), (short)0, knew ? kIdxDim * 2 : 0, kRawBufferWord3);
+  uint32_t wq[NHT][16], wk[16];
+#pragma unroll
+  for (int i = 0; i < NHT; ++i) {
+    const int h = 16 * i + hr;
+    load_pieces(rq, h < P.H ? (uint32_t)(h * kIdxDim * 2) : 0x7FFFF000u, wq[i]);
+  }
+  load_pieces(rk, 0u, wk);
+  quant_operand_row(wk, true, kn, ksn);
+#pragma unroll
+  for (int i = 0; i < NHT; ++i) quant_operand_row(wq[i], 16 * i + hr < P.H, Q.a[i], Q.s[i]);
+  // the head weights after the raw queries are consumed (fewer live registers)
+  load_w<NHT>(P, row, Q);
+  if (uir == 0) {
+#pragma unroll
+    for (int i = 0; i < NHT; ++i) {
+      const int h = 16 * i + hr;
+      if (h < P.H) {
+        uint8_t* dst = P.q_ws + ((int64_t)row * P.H + h) * kIdxDim;
+        *reinterpret_cast<uint4*>(dst + 16 * g) =
+            make_uint4((uint32_t)Q.a[i][0], (uint32_t)Q.a[i][1], (uint32_t)Q.a[i][2], (uint32_t)Q.a[i][3]);
+        *reinterpret_cast<uint4*>(dst + 64 + 16 * g) =
+            make_uint4((uint32_t)Q.a[i][4], (uint32_t)Q.a[i][5], (uint32_t)Q.a[i][6], (uint32_t)Q.a[i][7]);
+        P.qs_ws[((int64_t)row * P.H + h) * 4 + g] = (uint8_t)Q.s[i];
+      }
+    }
+  }
+  return knew;
+}
+
+// ONE: the launch guarantees at most one unit per wave (the unit bound is
+// within four per work-group), so there is no next unit to prefetch and no
+// row change: fewer live registers through the scoring loop.
+template <int NHT, bool FUSED, bool ONE>
+__global__ __launch_bounds__(kScanThreads, 2) void indexer_wave_kernel(Params P) {
+  __shared__ ScanSmem S;
+  __shared__ typename std::conditional<FUSED, FusedSmem, NoSmem>::type F;
+  const int scan_wgs = (int)gridDim.x - (FUSED ? P.extra_wgs : 0);
+  if constexpr (FUSED) {
+    if ((int)blockIdx.x >= scan_wgs) {
+      write_new_tokens(P, scan_wgs);
+      return;
+    }
+  }
+  plan_rows<kScanThreads>(P, S);   // ends with a barrier
+  const uint32_t U_total = S.rowpre[P.R];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t nw = (uint32_t)scan_wgs * kScanWaves;
+  const uint32_t per = (U_total + nw - 1) / nw;
+  const uint32_t u_wg = (uint32_t)blockIdx.x * kScanWaves * per;   // wave 0's first unit
+  if (u_wg >= U_total) return;   // no wave of the work-group has a unit (uniform)
+  uint32_t u = u_wg + (uint32_t)wv * per;
+  const uint32_t uend = min(U_total, u + per);
+  const bool has = u < uend;
+  bool bad = false;        // a page id out of the pool (flagged once at the end)
+  Unit U = decode_unit(P, S, has ? u : u_wg);
+  // fused: the slot of the wave's row's new token, requested first
+  const int64_t nslot = FUSED ? P.new_slot[U.row] : -1;
+  int32_t pid = unit_pages(P, U, S.rowseq[U.row]);
+  QOperand<NHT> Q;
+  v8i kn = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  int ksn = 0;
+  // key of the row's new token, scored once per row; 0 when the row brings
+  // none (no finite score has key 0).  One scalar through the loop.
+  uint32_t nkey = 0u;
+  HalfRegs b[kRing];
+  bool ok[kRing];
+  if constexpr (FUSED) {
+    // The work-group quantises the rows of its waves' first units into LDS,
+    // one row at a time (one 32-value group per thread; usually all four
+    // waves start in one row), while the waves' rings are in flight; each
+    // wave takes its operands from the copy of its row.  The work-group that
+    // holds a row's first unit writes the row's quantised queries to the
+    // workspace for the select.
+    // The first row's inputs and the head weights are requested before the
+    // ring, so waiting for them never waits for the ring.
+    // Issued by every wave (one without a unit gets page id -1 loads that
+    // move nothing): conditional loads would leave the compiler's wait
+    // counts inexact, and the waits below would then wait for the ring.
+    RowIn in;
+    row_in_load(P, decode_unit(P, S, u_wg).row, in);
+    load_w<NHT>(P, U.row, Q);
+    __builtin_amdgcn_sched_barrier(0);   // keep these loads ahead of the ring's
+    {
+      Unit Ur = U;
+      if (!has) Ur.t = -1;
+#pragma unroll
+      for (int k = 0; k < kRing; ++k) ok[k] = fetch_half(P, Ur, pid, k, b[k], &bad);
+    }
+    for (int w = 0; w < kScanWaves; ++w) {   // uniform over the work-group
+      const uint32_t uw = u_wg + (uint32_t)w * per;
+      if (uw >= U_total) break;
+      const Unit Uw = decode_unit(P, S, uw);
+      bool seen = false;                     // an earlier wave starts in this row
+      for (int w2 = 0; w2 < w; ++w2) seen |= decode_unit(P, S, u_wg + (uint32_t)w2 * per).row == Uw.row;
+      if (seen) continue;
+      if (w > 0) row_in_load(P, Uw.row, in);
+      row_in_store(in, F);
+      __syncthreads();
+      if (Uw.uir == 0) {
+        const int t = threadIdx.x;
+        if (t * 32 < P.H * kIdxDim) {
+          uint4* dst = reinterpret_cast<uint4*>(P.q_ws + (int64_t)Uw.row * P.H * kIdxDim + t * 32);
+          const uint4* src = reinterpret_cast<const uint4*>(F.qc + t * 32);
+          dst[0] = src[0];
+          dst[1] = src[1];
+        }
+        if (t < P.H * 4) P.qs_ws[(int64_t)Uw.row * P.H * 4 + t] = F.qsc[t];
+      }
+      if (has && U.row == Uw.row) {
+        load_q_codes_lds<NHT>(F, Q);
+        const int g = lane >> 4;
+        const uint4 lo = *reinterpret_cast<const uint4*>(F.kc + 16 * g);
+        const uint4 hi = *reinterpret_cast<const uint4*>(F.kc + 64 + 16 * g);
+        kn = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        ksn = (int)F.ksc[g];
+      }
+      __syncthreads();   // every wave has its copy before the next row overwrites it
+    }
+    if (!has) return;    // no barrier follows
+    if (nslot >= 0 && nslot < P.pool_pages * kPage)
+      nkey = __builtin_amdgcn_readfirstlane(score_key(rows_sum(head_part<NHT>(Q, kn, ksn))));
+  } else {
+    if (!has) return;
+#pragma unroll
+    for (int k = 0; k < kRing; ++k) ok[k] = fetch_half(P, U, pid, k, b[k], &bad);
+    load_q<NHT>(P, U.row, Q);
+  }
+  int qrow = U.row;
+  for (;;) {
+    const bool more = !ONE && u + 1 < uend;
+    // the next unit (the current one again when there is none: its ring
+    // loads then get page id -1 and move nothing).  Fused: a next unit of
+    // another row is not prefetched either; its ring is issued after that
+    // row's quantisation.
+    const Unit V = ONE ? U : decode_unit(P, S, more ? u + 1 : u);
+    const int32_t pidn = ONE ? pid : unit_pages(P, V, S.rowseq[V.row]);
+    Unit Vf = V;
+    if (!more || (FUSED && V.row != U.row)) Vf.t = -1;
+    uint32_t key[kUnitPages];
+#pragma unroll
+    for (int pi = 0; pi < kUnitPages; ++pi) {
+      float part[4];
+      bool pok = false;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int h = 2 * pi + hh, sl = h % kRing;
+        pok = ok[sl];   // both halves of a page are present or absent together
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const uint4 lo = b[sl].d[2 * jj], hi = b[sl].d[2 * jj + 1];
+          const v8i kb = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          part[2 * hh + jj] = head_part<NHT>(Q, kb, (int)b[sl].s[jj]);
+        }
+        const int hn = h + kRing;
+        if (hn < 2 * kUnitPages)
+          ok[sl] = fetch_half(P, U, pid, hn, b[sl], &bad);
+        else if (!ONE)
+          ok[sl] = fetch_half(P, Vf, pidn, hn - 2 * kUnitPages, b[sl], &bad);
+      }
+      // lane group j receives token tile j: lane l holds position 64p + l
+      const float sc = rows_sum_scatter(part);
+      const int pos = (U.pg0 + pi) * kPage + lane;
+      key[pi] = pok && pos <= U.t ? score_key(sc) : 0u;
+    }
+    if constexpr (FUSED) {
+      // the new token's key, when it lies in this unit, from the wave's own
+      // quantisation (the cache slot at t is written by this launch); a key
+      // of 0 (the page is absent) stays 0
+      const int tl = U.t - U.pg0 * kPage;
+      if (nkey != 0u && tl >= 0 && U.t < U.pg1 * kPage) {
+#pragma unroll
+        for (int pi = 0; pi < kUnitPages; ++pi)
+          if (pi == (tl >> 6) && lane == (tl & 63) && key[pi] != 0u) key[pi] = nkey;
+      }
+    }
+    emit_wave(P, U.row, true, row_pages(U.t, P.bt_stride), U.uir, key, wave_edge(P, U, key));
+    if (ONE || !more) break;
+    if (V.row != qrow) {
+      if constexpr (FUSED) {
+        const bool knew = fused_row_regs<NHT>(P, V.row, V.uir, Q, kn, ksn);
+        nkey = knew ? __builtin_amdgcn_readfirstlane(score_key(rows_sum(head_part<NHT>(Q, kn, ksn)))) : 0u;
+#pragma unroll
+        for (int k = 0; k < kRing; ++k) ok[k] = fetch_half(P, V, pidn, k, b[k], &bad);
+      } else {
+        load_q<NHT>(P, V.row, Q);
+      }
+      qrow = V.row;
+    }
+    U = V;
+    pid = pidn;
+    ++u;
+  }
+  if (bad && lane == 0) flag_error(P.hdr, kErrBadPage);
+}
+
 // ---- host side ----------------------------------------------------------------
 
 struct Layout {
@@ -2116,13 +2450,18 @@ Layout layout_for(int64_t rows, int64_t bt_stride) {
   return L;
 }
 
-enum KernelKind { kScan = 0, kSelect = 1, kDump = 2, kSelectShort = 3, kScanFused = 4 };
+enum KernelKind { kScan = 0, kSelect = 1, kDump = 2, kSelectShort = 3, kScanFused = 4, kWave = 5,
+                  kWaveFused = 6, kWaveOne = 7, kWaveOneFused = 8 };
 
 template <int NHT>
 void* pick_kernel_t(KernelKind kind) {
   switch (kind) {
     case kScan: return (void*)&indexer_scan_kernel<NHT, false>;
     case kScanFused: return (void*)&indexer_scan_kernel<NHT, true>;
+    case kWave: return (void*)&indexer_wave_kernel<NHT, false, false>;
+    case kWaveFused: return (void*)&indexer_wave_kernel<NHT, true, false>;
+    case kWaveOne: return (void*)&indexer_wave_kernel<NHT, false, true>;
+    case kWaveOneFused: return (void*)&indexer_wave_kernel<NHT, true, true>;
     case kSelect: return (void*)&indexer_select_kernel<NHT, false>;
     case kSelectShort: return (void*)&indexer_select_kernel<NHT, true>;
     default: return (void*)&indexer_dump_kernel<NHT>;
@@ -2152,7 +2491,7 @@ void* pick_tile_kernel(int nht, bool two) {
 // same time both compute the same value and store it, so no lock is needed
 // and a reader never sees a torn value (0 = not computed yet).
 constexpr int kCapDevices = 64;
-constexpr int kCapSlots = 24;
+constexpr int kCapSlots = 40;
 std::atomic<int> g_capacity[kCapDevices][kCapSlots];
 
 int resident_capacity(void* fn, int slot, int threads) {
@@ -2195,6 +2534,14 @@ int run(Params P, bool dump, hipStream_t stream, bool fused = false) {
   if (cap <= 0) return DSA_ERR_HIP;
   const int R = P.R;
   const int upr = units_stride(P.bt_stride);
+  // Launches with more units than the work-group scan has resident
+  // work-groups (bounded by rows x the block table's units) take the
+  // one-wave-per-unit scan; smaller ones keep four waves on every unit.
+  void* wave = pick_kernel(nht, fused ? kWaveFused : kWave);
+  void* wave1 = pick_kernel(nht, fused ? kWaveOneFused : kWaveOne);
+  const int wave_cap = dump ? 0 : resident_capacity(wave, (fused ? 28 : 24) + nht - 1, kScanThreads);
+  const int wave1_cap = dump ? 0 : resident_capacity(wave1, (fused ? 36 : 32) + nht - 1, kScanThreads);
+  if (!dump && (wave_cap <= 0 || wave1_cap <= 0)) return DSA_ERR_HIP;
   for (int r0 = 0; r0 < R; r0 += kMaxRows) {
     Params Q = P;
     const int rn = std::min(kMaxRows, R - r0);
@@ -2218,10 +2565,18 @@ int run(Params P, bool dump, hipStream_t stream, bool fused = false) {
       Q.out_idx = P.out_idx + (int64_t)r0 * P.topk;
       Q.out_score = P.out_score ? P.out_score + (int64_t)r0 * P.topk : nullptr;
     }
-    const int64_t G = std::min<int64_t>((int64_t)cap, (int64_t)rn * upr);
+    const int64_t units = (int64_t)rn * upr;
+    const bool by_wave = !dump && units > cap;
+    // a unit per wave at most: the grid has a wave for every unit the block
+    // table allows
+    const bool one = by_wave && units <= (int64_t)kScanWaves * wave1_cap;
+    const int64_t G = one ? (units + kScanWaves - 1) / kScanWaves
+                    : by_wave ? std::min<int64_t>((int64_t)wave_cap, (units + kScanWaves - 1) / kScanWaves)
+                              : std::min<int64_t>((int64_t)cap, units);
     Q.extra_wgs = fused ? (rn + kScanWaves - 1) / kScanWaves : 0;
     void* args[] = {&Q};
-    if (hipLaunchKernel(scan, dim3((unsigned)(G + Q.extra_wgs)), dim3(scan_threads), args, 0, stream) != hipSuccess)
+    if (hipLaunchKernel(one ? wave1 : by_wave ? wave : scan, dim3((unsigned)(G + Q.extra_wgs)),
+                        dim3(scan_threads), args, 0, stream) != hipSuccess)
       return DSA_ERR_HIP;
     if (!dump && hipLaunchKernel(sel, dim3((unsigned)rn), dim3(kSelThreads), args, 0, stream) != hipSuccess)
       return DSA_ERR_HIP;

@@ -54,8 +54,8 @@ __device__ __forceinline__ void mxfp8_quant_range(
       if (slot < 0 || slot >= pool_slots) continue;
       uint8_t* page = kpool + (slot >> 6) * (int64_t)kKPageBytes;
       const int off = (int)(slot & 63);
-      *reinterpret_cast<uint2*>(page + off * kIdxDim + c8 * 8) = make_uint2(lo, hi);
-      if ((c8 & 3) == 0) page[kKScaleOff + off * 4 + (c8 >> 2)] = sbyte;
+      *reinterpret_cast<uint2*>(page + k_code_off(off, c8 * 8)) = make_uint2(lo, hi);
+      if ((c8 & 3) == 0) page[k_scale_off(off, c8 >> 2)] = sbyte;
     }
   }
 }

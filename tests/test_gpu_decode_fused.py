@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import pools
 from oracle.pipeline import Oracle
 from sparse_attention_decode_topk_amd import ops, synth
 from tests.dsa_state import DeviceState, bf16_tensor, check_topk_row, say
@@ -23,8 +24,10 @@ def _stale(st, slots, seed):
         if s < 0 or s >= st.pages * 64:
             continue
         p, o = divmod(int(s), 64)
-        kp[p, o * 128:(o + 1) * 128] = torch.from_numpy(rng.integers(0, 256, 128, dtype=np.uint8)).cuda()
-        kp[p, 8192 + o * 4:8192 + o * 4 + 4] = torch.from_numpy(rng.integers(100, 140, 4, dtype=np.uint8)).cuda()
+        kp[p, torch.from_numpy(pools.K_CODE_OFF[o]).cuda()] = \
+            torch.from_numpy(rng.integers(0, 256, 128, dtype=np.uint8)).cuda()
+        kp[p, torch.from_numpy(pools.K_SCALE_OFF[o]).cuda()] = \
+            torch.from_numpy(rng.integers(100, 140, 4, dtype=np.uint8)).cuda()
         kvp[p, o * 656:(o + 1) * 656] = torch.from_numpy(rng.integers(0, 256, 656, dtype=np.uint8)).cuda()
     return kp, kvp
 
@@ -93,3 +96,84 @@ def test_fused_prolog_edge_rows(need_gpu):
     slots[4] = npages * 64 + 5
     for K in (300, 1):
         _run_both(st, inp, slots, K, f"edge rows K={K}")
+
+
+def _subset_matches_batch(st, inp, slots_np, K, nsub, tag):
+    """The first nsub rows launched alone (few enough units for the
+    work-group scan, four waves on every unit) against the same rows inside
+    the whole batch (enough units for the one-wave-per-unit scan): indices
+    and scores bit-equal, for dsa_indexer_topk and dsa_decode_indexer_topk."""
+    dev = st.dev
+    new_tok = inp["seq_starts"][inp["row_seq"]].astype(np.int64) + inp["row_pos"].astype(np.int64)
+    k_new = bf16_tensor(inp["k_idx"][new_tok], dev)
+    kv_new = bf16_tensor(inp["kv"][new_tok], dev)
+    q_bf = bf16_tensor(inp["q_idx"], dev)
+    slots = torch.from_numpy(slots_np).to(dev)
+    n = nsub
+    a_idx, a_sc = ops.dsa_indexer_topk(st.q_fp8, st.q_e8m0, st.w, st.k_pool, st.block_table,
+                                       st.row_seq, st.row_pos, K)
+    s_idx, s_sc = ops.dsa_indexer_topk(st.q_fp8[:n], st.q_e8m0[:n], st.w[:n], st.k_pool,
+                                       st.block_table, st.row_seq[:n], st.row_pos[:n], K)
+    kpa, kvpa = st.k_pool.clone(), st.kv_pool.clone()
+    b_idx, b_sc = ops.dsa_decode_indexer_topk(q_bf, st.w, k_new, kv_new, slots, kpa, kvpa,
+                                              st.block_table, st.row_seq, st.row_pos, K)
+    kpb, kvpb = st.k_pool.clone(), st.kv_pool.clone()
+    c_idx, c_sc = ops.dsa_decode_indexer_topk(q_bf[:n], st.w[:n], k_new[:n], kv_new[:n], slots[:n],
+                                              kpb, kvpb, st.block_table, st.row_seq[:n],
+                                              st.row_pos[:n], K)
+    torch.cuda.synchronize()
+    assert torch.equal(a_idx[:n], s_idx) and torch.equal(a_sc[:n], s_sc), f"{tag}: unfused"
+    assert torch.equal(b_idx[:n], c_idx) and torch.equal(b_sc[:n], c_sc), f"{tag}: fused"
+    assert torch.equal(a_idx, b_idx) and torch.equal(a_sc, b_sc), f"{tag}: fused vs unfused"
+    say(f"[scan forms] {tag}: {n} rows alone equal to the same rows in {st.R}")
+
+
+def test_wave_scan_matches_workgroup_scan(need_gpu):
+    """Ragged decode (64 heads, 32 rows of 4K-64K: 2048 units by the block
+    table's width) against its first 4 rows (256 units)."""
+    inp = synth.make("decode_ragged_b32")
+    st = DeviceState(inp)
+    new_tok = inp["seq_starts"] + inp["seq_lens"] - 1
+    _subset_matches_batch(st, inp, inp["slot_mapping"][new_tok].astype(np.int64), st.topk, 4,
+                          "ragged decode")
+
+
+def test_wave_scan_edge_rows(need_gpu):
+    """160 rows of 20 indexer heads (a partial head tile), lengths 1..4096
+    with new tokens at page offsets 0 and 63, rows without a new token (slot
+    -1, a slot past the pool) and Top-K of 300 and 1: the batch takes the
+    one-wave-per-unit scan (640 units), its first 8 rows the work-group scan."""
+    rng = np.random.default_rng(23)
+    B = 160
+    lens = rng.integers(1, 4097, B).astype(np.int32)
+    lens[:6] = [65, 128, 1000, 4096, 3333, 64]
+    lens[7] = 1
+    cfg = synth.Config(97, "wave_edge", batch=B, h_index=20, h_attn=16, topk=300,
+                       ragged=(int(lens.min()), int(lens.max())))
+    bt, slots_all, starts, npages = synth.page_tables(cfg, lens, rng)
+    assert bt.shape[1] == 64
+    inp = dict(seq_lens=lens, block_table=bt, slot_mapping=slots_all, seq_starts=starts,
+               total_pages=np.int64(npages), topk=np.int32(300),
+               row_seq=np.arange(B, dtype=np.int32), row_pos=(lens - 1).astype(np.int32),
+               q_idx=synth.f32_to_bf16_bits(rng.standard_normal((B, 20, 128)).astype(np.float32)),
+               k_idx=synth.f32_to_bf16_bits(rng.standard_normal((int(lens.sum()), 128)).astype(np.float32)),
+               w=(rng.standard_normal((B, 20)) / np.sqrt(20)).astype(np.float32),
+               q_sfa=synth.f32_to_bf16_bits(rng.standard_normal((B, 16, 576)).astype(np.float32)),
+               kv=synth.f32_to_bf16_bits(rng.standard_normal((int(lens.sum()), 576)).astype(np.float32)))
+    st = DeviceState(inp)
+    new_tok = starts.astype(np.int64) + (lens - 1).astype(np.int64)
+    slots = slots_all[new_tok].astype(np.int64)
+    slots[2] = -1
+    slots[4] = npages * 64 + 5
+    slots[100] = -1
+    for K in (300, 1):
+        _subset_matches_batch(st, inp, slots, K, 8, f"edge rows K={K}")
+    # the batch against the oracle on a few rows, the no-new-token ones included
+    idx, sc = ops.dsa_decode_indexer_topk(
+        bf16_tensor(inp["q_idx"], st.dev), st.w, bf16_tensor(inp["k_idx"][new_tok], st.dev),
+        bf16_tensor(inp["kv"][new_tok], st.dev), torch.from_numpy(slots).to(st.dev),
+        st.k_pool.clone(), st.kv_pool.clone(), st.block_table, st.row_seq, st.row_pos, 300)
+    gi, gs = idx.cpu().numpy(), sc.cpu().numpy()
+    o = Oracle(inp)
+    for r in (0, 2, 3, 4, 7, 100, B - 1):
+        check_topk_row(gi[r], gs[r], o.topk(r), 300, int(lens[r] - 1))

@@ -103,8 +103,8 @@ def test_big_pools_sampled(need_gpu, cfg):
     kp = kpool.cpu().numpy()
     for i, s in enumerate(sl):
         p, o = divmod(int(s), 64)
-        assert np.array_equal(kp[p, o * 128:(o + 1) * 128], codes[i])
-        assert np.array_equal(kp[p, 8192 + o * 4:8192 + o * 4 + 4], e8[i])
+        assert np.array_equal(kp[p, pools.K_CODE_OFF[o]], codes[i])
+        assert np.array_equal(kp[p, pools.K_SCALE_OFF[o]], e8[i])
     rec = quant.kv_quant(inp["kv"][tok])
     kvp = kvpool.view(npages * 64, 656)[torch.from_numpy(sl).cuda()].cpu().numpy()
     assert np.array_equal(kvp, rec)

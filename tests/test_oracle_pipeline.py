@@ -85,12 +85,32 @@ def test_kv_pool_read_hand_example():
 
 
 def test_k_pool_read_hand_example():
-    # the K page stores codes token-major, then 4 scale bytes per token:
-    # position 65 of block-table row [1, 0] is page 0, offset 1 -> code bytes
-    # [128, 256) and scale bytes [8196, 8200) of page 0
+    # position 65 of block-table row [1, 0] is page 0, offset 1: token 1 of
+    # the page's first 16-token tile.  Its codes sit in 16-byte pieces at
+    # 16*1 + 256*q (dims 16q..16q+15, q < 4) and 1024 + 16*1 + 256*q (dims
+    # 64+16q..), its scale bytes at 8192 + 16*b + 1
     pool = np.zeros((2, pools.K_PAGE_BYTES), dtype=np.uint8)
-    pool[0, 128:256] = 7
-    pool[0, 8192 + 4:8192 + 8] = [120, 121, 122, 123]
+    want = np.arange(128, dtype=np.uint8) + 1
+    for q in range(4):
+        pool[0, 16 + 256 * q:32 + 256 * q] = want[16 * q:16 * q + 16]
+        pool[0, 1040 + 256 * q:1056 + 256 * q] = want[64 + 16 * q:80 + 16 * q]
+    pool[0, [8193, 8209, 8225, 8241]] = [120, 121, 122, 123]
     c, x = pools.k_pool_read(pool, np.array([1, 0], dtype=np.int32), 66)
-    assert np.all(c[65] == 7) and x[65].tolist() == [120, 121, 122, 123]
-    assert np.all(c[:64] == 0) and np.all(x[:64] == 0)
+    assert np.array_equal(c[65], want) and x[65].tolist() == [120, 121, 122, 123]
+    assert np.all(c[:65] == 0) and np.all(x[:65] == 0)
+    # offset 50 (tile 3, token 2): dim 0 at 3*2048 + 32, scale 0 at 8192 + 3*64 + 2
+    assert pools.K_CODE_OFF[50, 0] == 6176 and pools.K_SCALE_OFF[50, 0] == 8386
+
+
+def test_k_page_layout_is_a_permutation():
+    # every byte of a page holds exactly one (token, code) or (token, scale)
+    offs = np.concatenate([pools.K_CODE_OFF.ravel(), pools.K_SCALE_OFF.ravel()])
+    assert np.array_equal(np.sort(offs), np.arange(pools.K_PAGE_BYTES))
+    # the 16-byte piece of dims 16g..16g+15 of tile token n is piece n + 16g
+    # of the tile's first kilobyte (dims 64+ of its second)
+    for o in (0, 17, 63):
+        j, n = divmod(o, 16)
+        for g in range(4):
+            assert pools.K_CODE_OFF[o, 16 * g] == 2048 * j + 16 * (n + 16 * g)
+            assert pools.K_CODE_OFF[o, 64 + 16 * g] == 2048 * j + 1024 + 16 * (n + 16 * g)
+            assert pools.K_SCALE_OFF[o, g] == 8192 + 64 * j + n + 16 * g

@@ -182,10 +182,14 @@ def test_k_pool_roundtrip_permuted():
         st = int(starts[b])
         assert np.array_equal(c, codes[st:st + lens[b]]) and np.array_equal(e, e8[st:st + lens[b]])
     # byte placement: token 65 of sequence 1 -> page bt[1][1], offset 1
+    # (tile 0, token 1): code pieces at 16 + 256q and 1040 + 256q, scale
+    # bytes at 8193 + 16b
     p = bt[1][1]
     st = int(starts[1])
-    assert np.array_equal(pool[p, 128:256], codes[st + 65])
-    assert np.array_equal(pool[p, 8192 + 4:8192 + 8], e8[st + 65])
+    for q in range(4):
+        assert np.array_equal(pool[p, 16 + 256 * q:32 + 256 * q], codes[st + 65][16 * q:16 * q + 16])
+        assert np.array_equal(pool[p, 1040 + 256 * q:1056 + 256 * q], codes[st + 65][64 + 16 * q:80 + 16 * q])
+    assert np.array_equal(pool[p, [8193, 8209, 8225, 8241]], e8[st + 65])
 
 
 def test_kv_pool_roundtrip_and_skip():
