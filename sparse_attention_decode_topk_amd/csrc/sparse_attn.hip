@@ -6,18 +6,19 @@
 //
 // One workgroup = (query row, group of 32 heads, split of the index list);
 // the groups of one (row, split) are placed on one XCD so the records they
-// all read are served by that XCD's L2.  Eight waves in two groups of four:
-// group G takes tile G (32 tokens) of every step of 64 tokens and keeps its
-// own softmax state; the groups are merged in LDS at the end, so two waves
-// share every SIMD and each hides the other's latencies.  In a group, wave
-// (ht, dh) owns head tile ht (16 heads) and latent half dh (256 of the 512
-// dims, plus half of the rope dims).
+// all read are served by that XCD's L2.  The waves form G groups of four
+// (G = 2, or G = 3 for an unsplit list of at least 1024 entries): group g
+// takes tile g (32 tokens) of every step of 32G tokens and keeps its own
+// softmax state; the groups are merged in LDS at the end, so G waves share
+// every SIMD and hide each other's latencies.  In a group, wave (ht, dh)
+// owns head tile ht (16 heads) and latent half dh (256 of the 512 dims,
+// plus half of the rope dims).
 //  * up front, every entry of the split is translated position -> page ->
 //    record slot (two dependent loads, all entries in flight together);
 //  * the selected 656-byte records are copied 32 per tile straight from
 //    global memory into LDS (global_load_lds_dwordx4, no registers), into a
-//    ring of three steps, two steps ahead of the compute; a group's four
-//    waves copy its tile;
+//    ring of six tiles: three steps, two ahead of the compute, for G = 2;
+//    two steps, one ahead, for G = 3; a group's four waves copy its tile;
 //  * logits S^T = K Q^T on v_mfma_f32_16x16x32_bf16, each wave over its
 //    half of the 576 dims: E4M3 latent -> bf16 is exact, each 128-wide
 //    latent tile accumulates separately and is scaled by its fp32 tile
@@ -43,17 +44,14 @@ namespace {
 
 using namespace dsa;
 
-constexpr int kThreads = 512;                 // attention workgroup: 8 waves
 constexpr int kCombineThreads = 256;
 constexpr int kHeadsWG = 32;                  // heads per workgroup (two MFMA tiles)
 constexpr int kTileTok = 32;                  // tokens per tile
-constexpr int kStepTok = 2 * kTileTok;        // tokens per step (one tile per wave group)
 constexpr int kPieces = kRec / 16;            // 41 16-byte pieces per record
 constexpr int kDmaPerTile = 21;               // ceil(32 * 41 / 64) DMA instructions per tile
 constexpr int kDmaPerWave = 6;                // per wave per step (the last ones are padding)
 constexpr int kSlotBytes = kDmaPerTile * 1024;  // 21504: 32 records + padding
-constexpr int kRingSteps = 3;
-constexpr int kRingBytes = kRingSteps * 2 * kSlotBytes;   // 129024
+constexpr int kRingBytes = 6 * kSlotBytes;    // 129024: six tiles of records
 constexpr int kMaxEntries = DSA_MAX_TOPK;     // entries of one split
 constexpr int kMaxSplits = 16;                // a row of 2048 entries: two 64-entry steps per split
 constexpr int kWideSplits = 8;                // splits the eight-dim combine holds in registers
@@ -68,6 +66,22 @@ static_assert(kDmaPerWave * 4 >= kDmaPerTile, "a group's DMA assignment covers i
 static_assert(32 * kPieces <= kDmaPerTile * 64, "a tile fits its DMA instructions");
 static_assert(kMargin + 1 + kPBias < 16, "P' stays below the fp16 maximum");
 static_assert(4 * kMergeWords * 64 * 4 <= kRingBytes, "the merge fits the ring");
+
+// An attention work-group is G wave groups of four waves, each group taking
+// one tile of 32 records per step.  G = 2: eight waves (two per SIMD) and a
+// ring of three steps, two copied ahead.  G = 3: twelve waves (three per
+// SIMD), a ring of two steps, one copied ahead; it fits three waves per
+// SIMD in registers by rebuilding its copy addresses at every step and
+// reading each token's scale again for P.V instead of holding them.
+template <int G>
+struct Cfg {
+  static constexpr int kThreads = 256 * G;
+  static constexpr int kStepTok = G * kTileTok;                 // tokens per step
+  static constexpr int kRingSteps = kRingBytes / (G * kSlotBytes);   // 3 or 2
+  static constexpr int kAhead = kRingSteps - 1;                 // steps copied ahead
+  static constexpr int kSlotCap = (kMaxEntries + kStepTok - 1) / kStepTok * kStepTok;   // whole steps
+};
+static_assert(Cfg<2>::kRingSteps == 3 && Cfg<3>::kRingSteps == 2, "ring depths");
 
 struct Params {
   const uint16_t* q;      // [R, H, 576] bf16
@@ -89,12 +103,13 @@ struct Params {
   uint32_t* err;
 };
 
+template <int G>
 struct Smem {
   uint8_t ring[kRingBytes];            // record tiles; the group merge at the end
   uint8_t junk[1024];                  // target of padding DMA instructions
-  int32_t slot[kMaxEntries];           // record slot per entry of the split, -1 = none
-  float zx[2][2][2][8 * 64];           // partial logits [group][ht][dh], swapped between partners
-  uint32_t vmask[kMaxEntries / 32];   // entry validity, one bit per entry of the split
+  int32_t slot[Cfg<G>::kSlotCap];      // record slot per entry of the split, -1 = none
+  float zx[G][2][2][8 * 64];           // partial logits [group][ht][dh], swapped between partners
+  uint32_t vmask[Cfg<G>::kSlotCap / 32];   // entry validity, one bit per entry of the split
 };
 
 __device__ __forceinline__ void flag(uint32_t* err, uint32_t bits) {
@@ -103,6 +118,23 @@ __device__ __forceinline__ void flag(uint32_t* err, uint32_t bits) {
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 8, 16 and 8 bytes at LDS byte address a (the loop addresses the ring by
+// 32-bit LDS offsets, so that the constant part of every read folds into its
+// offset field).
+typedef unsigned int lds_v2u __attribute__((ext_vector_type(2)));
+typedef unsigned int lds_v4u __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_u2(uint32_t a) {
+  const lds_v2u v = *(const __attribute__((address_space(3))) lds_v2u*)(size_t)a;
+  return make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ uint4 lds_u4(uint32_t a) {
+  const lds_v4u v = *(const __attribute__((address_space(3))) lds_v4u*)(size_t)a;
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ float lds_f(uint32_t a) {
+  return *(const __attribute__((address_space(3))) float*)(size_t)a;
 }
 
 // 16 bytes per lane from global memory into LDS at lds_base + 16*lane.  Issued
@@ -148,8 +180,12 @@ __device__ __forceinline__ float rows_sum(float x) {
 // logits of those tokens land in the output of the two 16-token MFMAs.
 __device__ __forceinline__ int ktok(int g, int i) { return i < 4 ? 4 * g + i : 12 + 4 * g + i; }
 
-__global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
-  __shared__ __attribute__((aligned(16))) Smem S;
+template <int G>
+__global__ __launch_bounds__(256 * G, 1) void sfa_kernel(Params P) {
+  constexpr int kGroups = G, kThreads = Cfg<G>::kThreads, kStepTok = Cfg<G>::kStepTok;
+  constexpr int kRingSteps = Cfg<G>::kRingSteps, kSlotCap = Cfg<G>::kSlotCap;
+  constexpr bool kLean = G > 2;   // three waves per SIMD: registers are short
+  __shared__ __attribute__((aligned(16))) Smem<G> S;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hr = lane & 15, g = lane >> 4;
@@ -208,7 +244,7 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
   {
     const int32_t* idxrow = P.idx + (int64_t)row * P.topk + j0;
     const int32_t* btrow = P.bt + (int64_t)seq * P.bt_stride;
-    constexpr int kPer = kMaxEntries / kThreads;   // 4
+    constexpr int kPer = (kSlotCap + kThreads - 1) / kThreads;   // 4 or 3
     int32_t v[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -243,33 +279,40 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
   }
   __syncthreads();
 
-  // ---- DMA of one step into ring slot k % 3: the four waves of group G copy
-  //      tile G, each issuing exactly kDmaPerWave instructions per step,
+  // ---- DMA of one step into ring slot k % kRingSteps: the four waves of
+  //      group grp copy tile grp of the step, each issuing exactly kDmaPerWave instructions per step,
   //      padding ones included, so the waits below can count them.
   //      Instruction m of a wave covers pieces 64j + lane (j = wv%4 + 4m) of
   //      the tile: record rec_m, 16-byte piece part_m.
   const uint32_t ring0 = lds_addr(S.ring), junk = lds_addr(S.junk);
   const int wq = wv & 3;
-  int rec_m[kDmaPerWave], off_m[kDmaPerWave];
-#pragma unroll
-  for (int m = 0; m < kDmaPerWave; ++m) {
-    const int piece = 64 * (wq + 4 * m) + lane;
-    rec_m[m] = piece / kPieces;
-    off_m[m] = (piece - kPieces * rec_m[m]) * 16;
-  }
+  // (with three waves per SIMD too few registers are left to keep the
+  // record and byte offset of instruction m's piece: they are recomputed at
+  // every step from an opaque copy of the lane id; two groups keep them)
   auto issue_step = [&](int k) {
+    uint32_t ln = (uint32_t)lane;
+    if constexpr (kLean) asm volatile("" : "+v"(ln));
+    uint32_t ro_m[kDmaPerWave];
+#pragma unroll
+    for (int m = 0; m < kDmaPerWave; ++m) {
+      const uint32_t piece = 64u * (uint32_t)(wq + 4 * m) + ln;
+      const uint32_t rec = piece / (uint32_t)kPieces;
+      ro_m[m] = rec | ((piece - (uint32_t)kPieces * rec) * 16u) << 16;
+    }
     int32_t sl[kDmaPerWave];
 #pragma unroll
     for (int m = 0; m < kDmaPerWave; ++m) {
-      const bool live = wq + 4 * m < kDmaPerTile && k < nsteps && rec_m[m] < kTileTok;
-      sl[m] = live ? S.slot[(2 * k + grp) * kTileTok + rec_m[m]] : -1;
+      const int rec = (int)(ro_m[m] & 0xFFFFu);
+      const bool live = wq + 4 * m < kDmaPerTile && k < nsteps && rec < kTileTok;
+      sl[m] = live ? S.slot[(kGroups * k + grp) * kTileTok + rec] : -1;
     }
-    const uint32_t base = ring0 + (uint32_t)(((k % kRingSteps) * 2 + grp) * kSlotBytes);
+    const uint32_t base = ring0 + (uint32_t)(((k % kRingSteps) * kGroups + grp) * kSlotBytes);
 #pragma unroll
     for (int m = 0; m < kDmaPerWave; ++m) {
       const bool inst = wq + 4 * m < kDmaPerTile && k < nsteps;   // wave-uniform
       const int32_t sv = sl[m];
-      const uint8_t* src = sv >= 0 ? P.pool + (int64_t)sv * kRec + off_m[m] : P.zero + off_m[m];
+      const uint8_t* rb = sv >= 0 ? P.pool + (int64_t)sv * kRec : P.zero;   // the record, or zeros
+      const uint8_t* src = rb + (ro_m[m] >> 16);
       dma16(src, inst ? base + (uint32_t)((wq + 4 * m) * 1024) : junk);
     }
   };
@@ -289,23 +332,37 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
   float* zx = S.zx[grp][ht][dh];
   const float* zpart = S.zx[grp][ht][dh ^ 1];
 
-  issue_step(0);
-  issue_step(1);
-  // Group 1 runs one barrier behind group 0: every s_barrier of the loop is
-  // then group 0's step-top barrier and group 1's mid-step barrier or the
-  // reverse, so one group computes logits while the other runs the softmax
-  // and P.V (the two waves sharing a SIMD are in different phases).  A
-  // group's ring slots, partial logits and DMA are its own, so only its own
-  // waves' ordering matters; the counts match through one extra barrier of
-  // group 0 after the loop.
-  if (grp == 1) __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int a = 0; a < Cfg<G>::kAhead; ++a) issue_step(a);
+  // Group g runs g barriers behind group 0: every s_barrier of the loop is
+  // then one group's step-top barrier and another's mid-step barrier, so the
+  // waves sharing a SIMD are not all in the same phase.  A group's ring
+  // slots, partial logits and DMA are its own, so only its own waves'
+  // ordering matters; the counts match through the extra barriers after the
+  // loop.
+  for (int b = 0; b < grp; ++b) __builtin_amdgcn_s_barrier();
   for (int k = 0; k < nsteps; ++k) {
-    // this step's copies are complete once only the next step's remain; the
-    // barrier also releases the slots of step k-1
-    asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
-    issue_step(k + 2);
-    const uint8_t* tq = S.ring + ((k % kRingSteps) * 2 + grp) * kSlotBytes;   // the group's tile
-    const int eq0 = (2 * k + grp) * kTileTok;   // its first entry
+    // this step's copies are complete once only the later steps' remain
+    // (kDmaPerWave per step copied ahead of this one); the barrier also
+    // releases the slots of step k-1, which take step k + kAhead
+    if constexpr (G == 2)
+      asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    issue_step(k + Cfg<G>::kAhead);
+    const uint32_t tq = ring0 + (uint32_t)(((k % kRingSteps) * kGroups + grp) * kSlotBytes);   // the group's tile
+    const int eq0 = (kGroups * k + grp) * kTileTok;   // its first entry
+    // this step's base addresses of the lane's reads, built from an opaque
+    // lane id so that the compiler rebuilds them per step instead of holding
+    // one hoisted address per read: the constant parts of every read fold
+    // into its offset field and neighbouring reads pair up
+    uint32_t ln = (uint32_t)lane;
+    asm volatile("" : "+v"(ln));
+    const uint32_t hr_ = ln & 15u, g_ = ln >> 4;
+    const uint32_t rec0 = tq + hr_ * kRec + 256u * dh + 8u * g_;
+    const uint32_t rope0 = tq + hr_ * kRec + kRecRopeOff + 64u * dh + 16u * g_;
+    const uint32_t scl0 = tq + 4u * g_ * kRec + kRecScaleOff + 8u * dh;
+    const uint32_t vrow0 = tq + (uint32_t)ktok((int)g_, (int)(hr_ >> 1)) * kRec + 8u * (hr_ & 1u) + 256u * dh;
 
     // ---- partial logits over the wave's half of the dims: accumulators
     //      acc[u][t] of token rows 16u + (0..15), latent tile 2dh + t (t < 2)
@@ -315,8 +372,6 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int t = 0; t < 3; ++t) acc[u][t] = v4f{0.f, 0.f, 0.f, 0.f};
-    const uint8_t* rec0 = tq + hr * kRec + 256 * dh + 8 * g;   // A-operand rows of this lane
-    const uint8_t* rec1 = rec0 + 16 * kRec;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
 #pragma unroll
@@ -324,7 +379,7 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
         const int j = 4 * t + jj;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const uint2 raw = *reinterpret_cast<const uint2*>((u ? rec1 : rec0) + 32 * j);
+          const uint2 raw = lds_u2(rec0 + (uint32_t)(u * 16 * kRec + 32 * j));
           const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, false);
           const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, true);
           const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, 1.0f, false);
@@ -336,8 +391,7 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const uint4 r4 = *reinterpret_cast<const uint4*>(tq + (16 * u + hr) * kRec + kRecRopeOff +
-                                                       64 * dh + 16 * g);
+      const uint4 r4 = lds_u4(rope0 + (uint32_t)(16 * u * kRec));
       acc[u][2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, r4), qv[8],
                                                           acc[u][2], 0, 0, 0);
     }
@@ -345,9 +399,9 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
     float sc[8][2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float2 s2 = *reinterpret_cast<const float2*>(tq + ktok(g, i) * kRec + kRecScaleOff + 8 * dh);
-      sc[i][0] = s2.x;
-      sc[i][1] = s2.y;
+      const uint2 s2 = lds_u2(scl0 + (uint32_t)(ktok(0, i) * kRec));
+      sc[i][0] = __uint_as_float(s2.x);
+      sc[i][1] = __uint_as_float(s2.y);
     }
     // this half's part of the logits of the lane's 8 tokens, shared with the
     // partner (same heads, other half)
@@ -361,12 +415,14 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     float z[8];
-    const uint32_t tmask = S.vmask[eq0 >> 5];   // validity of the tile's 32 entries
+    // validity of the tile's 32 entries, shifted so that bit i (i < 4) and
+    // bit 12 + i (i >= 4) are token ktok(g, i)'s
+    const uint32_t tmask = S.vmask[eq0 >> 5] >> (4 * g);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float own = zx[i * 64 + lane], other = zpart[i * 64 + lane];
       const float v = dh ? other + own : own + other;   // half 0 first in both partners
-      z[i] = (tmask >> ktok(g, i)) & 1u ? v * P.scale_log2 : -__builtin_huge_valf();
+      z[i] = (tmask >> ktok(0, i)) & 1u ? v * P.scale_log2 : -__builtin_huge_valf();
     }
     uint32_t smax[2] = {0u, 0u};
 #pragma unroll
@@ -427,13 +483,16 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
       const float mul = eref[t] > -1000 ? pow2f(max(-126, min(127, kPBias - eref[t]))) : 0.f;
       _Float16 h[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) h[i] = (_Float16)(pr[i] * sc[i][t] * mul);
+      for (int i = 0; i < 8; ++i) {
+        // (three groups read the scale again rather than hold it)
+        const float st = kLean ? lds_f(scl0 + (uint32_t)(ktok(0, i) * kRec + 4 * t)) : sc[i][t];
+        h[i] = (_Float16)(pr[i] * st * mul);
+      }
       const v8h b = v8h{h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7]};
-      const uint8_t* vrow = tq + ktok(g, hr >> 1) * kRec + 8 * (hr & 1) + 128 * (2 * dh + t);
+      const uint32_t vrow = vrow0 + (uint32_t)(128 * t);
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
-        const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (lds_v2i*)((__attribute__((address_space(3))) uint8_t*)(vrow + 16 * dd)));
+        const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(size_t)(vrow + 16 * dd));
         const v2h v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[0], 1.0f, false);
         const v2h v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[0], 1.0f, true);
         const v2h v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[1], 1.0f, false);
@@ -446,7 +505,7 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
   // no copy may still be landing in LDS when the ring is reused or the
   // workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (grp == 0) __builtin_amdgcn_s_barrier();
+  for (int b = grp; b < kGroups - 1; ++b) __builtin_amdgcn_s_barrier();
 
   // ---- true O relative to m_ref: o * 2^(eref - kPBias) ----
 #pragma unroll
@@ -457,31 +516,34 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_kernel(Params P) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) o[8 * t + dd][c] *= f;
   }
-  // ---- merge group 1 into group 0 (same lane, same wave role) ----
-  __syncthreads();
+  // ---- merge groups 1 .. kGroups-1 into group 0 (same lane, same wave
+  //      role), one group at a time through the ring ----
   float* mg = reinterpret_cast<float*>(S.ring) + (wv & 3) * kMergeWords * 64 + lane;
-  if (grp == 1) {
+  for (int src = 1; src < kGroups; ++src) {
+    __syncthreads();   // the ring (and the previous group's copy) is free
+    if (grp == src) {
 #pragma unroll
-    for (int d = 0; d < 16; ++d)
+      for (int d = 0; d < 16; ++d)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) mg[(4 * d + c) * 64] = o[d][c];
-    mg[64 * 64] = m_ref;
-    mg[65 * 64] = l_run;
+        for (int c = 0; c < 4; ++c) mg[(4 * d + c) * 64] = o[d][c];
+      mg[64 * 64] = m_ref;
+      mg[65 * 64] = l_run;
+    }
+    __syncthreads();
+    if (grp == 0) {
+      const float m1 = mg[64 * 64], l1 = mg[65 * 64];
+      const float M = fmaxf(m_ref, m1);
+      const float f0 = m_ref == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(m_ref - M);
+      const float f1 = m1 == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+#pragma unroll
+      for (int d = 0; d < 16; ++d)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o[d][c] = o[d][c] * f0 + mg[(4 * d + c) * 64] * f1;
+      l_run = l_run * f0 + l1 * f1;
+      m_ref = M;
+    }
   }
-  __syncthreads();
-  if (grp == 1) return;
-  {
-    const float m1 = mg[64 * 64], l1 = mg[65 * 64];
-    const float M = fmaxf(m_ref, m1);
-    const float f0 = m_ref == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(m_ref - M);
-    const float f1 = m1 == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
-#pragma unroll
-    for (int d = 0; d < 16; ++d)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) o[d][c] = o[d][c] * f0 + mg[(4 * d + c) * 64] * f1;
-    l_run = l_run * f0 + l1 * f1;
-    m_ref = M;
-  }
+  if (grp != 0) return;
   if (!head_ok) return;
   if (P.S == 1) {
     const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
@@ -571,12 +633,14 @@ struct Plan {
 Plan plan_for(int R, int H, int topk) {
   Plan p;
   p.hg = (H + kHeadsWG - 1) / kHeadsWG;
-  const int steps = (topk + kStepTok - 1) / kStepTok;
+  // splits are whole steps of the two-group form (64 records)
+  constexpr int kSplitTok = Cfg<2>::kStepTok;
+  const int steps = (topk + kSplitTok - 1) / kSplitTok;
   const int64_t groups = (int64_t)R * p.hg;
   int S = (int)std::min<int64_t>((kTargetWgs + groups - 1) / groups, (int64_t)steps);
   S = std::max(1, std::min(S, kMaxSplits));
   const int steps_per = (steps + S - 1) / S;
-  p.per_split = steps_per * kStepTok;
+  p.per_split = steps_per * kSplitTok;
   p.S = (topk + p.per_split - 1) / p.per_split;
   return p;
 }
@@ -648,7 +712,12 @@ extern "C" int dsa_sparse_attn(const void* q_bf16, const void* kv_pool, int64_t 
   const int64_t grid = (int64_t)R * pl.hg * pl.S;
   if (grid > 0x7FFFFFFF) return DSA_ERR_UNSUPPORTED;
   hipStream_t s = dsa_host::as_stream(stream);
-  hipLaunchKernelGGL(sfa_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, P);
+  // three wave groups for a list taken whole by one work-group (no split)
+  // and long enough for steps of 96 records (chunked prefill); two otherwise
+  if (pl.S == 1 && topk >= 1024)
+    hipLaunchKernelGGL(sfa_kernel<3>, dim3((unsigned)grid), dim3(Cfg<3>::kThreads), 0, s, P);
+  else
+    hipLaunchKernelGGL(sfa_kernel<2>, dim3((unsigned)grid), dim3(Cfg<2>::kThreads), 0, s, P);
   if (hipGetLastError() != hipSuccess) return DSA_ERR_HIP;
   if (pl.S > 1) {
     // V = 8 needs a block per CU and at most 8 splits; more than 8 splits

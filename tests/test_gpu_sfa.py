@@ -171,6 +171,33 @@ def test_sfa_prefill_chunk_every_64th_row(need_gpu):
     o.drop_cache()
 
 
+@pytest.mark.parametrize("W", [1024, 1100, 2048])
+def test_sfa_unsplit_long_lists(need_gpu, W):
+    """Lists of at least 1024 entries taken whole by one work-group (8192
+    rows of 128 heads: no split) run in steps of 96 records.  Index lists of
+    width W with -1 holes, lists shorter than one step and one entry past
+    it, a single entry in the last (partial) step, one position listed 200
+    times, and an empty row."""
+    st = state("prefill_chunk_8k_of_128k")
+    o = Oracle(st.inp)
+    R = st.R
+    rng = np.random.default_rng(57 + W)
+    idx = np.full((R, W), -1, dtype=np.int32)
+    t = lambda r: int(st.inp["row_pos"][r])
+    idx[0] = rng.choice(t(0) + 1, W, replace=False)
+    idx[0, ::5] = -1                                          # holes
+    idx[1, :95] = rng.choice(t(1) + 1, 95, replace=False)     # under one step
+    idx[2, :97] = rng.choice(t(2) + 1, 97, replace=False)     # one past a step
+    idx[3, W - 1] = t(3)                                      # last step only
+    idx[4] = rng.choice(t(4) + 1, W, replace=False)
+    idx[4, 300:500] = idx[4, 77]                              # 200 duplicates
+    idx[R - 1] = rng.choice(t(R - 1) + 1, W, replace=False)
+    # row 5 stays empty -> out 0, lse -inf
+    rows = [0, 1, 2, 3, 4, 5, R - 1]
+    out, lse = _compare(st, o, idx, rows, f"unsplit lists of width {W}")
+    assert np.all(out[5] == 0) and np.all(np.isneginf(lse[5]))
+
+
 def _seq_topk_all(st):
     bt_row = st.block_table[int(st.inp["row_seq"][0])].contiguous()
     idx, sc = ops.dsa_indexer_topk_seq(st.q_fp8, st.q_e8m0, st.w, st.k_pool, bt_row, st.row_pos,
