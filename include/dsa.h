@@ -291,9 +291,10 @@ int dsa_indexer_topk_seq(const void* q_fp8, const void* q_e8m0, const float* w,
  * Sparse Attention", section "3. Decoding Phase Optimization"; Day0 page,
  * "System-Level Coordination").  Rows
  * r = b*q_per_seq .. b*q_per_seq + q_per_seq - 1 form one tile whose K pages
- * are read once for all of them; each row keeps its own causal limit
- * row_pos[r] and its own Top-K.  A tile's pages are dealt to work-groups in
- * chunks of 16-page units.
+ * are read once per pair of rows (one wave scores a 16-page unit for two
+ * rows of the tile; the pairs of one unit run side by side in one
+ * work-group); each row keeps its own causal limit row_pos[r] and its own
+ * Top-K.
  *
  *   R          B * q_per_seq (a multiple of q_per_seq, else
  *              DSA_ERR_INVALID_ARG);  q_per_seq 1..8

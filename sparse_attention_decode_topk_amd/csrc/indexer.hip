@@ -1803,8 +1803,9 @@ __global__ __launch_bounds__(kSelThreads, 1) void indexer_select_kernel(Params P
 
 // ---- row-tiled scan: query rows of one sequence share the K stream -------------
 //
-// The rows of a chunked prefill (or the several query tokens of one sequence)
-// read the same K pages.  A work-group takes a tile of kTileRows consecutive
+// The rows of a chunked prefill read the same K pages.  (The several query
+// tokens of multi-query decode take the wave form further below.)  A
+// work-group takes a tile of kTileRows consecutive
 // rows; each page is copied once, as it is in the cache, into an LDS ring
 // (global_load_lds, kPgRing pages, kPgAhead ahead; the page's tile layout
 // puts every operand chunk a lane reads at 16 * lane of a contiguous
@@ -1949,9 +1950,8 @@ __device__ __forceinline__ void emit_wave(const Params& P, int row, bool live_ro
   __builtin_amdgcn_raw_buffer_store_b32(edge, re, uoff, 0, 0);
 }
 
-// TWO: two rows per wave (tiles of up to 8 rows); otherwise one row per wave
-// (tiles of up to 4 rows), so that every wave of a small tile scores a row.
-template <int NHT, bool TWO>
+// Two rows per wave: tiles of up to 8 rows.
+template <int NHT>
 __global__ __launch_bounds__(kThreads, 2) void indexer_tile_kernel(Params P) {
   __shared__ __attribute__((aligned(16))) TileSmem S;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1983,14 +1983,13 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_tile_kernel(Params P) {
       mixed |= __builtin_amdgcn_ballot_w64(s_l != seq) != 0;
     }
     const int32_t* btrow = P.bt + (int64_t)seq * P.bt_stride;
-    constexpr int RPW = TWO ? 2 : 1;   // rows per wave
-    const int ra = r0 + RPW * wv, rb = ra + 1;
-    const bool la = RPW * wv < TR && ra < P.R;
-    const bool lb = TWO && RPW * wv + 1 < TR && rb < P.R;
-    const int ta = __builtin_amdgcn_readlane(t_l, RPW * wv);
-    const int tb = __builtin_amdgcn_readlane(t_l, RPW * wv + RPW - 1);
-    const int npa = __builtin_amdgcn_readlane(np_l, RPW * wv);
-    const int npb = __builtin_amdgcn_readlane(np_l, RPW * wv + RPW - 1);
+    const int ra = r0 + 2 * wv, rb = ra + 1;   // the wave's two rows
+    const bool la = 2 * wv < TR && ra < P.R;
+    const bool lb = 2 * wv + 1 < TR && rb < P.R;
+    const int ta = __builtin_amdgcn_readlane(t_l, 2 * wv);
+    const int tb = __builtin_amdgcn_readlane(t_l, 2 * wv + 1);
+    const int npa = __builtin_amdgcn_readlane(np_l, 2 * wv);
+    const int npb = __builtin_amdgcn_readlane(np_l, 2 * wv + 1);
     // the chunk's units [cu0, cu0 + nun) of the tile's ceil(npt / 16)
     const int nun_t = (npt + kUnitPages - 1) / kUnitPages;
     const int cu0 = P.chunk_units > 0 ? chunk * P.chunk_units : 0;
@@ -2007,7 +2006,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_tile_kernel(Params P) {
     }
     QOperand<NHT> Qa, Qb;
     load_q<NHT>(P, la ? ra : r0, Qa);
-    if (TWO) load_q<NHT>(P, lb ? rb : r0, Qb);
+    load_q<NHT>(P, lb ? rb : r0, Qb);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): nothing but page copies outstanding below
     __syncthreads();
     // Units are visited in rotated order, starting at a phase that depends on
@@ -2071,7 +2070,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_tile_kernel(Params P) {
         // token tile's first, is issued before the FMA chain reads MFMA m,
         // so the matrix unit works while the vector unit consumes.  Per row
         // and token tile the chain is head_part's.
-        constexpr int kM = TWO ? 2 * NHT : NHT;
+        constexpr int kM = 2 * NHT;
         float pa[4], pb[4];
         v8i kc, kn;
         int sc, sn = 0;
@@ -2095,10 +2094,10 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_tile_kernel(Params P) {
           sc = sn;
         }
         // lane group g receives token tile g: lane l holds position 64p + l
-        const float sa = rows_sum_scatter(pa), sb = TWO ? rows_sum_scatter(pb) : 0.f;
+        const float sa = rows_sum_scatter(pa), sb = rows_sum_scatter(pb);
         const int pos = p * kPage + lane;
         ka[pi] = pok && pos <= ta ? score_key(sa) : 0u;
-        kb[pi] = TWO && pok && pos <= tb ? score_key(sb) : 0u;
+        kb[pi] = pok && pos <= tb ? score_key(sb) : 0u;
       }
       uint32_t ea, eb;
       tile_edges(P, u, la, ta, npa, ka, lb, tb, npb, kb, &ea, &eb);
@@ -2424,6 +2423,129 @@ __global__ __launch_bounds__(kScanThreads, 2) void indexer_wave_kernel(Params P)
   if (bad && lane == 0) flag_error(P.hdr, kErrBadPage);
 }
 
+// ---- multi-query decode, one wave per (row group, unit) --------------------------
+//
+// A tile is the P.tile_rows consecutive rows of one sequence; it is cut into
+// groups of up to kMqRows rows.  A wave
+// takes one unit of one group: it streams the unit's 16 pages once through
+// the per-row scan's register ring (the pages of the group's longest row)
+// and scores every page for each row of the group with that row's query
+// operand.  Every row's keys come from the per-row scan's operations in the
+// same order (head_part, rows_sum_scatter), with the row's own causal limit;
+// the row's filter and candidate stores follow the unit, for units within
+// the row's own length.  The group reads the pages of its tile's first row's
+// sequence; a group whose rows name another sequence sets kErrMixedTile.
+// Two rows per wave fit two waves per SIMD (four rows per wave need one
+// wave per SIMD, whose scoring chains then go unhidden: 43% slower), with
+// three half pages in flight (a fourth does not fit beside the pipelined
+// scoring's operands without spilling).
+constexpr int kMqRows = 2;
+constexpr int kMqRing = 3;
+template <int NHT>
+__global__ __launch_bounds__(kScanThreads, 2) void indexer_mq_wave_kernel(Params P) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int TR = P.tile_rows;
+  const int gpt = (TR + kMqRows - 1) / kMqRows;         // groups per tile
+  const int ntiles = (P.R + TR - 1) / TR;
+  const uint32_t item = (uint32_t)blockIdx.x * kScanWaves + (uint32_t)wv;
+  if (item >= (uint32_t)(ntiles * gpt) * (uint32_t)P.upr) return;
+  // the groups of one unit are neighbouring waves (one work-group when the
+  // tile has four groups or fewer), so they request the same pages together
+  const int sub = (int)(item % (uint32_t)gpt);
+  const uint32_t tu = item / (uint32_t)gpt;
+  const int tile = (int)(tu / (uint32_t)P.upr), uir = (int)(tu % (uint32_t)P.upr);
+  const int rt = tile * TR;                              // the tile's first row
+  const int r0 = rt + sub * kMqRows;                     // the group's rows r0, r0 + 1
+  const int nr = min(min(kMqRows, TR - sub * kMqRows), P.R - r0);   // 1 or 2
+  // lane j < nr: row r0 + j's position and sequence
+  const int t_l = lane < nr ? P.row_pos[r0 + lane] : -1;
+  int seq = 0;
+  bool mixed = false;
+  if (P.row_seq) {
+    seq = __builtin_amdgcn_readfirstlane(P.row_seq[rt]);
+    const int s_l = lane < nr ? P.row_seq[r0 + lane] : seq;
+    mixed = __builtin_amdgcn_ballot_w64(s_l != seq) != 0;
+  }
+  const int ta = __builtin_amdgcn_readlane(t_l, 0);
+  const int tb = nr > 1 ? __builtin_amdgcn_readlane(t_l, 1) : -1;
+  const Unit U = row_unit(P, r0, max(ta, tb), uir);   // the pages of the group's longer row
+  if (uir >= U.units_r) return;                       // past the group's pages (uniform)
+  bool bad = false;
+  const int32_t pid = unit_pages(P, U, seq);
+  HalfRegs b[kMqRing];
+  bool ok[kMqRing];
+#pragma unroll
+  for (int k = 0; k < kMqRing; ++k) ok[k] = fetch_half(P, U, pid, k, b[k], &bad);
+  // a group of one row scores that row twice (the second copy is not kept):
+  // every load and MFMA is issued on every path
+  QOperand<NHT> Qa, Qb;
+  load_q<NHT>(P, r0, Qa);
+  load_q<NHT>(P, r0 + nr - 1, Qb);
+  uint32_t ka[kUnitPages], kb[kUnitPages];
+#pragma unroll
+  for (int pi = 0; pi < kUnitPages; ++pi) {
+    const bool pok = ok[(2 * pi) % kMqRing];   // both halves of a page are present or absent together
+    // token tile j of the page: half j/2 (ring slot (2pi + j/2) % kMqRing), tile j%2
+    auto operand = [&](int j, v8i& kv, int& ks) {
+      const int sl = (2 * pi + (j >> 1)) % kMqRing, jj = j & 1;
+      const uint4 lo = b[sl].d[2 * jj], hi = b[sl].d[2 * jj + 1];
+      kv = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      ks = (int)b[sl].s[jj];
+    };
+    // 2*NHT MFMAs per token tile (m < NHT: row a's head tile m, else row b's
+    // head tile m - NHT), software-pipelined as in the row-tiled kernel:
+    // MFMA m+1, or the next token tile's first, is issued before the FMA
+    // chain reads MFMA m.  Per row and token tile the chain is head_part's.
+    constexpr int kM = 2 * NHT;
+    float pa[4], pb[4];
+    v8i kc, kn;
+    int sc, sn = 0;
+    operand(0, kc, sc);
+    v4f cur = head_mfma(Qa, 0, kc, sc);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pa[j] = pb[j] = 0.f;
+      if (j + 1 < 4) operand(j + 1, kn, sn);
+#pragma unroll
+      for (int m = 0; m < kM; ++m) {
+        v4f nxt = cur;
+        if (m + 1 < NHT) nxt = head_mfma(Qa, m + 1, kc, sc);
+        else if (m + 1 < kM) nxt = head_mfma(Qb, m + 1 - NHT, kc, sc);
+        else if (j + 1 < 4) nxt = head_mfma(Qa, 0, kn, sn);
+        if (m < NHT) pa[j] = head_acc(Qa, m, cur, pa[j]);
+        else pb[j] = head_acc(Qb, m - NHT, cur, pb[j]);
+        cur = nxt;
+      }
+      kc = kn;
+      sc = sn;
+      if (j & 1) {
+        // both token tiles of half j/2 are taken: its slot takes the half
+        // kMqRing ahead
+        const int h = 2 * pi + (j >> 1), hn = h + kMqRing;
+        if (hn < 2 * kUnitPages) ok[h % kMqRing] = fetch_half(P, U, pid, hn, b[h % kMqRing], &bad);
+      }
+    }
+    // lane group g receives token tile g: lane l holds position 64p + l
+    const float sa = rows_sum_scatter(pa), sb = rows_sum_scatter(pb);
+    const int pos = (U.pg0 + pi) * kPage + lane;
+    ka[pi] = pok && pos <= ta ? score_key(sa) : 0u;
+    kb[pi] = pok && pos <= tb ? score_key(sb) : 0u;
+  }
+  {
+    const Unit Ua = row_unit(P, r0, ta, uir);
+    emit_wave(P, r0, true, row_pages(ta, P.bt_stride), uir, ka, uir < Ua.units_r ? wave_edge(P, Ua, ka) : 0u);
+  }
+  if (nr > 1) {   // uniform
+    const Unit Ub = row_unit(P, r0 + 1, tb, uir);
+    emit_wave(P, r0 + 1, true, row_pages(tb, P.bt_stride), uir, kb, uir < Ub.units_r ? wave_edge(P, Ub, kb) : 0u);
+  }
+  if (lane == 0) {
+    if (bad) flag_error(P.hdr, kErrBadPage);
+    if (mixed) flag_error(P.hdr, kErrMixedTile);
+  }
+}
+
 // ---- host side ----------------------------------------------------------------
 
 struct Layout {
@@ -2477,12 +2599,21 @@ void* pick_kernel(int nht, KernelKind kind) {
   }
 }
 
-void* pick_tile_kernel(int nht, bool two) {
+void* pick_tile_kernel(int nht) {
   switch (nht) {
-    case 1: return two ? (void*)&indexer_tile_kernel<1, true> : (void*)&indexer_tile_kernel<1, false>;
-    case 2: return two ? (void*)&indexer_tile_kernel<2, true> : (void*)&indexer_tile_kernel<2, false>;
-    case 3: return two ? (void*)&indexer_tile_kernel<3, true> : (void*)&indexer_tile_kernel<3, false>;
-    default: return two ? (void*)&indexer_tile_kernel<4, true> : (void*)&indexer_tile_kernel<4, false>;
+    case 1: return (void*)&indexer_tile_kernel<1>;
+    case 2: return (void*)&indexer_tile_kernel<2>;
+    case 3: return (void*)&indexer_tile_kernel<3>;
+    default: return (void*)&indexer_tile_kernel<4>;
+  }
+}
+
+void* pick_mq_wave_kernel(int nht) {
+  switch (nht) {
+    case 1: return (void*)&indexer_mq_wave_kernel<1>;
+    case 2: return (void*)&indexer_mq_wave_kernel<2>;
+    case 3: return (void*)&indexer_mq_wave_kernel<3>;
+    default: return (void*)&indexer_mq_wave_kernel<4>;
   }
 }
 
@@ -2840,7 +2971,7 @@ extern "C" int dsa_indexer_topk_seq(const void* q_fp8, const void* q_e8m0, const
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   hipStream_t s = dsa_host::as_stream(stream);
   const int nht = (H_I + 15) / 16;
-  void* tk = pick_tile_kernel(nht, true);
+  void* tk = pick_tile_kernel(nht);
   void* sel = pick_kernel(nht, kSelect);
   const int cap = resident_capacity(tk, 12 + nht - 1, kThreads);
   if (cap <= 0) return DSA_ERR_HIP;
@@ -2899,11 +3030,8 @@ extern "C" int dsa_indexer_topk_mq(const void* q_fp8, const void* q_e8m0, const 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   hipStream_t s = dsa_host::as_stream(stream);
   const int nht = (H_I + 15) / 16;
-  const bool two = q_per_seq > kWaves;   // more rows per tile than waves
-  void* tk = pick_tile_kernel(nht, two);
+  void* mk = pick_mq_wave_kernel(nht);
   void* sel = pick_kernel(nht, kSelect);
-  const int cap = resident_capacity(tk, (two ? 12 : 16) + nht - 1, kThreads);
-  if (cap <= 0) return DSA_ERR_HIP;
   const int upr = units_stride(bt_stride);
   const int step = kMaxRows - kMaxRows % q_per_seq;   // whole sequences per launch
   for (int r0 = 0; r0 < R; r0 += step) {
@@ -2920,15 +3048,15 @@ extern "C" int dsa_indexer_topk_mq(const void* q_fp8, const void* q_e8m0, const 
     P.ucount = reinterpret_cast<uint32_t*>(ws + L.ucount);
     P.uedge = reinterpret_cast<uint32_t*>(ws + L.uedge);
     P.cand = reinterpret_cast<uint2*>(ws + L.cand);
-    // one tile per sequence, its units dealt in chunks so that about one
-    // work item per resident workgroup exists
     const int64_t ntiles = rn / q_per_seq;
     P.tile_rows = q_per_seq;
-    P.chunk_units = (int)std::max<int64_t>(1, (ntiles * upr + cap - 1) / cap);
-    const int64_t nitems = ntiles * ((upr + P.chunk_units - 1) / P.chunk_units);
-    const int64_t G = std::min<int64_t>(cap, nitems);
     void* args[] = {&P};
-    if (hipLaunchKernel(tk, dim3((unsigned)G), dim3(kThreads), args, 0, s) != hipSuccess)
+    // one wave per (pair of rows, unit) (decode 128K x 8, four rows per
+    // sequence: 60.7-62.5 -> 56.0-57.2 us per call against the row-tiled
+    // kernel's tiles; eight rows per sequence: 100.2-102.8 -> 94.6-95.4 us)
+    const int64_t items = ntiles * ((q_per_seq + kMqRows - 1) / kMqRows) * upr;
+    if (hipLaunchKernel(mk, dim3((unsigned)((items + kScanWaves - 1) / kScanWaves)), dim3(kScanThreads),
+                        args, 0, s) != hipSuccess)
       return DSA_ERR_HIP;
     if (hipLaunchKernel(sel, dim3((unsigned)rn), dim3(kSelThreads), args, 0, s) != hipSuccess)
       return DSA_ERR_HIP;
