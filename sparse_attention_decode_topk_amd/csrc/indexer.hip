@@ -2677,18 +2677,19 @@ int run(Params P, bool dump, hipStream_t stream, bool fused = false) {
     Params Q = P;
     const int rn = std::min(kMaxRows, R - r0);
     Q.R = rn;
-    Q.q = P.q + (int64_t)r0 * P.H * kIdxDim;
-    Q.qs = P.qs + (int64_t)r0 * P.H * 4;
     Q.w = P.w + (int64_t)r0 * P.H;
     Q.row_seq = P.row_seq + r0;
     Q.row_pos = P.row_pos + r0;
     if (fused) {
+      // the quantised queries live in the workspace, sized for one launch's
+      // rows: every launch uses it from its start (launches are stream-ordered)
       Q.q_bf16 = P.q_bf16 + (int64_t)r0 * P.H * kIdxDim;
       Q.k_new = P.k_new + (int64_t)r0 * kIdxDim;
       Q.kv_new = P.kv_new + (int64_t)r0 * kQK;
       Q.new_slot = P.new_slot + r0;
-      Q.q_ws = P.q_ws + (int64_t)r0 * P.H * kIdxDim;
-      Q.qs_ws = P.qs_ws + (int64_t)r0 * P.H * 4;
+    } else {
+      Q.q = P.q + (int64_t)r0 * P.H * kIdxDim;
+      Q.qs = P.qs + (int64_t)r0 * P.H * 4;
     }
     if (dump) {
       Q.dump = P.dump + (int64_t)r0 * P.ld;

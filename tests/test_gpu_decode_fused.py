@@ -177,3 +177,28 @@ def test_wave_scan_edge_rows(need_gpu):
     o = Oracle(inp)
     for r in (0, 2, 3, 4, 7, 100, B - 1):
         check_topk_row(gi[r], gs[r], o.topk(r), 300, int(lens[r] - 1))
+
+
+
+def test_fused_prolog_more_rows_than_one_launch(need_gpu):
+    """1100 rows (sequences of 1..300 tokens, 64 indexer heads, Top-K 64)
+    take two launches of at most 1024 rows: each launch keeps its quantised
+    queries in the workspace region sized for one launch.  The fused entry
+    point against the prolog then the indexer."""
+    rng = np.random.default_rng(61)
+    B, H_I, K = 1100, 64, 64
+    lens = rng.integers(1, 301, B).astype(np.int32)
+    cfg = synth.Config(99, "fused_many_rows", batch=B, h_index=H_I, h_attn=16, topk=K,
+                       ragged=(int(lens.min()), int(lens.max())))
+    bt, slots_all, starts, npages = synth.page_tables(cfg, lens, rng)
+    inp = dict(seq_lens=lens, block_table=bt, slot_mapping=slots_all, seq_starts=starts,
+               total_pages=np.int64(npages), topk=np.int32(K),
+               row_seq=np.arange(B, dtype=np.int32), row_pos=(lens - 1).astype(np.int32),
+               q_idx=synth.f32_to_bf16_bits(rng.standard_normal((B, H_I, 128)).astype(np.float32)),
+               k_idx=synth.f32_to_bf16_bits(rng.standard_normal((int(lens.sum()), 128)).astype(np.float32)),
+               w=(rng.standard_normal((B, H_I)) / np.sqrt(H_I)).astype(np.float32),
+               q_sfa=synth.f32_to_bf16_bits(rng.standard_normal((B, 16, 576)).astype(np.float32)),
+               kv=synth.f32_to_bf16_bits(rng.standard_normal((int(lens.sum()), 576)).astype(np.float32)))
+    st = DeviceState(inp)
+    new_tok = starts.astype(np.int64) + (lens - 1).astype(np.int64)
+    _run_both(st, inp, slots_all[new_tok].astype(np.int64), K, "1100 rows")
