@@ -198,6 +198,26 @@ def test_sfa_unsplit_long_lists(need_gpu, W):
     assert np.all(out[5] == 0) and np.all(np.isneginf(lse[5]))
 
 
+def test_sfa_unsplit_partial_head_group(need_gpu):
+    """24 heads (one head group of 32 with 8 absent heads) over 256 rows of a
+    2048-token sequence: one split per row of 1024 entries, so steps of 96
+    records; lists with holes and a ragged last step."""
+    cfg = synth.Config(95, "sfa_unsplit_h24", batch=1, h_index=4, h_attn=24, topk=1024, ctx=2048,
+                       rows=(1536, 256))
+    inp = synth.make(cfg)
+    st = DeviceState(inp)
+    o = Oracle(inp)
+    rng = np.random.default_rng(71)
+    R, K = st.R, st.topk
+    idx = np.empty((R, K), dtype=np.int32)
+    for r in range(R):
+        idx[r] = rng.choice(int(inp["row_pos"][r]) + 1, K, replace=False)
+    idx[:, ::7] = -1
+    idx[R - 1, 1000:] = -1
+    rows = [0, 1, 77, 128, 200, R - 1]
+    _compare(st, o, idx, rows, "unsplit lists, 24 heads")
+
+
 def _seq_topk_all(st):
     bt_row = st.block_table[int(st.inp["row_seq"][0])].contiguous()
     idx, sc = ops.dsa_indexer_topk_seq(st.q_fp8, st.q_e8m0, st.w, st.k_pool, bt_row, st.row_pos,
