@@ -6,19 +6,22 @@
 //
 // One workgroup = (query row, group of 32 heads, split of the index list);
 // the groups of one (row, split) are placed on one XCD so the records they
-// all read are served by that XCD's L2.  The waves form G groups of four
-// (G = 2, or G = 3 for an unsplit list of at least 1024 entries): group g
-// takes tile g (32 tokens) of every step of 32G tokens and keeps its own
-// softmax state; the groups are merged in LDS at the end, so G waves share
-// every SIMD and hide each other's latencies.  In a group, wave (ht, dh)
+// all read are served by that XCD's L2.  The waves form G groups of four:
+// group g takes tile g (32 tokens) of every step of 32G tokens and keeps its
+// own softmax state, and the groups are merged in LDS at the end.  A split
+// list takes G = 2 (one work-group per CU, two waves per SIMD); a list taken
+// whole takes G = 1 with a smaller ring, so that two independent
+// work-groups share every CU (again two waves per SIMD, but not tied by each
+// other's barriers, and one's start and end overlap the other's steps).  In
+// a group, wave (ht, dh)
 // owns head tile ht (16 heads) and latent half dh (256 of the 512 dims,
 // plus half of the rope dims).
 //  * up front, every entry of the split is translated position -> page ->
 //    record slot (two dependent loads, all entries in flight together);
 //  * the selected 656-byte records are copied 32 per tile straight from
 //    global memory into LDS (global_load_lds_dwordx4, no registers), into a
-//    ring of six tiles: three steps, two ahead of the compute, for G = 2;
-//    two steps, one ahead, for G = 3; a group's four waves copy its tile;
+//    ring of six tiles (three steps, two ahead of the compute) for G = 2, of
+//    two (two steps, one ahead) for G = 1; a group's four waves copy its tile;
 //  * logits S^T = K Q^T on v_mfma_f32_16x16x32_bf16, each wave over its
 //    half of the 576 dims: E4M3 latent -> bf16 is exact, each 128-wide
 //    latent tile accumulates separately and is scaled by its fp32 tile
@@ -68,20 +71,20 @@ static_assert(kMargin + 1 + kPBias < 16, "P' stays below the fp16 maximum");
 static_assert(4 * kMergeWords * 64 * 4 <= kRingBytes, "the merge fits the ring");
 
 // An attention work-group is G wave groups of four waves, each group taking
-// one tile of 32 records per step.  G = 2: eight waves (two per SIMD) and a
-// ring of three steps, two copied ahead.  G = 3: twelve waves (three per
-// SIMD), a ring of two steps, one copied ahead; it fits three waves per
-// SIMD in registers by rebuilding its copy addresses at every step and
-// reading each token's scale again for P.V instead of holding them.
+// one tile of 32 records per step.  G = 2: eight waves (two per SIMD), a
+// ring of three steps, two copied ahead, one work-group per CU.  G = 1: four
+// waves, a ring of two steps, one copied ahead, in about 60 KB of LDS: two
+// work-groups per CU.
 template <int G>
 struct Cfg {
   static constexpr int kThreads = 256 * G;
   static constexpr int kStepTok = G * kTileTok;                 // tokens per step
-  static constexpr int kRingSteps = kRingBytes / (G * kSlotBytes);   // 3 or 2
+  static constexpr int kRing = G == 1 ? 2 * kSlotBytes : kRingBytes;   // ring bytes
+  static constexpr int kRingSteps = kRing / (G * kSlotBytes);   // 2 or 3
   static constexpr int kAhead = kRingSteps - 1;                 // steps copied ahead
   static constexpr int kSlotCap = (kMaxEntries + kStepTok - 1) / kStepTok * kStepTok;   // whole steps
 };
-static_assert(Cfg<2>::kRingSteps == 3 && Cfg<3>::kRingSteps == 2, "ring depths");
+static_assert(Cfg<1>::kRingSteps == 2 && Cfg<2>::kRingSteps == 3, "ring depths");
 
 struct Params {
   const uint16_t* q;      // [R, H, 576] bf16
@@ -105,7 +108,7 @@ struct Params {
 
 template <int G>
 struct Smem {
-  uint8_t ring[kRingBytes];            // record tiles; the group merge at the end
+  uint8_t ring[Cfg<G>::kRing];         // record tiles; the group merge at the end
   uint8_t junk[1024];                  // target of padding DMA instructions
   int32_t slot[Cfg<G>::kSlotCap];      // record slot per entry of the split, -1 = none
   float zx[G][2][2][8 * 64];           // partial logits [group][ht][dh], swapped between partners
@@ -120,7 +123,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// 8, 16 and 8 bytes at LDS byte address a (the loop addresses the ring by
+// 8 and 16 bytes at LDS byte address a (the loop addresses the ring by
 // 32-bit LDS offsets, so that the constant part of every read folds into its
 // offset field).
 typedef unsigned int lds_v2u __attribute__((ext_vector_type(2)));
@@ -132,9 +135,6 @@ __device__ __forceinline__ uint2 lds_u2(uint32_t a) {
 __device__ __forceinline__ uint4 lds_u4(uint32_t a) {
   const lds_v4u v = *(const __attribute__((address_space(3))) lds_v4u*)(size_t)a;
   return make_uint4(v[0], v[1], v[2], v[3]);
-}
-__device__ __forceinline__ float lds_f(uint32_t a) {
-  return *(const __attribute__((address_space(3))) float*)(size_t)a;
 }
 
 // 16 bytes per lane from global memory into LDS at lds_base + 16*lane.  Issued
@@ -181,10 +181,9 @@ __device__ __forceinline__ float rows_sum(float x) {
 __device__ __forceinline__ int ktok(int g, int i) { return i < 4 ? 4 * g + i : 12 + 4 * g + i; }
 
 template <int G>
-__global__ __launch_bounds__(256 * G, 1) void sfa_kernel(Params P) {
+__global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void sfa_kernel(Params P) {
   constexpr int kGroups = G, kThreads = Cfg<G>::kThreads, kStepTok = Cfg<G>::kStepTok;
   constexpr int kRingSteps = Cfg<G>::kRingSteps, kSlotCap = Cfg<G>::kSlotCap;
-  constexpr bool kLean = G > 2;   // three waves per SIMD: registers are short
   __shared__ __attribute__((aligned(16))) Smem<G> S;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -286,12 +285,8 @@ __global__ __launch_bounds__(256 * G, 1) void sfa_kernel(Params P) {
   //      the tile: record rec_m, 16-byte piece part_m.
   const uint32_t ring0 = lds_addr(S.ring), junk = lds_addr(S.junk);
   const int wq = wv & 3;
-  // (with three waves per SIMD too few registers are left to keep the
-  // record and byte offset of instruction m's piece: they are recomputed at
-  // every step from an opaque copy of the lane id; two groups keep them)
   auto issue_step = [&](int k) {
-    uint32_t ln = (uint32_t)lane;
-    if constexpr (kLean) asm volatile("" : "+v"(ln));
+    const uint32_t ln = (uint32_t)lane;
     uint32_t ro_m[kDmaPerWave];
 #pragma unroll
     for (int m = 0; m < kDmaPerWave; ++m) {
@@ -345,7 +340,8 @@ __global__ __launch_bounds__(256 * G, 1) void sfa_kernel(Params P) {
     // this step's copies are complete once only the later steps' remain
     // (kDmaPerWave per step copied ahead of this one); the barrier also
     // releases the slots of step k-1, which take step k + kAhead
-    if constexpr (G == 2)
+    static_assert(Cfg<G>::kAhead == 1 || Cfg<G>::kAhead == 2, "the wait below");
+    if constexpr (Cfg<G>::kAhead == 2)
       asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
@@ -483,11 +479,7 @@ __global__ __launch_bounds__(256 * G, 1) void sfa_kernel(Params P) {
       const float mul = eref[t] > -1000 ? pow2f(max(-126, min(127, kPBias - eref[t]))) : 0.f;
       _Float16 h[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // (three groups read the scale again rather than hold it)
-        const float st = kLean ? lds_f(scl0 + (uint32_t)(ktok(0, i) * kRec + 4 * t)) : sc[i][t];
-        h[i] = (_Float16)(pr[i] * st * mul);
-      }
+      for (int i = 0; i < 8; ++i) h[i] = (_Float16)(pr[i] * sc[i][t] * mul);
       const v8h b = v8h{h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7]};
       const uint32_t vrow = vrow0 + (uint32_t)(128 * t);
 #pragma unroll
@@ -712,10 +704,11 @@ extern "C" int dsa_sparse_attn(const void* q_bf16, const void* kv_pool, int64_t 
   const int64_t grid = (int64_t)R * pl.hg * pl.S;
   if (grid > 0x7FFFFFFF) return DSA_ERR_UNSUPPORTED;
   hipStream_t s = dsa_host::as_stream(stream);
-  // three wave groups for a list taken whole by one work-group (no split)
-  // and long enough for steps of 96 records (chunked prefill); two otherwise
-  if (pl.S == 1 && topk >= 1024)
-    hipLaunchKernelGGL(sfa_kernel<3>, dim3((unsigned)grid), dim3(Cfg<3>::kThreads), 0, s, P);
+  // one group (two work-groups per CU) for lists taken whole, two for
+  // splits (one group there would need twice the splits, and partials, for
+  // chains as short: decode 128K x 8 26.0 -> 31.1 us per call)
+  if (pl.S == 1)
+    hipLaunchKernelGGL(sfa_kernel<1>, dim3((unsigned)grid), dim3(Cfg<1>::kThreads), 0, s, P);
   else
     hipLaunchKernelGGL(sfa_kernel<2>, dim3((unsigned)grid), dim3(Cfg<2>::kThreads), 0, s, P);
   if (hipGetLastError() != hipSuccess) return DSA_ERR_HIP;
