@@ -174,10 +174,10 @@ def test_sfa_prefill_chunk_every_64th_row(need_gpu):
 @pytest.mark.parametrize("W", [1024, 1100, 2048])
 def test_sfa_unsplit_long_lists(need_gpu, W):
     """Lists of at least 1024 entries taken whole by one work-group (8192
-    rows of 128 heads: no split) run in steps of 96 records.  Index lists of
-    width W with -1 holes, lists shorter than one step and one entry past
-    it, a single entry in the last (partial) step, one position listed 200
-    times, and an empty row."""
+    rows of 128 heads: no split; one wave group, two work-groups per CU,
+    steps of 32 records).  Index lists of width W with -1 holes, lists of
+    95 and 97 entries, a single entry in the last (partial) step, one
+    position listed 200 times, and an empty row."""
     st = state("prefill_chunk_8k_of_128k")
     o = Oracle(st.inp)
     R = st.R
@@ -186,8 +186,8 @@ def test_sfa_unsplit_long_lists(need_gpu, W):
     t = lambda r: int(st.inp["row_pos"][r])
     idx[0] = rng.choice(t(0) + 1, W, replace=False)
     idx[0, ::5] = -1                                          # holes
-    idx[1, :95] = rng.choice(t(1) + 1, 95, replace=False)     # under one step
-    idx[2, :97] = rng.choice(t(2) + 1, 97, replace=False)     # one past a step
+    idx[1, :95] = rng.choice(t(1) + 1, 95, replace=False)     # one short of a step boundary
+    idx[2, :97] = rng.choice(t(2) + 1, 97, replace=False)     # one past a step boundary
     idx[3, W - 1] = t(3)                                      # last step only
     idx[4] = rng.choice(t(4) + 1, W, replace=False)
     idx[4, 300:500] = idx[4, 77]                              # 200 duplicates
@@ -200,8 +200,8 @@ def test_sfa_unsplit_long_lists(need_gpu, W):
 
 def test_sfa_unsplit_partial_head_group(need_gpu):
     """24 heads (one head group of 32 with 8 absent heads) over 256 rows of a
-    2048-token sequence: one split per row of 1024 entries, so steps of 96
-    records; lists with holes and a ragged last step."""
+    2048-token sequence: one split per row of 1024 entries (the one-group
+    form); lists with holes and a ragged last step."""
     cfg = synth.Config(95, "sfa_unsplit_h24", batch=1, h_index=4, h_attn=24, topk=1024, ctx=2048,
                        rows=(1536, 256))
     inp = synth.make(cfg)
