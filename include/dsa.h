@@ -263,11 +263,13 @@ size_t dsa_indexer_topk_seq_workspace_size(int32_t R, int32_t n_pages,
  * of a causal prefill (each query scores its own history, "Lightning Indexer
  * ... scores every causal history position" with the triangular workload of
  * the chunked-prefill case) or the several query tokens of one sequence.  The
- * rows are taken in tiles of 8 consecutive rows whose K pages are read once
- * per tile; tiles are dealt to work-groups longest first in alternating
- * order, which balances the triangle (the load-balancing concern of the
+ * rows are taken in tiles of 8 consecutive rows; one wave scores one 16-page
+ * unit for a pair of rows of a tile, and the four pairs of a unit run side
+ * by side in one work-group, so the unit's pages are streamed together.
+ * Every work item is one unit of one pair, so the triangle's long rows do
+ * not leave a tail of long work items (the load-balancing concern of the
  * pages' context-parallel zigzag split, "Adapting and Optimizing Kimi K3.1
- * Pro for Long-Sequence Inference", applied to work-groups on one GPU).
+ * Pro for Long-Sequence Inference", met on one GPU by that granularity).
  *
  *   block_table_row [n_pages] int32 page ids of the sequence (n_pages <= 4096)
  *   row_pos         [R] int32, t of each row (any order; < 0 = no positions)

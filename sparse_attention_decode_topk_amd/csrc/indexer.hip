@@ -89,8 +89,7 @@ struct Params {
   int32_t H;
   int32_t topk;
   int32_t upr;           // units-per-row stride of ucount / uedge
-  int32_t tile_rows;     // row-tiled path: rows per tile (<= kTileRows), all of one sequence
-  int32_t chunk_units;   // row-tiled path: units per work item (0 = the whole tile)
+  int32_t tile_rows;     // tiled paths: rows per tile (<= kTileRows), all of one sequence
   int32_t j_start;       // select: the first layout tried (slots per unit / 64)
   int32_t* out_idx;
   float* out_score;
@@ -559,34 +558,12 @@ __device__ __forceinline__ void lane_top(const uint32_t (&k)[kUnitPages], uint32
   }
 }
 
-// Edges of two rows' units (values va, vb: D per lane over the wave): the
-// largest key T with zero low 16 bits such that at least `need` of the
-// values are >= T, found bit by bit from the top with ballot counts (no
-// memory traffic, no atomics); 0 when fewer than `need` values reach
-// 2^16.  The values are the unit's keys or a subset of them, so at least
-// `need` of the unit's keys are >= T: T never exceeds the unit's need-th
-// largest key.
-template <int D>
-__device__ __forceinline__ void key_floor2(const uint32_t (&va)[D], const uint32_t (&vb)[D],
-                                           uint32_t na, uint32_t nb, uint32_t* ta, uint32_t* tb) {
-  uint32_t a = 0u, b = 0u;
-#pragma unroll
-  for (int bit = 31; bit >= 16; --bit) {
-    const uint32_t ca = a | (1u << bit), cb = b | (1u << bit);
-    uint32_t sa = 0u, sb = 0u;
-#pragma unroll
-    for (int i = 0; i < D; ++i) {
-      sa += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(va[i] >= ca));
-      sb += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(vb[i] >= cb));
-    }
-    if (sa >= na) a = ca;
-    if (sb >= nb) b = cb;
-  }
-  *ta = a;
-  *tb = b;
-}
-
-// key_floor2 for one row.
+// A unit's edge (values v: D per lane over the wave): the largest key T
+// with zero low 16 bits such that at least `need` of the values are >= T,
+// found bit by bit from the top with ballot counts (no memory traffic, no
+// atomics); 0 when fewer than `need` values reach 2^16.  The values are the
+// unit's keys or a subset of them, so at least `need` of the unit's keys are
+// >= T: T never exceeds the unit's need-th largest key.
 template <int D>
 __device__ __forceinline__ uint32_t key_floor(const uint32_t (&v)[D], uint32_t need) {
   uint32_t a = 0u;
@@ -1801,123 +1778,28 @@ __global__ __launch_bounds__(kSelThreads, 1) void indexer_select_kernel(Params P
   seg_emit(P, S, row, units_r, n_c, sg, T, ties);
 }
 
-// ---- row-tiled scan: query rows of one sequence share the K stream -------------
+// ---- rows of one sequence in tiles ------------------------------------------------
 //
-// The rows of a chunked prefill read the same K pages.  (The several query
-// tokens of multi-query decode take the wave form further below.)  A
-// work-group takes a tile of kTileRows consecutive
-// rows; each page is copied once, as it is in the cache, into an LDS ring
-// (global_load_lds, kPgRing pages, kPgAhead ahead; the page's tile layout
-// puts every operand chunk a lane reads at 16 * lane of a contiguous
-// kilobyte, free of bank conflicts) and every wave scores it for its two rows, whose
-// query operands stay in registers.  Lane l ends a page with the key of
-// position 64p + l of each of its rows, so after the 16 pages of a unit a
-// row's 1024 keys sit 16 per lane in position order: the wave runs the
-// unit's local filter itself (a bitwise search for the edge with ballot
-// counts, no LDS, no work-group barrier) and writes the candidates, count
-// and edge in the per-row scan's layout.  Its edge never exceeds the unit's
-// quota-th largest key, as the per-row filter's does not, though the two
-// edges may differ.  A score takes the per-row scan's operations in the
-// same order, so both paths produce the same bits, and the exact selection
-// the same Top-K.
-//
-// The scoring of a page is software-pipelined: the next scaled MFMA is
-// issued before the ReLU/FMA chain reads the previous one, so the matrix
-// and vector units overlap.
-//
-// Tiles are dealt to work-groups in rounds, longest first, alternating the
-// direction every round, so a work-group's tiles pair long with short rows of
-// a triangular (causal) chunk.
+// Multi-query decode and chunked prefill bring many query rows of one
+// sequence.  Both take them in tiles of consecutive rows of one sequence,
+// scored by the pair-per-wave kernel further below (two rows per wave, each
+// unit's pages streamed once per pair, the pairs of a unit side by side in
+// one work-group).
 
-constexpr int kTileRows = 8;
-constexpr int kTileRowsPerWave = kTileRows / kWaves;   // 2
-constexpr int kPgRing = 4;                             // page buffers
-constexpr int kPgAhead = kPgRing - 1;                  // pages copied ahead
-// vmcnt of the page loop's waits (immediates of its inline assembly): a
-// page's copies have landed once only the younger pages' copies remain, plus,
-// for the first pages after a unit's filter, the filter's stores
-#define DSA_PG_WAIT 6
-#define DSA_PG_WAIT_AFTER_FILTER 42
-#define DSA_STR2(x) #x
-#define DSA_STR(x) DSA_STR2(x)
-// A page in LDS: its 8448 bytes as in the cache, counted in 16-byte granules
-constexpr int kPgGran = kKPageBytes / 16;              // 528
-constexpr int kPgBlocks = (kPgGran + 63) / 64;         // 9 one-KB copy blocks per page
-constexpr int kPgDmaPerWave = (kPgBlocks + kWaves - 1) / kWaves;   // 3
-constexpr int kPgBytes = kPgBlocks * 1024;
-constexpr int kTileMaxPages = 4096;                    // page ids of a tile held in LDS
-constexpr int kSeqChunkRows = 4096;                    // rows per launch of the tiled path (most)
+constexpr int kTileRows = 8;          // rows per tile of a prefill chunk; the multi-query maximum
+constexpr int kTileMaxPages = 4096;   // block-table width the tiled entry points accept
+constexpr int kSeqChunkRows = 4096;   // rows per launch of the sequence path (most)
 // The candidate region of a launch holds 8 bytes per history slot of every
 // row (a unit's slice has room for all 1024 of its keys, which the exact
 // rescoring path may write).  A chunked prefill over a long context takes
 // fewer rows per launch so that the region stays within this size (at 2048
-// pages: 512 rows, 512 MiB, instead of 4 GiB for 4096 rows); the units of
-// its tiles are then dealt in chunks so that the launch still has work for
-// every resident work-group.  Measured at 8192 rows of a 128K context: 256
-// MiB (32 launches) costs 4% of the indexer's time, 512 MiB 0.6%.
+// pages: 512 rows, 512 MiB, instead of 4 GiB for 4096 rows).
 constexpr int64_t kSeqCandBytes = int64_t(512) << 20;
-static_assert(kTileRowsPerWave == 2, "two rows per wave");
-static_assert(kPgDmaPerWave * kWaves >= kPgBlocks, "the copy blocks cover a page");
 static_assert(kUnitPages == 16, "16 pages per unit: one key per lane and page");
 
-struct TileSmem {
-  uint8_t ring[kPgRing][kPgBytes];
-  uint8_t junk[1024];                 // target of padding copies
-  int32_t pt[kTileMaxPages];          // page id per page of the tile, -1 = absent
-};
-
-// LDS byte address of a shared object: the low half of its flat address in
-// the shared aperture (no address-space cast, hence no null check).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
-
-// 16 bytes per lane from global memory into LDS at lds_base + 16*lane.
-// Inline assembly so that the compiler pairs it with no automatic wait;
-// completion is tracked by the explicit vmcnt waits of the page loop.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(lds_base)
-               : "memory", "m0");
-}
-
-// Local filter edges of unit u for a wave's two rows (keys k[i] = position
-// 64(16u+i) + lane).  A unit keeps every key >= its edge: at least its
-// quota of keys (all of them when it has no more than the quota).  The
-// search runs over each lane's three or five largest keys (kTop3Quota,
-// kTop5Quota), a subset that holds the unit's quota largest keys unless a
-// lane holds more of them (then the edge is lower and more keys are kept).
-__device__ __forceinline__ void tile_edges(const Params& P, int u, bool la, int ta, int npa,
-                                           const uint32_t (&ka)[kUnitPages], bool lb, int tb,
-                                           int npb, const uint32_t (&kb)[kUnitPages],
-                                           uint32_t* ea, uint32_t* eb) {
-  const int pg0 = kUnitPages * u;
-  const int ga = min(npa, pg0 + kUnitPages) - pg0, gb = min(npb, pg0 + kUnitPages) - pg0;
-  const uint32_t qa = unit_quota(ta, P.topk), qb = unit_quota(tb, P.topk);
-  // need = ~0: no filtering for that row (edge 0)
-  const uint32_t na = la && ga > 0 && qa < (uint32_t)(ga * kPage) ? qa : 0xFFFFFFFFu;
-  const uint32_t nb = lb && gb > 0 && qb < (uint32_t)(gb * kPage) ? qb : 0xFFFFFFFFu;
-  *ea = *eb = 0u;
-  if (na == 0xFFFFFFFFu && nb == 0xFFFFFFFFu) return;
-  if ((na <= kTop3Quota || na == 0xFFFFFFFFu) && (nb <= kTop3Quota || nb == 0xFFFFFFFFu)) {
-    uint32_t ma[3], mb[3];
-    lane_top<3>(ka, ma);
-    lane_top<3>(kb, mb);
-    key_floor2<3>(ma, mb, na, nb, ea, eb);
-  } else if ((na <= kTop5Quota || na == 0xFFFFFFFFu) && (nb <= kTop5Quota || nb == 0xFFFFFFFFu)) {
-    uint32_t ma[5], mb[5];
-    lane_top<5>(ka, ma);
-    lane_top<5>(kb, mb);
-    key_floor2<5>(ma, mb, na, nb, ea, eb);
-  } else {
-    key_floor2<kUnitPages>(ka, kb, na, nb, ea, eb);
-  }
-}
-
 // Candidates of unit u of one row: keys >= edge, in position order, then
-// the unit's count and edge.  Every call issues exactly kTileStores buffer
-// stores (lanes with nothing to write address out of range), so the page
-// loop can count them in its waits.
-constexpr int kTileStores = kUnitPages + 2;
+// the unit's count and edge.  Every call issues the same buffer stores
+// (lanes with nothing to write address out of range).
 __device__ __forceinline__ void emit_wave(const Params& P, int row, bool live_row, int np_row, int u,
                                           const uint32_t (&k)[kUnitPages], uint32_t edge) {
   const int lane = threadIdx.x & 63;
@@ -1949,170 +1831,6 @@ __device__ __forceinline__ void emit_wave(const Params& P, int row, bool live_ro
   __builtin_amdgcn_raw_buffer_store_b32(cnt, rn, uoff, 0, 0);
   __builtin_amdgcn_raw_buffer_store_b32(edge, re, uoff, 0, 0);
 }
-
-// Two rows per wave: tiles of up to 8 rows.
-template <int NHT>
-__global__ __launch_bounds__(kThreads, 2) void indexer_tile_kernel(Params P) {
-  __shared__ __attribute__((aligned(16))) TileSmem S;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hr = lane & 15, g = lane >> 4;
-  const uint32_t ring0 = lds_addr(S.ring), junk = lds_addr(S.junk);
-  const int TR = P.tile_rows;
-  const int ntiles = (P.R + TR - 1) / TR;
-  // work items: (tile, chunk of chunk_units units), or whole tiles
-  const int nchunks = P.chunk_units > 0 ? (P.upr + P.chunk_units - 1) / P.chunk_units : 1;
-  const int nitems = ntiles * nchunks;
-  bool bad = false, mixed = false;
-  for (int round = 0;; ++round) {
-    const int slot = round * (int)gridDim.x +
-                     ((round & 1) ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x);
-    if (slot >= nitems) break;
-    const int tslot = slot / nchunks, chunk = slot - tslot * nchunks;
-    const int r0 = (ntiles - 1 - tslot) * TR;   // longest (last) tiles first
-    // rows of the tile: lane i < TR holds row r0+i's position and page count;
-    // the tile's pages are those of the sequence of its first row
-    const bool rin = lane < TR && r0 + lane < P.R;
-    const int t_l = rin ? P.row_pos[r0 + lane] : -1;
-    const int np_l = rin ? row_pages(t_l, P.bt_stride) : 0;
-    const int npt = __builtin_amdgcn_readlane((int)wave_incl_max((uint32_t)np_l), 63);
-    int seq = 0;
-    if (P.row_seq) {
-      seq = __builtin_amdgcn_readfirstlane(P.row_seq[r0]);
-      const int s_l = rin ? P.row_seq[r0 + lane] : seq;
-      mixed |= __builtin_amdgcn_ballot_w64(s_l != seq) != 0;
-    }
-    const int32_t* btrow = P.bt + (int64_t)seq * P.bt_stride;
-    const int ra = r0 + 2 * wv, rb = ra + 1;   // the wave's two rows
-    const bool la = 2 * wv < TR && ra < P.R;
-    const bool lb = 2 * wv + 1 < TR && rb < P.R;
-    const int ta = __builtin_amdgcn_readlane(t_l, 2 * wv);
-    const int tb = __builtin_amdgcn_readlane(t_l, 2 * wv + 1);
-    const int npa = __builtin_amdgcn_readlane(np_l, 2 * wv);
-    const int npb = __builtin_amdgcn_readlane(np_l, 2 * wv + 1);
-    // the chunk's units [cu0, cu0 + nun) of the tile's ceil(npt / 16)
-    const int nun_t = (npt + kUnitPages - 1) / kUnitPages;
-    const int cu0 = P.chunk_units > 0 ? chunk * P.chunk_units : 0;
-    const int nun = P.chunk_units > 0 ? min(P.chunk_units, nun_t - cu0) : nun_t;
-    if (nun <= 0) continue;   // uniform: the chunk lies past this tile's pages
-    const int pg_lo = kUnitPages * cu0, pg_hi = min(npt, kUnitPages * (cu0 + nun));
-    // every wave is done with the previous item's ring and page ids
-    __syncthreads();
-    for (int p = pg_lo + tid; p < pg_hi; p += kThreads) {
-      const int32_t id = btrow[p];
-      const bool ok = id >= 0 && (int64_t)id < P.pool_pages;
-      bad |= !ok;
-      S.pt[p] = ok ? id : -1;
-    }
-    QOperand<NHT> Qa, Qb;
-    load_q<NHT>(P, la ? ra : r0, Qa);
-    load_q<NHT>(P, lb ? rb : r0, Qb);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): nothing but page copies outstanding below
-    __syncthreads();
-    // Units are visited in rotated order, starting at a phase that depends on
-    // the work-group's index within its XCD: the 64 work-groups of an XCD then
-    // stream 8 different pages at any time instead of all hammering the same
-    // L2 lines.  Logical page q is page 16*(cu0 + (q/16 + u0) % nun) + q%16.
-    const int u0 = (int)(((blockIdx.x >> 3) & 7) * (uint32_t)nun / 8u);
-    auto phys = [&](int q) {
-      const int uq = q / kUnitPages + u0;
-      return kUnitPages * (cu0 + (uq >= nun ? uq - nun : uq)) + q % kUnitPages;
-    };
-    auto issue_page = [&](int q) {
-      const int pq = phys(q);
-      const bool live = q < kUnitPages * nun && pq < npt;          // uniform
-      const int32_t id = __builtin_amdgcn_readfirstlane(live ? S.pt[pq] : -1);
-      const uint8_t* page = P.kpool + (int64_t)(id >= 0 ? id : 0) * kKPageBytes;
-      const uint32_t base = ring0 + (uint32_t)((q % kPgRing) * kPgBytes);
-#pragma unroll
-      for (int m = 0; m < kPgDmaPerWave; ++m) {
-        const int j = wv + kWaves * m;                             // copy block
-        const int gs = 64 * j + lane;                              // granule of this lane
-        // past the page's end (the last block's padding lanes): any granule
-        dma16(page + 16 * (gs < kPgGran ? gs : 0), live && j < kPgBlocks ? base + (uint32_t)(j * 1024) : junk);
-      }
-    };
-#pragma unroll
-    for (int q = 0; q < kPgAhead; ++q) issue_page(q);
-    for (int uu = 0; uu < nun; ++uu) {
-      const int u = cu0 + (uu + u0 >= nun ? uu + u0 - nun : uu + u0);   // physical unit
-      uint32_t ka[kUnitPages], kb[kUnitPages];
-#pragma unroll
-      for (int pi = 0; pi < kUnitPages; ++pi) {
-        ka[pi] = 0u;
-        kb[pi] = 0u;
-        const int L = kUnitPages * uu + pi;                        // logical page
-        const int p = kUnitPages * u + pi;                         // physical page
-        // page L has landed once only the kPgAhead-1 younger pages (and, just
-        // after a unit's filter, its kTileStores stores per row) remain.
-        // Every logical page takes this step, present or not, so that each
-        // step consumes exactly one page's copies.
-        if (uu > 0 && pi < kPgAhead)
-          asm volatile("s_waitcnt vmcnt(" DSA_STR(DSA_PG_WAIT_AFTER_FILTER) ")\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(" DSA_STR(DSA_PG_WAIT) ")\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        issue_page(L + kPgAhead);
-        if (p >= npt) continue;                                    // uniform: past the tile
-        if (!la && !lb) continue;                                  // uniform: a wave without rows
-        const uint8_t* pg = S.ring[L % kPgRing];
-        const bool pok = S.pt[p] >= 0;
-        // Token tile j's key operand: two 16-byte reads and a scale byte.
-        auto operand = [&](int j, v8i& kv, int& ks) {
-          const int o = 16 * j + hr;
-          const uint4 lo = *reinterpret_cast<const uint4*>(pg + k_code_off(o, 16 * g));
-          const uint4 hi = *reinterpret_cast<const uint4*>(pg + k_code_off(o, 64 + 16 * g));
-          ks = (int)pg[k_scale_off(o, g)];
-          kv = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                   (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        };
-        // 2*NHT MFMAs per token tile (m < NHT: row a's head tile m, else row
-        // b's head tile m - NHT), software-pipelined: MFMA m+1, or the next
-        // token tile's first, is issued before the FMA chain reads MFMA m,
-        // so the matrix unit works while the vector unit consumes.  Per row
-        // and token tile the chain is head_part's.
-        constexpr int kM = 2 * NHT;
-        float pa[4], pb[4];
-        v8i kc, kn;
-        int sc, sn = 0;
-        operand(0, kc, sc);
-        v4f cur = head_mfma(Qa, 0, kc, sc);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          pa[j] = pb[j] = 0.f;
-          if (j + 1 < 4) operand(j + 1, kn, sn);
-#pragma unroll
-          for (int m = 0; m < kM; ++m) {
-            v4f nxt = cur;
-            if (m + 1 < NHT) nxt = head_mfma(Qa, m + 1, kc, sc);
-            else if (m + 1 < kM) nxt = head_mfma(Qb, m + 1 - NHT, kc, sc);
-            else if (j + 1 < 4) nxt = head_mfma(Qa, 0, kn, sn);
-            if (m < NHT) pa[j] = head_acc(Qa, m, cur, pa[j]);
-            else pb[j] = head_acc(Qb, m - NHT, cur, pb[j]);
-            cur = nxt;
-          }
-          kc = kn;
-          sc = sn;
-        }
-        // lane group g receives token tile g: lane l holds position 64p + l
-        const float sa = rows_sum_scatter(pa), sb = rows_sum_scatter(pb);
-        const int pos = p * kPage + lane;
-        ka[pi] = pok && pos <= ta ? score_key(sa) : 0u;
-        kb[pi] = pok && pos <= tb ? score_key(sb) : 0u;
-      }
-      uint32_t ea, eb;
-      tile_edges(P, u, la, ta, npa, ka, lb, tb, npb, kb, &ea, &eb);
-      emit_wave(P, ra, la, npa, u, ka, ea);
-      emit_wave(P, rb, lb, npb, u, kb, eb);
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // the padding copies past the tile have landed
-  }
-  if (bad && tid == 0) flag_error(P.hdr, kErrBadPage);
-  if (mixed && tid == 0) flag_error(P.hdr, kErrMixedTile);
-}
-static_assert(kTileRowsPerWave * kTileStores + kPgDmaPerWave * (kPgAhead - 1) == DSA_PG_WAIT_AFTER_FILTER,
-              "the page loop's wait after a filter");
-static_assert(kPgDmaPerWave * (kPgAhead - 1) == DSA_PG_WAIT, "the page loop's wait");
-static_assert(DSA_PG_WAIT_AFTER_FILTER < 64, "vmcnt holds 6 bits");
 
 // ---- per-row scan, one wave per unit ---------------------------------------------
 //
@@ -2458,6 +2176,7 @@ __global__ __launch_bounds__(kScanThreads, 2) void indexer_mq_wave_kernel(Params
   const int rt = tile * TR;                              // the tile's first row
   const int r0 = rt + sub * kMqRows;                     // the group's rows r0, r0 + 1
   const int nr = min(min(kMqRows, TR - sub * kMqRows), P.R - r0);   // 1 or 2
+  if (nr <= 0) return;   // past the rows of a partial last tile (uniform)
   // lane j < nr: row r0 + j's position and sequence
   const int t_l = lane < nr ? P.row_pos[r0 + lane] : -1;
   int seq = 0;
@@ -2494,7 +2213,7 @@ __global__ __launch_bounds__(kScanThreads, 2) void indexer_mq_wave_kernel(Params
       ks = (int)b[sl].s[jj];
     };
     // 2*NHT MFMAs per token tile (m < NHT: row a's head tile m, else row b's
-    // head tile m - NHT), software-pipelined as in the row-tiled kernel:
+    // head tile m - NHT), software-pipelined:
     // MFMA m+1, or the next token tile's first, is issued before the FMA
     // chain reads MFMA m.  Per row and token tile the chain is head_part's.
     constexpr int kM = 2 * NHT;
@@ -2596,15 +2315,6 @@ void* pick_kernel(int nht, KernelKind kind) {
     case 2: return pick_kernel_t<2>(kind);
     case 3: return pick_kernel_t<3>(kind);
     default: return pick_kernel_t<4>(kind);
-  }
-}
-
-void* pick_tile_kernel(int nht) {
-  switch (nht) {
-    case 1: return (void*)&indexer_tile_kernel<1>;
-    case 2: return (void*)&indexer_tile_kernel<2>;
-    case 3: return (void*)&indexer_tile_kernel<3>;
-    default: return (void*)&indexer_tile_kernel<4>;
   }
 }
 
@@ -2737,7 +2447,6 @@ Params base_params(const void* q_fp8, const void* q_e8m0, const float* w, const 
   P.H = H_I;
   P.upr = units_stride(bt_stride);
   P.tile_rows = kTileRows;
-  P.chunk_units = 0;
   P.j_start = 1;
   return P;
 }
@@ -2972,10 +2681,8 @@ extern "C" int dsa_indexer_topk_seq(const void* q_fp8, const void* q_e8m0, const
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   hipStream_t s = dsa_host::as_stream(stream);
   const int nht = (H_I + 15) / 16;
-  void* tk = pick_tile_kernel(nht);
+  void* mk = pick_mq_wave_kernel(nht);
   void* sel = pick_kernel(nht, kSelect);
-  const int cap = resident_capacity(tk, 12 + nht - 1, kThreads);
-  if (cap <= 0) return DSA_ERR_HIP;
   const int64_t upr = units_stride(n_pages);
   for (int r0 = 0; r0 < R; r0 += per_launch) {
     const int rn = std::min(per_launch, R - r0);
@@ -2991,17 +2698,15 @@ extern "C" int dsa_indexer_topk_seq(const void* q_fp8, const void* q_e8m0, const
     P.ucount = reinterpret_cast<uint32_t*>(ws + L.ucount);
     P.uedge = reinterpret_cast<uint32_t*>(ws + L.uedge);
     P.cand = reinterpret_cast<uint2*>(ws + L.cand);
-    const int64_t ntiles = (rn + kTileRows - 1) / kTileRows;
-    // whole tiles when there are two per resident work-group; otherwise
-    // the tiles' units in chunks, about two work items per work-group
-    P.chunk_units = ntiles >= 2 * (int64_t)cap
-                        ? 0
-                        : (int)std::max<int64_t>(1, (ntiles * upr + 2 * cap - 1) / (2 * cap));
-    const int64_t nitems = P.chunk_units > 0 ? ntiles * ((upr + P.chunk_units - 1) / P.chunk_units)
-                                             : ntiles;
-    const int64_t G = std::min<int64_t>(cap, nitems);
+    // the rows in tiles of kTileRows, one wave per (pair of rows, unit) as
+    // for multi-query decode; every row reads the one block-table row
+    // (chunked prefill 8192 x 131072: 8.35 -> 7.80 ms per call against the
+    // row-tiled kernel that shared each page through LDS)
+    P.tile_rows = kTileRows;
+    const int64_t items = (rn + kTileRows - 1) / kTileRows * (kTileRows / kMqRows) * upr;
     void* args[] = {&P};
-    if (hipLaunchKernel(tk, dim3((unsigned)G), dim3(kThreads), args, 0, s) != hipSuccess)
+    if (hipLaunchKernel(mk, dim3((unsigned)((items + kScanWaves - 1) / kScanWaves)), dim3(kScanThreads),
+                        args, 0, s) != hipSuccess)
       return DSA_ERR_HIP;
     if (hipLaunchKernel(sel, dim3((unsigned)rn), dim3(kSelThreads), args, 0, s) != hipSuccess)
       return DSA_ERR_HIP;

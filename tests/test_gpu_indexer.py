@@ -240,7 +240,7 @@ def _seq_topk(st, q_fp8=None, q_e8m0=None, w=None, row_pos=None, topk=None, work
 
 @pytest.mark.parametrize("cfg", ["tiny_prefill", "decode_8k_needles", "prefill_chunk_8k_of_128k"])
 def test_seq_path_matches_per_row(need_gpu, cfg):
-    """The row-tiled entry point returns the per-row entry point's bits
+    """The sequence entry point returns the per-row entry point's bits
     (indices and scores) on every row, and passes the oracle rule."""
     st = state(cfg)
     say(f"[indexer seq] {cfg} R={st.R}")
@@ -279,7 +279,7 @@ def test_seq_path_ragged_rows(need_gpu):
 
 def test_seq_path_exact_fallback(need_gpu):
     """The rescoring path of the selection (a unit holding far more than its
-    quota) through the row-tiled entry point: same bits as the per-row path,
+    quota) through the sequence entry point: same bits as the per-row path,
     status bit 3 set."""
     say("[indexer seq] concentrated Top-K (rescore path)")
     inp = dict(synth.make("decode_8k_needles", with_sfa=False))
