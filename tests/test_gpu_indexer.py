@@ -323,7 +323,7 @@ def test_multi_query_decode_parity(need_gpu):
     o.drop_cache()
 
 
-@pytest.mark.parametrize("q_per_seq,h_index", [(1, 64), (3, 64), (8, 64), (2, 20)])
+@pytest.mark.parametrize("q_per_seq,h_index", [(1, 64), (3, 64), (5, 64), (7, 20), (8, 64), (2, 20)])
 def test_multi_query_ragged(need_gpu, q_per_seq, h_index):
     """Ragged histories, rows of a group with different limits (short ones,
     t < 0, t beyond the group's longest), several Top-K sizes, a head count
