@@ -10,6 +10,7 @@ import sys
 import numpy as np
 import torch
 
+from oracle import pools
 from sparse_attention_decode_topk_amd import ops, synth
 
 
@@ -64,6 +65,24 @@ class DeviceState:
     def sfa(self, idx: torch.Tensor, workspace=None):
         return ops.dsa_sparse_attn(self.q_sfa, self.kv_pool, self.block_table, self.row_seq, idx,
                                    workspace=workspace)
+
+
+def stale_caches(st, slots, seed):
+    """Copies of the state's caches with the given slots overwritten by
+    random bytes (what a cache holds before a step writes its new tokens);
+    slots < 0 or past the pool are left alone."""
+    rng = np.random.default_rng(seed)
+    kp, kvp = st.k_pool.clone(), st.kv_pool.clone()
+    for s in slots:
+        if s < 0 or s >= st.pages * 64:
+            continue
+        p, o = divmod(int(s), 64)
+        kp[p, torch.from_numpy(pools.K_CODE_OFF[o]).cuda()] = \
+            torch.from_numpy(rng.integers(0, 256, 128, dtype=np.uint8)).cuda()
+        kp[p, torch.from_numpy(pools.K_SCALE_OFF[o]).cuda()] = \
+            torch.from_numpy(rng.integers(100, 140, 4, dtype=np.uint8)).cuda()
+        kvp[p, o * 656:(o + 1) * 656] = torch.from_numpy(rng.integers(0, 256, 656, dtype=np.uint8)).cuda()
+    return kp, kvp
 
 
 def check_topk_row(gidx, gsc, ora, K, t, tol_rel=1e-4):

@@ -7,29 +7,11 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import pools
 from oracle.pipeline import Oracle
 from sparse_attention_decode_topk_amd import ops, synth
-from tests.dsa_state import DeviceState, bf16_tensor, check_topk_row, say
+from tests.dsa_state import DeviceState, bf16_tensor, check_topk_row, say, stale_caches
 
 pytestmark = pytest.mark.gpu
-
-
-def _stale(st, slots, seed):
-    """Copies of the caches with the new tokens' slots overwritten by
-    random bytes (what a cache holds before the step writes it)."""
-    rng = np.random.default_rng(seed)
-    kp, kvp = st.k_pool.clone(), st.kv_pool.clone()
-    for s in slots:
-        if s < 0 or s >= st.pages * 64:
-            continue
-        p, o = divmod(int(s), 64)
-        kp[p, torch.from_numpy(pools.K_CODE_OFF[o]).cuda()] = \
-            torch.from_numpy(rng.integers(0, 256, 128, dtype=np.uint8)).cuda()
-        kp[p, torch.from_numpy(pools.K_SCALE_OFF[o]).cuda()] = \
-            torch.from_numpy(rng.integers(100, 140, 4, dtype=np.uint8)).cuda()
-        kvp[p, o * 656:(o + 1) * 656] = torch.from_numpy(rng.integers(0, 256, 656, dtype=np.uint8)).cuda()
-    return kp, kvp
 
 
 def _run_both(st, inp, slots_np, K, tag):
@@ -40,7 +22,7 @@ def _run_both(st, inp, slots_np, K, tag):
     kv_new = bf16_tensor(inp["kv"][new_tok], dev)
     q_bf = bf16_tensor(inp["q_idx"], dev)
     slots = torch.from_numpy(slots_np).to(dev)
-    kpa, kvpa = _stale(st, slots_np, 5)
+    kpa, kvpa = stale_caches(st, slots_np, 5)
     kpb, kvpb = kpa.clone(), kvpa.clone()
     # A: prolog, then the indexer
     q_fp8, q_e8 = ops.decode_prolog(q_bf, k_new, kv_new, slots, kpa, kvpa)
