@@ -151,7 +151,8 @@ def main():
     k_new = bf16(inp["k_idx"][new_tok])
     kv_new = bf16(inp["kv"][new_tok])
     slots_new = torch.from_numpy(inp["slot_mapping"][new_tok]).to(dev)
-    # rows of one sequence (a prefill chunk) take the row-tiled indexer entry
+    # rows of one sequence (a prefill chunk) take the sequence entry point
+    # (dsa_indexer_topk_seq: one block-table row, K read once per pair of rows)
     one_seq = len(np.unique(inp["row_seq"])) == 1 and R > B
     # several query rows per sequence (multi-query decode) take the entry
     # point that reads each sequence's K once for its group of rows

@@ -59,7 +59,7 @@ def test_workspace_sizes_are_host_only(lib):
 
 
 def test_chunked_prefill_workspace_is_bounded(lib):
-    # the row-tiled prefill path keeps a launch's candidate region (8 bytes
+    # the sequence entry point keeps a launch's candidate region (8 bytes
     # per history slot of every row) within 512 MiB by taking fewer rows per
     # launch: 8192 rows of a 2048-page sequence need 512 rows' worth, not
     # 4096 rows' (4 GiB)
