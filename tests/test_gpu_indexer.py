@@ -441,3 +441,31 @@ def test_long_context_rows(need_gpu):
         assert int(ws.view(torch.int32)[2].item()) & 4 == 0
         say(f"[indexer] long rows K={K} ok")
     o.drop_cache()
+
+
+@pytest.mark.parametrize("q_per_seq", [3, 4])
+def test_multi_query_more_rows_than_one_launch(need_gpu, q_per_seq):
+    """Several hundred sequences of a few query tokens (histories of 4..300
+    tokens, Top-K 64) take two launches of whole sequences of at most 1024
+    rows (1023 rows for three tokens per sequence); every launch offsets its
+    rows' inputs and outputs: bit-equal to the per-row entry point and the
+    oracle rule on rows of both launches."""
+    B = 1200 // q_per_seq
+    cfg = synth.Config(98, "mq_many", batch=B, h_index=64, h_attn=16, topk=64, ragged=(4, 300),
+                       q_per_seq=q_per_seq)
+    inp = synth.make(cfg, with_sfa=False)
+    st = DeviceState(inp, with_sfa=False)
+    say(f"[indexer mq] {st.R} rows, q_per_seq={q_per_seq}")
+    a_idx, a_sc = st.indexer()
+    b_idx, b_sc = _mq_topk(st, q_per_seq)
+    torch.cuda.synchronize()
+    assert torch.equal(a_idx, b_idx) and torch.equal(a_sc, b_sc)
+    o = Oracle(inp)
+    gi, gs = b_idx.cpu().numpy(), b_sc.cpu().numpy()
+    # rows on both sides of the launch boundary; rows of fewer than 16
+    # positions are left to the bit-equality above (their scores' error is
+    # bounded by the sum of |q_i k_i|, not by their largest score)
+    pos = inp["row_pos"]
+    near = [r for r in range(1012, 1036) if pos[r] + 1 >= 16]
+    for r in [0, st.R - 1] + near:
+        check_topk_row(gi[r], gs[r], o.topk(r), st.topk, int(pos[r]))
