@@ -80,3 +80,17 @@ def test_noalloc_rejects_launches_beyond_its_array(need_gpu):
     code = ops.lib().dsa_indexer_topk_noalloc(p, p, p, p, 10, p, 16384, p, p, 8, 64, 2048, p, None,
                                               P(torch.cuda.current_stream().cuda_stream))
     assert code == 3
+
+
+def test_noalloc_more_rows_than_one_launch(need_gpu):
+    """1100 rows (histories of 1..300 tokens, Top-K 64) take two launches of
+    at most 1024 rows, both on the one array: bit-identical to the entry
+    point with a caller workspace."""
+    cfg = synth.Config(99, "noalloc_many_rows", batch=1100, h_index=64, h_attn=16, topk=64,
+                       ragged=(1, 300))
+    st = DeviceState(synth.make(cfg, with_sfa=False), with_sfa=False)
+    say(f"[noalloc] {st.R} rows in two launches")
+    a_idx, a_sc, args = _noalloc_raw(st, st.topk)
+    b_idx, b_sc = _with_workspace(st, st.topk, args)
+    torch.cuda.synchronize()
+    assert torch.equal(a_idx, b_idx) and torch.equal(a_sc, b_sc)
