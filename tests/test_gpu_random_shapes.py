@@ -1,4 +1,5 @@
-"""Parity over seeded random shapes of the decode path: batch, ragged
+"""Parity over seeded random shapes of the decode path and of prefill
+chunks.  Decode: batch, ragged
 history lengths, indexer and attention head counts (1 and counts that are
 not multiples of 16 included), Top-K sizes and query rows per sequence are
 drawn per case.  Each case runs the per-row indexer, then the fused decode
@@ -98,4 +99,54 @@ def test_random_shape(need_gpu, case):
     fin = np.isfinite(ref_l)
     assert np.array_equal(np.isfinite(lse), fin)
     assert np.all(np.abs(lse[fin] - ref_l[fin]) <= 1e-3)
+    o.drop_cache()
+
+
+def _chunk_case(i):
+    rng = np.random.default_rng(700 + i)
+    L = int(rng.integers(500, 20000))
+    count = int(rng.integers(1, 300))
+    return synth.Config(
+        340 + i, f"random_chunk_{i}", batch=1, ctx=L, rows=(L - count, count),
+        h_index=int(rng.choice([1, 5, 16, 40, 64])), h_attn=int(rng.choice([3, 16, 32, 77, 128])),
+        topk=(64, 2048, 1, 500, 2048, 300)[i])
+
+
+CHUNK_CASES = [_chunk_case(i) for i in range(6)]
+
+
+@pytest.mark.parametrize("case", range(len(CHUNK_CASES)))
+def test_random_prefill_chunk(need_gpu, case):
+    """The last rows of one sequence as a prefill chunk: the sequence entry
+    point bit-equal to the per-row one, the selection rules above on every
+    row, and SFA over the GPU's own indices."""
+    cfg = CHUNK_CASES[case]
+    inp = synth.make(cfg)
+    st = DeviceState(inp)
+    K = st.topk
+    say(f"[random] {cfg.name}: L={cfg.ctx} rows={cfg.rows} H_I={cfg.h_index} H={cfg.h_attn} K={K}")
+    a_idx, a_sc = st.indexer()
+    b_idx, b_sc = ops.dsa_indexer_topk_seq(st.q_fp8, st.q_e8m0, st.w, st.k_pool,
+                                           st.block_table[0].contiguous(), st.row_pos, K)
+    torch.cuda.synchronize()
+    assert torch.equal(a_idx, b_idx) and torch.equal(a_sc, b_sc)
+    out, lse = st.sfa(b_idx)
+    torch.cuda.synchronize()
+    gi, gs = b_idx.cpu().numpy(), b_sc.cpu().numpy()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    o = Oracle(inp)
+    pos = inp["row_pos"].astype(np.int64)
+    rows = range(st.R) if st.R <= 40 else sorted(set(range(0, st.R, st.R // 20)) | {st.R - 1})
+    swaps = sum(_check_row(gi[r], gs[r], o, r, K, int(pos[r])) for r in rows)
+    ref_o, ref_l = zip(*(o.sfa(r, gi[r]) for r in rows))
+    ref_o, ref_l = np.stack(ref_o), np.stack(ref_l)
+    got_o, got_l = out[list(rows)], lse[list(rows)]
+    err = np.abs(got_o - ref_o).max()
+    bar = 1e-3 * np.abs(ref_o).max()
+    say(f"[random] {cfg.name}: {len(rows)} rows checked ({swaps} tolerated swaps); "
+        f"SFA max err {err:.3g} vs bar {bar:.3g}")
+    assert err <= bar
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(np.isfinite(got_l), fin)
+    assert np.all(np.abs(got_l[fin] - ref_l[fin]) <= 1e-3)
     o.drop_cache()
