@@ -1,8 +1,7 @@
 """Parity over seeded random shapes of the decode path and of prefill
-chunks.  Decode: batch, ragged
-history lengths, indexer and attention head counts (1 and counts that are
-not multiples of 16 included), Top-K sizes and query rows per sequence are
-drawn per case.  Each case runs the per-row indexer, then the fused decode
+chunks.  Decode: batch, ragged history lengths, indexer and attention head
+counts (1 and counts that are not multiples of 16 included), Top-K sizes
+and query rows per sequence are drawn per case.  Each case runs the per-row indexer, then the fused decode
 entry point (one row per sequence) or the multi-query entry point (several),
 both bit-equal to the per-row one, and SFA over the GPU's own indices:
   - a row with no more positions than K must select every position;
